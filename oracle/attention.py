@@ -1,0 +1,190 @@
+"""Attn-QAT attention, forward and straight-through backward (fp64 numpy).
+
+TEST INFRASTRUCTURE: this module is part of the CPU oracle. Only the test
+suite, the smoke check and the benchmark's CPU-baseline leg may import it.
+
+What is computed (plain reading of the pages, steps in order):
+
+* FastVideo VSA checkpoint metadata, ``precision``: "fine: NVFP4 fake-quant with
+  BF16 matmul", ``quant_p`` / ``quant_v`` / ``quantize_fine`` true, no global
+  scale factors. So Q, K, V and the probability matrix P are fake-quantized
+  (``oracle.nvfp4.fake_quant``) and the two products use the quantized values.
+* FastVideo Attn-QAT training guide, environment-variable table
+  (``FWD_EXACT_M`` row) and the fastvideo-kernel commit message (SM100 route
+  paragraph): the forward saves per-row softmax statistics and the backward
+  recomputes P from them, so the quantized P is that of the *normalised*
+  probabilities P = exp(S - LSE).
+
+Forward, with quant mask bits Q=1, K=2, V=4, P=8 (a cleared bit means identity)::
+
+    Qq = FQ_d(Q)            groups of 16 along the head dimension
+    Kq = FQ_d(K)
+    Vq = FQ_tokens(V)       groups of 16 along the key axis
+    S  = sm_scale * Qq Kq^T
+    LSE_i = ln sum_j exp(S_ij)
+    P  = exp(S - LSE)
+    Pq = FQ_keys(P)         groups of 16 keys per query row, aligned at key 0
+    O  = Pq Vq              (no renormalisation of Pq)
+
+Backward (straight-through estimator: every quantizer passes the gradient as
+the identity; the softmax Jacobian uses the unquantized P)::
+
+    dV = Pq^T dO
+    dP = dO Vq^T
+    D_i = sum_c dO_ic O_ic
+    dS = P * (dP - D)
+    dQ = sm_scale * dS Kq
+    dK = sm_scale * dS^T Qq
+
+Everything is float64; S and P are materialised in row blocks.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .nvfp4 import fake_quant
+
+MASK_Q, MASK_K, MASK_V, MASK_P = 1, 2, 4, 8
+MASK_ALL = 15
+
+
+def quantize_operands(q, k, v, mask: int):
+    """Qq, Kq, Vq for one or many heads (axes [..., N, D])."""
+    qq = fake_quant(q, axis=-1) if mask & MASK_Q else np.asarray(q, np.float64)
+    kq = fake_quant(k, axis=-1) if mask & MASK_K else np.asarray(k, np.float64)
+    vq = fake_quant(v, axis=-2) if mask & MASK_V else np.asarray(v, np.float64)
+    return qq, kq, vq
+
+
+def _lse(S: np.ndarray) -> np.ndarray:
+    m = np.max(S, axis=-1, keepdims=True)
+    return (m + np.log(np.sum(np.exp(S - m), axis=-1, keepdims=True)))[..., 0]
+
+
+def head_forward(qq, kq, vq, sm_scale: float, mask: int, rows=None, row_block: int = 512):
+    """Forward for one head on already-quantized operands.
+
+    ``rows`` (optional index array) restricts the query rows computed; the
+    result then has len(rows) rows. Returns (O [n, D], LSE [n]).
+    """
+    qsel = qq if rows is None else qq[rows]
+    n = qsel.shape[0]
+    O = np.empty((n, vq.shape[1]))
+    L = np.empty(n)
+    for r0 in range(0, n, row_block):
+        r1 = min(n, r0 + row_block)
+        S = sm_scale * (qsel[r0:r1] @ kq.T)
+        lse = _lse(S)
+        P = np.exp(S - lse[:, None])
+        Pq = fake_quant(P, axis=-1) if mask & MASK_P else P
+        O[r0:r1] = Pq @ vq
+        L[r0:r1] = lse
+    return O, L
+
+
+def forward(q, k, v, sm_scale: float, mask: int = MASK_ALL, row_block: int = 512):
+    """O [B,H,Nq,D] and LSE [B,H,Nq] for real-valued inputs q, k, v."""
+    q = np.asarray(q, np.float64)
+    B, H, Nq, D = q.shape
+    qq, kq, vq = quantize_operands(q, k, v, mask)
+    O = np.empty((B, H, Nq, vq.shape[-1]))
+    L = np.empty((B, H, Nq))
+    for b in range(B):
+        for h in range(H):
+            O[b, h], L[b, h] = head_forward(qq[b, h], kq[b, h], vq[b, h], sm_scale,
+                                            mask, row_block=row_block)
+    return O, L
+
+
+def head_backward(qq, kq, vq, do, O, lse, sm_scale: float, mask: int,
+                  row_block: int = 512):
+    """dQ, dK, dV for one head on quantized operands (STE through quantizers).
+
+    ``O`` and ``lse`` are this head's forward output and statistics (all rows).
+    """
+    Nq = qq.shape[0]
+    dq = np.zeros_like(qq)
+    dk = np.zeros_like(kq)
+    dv = np.zeros_like(vq)
+    Dd = np.sum(do * O, axis=-1)
+    for r0 in range(0, Nq, row_block):
+        r1 = min(Nq, r0 + row_block)
+        S = sm_scale * (qq[r0:r1] @ kq.T)
+        P = np.exp(S - lse[r0:r1, None])
+        Pq = fake_quant(P, axis=-1) if mask & MASK_P else P
+        dv += Pq.T @ do[r0:r1]
+        dP = do[r0:r1] @ vq.T
+        dS = P * (dP - Dd[r0:r1, None])
+        dq[r0:r1] = sm_scale * (dS @ kq)
+        dk += sm_scale * (dS.T @ qq[r0:r1])
+    return dq, dk, dv
+
+
+def backward(q, k, v, do, sm_scale: float, mask: int = MASK_ALL, O=None, lse=None,
+             row_block: int = 512):
+    """dQ, dK, dV [B,H,N,D]. O / LSE default to this oracle's own forward."""
+    q = np.asarray(q, np.float64)
+    do = np.asarray(do, np.float64)
+    B, H, Nq, D = q.shape
+    qq, kq, vq = quantize_operands(q, k, v, mask)
+    if O is None or lse is None:
+        O, lse = forward(q, k, v, sm_scale, mask, row_block)
+    dq = np.empty_like(qq)
+    dk = np.empty_like(kq)
+    dv = np.empty_like(vq)
+    for b in range(B):
+        for h in range(H):
+            dq[b, h], dk[b, h], dv[b, h] = head_backward(
+                qq[b, h], kq[b, h], vq[b, h], do[b, h], O[b, h], lse[b, h],
+                sm_scale, mask, row_block)
+    return dq, dk, dv
+
+
+def head_backward_keys(qq, kq, vq, do, O, lse, sm_scale: float, mask: int, keys,
+                       row_block: int = 2048):
+    """dK and dV of one head restricted to the key rows ``keys``.
+
+    Needs this head's O and LSE for all query rows. P is quantized per
+    16-key group, so every group that contains a requested key is evaluated
+    whole. Returns (dK[keys], dV[keys]).
+    """
+    keys = np.asarray(keys)
+    Nk = kq.shape[0]
+    groups = np.unique(keys // 16)
+    cols = np.concatenate([np.arange(g * 16, min(Nk, g * 16 + 16)) for g in groups])
+    pos = {c: i for i, c in enumerate(cols)}
+    sel = np.array([pos[c] for c in keys])
+    Dd = np.sum(do * O, axis=-1)
+    dk = np.zeros((len(cols), kq.shape[1]))
+    dv = np.zeros((len(cols), vq.shape[1]))
+    Nq = qq.shape[0]
+    # Every group in ``cols`` is whole and listed in key order, so quantizing
+    # along the gathered axis reproduces the per-group quantization of P.
+    starts = np.array([np.searchsorted(cols, g * 16) for g in groups])
+    for r0 in range(0, Nq, row_block):
+        r1 = min(Nq, r0 + row_block)
+        S = sm_scale * (qq[r0:r1] @ kq[cols].T)
+        P = np.exp(S - lse[r0:r1, None])
+        if mask & MASK_P:
+            Pq = np.empty_like(P)
+            for gi, st in enumerate(starts):
+                en = starts[gi + 1] if gi + 1 < len(starts) else len(cols)
+                Pq[:, st:en] = fake_quant(P[:, st:en], axis=-1)
+        else:
+            Pq = P
+        dv += Pq.T @ do[r0:r1]
+        dP = do[r0:r1] @ vq[cols].T
+        dS = P * (dP - Dd[r0:r1, None])
+        dk += sm_scale * (dS.T @ qq[r0:r1])
+    return dk[sel], dv[sel]
+
+
+def head_backward_rows(qq, kq, vq, do_rows, O_rows, lse_rows, q_rows_idx, sm_scale: float,
+                       mask: int):
+    """dQ of one head restricted to query rows ``q_rows_idx`` (row-local)."""
+    S = sm_scale * (qq[q_rows_idx] @ kq.T)
+    P = np.exp(S - lse_rows[:, None])
+    Dd = np.sum(do_rows * O_rows, axis=-1)
+    dP = do_rows @ vq.T
+    dS = P * (dP - Dd[:, None])
+    return sm_scale * (dS @ kq)

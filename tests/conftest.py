@@ -1,0 +1,24 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    config.addinivalue_line("markers", "slow: long-running CPU test")
+
+
+@pytest.fixture(scope="session")
+def gpu_lib():
+    """The HIP library and its Python binding; fails loudly without a GPU."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test requested but no GPU is visible")
+    import quantization_aware_attention_amd as qaa
+    qaa.load()
+    return qaa
