@@ -1,0 +1,184 @@
+/*
+ * attnqat.h -- C ABI of the Attn-QAT attention library for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The library computes quantization-aware-training attention: non-causal
+ * softmax attention in which Q, K, V and the probability matrix P are NVFP4
+ * fake-quantized (16-element groups, an FP8 E4M3 scale per group, E2M1 values,
+ * no global scale), both products take BF16 operands with FP32 accumulation,
+ * and the backward pass treats every quantizer as straight-through.
+ *
+ * Sources (the FastVideo pages this work follows):
+ *  - "Attn-QAT Training" guide, section "Architecture-specific Triton
+ *    routing": query and key/value lengths may differ (cross-attention), K and
+ *    V share a length; the training kernel must fail rather than fall back to
+ *    dense attention ("Prerequisites").
+ *  - FastVideo VSA checkpoint metadata (vsqa-test-1.3b), keys
+ *    attention.precision (quant_p, quant_v, quantize_fine, no global scale
+ *    factors, "NVFP4 fake-quant with BF16 matmul"), linear_quantization.format
+ *    (the NVFP4 block format), attention.selection and cube_shape (block
+ *    sparse selection over 128-token blocks).
+ *  - fastvideo-kernel commit message, SM100 Attn-QAT route paragraph: the
+ *    forward saves softmax statistics, the backward recomputes P, and outputs,
+ *    statistics and gradients are bitwise reproducible.
+ *  - Attn-QAT inference backend pull request, review finding on sm_scale: the
+ *    softmax scale passed by the caller must be honoured; the review's note on
+ *    in-place K smoothing: inputs must not be modified.
+ *
+ * Conventions shared by every entry point
+ *  - Tensors are bfloat16 (raw 16-bit patterns) in a [B, H, N, D] index space
+ *    with the last dimension contiguous. Element strides for the B, H and N
+ *    axes are given per tensor (attnqat_strides); an all-zero triple means the
+ *    contiguous layout {H*N*D, N*D, D}. Pointers must be 16-byte aligned and
+ *    every stride a multiple of 8 elements.
+ *  - All pointers to tensor data, statistics and workspaces are device
+ *    pointers. The caller owns every buffer; the library allocates no memory
+ *    and keeps no state besides the device-architecture check below.
+ *  - All work is enqueued in order on `stream` (a hipStream_t; NULL is the
+ *    default stream). No call synchronises the host; results are valid once
+ *    the caller has synchronised the stream.
+ *  - Inputs are never written.
+ *  - Results are bitwise reproducible run to run (no atomics, fixed
+ *    accumulation order).
+ *  - Arguments are validated before any HIP call. On failure a call returns a
+ *    non-zero status, enqueues nothing, and attnqat_last_error() describes the
+ *    problem. There is no fallback path.
+ */
+#ifndef ATTNQAT_H
+#define ATTNQAT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTNQAT_ABI_VERSION 1
+
+/* status codes */
+#define ATTNQAT_OK 0
+#define ATTNQAT_E_INVALID 1     /* null pointer, bad size, bad mask, bad scale, aliasing */
+#define ATTNQAT_E_UNSUPPORTED 2 /* head dim not 64/128, device is not gfx950 */
+#define ATTNQAT_E_MISALIGNED 3  /* pointer not 16-byte aligned or stride not a multiple of 8 */
+#define ATTNQAT_E_WORKSPACE 4   /* workspace missing or too small */
+#define ATTNQAT_E_HIP 5         /* a HIP call or kernel launch failed */
+
+/* quantization mask bits: which operands are NVFP4 fake-quantized */
+#define ATTNQAT_QUANT_Q 1u
+#define ATTNQAT_QUANT_K 2u
+#define ATTNQAT_QUANT_V 4u
+#define ATTNQAT_QUANT_P 8u
+#define ATTNQAT_QUANT_ALL 15u
+
+/* group axis of the standalone fake quantizer */
+#define ATTNQAT_AXIS_D 0 /* 16 consecutive elements of the last (head) dimension: Q, K */
+#define ATTNQAT_AXIS_N 1 /* 16 consecutive tokens of one column: V */
+
+typedef struct {
+    int64_t b, h, n; /* element strides of the B, H and N axes; {0,0,0} = contiguous */
+} attnqat_strides;
+
+typedef struct {
+    int64_t B, H;   /* batch and heads, >= 1 */
+    int64_t Nq, Nk; /* query tokens and key/value tokens, >= 1 */
+    int64_t D;      /* head dimension: 64 or 128 */
+    float sm_scale; /* softmax scale, used verbatim; finite and > 0 */
+    uint32_t quant_mask; /* OR of ATTNQAT_QUANT_* bits (0 = plain attention) */
+    attnqat_strides q, k, v, o, dout, dq, dk, dv;
+    /* Block-sparse fine attention (VSA-style), NULL for dense attention.
+     * Device array int32 [B, H, ceil(Nq/block_tokens), topk] of key-block
+     * indices, ascending and distinct within each row, each in
+     * [0, ceil(Nk/block_tokens)). Query block i attends only to the keys of
+     * the listed key blocks; LSE and P are taken over those keys only. */
+    const int32_t* kv_block_idx;
+    int32_t topk;         /* entries per row of kv_block_idx (ignored when dense) */
+    int32_t block_tokens; /* tokens per block; must be 128 when kv_block_idx != NULL */
+} attnqat_problem;
+
+/* ABI version of the loaded library (ATTNQAT_ABI_VERSION it was built with). */
+int attnqat_abi_version(void);
+
+/* Static description of a status code. */
+const char* attnqat_status_string(int status);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* attnqat_last_error(void);
+
+/*
+ * NVFP4 fake quantization, y = FQ(x) (VSA checkpoint metadata,
+ * linear_quantization.format, with no global scale as in attention.precision).
+ * For each group of 16 consecutive elements along `group_axis` (groups start at
+ * index 0; a partial last group is padded with zeros):
+ *   s = E4M3(max|x| / 6)   round to nearest even, saturating at 448
+ *   y = sign(x) * E2M1(|x| / s) * s   round to nearest even on
+ *       {0, .5, 1, 1.5, 2, 3, 4, 6}, saturating at 6; s == 0 gives signed 0.
+ * The result is exact: y is bitwise identical to an exact-arithmetic
+ * evaluation of these steps.
+ *   x, y        bf16 tensors [B,H,N,D] with strides xs, ys (y may not overlap x)
+ *   scale_codes optional (NULL allowed) uint8 OCP E4M3FN codes, contiguous
+ *               [B,H,N,D/16] for ATTNQAT_AXIS_D, [B,H,ceil(N/16),D] for
+ *               ATTNQAT_AXIS_N.
+ *   D           a multiple of 16 (axis D) or of 8 (axis N), at most 1024.
+ */
+int attnqat_fakequant_nvfp4(const void* x, attnqat_strides xs, void* y, attnqat_strides ys,
+                            uint8_t* scale_codes, int64_t B, int64_t H, int64_t N, int64_t D,
+                            int group_axis, void* stream);
+
+/* Workspace bytes attnqat_fwd needs for problem p (quantized operand copies). */
+size_t attnqat_fwd_workspace_bytes(const attnqat_problem* p);
+
+/*
+ * Forward pass. Writes
+ *   o    bf16 [B,H,Nq,D] (strides p->o):  O = FQ_keys(P) FQ_tokens(V)
+ *   lse  fp32 [B,H,Nq] contiguous:        LSE = ln sum_j exp(S_ij)
+ * with S = sm_scale FQ_d(Q) FQ_d(K)^T and P = exp(S - LSE) (normalised); each
+ * quantizer applies only if its mask bit is set. P is quantized per 16-key
+ * group of each query row, groups aligned at key 0; there is no
+ * renormalisation after quantization.
+ * `workspace` (device, 256-byte aligned) of at least
+ * attnqat_fwd_workspace_bytes(p) bytes is scratch owned by the caller; its
+ * contents are undefined afterwards.
+ */
+int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const void* v, void* o,
+                float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attnqat_bwd needs for problem p. */
+size_t attnqat_bwd_workspace_bytes(const attnqat_problem* p);
+
+/*
+ * Backward pass with straight-through quantizers. Given the forward inputs,
+ * the forward output `o` and statistics `lse` (as written by attnqat_fwd) and
+ * the output gradient `dout`, writes bf16 dq, dk, dv:
+ *   Dl = rowsum(dout * o)
+ *   dP = dout FQ_tokens(V)^T,  dS = P * (dP - Dl)   (P unquantized, from lse)
+ *   dV = FQ_keys(P)^T dout
+ *   dQ = sm_scale dS FQ_d(K),  dK = sm_scale dS^T FQ_d(Q)
+ * Outputs must not overlap each other or any input.
+ */
+int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const void* v,
+                const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attnqat_block_select needs. */
+size_t attnqat_block_select_workspace_bytes(const attnqat_problem* p);
+
+/*
+ * VSA-style coarse block selection (checkpoint metadata, attention.selection
+ * and precision.coarse = BF16, quantize_coarse = false). Q and K are
+ * mean-pooled over blocks of p->block_tokens tokens (a partial last block over
+ * its own tokens); the means and the block scores qbar_i . kbar_j are rounded
+ * to bfloat16 from their exact values; each query block keeps the p->topk
+ * highest-scoring key blocks (ties to the lower index), written ascending to
+ * kv_block_idx, int32 [B, H, ceil(Nq/bt), topk]. p->kv_block_idx is ignored.
+ * topk must be in [1, ceil(Nk/bt)] and ceil(Nk/bt) <= 1024.
+ */
+int attnqat_block_select(const attnqat_problem* p, const void* q, const void* k,
+                         int32_t* kv_block_idx, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTNQAT_H */

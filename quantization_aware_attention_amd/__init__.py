@@ -1,0 +1,281 @@
+"""Python binding of the Attn-QAT HIP library (``libattnqat.so``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/attnqat.h``. PyTorch provides
+device memory and the current stream. There is no CPU path: if the library is
+not built or no gfx950 GPU is present, calls raise.
+
+    o, lse = fwd(q, k, v)                     # bf16 [B,H,N,D] tensors on the GPU
+    dq, dk, dv = bwd(q, k, v, o, lse, do)
+    y = fakequant(x, axis="d")               # NVFP4 fake quantization
+    idx = block_select(q, k, topk=26)        # VSA-style block selection
+    o = attention(q, k, v)                   # autograd-aware wrapper
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # noqa: F401  (load torch's HIP runtime before the library)
+
+from .build import LIB_PATH
+
+QUANT_Q, QUANT_K, QUANT_V, QUANT_P = 1, 2, 4, 8
+QUANT_ALL = 15
+AXIS_D, AXIS_N = 0, 1
+
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "misaligned",
+          4: "workspace too small", 5: "HIP error"}
+
+
+class Strides(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("h", ctypes.c_int64), ("n", ctypes.c_int64)]
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int64), ("H", ctypes.c_int64), ("Nq", ctypes.c_int64),
+        ("Nk", ctypes.c_int64), ("D", ctypes.c_int64), ("sm_scale", ctypes.c_float),
+        ("quant_mask", ctypes.c_uint32),
+        ("q", Strides), ("k", Strides), ("v", Strides), ("o", Strides),
+        ("dout", Strides), ("dq", Strides), ("dk", Strides), ("dv", Strides),
+        ("kv_block_idx", ctypes.c_void_p), ("topk", ctypes.c_int32),
+        ("block_tokens", ctypes.c_int32),
+    ]
+
+
+EXPORTS = [
+    "attnqat_abi_version", "attnqat_status_string", "attnqat_last_error",
+    "attnqat_fakequant_nvfp4", "attnqat_fwd_workspace_bytes", "attnqat_fwd",
+    "attnqat_bwd_workspace_bytes", "attnqat_bwd", "attnqat_block_select_workspace_bytes",
+    "attnqat_block_select",
+]
+
+_lib = None
+
+
+class AttnQatError(RuntimeError):
+    pass
+
+
+def _hip_runtimes_mapped() -> set:
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                p = line.split()[-1] if line.strip() else ""
+                if "libamdhip64.so" in p:
+                    paths.add(os.path.realpath(p))
+    except OSError:
+        pass
+    return paths
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load the HIP library (once). Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise AttnQatError(f"{path} is missing: build it with quantization_aware_attention_amd."
+                           "build.build() (there is no fallback path)")
+    lib = ctypes.CDLL(path)
+    P, V, I64, SZ = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    pp = ctypes.POINTER(Problem)
+    lib.attnqat_abi_version.restype = ctypes.c_int
+    lib.attnqat_status_string.restype = ctypes.c_char_p
+    lib.attnqat_status_string.argtypes = [ctypes.c_int]
+    lib.attnqat_last_error.restype = ctypes.c_char_p
+    lib.attnqat_fakequant_nvfp4.restype = ctypes.c_int
+    lib.attnqat_fakequant_nvfp4.argtypes = [P, Strides, P, Strides, P, I64, I64, I64, I64,
+                                            ctypes.c_int, V]
+    lib.attnqat_fwd_workspace_bytes.restype = SZ
+    lib.attnqat_fwd_workspace_bytes.argtypes = [pp]
+    lib.attnqat_fwd.restype = ctypes.c_int
+    lib.attnqat_fwd.argtypes = [pp, P, P, P, P, P, P, SZ, V]
+    lib.attnqat_bwd_workspace_bytes.restype = SZ
+    lib.attnqat_bwd_workspace_bytes.argtypes = [pp]
+    lib.attnqat_bwd.restype = ctypes.c_int
+    lib.attnqat_bwd.argtypes = [pp, P, P, P, P, P, P, P, P, P, P, SZ, V]
+    lib.attnqat_block_select_workspace_bytes.restype = SZ
+    lib.attnqat_block_select_workspace_bytes.argtypes = [pp]
+    lib.attnqat_block_select.restype = ctypes.c_int
+    lib.attnqat_block_select.argtypes = [pp, P, P, P, P, SZ, V]
+    rts = _hip_runtimes_mapped()
+    if len(rts) > 1:
+        raise AttnQatError(f"two HIP runtimes are mapped ({sorted(rts)}); streams would not "
+                           "be shared with torch")
+    _lib = lib
+    return lib
+
+
+def lib() -> ctypes.CDLL:
+    return load()
+
+
+def check(rc: int) -> None:
+    if rc != 0:
+        msg = _lib.attnqat_last_error().decode() if _lib else ""
+        raise AttnQatError(f"attnqat status {rc} ({STATUS.get(rc, '?')}): {msg}")
+
+
+def parse_mask(quant) -> int:
+    if isinstance(quant, int):
+        return quant
+    m = 0
+    for ch in str(quant).lower():
+        m |= {"q": QUANT_Q, "k": QUANT_K, "v": QUANT_V, "p": QUANT_P}[ch]
+    return m
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _check4(name, t):
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda:
+        raise AttnQatError(f"{name} must be a bf16 CUDA tensor")
+    if t.dim() != 4 or t.stride(-1) != 1:
+        raise AttnQatError(f"{name} must be [B,H,N,D] with a contiguous last dimension")
+
+
+def strides_of(t: torch.Tensor) -> Strides:
+    return Strides(t.stride(0), t.stride(1), t.stride(2))
+
+
+def make_problem(q, k, sm_scale, quant_mask, *, v=None, o=None, do=None, dq=None, dk=None,
+                 dv=None, kv_block_idx=None, block_tokens=128) -> Problem:
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    p = Problem()
+    p.B, p.H, p.Nq, p.Nk, p.D = B, H, Nq, Nk, D
+    p.sm_scale = float(sm_scale)
+    p.quant_mask = parse_mask(quant_mask)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", do), ("dq", dq),
+                    ("dk", dk), ("dv", dv)):
+        if t is not None:
+            setattr(p, name, strides_of(t))
+    if kv_block_idx is not None:
+        p.kv_block_idx = kv_block_idx.data_ptr()
+        p.topk = kv_block_idx.shape[-1]
+    p.block_tokens = block_tokens
+    return p
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns 256-byte (at least) aligned blocks
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def fakequant(x: torch.Tensor, axis: str = "d", return_scale_codes: bool = False, stream=None):
+    """NVFP4 fake quantization of a bf16 [B,H,N,D] tensor along 'd' or 'n'."""
+    L = load()
+    _check4("x", x)
+    B, H, N, D = x.shape
+    ax = AXIS_D if axis == "d" else AXIS_N
+    y = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=x.device)
+    codes = None
+    if return_scale_codes:
+        shp = (B, H, N, D // 16) if ax == AXIS_D else (B, H, (N + 15) // 16, D)
+        codes = torch.empty(shp, dtype=torch.uint8, device=x.device)
+    check(L.attnqat_fakequant_nvfp4(x.data_ptr(), strides_of(x), y.data_ptr(), strides_of(y),
+                                    codes.data_ptr() if codes is not None else None,
+                                    B, H, N, D, ax, _stream(stream)))
+    return (y, codes) if return_scale_codes else y
+
+
+def fwd(q, k, v, sm_scale=None, quant="qkvp", kv_block_idx=None, block_tokens=128,
+        out=None, lse=None, workspace=None, stream=None):
+    """O (bf16) and LSE (fp32, natural log) of Attn-QAT attention."""
+    L = load()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check4(n, t)
+    B, H, Nq, D = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    o = out if out is not None else torch.empty((B, H, Nq, D), dtype=torch.bfloat16,
+                                                device=q.device)
+    lse = lse if lse is not None else torch.empty((B, H, Nq), dtype=torch.float32,
+                                                  device=q.device)
+    p = make_problem(q, k, sm_scale, quant, v=v, o=o, kv_block_idx=kv_block_idx,
+                     block_tokens=block_tokens)
+    need = L.attnqat_fwd_workspace_bytes(ctypes.byref(p))
+    if need == 0:
+        check(L.attnqat_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                            o.data_ptr(), lse.data_ptr(), None, 0, _stream(stream)))
+    ws = workspace if workspace is not None and workspace.numel() >= need else \
+        _workspace(need, q.device)
+    check(L.attnqat_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                        lse.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)))
+    return o, lse
+
+
+def bwd(q, k, v, o, lse, do, sm_scale=None, quant="qkvp", kv_block_idx=None, block_tokens=128,
+        dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """dQ, dK, dV (bf16) of Attn-QAT attention with straight-through quantizers."""
+    L = load()
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check4(n, t)
+    B, H, Nq, D = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    dq = dq if dq is not None else torch.empty_like(q, memory_format=torch.contiguous_format)
+    dk = dk if dk is not None else torch.empty_like(k, memory_format=torch.contiguous_format)
+    dv = dv if dv is not None else torch.empty_like(v, memory_format=torch.contiguous_format)
+    p = make_problem(q, k, sm_scale, quant, v=v, o=o, do=do, dq=dq, dk=dk, dv=dv,
+                     kv_block_idx=kv_block_idx, block_tokens=block_tokens)
+    need = L.attnqat_bwd_workspace_bytes(ctypes.byref(p))
+    if need == 0:
+        check(L.attnqat_bwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                            o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
+                            dk.data_ptr(), dv.data_ptr(), None, 0, _stream(stream)))
+    ws = workspace if workspace is not None and workspace.numel() >= need else \
+        _workspace(need, q.device)
+    check(L.attnqat_bwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                        lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                        dv.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)))
+    return dq, dk, dv
+
+
+def block_select(q, k, topk: int, block_tokens: int = 128, stream=None) -> torch.Tensor:
+    """int32 [B,H,ceil(Nq/bt),topk] ascending key-block indices (VSA coarse selection)."""
+    L = load()
+    _check4("q", q)
+    _check4("k", k)
+    B, H, Nq, D = q.shape
+    nbq = -(-Nq // block_tokens)
+    idx = torch.empty((B, H, nbq, topk), dtype=torch.int32, device=q.device)
+    p = make_problem(q, k, 1.0, 0, block_tokens=block_tokens)
+    p.topk = topk
+    need = L.attnqat_block_select_workspace_bytes(ctypes.byref(p))
+    ws = _workspace(need, q.device)
+    check(L.attnqat_block_select(ctypes.byref(p), q.data_ptr(), k.data_ptr(), idx.data_ptr(),
+                                 ws.data_ptr(), ws.numel(), _stream(stream)))
+    return idx
+
+
+class AttnQatFunction(torch.autograd.Function):
+    """Autograd wrapper: forward saves (O, LSE); backward is straight-through."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, sm_scale, quant, kv_block_idx):
+        o, lse = fwd(q, k, v, sm_scale, quant, kv_block_idx)
+        ctx.save_for_backward(q, k, v, o, lse, kv_block_idx)
+        ctx.sm_scale, ctx.quant = sm_scale, quant
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse, idx = ctx.saved_tensors
+        do = do.contiguous()
+        dq, dk, dv = bwd(q, k, v, o, lse, do, ctx.sm_scale, ctx.quant, idx)
+        return dq, dk, dv, None, None, None
+
+
+def attention(q, k, v, sm_scale=None, quant="qkvp", kv_block_idx=None):
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(q.shape[-1])
+    return AttnQatFunction.apply(q, k, v, sm_scale, quant, kv_block_idx)

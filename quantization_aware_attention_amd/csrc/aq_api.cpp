@@ -1,0 +1,566 @@
+// C ABI of the Attn-QAT library: argument validation, workspace planning and
+// kernel launch order. See include/attnqat.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/attnqat.h"
+#include "aq_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return ATTNQAT_OK;
+}
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other
+int g_dev_arch[kMaxDevices];
+std::mutex g_dev_mu;
+
+int check_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ATTNQAT_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(ATTNQAT_E_UNSUPPORTED, "device index %d", dev);
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_dev_arch[dev] == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess)
+            return fail(ATTNQAT_E_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+        g_dev_arch[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        if (g_dev_arch[dev] == 2)
+            return fail(ATTNQAT_E_UNSUPPORTED, "device %d is %s, this library is built for gfx950",
+                        dev, prop.gcnArchName);
+    }
+    if (g_dev_arch[dev] != 1)
+        return fail(ATTNQAT_E_UNSUPPORTED, "device %d is not gfx950", dev);
+    return ATTNQAT_OK;
+}
+
+int hip_check(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(ATTNQAT_E_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ATTNQAT_OK;
+}
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+struct Strides {
+    int64_t b, h, n;
+};
+
+Strides resolve(const attnqat_strides& s, int64_t H, int64_t N, int64_t D) {
+    if (s.b == 0 && s.h == 0 && s.n == 0) return {H * N * D, N * D, D};
+    return {s.b, s.h, s.n};
+}
+
+// Byte range [lo, hi) touched by a [B,H,N,D] tensor with strides s (elem bytes eb).
+struct Range {
+    uintptr_t lo, hi;
+};
+
+Range extent(const void* p, const Strides& s, int64_t B, int64_t H, int64_t N, int64_t D, int eb) {
+    const uintptr_t base = (uintptr_t)p;
+    const int64_t last = (B - 1) * s.b + (H - 1) * s.h + (N - 1) * s.n + (D - 1);
+    return {base, base + (uintptr_t)((last + 1) * eb)};
+}
+
+bool overlaps(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int check_tensor(const char* name, const void* p, const Strides& s, int64_t H, int64_t N,
+                 int64_t D) {
+    if (!p) return fail(ATTNQAT_E_INVALID, "%s is NULL", name);
+    if (s.b < 0 || s.h < 0 || s.n < 0)
+        return fail(ATTNQAT_E_INVALID, "%s has a negative stride", name);
+    if (((uintptr_t)p) % 16)
+        return fail(ATTNQAT_E_MISALIGNED, "%s is not 16-byte aligned", name);
+    if (s.b % 8 || s.h % 8 || s.n % 8)
+        return fail(ATTNQAT_E_MISALIGNED, "%s strides (%lld, %lld, %lld) are not multiples of 8",
+                    name, (long long)s.b, (long long)s.h, (long long)s.n);
+    if (s.n < D && N > 1) return fail(ATTNQAT_E_INVALID, "%s rows overlap (stride_n < D)", name);
+    (void)H;
+    return ATTNQAT_OK;
+}
+
+struct Plan {
+    int64_t B, H, BH, Nq, Nk, D, Nq_pad, Nk_pad;
+    Strides q, k, v, o, dout, dq, dk, dv;
+    bool sparse;
+    int nbq, nbk;
+};
+
+int validate_problem(const attnqat_problem* p, Plan& pl) {
+    if (!p) return fail(ATTNQAT_E_INVALID, "problem is NULL");
+    if (p->B < 1 || p->H < 1 || p->Nq < 1 || p->Nk < 1)
+        return fail(ATTNQAT_E_INVALID, "sizes must be >= 1 (B=%lld H=%lld Nq=%lld Nk=%lld)",
+                    (long long)p->B, (long long)p->H, (long long)p->Nq, (long long)p->Nk);
+    if (p->D != 64 && p->D != 128)
+        return fail(ATTNQAT_E_UNSUPPORTED, "head dimension %lld (supported: 64, 128)",
+                    (long long)p->D);
+    if (!std::isfinite(p->sm_scale) || !(p->sm_scale > 0.0f))
+        return fail(ATTNQAT_E_INVALID, "sm_scale must be finite and > 0");
+    if (p->quant_mask & ~ATTNQAT_QUANT_ALL)
+        return fail(ATTNQAT_E_INVALID, "unknown quant_mask bits 0x%x", p->quant_mask);
+    // the kernels index tokens with 32-bit ints
+    if (p->Nq > (1 << 30) || p->Nk > (1 << 30) || p->B * p->H > (1 << 30))
+        return fail(ATTNQAT_E_INVALID, "sizes too large");
+    pl.B = p->B;
+    pl.H = p->H;
+    pl.BH = p->B * p->H;
+    pl.Nq = p->Nq;
+    pl.Nk = p->Nk;
+    pl.D = p->D;
+    pl.Nq_pad = round_up(p->Nq, aq::kTileN);
+    pl.Nk_pad = round_up(p->Nk, aq::kTileN);
+    pl.q = resolve(p->q, p->H, p->Nq, p->D);
+    pl.k = resolve(p->k, p->H, p->Nk, p->D);
+    pl.v = resolve(p->v, p->H, p->Nk, p->D);
+    pl.o = resolve(p->o, p->H, p->Nq, p->D);
+    pl.dout = resolve(p->dout, p->H, p->Nq, p->D);
+    pl.dq = resolve(p->dq, p->H, p->Nq, p->D);
+    pl.dk = resolve(p->dk, p->H, p->Nk, p->D);
+    pl.dv = resolve(p->dv, p->H, p->Nk, p->D);
+    pl.sparse = p->kv_block_idx != nullptr;
+    pl.nbq = pl.nbk = 0;
+    if (pl.sparse) {
+        if (p->block_tokens != 128)
+            return fail(ATTNQAT_E_UNSUPPORTED, "block_tokens must be 128 (got %d)", p->block_tokens);
+        pl.nbq = (int)((p->Nq + 127) / 128);
+        pl.nbk = (int)((p->Nk + 127) / 128);
+        if (p->topk < 1 || p->topk > pl.nbk)
+            return fail(ATTNQAT_E_INVALID, "topk %d outside [1, %d]", p->topk, pl.nbk);
+        if (((uintptr_t)p->kv_block_idx) % 4)
+            return fail(ATTNQAT_E_MISALIGNED, "kv_block_idx is not 4-byte aligned");
+    }
+    return ATTNQAT_OK;
+}
+
+// Workspace layout (bytes, each region 256-byte aligned).
+struct Layout {
+    size_t qw, kw, vw, qt, kt, vt, dow, dot, lse2, delta, qlist, qcount, total;
+};
+
+Layout layout(const Plan& pl, bool bwd) {
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off += (bytes + 255) / 256 * 256;
+        return at;
+    };
+    const size_t qb = (size_t)pl.BH * pl.Nq_pad * pl.D * 2;
+    const size_t kb = (size_t)pl.BH * pl.Nk_pad * pl.D * 2;
+    L.qw = take(qb);
+    L.kw = take(kb);
+    if (bwd) {
+        L.vw = take(kb);
+        L.qt = take(qb);
+        L.kt = take(kb);
+        L.dow = take(qb);
+        L.dot = take(qb);
+        L.lse2 = take((size_t)pl.BH * pl.Nq_pad * 4);
+        L.delta = take((size_t)pl.BH * pl.Nq_pad * 4);
+        if (pl.sparse) {
+            L.qlist = take((size_t)pl.BH * pl.nbk * pl.nbq * 4);
+            L.qcount = take((size_t)pl.BH * pl.nbk * 4);
+        }
+    } else {
+        L.vw = take(kb);
+        L.vt = take(kb);
+    }
+    L.total = off;
+    return L;
+}
+
+aq::FqArgs fq_args(const void* x, const Strides& xs, void* y, const Strides& ys, uint8_t* codes,
+                   int64_t BH, int64_t H, int64_t N, int64_t Nout, int64_t D) {
+    aq::FqArgs a{};
+    a.x = (const uint16_t*)x;
+    a.xsb = xs.b;
+    a.xsh = xs.h;
+    a.xsn = xs.n;
+    a.y = (uint16_t*)y;
+    a.ysb = ys.b;
+    a.ysh = ys.h;
+    a.ysn = ys.n;
+    a.codes = codes;
+    a.BH = BH;
+    a.H = H;
+    a.N = N;
+    a.Nout = Nout;
+    a.D = (int)D;
+    return a;
+}
+
+// Quantize (or copy) q, k, v into the padded workspace operands.
+int prepare_operands(const Plan& pl, uint32_t mask, const void* q, const void* k, const void* v,
+                     char* ws, const Layout& L, bool bwd, hipStream_t st) {
+    const Strides wq{pl.H * pl.Nq_pad * pl.D, pl.Nq_pad * pl.D, pl.D};
+    const Strides wk{pl.H * pl.Nk_pad * pl.D, pl.Nk_pad * pl.D, pl.D};
+    int rc;
+    rc = hip_check(aq::launch_fq_axis_d(fq_args(q, pl.q, ws + L.qw, wq, nullptr, pl.BH, pl.H, pl.Nq,
+                                                pl.Nq_pad, pl.D),
+                                        mask & ATTNQAT_QUANT_Q, st),
+                   "fake-quant Q");
+    if (rc) return rc;
+    rc = hip_check(aq::launch_fq_axis_d(fq_args(k, pl.k, ws + L.kw, wk, nullptr, pl.BH, pl.H, pl.Nk,
+                                                pl.Nk_pad, pl.D),
+                                        mask & ATTNQAT_QUANT_K, st),
+                   "fake-quant K");
+    if (rc) return rc;
+    rc = hip_check(aq::launch_fq_axis_n(fq_args(v, pl.v, ws + L.vw, wk, nullptr, pl.BH, pl.H, pl.Nk,
+                                                pl.Nk_pad, pl.D),
+                                        mask & ATTNQAT_QUANT_V, st),
+                   "fake-quant V");
+    if (rc) return rc;
+    if (!bwd) {
+        return hip_check(aq::launch_transpose_perm((const uint16_t*)(ws + L.vw),
+                                                   (uint16_t*)(ws + L.vt), pl.BH, (int)pl.Nk_pad,
+                                                   (int)pl.D, st),
+                         "transpose V");
+    }
+    rc = hip_check(aq::launch_transpose_perm((const uint16_t*)(ws + L.qw), (uint16_t*)(ws + L.qt),
+                                             pl.BH, (int)pl.Nq_pad, (int)pl.D, st),
+                   "transpose Q");
+    if (rc) return rc;
+    return hip_check(aq::launch_transpose_perm((const uint16_t*)(ws + L.kw), (uint16_t*)(ws + L.kt),
+                                               pl.BH, (int)pl.Nk_pad, (int)pl.D, st),
+                     "transpose K");
+}
+
+aq::AttnArgs attn_args(const attnqat_problem* p, const Plan& pl, char* ws, const Layout& L) {
+    aq::AttnArgs a{};
+    a.Qw = (const uint16_t*)(ws + L.qw);
+    a.Kw = (const uint16_t*)(ws + L.kw);
+    a.Vw = (const uint16_t*)(ws + L.vw);
+    a.H = pl.H;
+    a.Nq = (int)pl.Nq;
+    a.Nk = (int)pl.Nk;
+    a.Nq_pad = (int)pl.Nq_pad;
+    a.Nk_pad = (int)pl.Nk_pad;
+    a.BH = (int)pl.BH;
+    a.sm_scale = p->sm_scale;
+    a.c = p->sm_scale * aq::kLog2e;
+    a.quant_p = (p->quant_mask & ATTNQAT_QUANT_P) ? 1 : 0;
+    if (pl.sparse) {
+        a.kv_idx = p->kv_block_idx;
+        a.topk = p->topk;
+        a.nbq = pl.nbq;
+        a.nbk = pl.nbk;
+    }
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attnqat_abi_version(void) { return ATTNQAT_ABI_VERSION; }
+
+const char* attnqat_status_string(int status) {
+    switch (status) {
+        case ATTNQAT_OK: return "ok";
+        case ATTNQAT_E_INVALID: return "invalid argument";
+        case ATTNQAT_E_UNSUPPORTED: return "unsupported configuration or device";
+        case ATTNQAT_E_MISALIGNED: return "misaligned pointer or stride";
+        case ATTNQAT_E_WORKSPACE: return "workspace missing or too small";
+        case ATTNQAT_E_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+const char* attnqat_last_error(void) { return g_last_error.c_str(); }
+
+int attnqat_fakequant_nvfp4(const void* x, attnqat_strides xs, void* y, attnqat_strides ys,
+                            uint8_t* scale_codes, int64_t B, int64_t H, int64_t N, int64_t D,
+                            int group_axis, void* stream) {
+    if (B < 1 || H < 1 || N < 1 || D < 1)
+        return fail(ATTNQAT_E_INVALID, "sizes must be >= 1");
+    if (group_axis != ATTNQAT_AXIS_D && group_axis != ATTNQAT_AXIS_N)
+        return fail(ATTNQAT_E_INVALID, "group_axis must be ATTNQAT_AXIS_D or ATTNQAT_AXIS_N");
+    if (D > 1024 || (group_axis == ATTNQAT_AXIS_D ? D % 16 : D % 8))
+        return fail(ATTNQAT_E_UNSUPPORTED, "D=%lld unsupported for this axis", (long long)D);
+    if (N > (int64_t)1 << 40 || B * H > (int64_t)1 << 31)
+        return fail(ATTNQAT_E_INVALID, "sizes too large");
+    const Strides sx = resolve(xs, H, N, D), sy = resolve(ys, H, N, D);
+    int rc = check_tensor("x", x, sx, H, N, D);
+    if (rc) return rc;
+    rc = check_tensor("y", y, sy, H, N, D);
+    if (rc) return rc;
+    if (overlaps(extent(x, sx, B, H, N, D, 2), extent(y, sy, B, H, N, D, 2)))
+        return fail(ATTNQAT_E_INVALID, "y overlaps x");
+    if (scale_codes) {
+        const int64_t nc = group_axis == ATTNQAT_AXIS_D ? B * H * N * (D / 16)
+                                                        : B * H * ((N + 15) / 16) * D;
+        const Range rc_ = {(uintptr_t)scale_codes, (uintptr_t)scale_codes + (uintptr_t)nc};
+        if (overlaps(rc_, extent(x, sx, B, H, N, D, 2)) || overlaps(rc_, extent(y, sy, B, H, N, D, 2)))
+            return fail(ATTNQAT_E_INVALID, "scale_codes overlaps x or y");
+    }
+    rc = check_device();
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const aq::FqArgs a = fq_args(x, sx, y, sy, scale_codes, B * H, H, N, N, D);
+    rc = hip_check(group_axis == ATTNQAT_AXIS_D ? aq::launch_fq_axis_d(a, true, st)
+                                                : aq::launch_fq_axis_n(a, true, st),
+                   "fake-quant launch");
+    return rc ? rc : ok();
+}
+
+size_t attnqat_fwd_workspace_bytes(const attnqat_problem* p) {
+    Plan pl;
+    if (validate_problem(p, pl)) return 0;
+    return layout(pl, false).total;
+}
+
+size_t attnqat_bwd_workspace_bytes(const attnqat_problem* p) {
+    Plan pl;
+    if (validate_problem(p, pl)) return 0;
+    return layout(pl, true).total;
+}
+
+int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const void* v, void* o,
+                float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    Plan pl;
+    int rc = validate_problem(p, pl);
+    if (rc) return rc;
+    if ((rc = check_tensor("q", q, pl.q, pl.H, pl.Nq, pl.D))) return rc;
+    if ((rc = check_tensor("k", k, pl.k, pl.H, pl.Nk, pl.D))) return rc;
+    if ((rc = check_tensor("v", v, pl.v, pl.H, pl.Nk, pl.D))) return rc;
+    if ((rc = check_tensor("o", o, pl.o, pl.H, pl.Nq, pl.D))) return rc;
+    if (!lse) return fail(ATTNQAT_E_INVALID, "lse is NULL");
+    if (((uintptr_t)lse) % 4) return fail(ATTNQAT_E_MISALIGNED, "lse is not 4-byte aligned");
+    const Layout L = layout(pl, false);
+    if (!workspace || workspace_bytes < L.total)
+        return fail(ATTNQAT_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", L.total,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (((uintptr_t)workspace) % 256)
+        return fail(ATTNQAT_E_MISALIGNED, "workspace is not 256-byte aligned");
+    const Range ro = extent(o, pl.o, pl.B, pl.H, pl.Nq, pl.D, 2);
+    const Range rl = {(uintptr_t)lse, (uintptr_t)lse + (uintptr_t)(pl.BH * pl.Nq * 4)};
+    const Range rw = {(uintptr_t)workspace, (uintptr_t)workspace + L.total};
+    const Range ins[3] = {extent(q, pl.q, pl.B, pl.H, pl.Nq, pl.D, 2),
+                          extent(k, pl.k, pl.B, pl.H, pl.Nk, pl.D, 2),
+                          extent(v, pl.v, pl.B, pl.H, pl.Nk, pl.D, 2)};
+    for (const Range& r : ins)
+        if (overlaps(r, ro) || overlaps(r, rl) || overlaps(r, rw))
+            return fail(ATTNQAT_E_INVALID, "an output or the workspace overlaps an input");
+    if (overlaps(ro, rl) || overlaps(ro, rw) || overlaps(rl, rw))
+        return fail(ATTNQAT_E_INVALID, "outputs overlap each other or the workspace");
+    if ((rc = check_device())) return rc;
+
+    hipStream_t st = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    if ((rc = prepare_operands(pl, p->quant_mask, q, k, v, ws, L, false, st))) return rc;
+    aq::AttnArgs a = attn_args(p, pl, ws, L);
+    a.Vt = (const uint16_t*)(ws + L.vt);
+    a.lse_out = lse;
+    a.lse = lse;
+    a.o = (uint16_t*)o;
+    a.osb = pl.o.b;
+    a.osh = pl.o.h;
+    a.osn = pl.o.n;
+    if ((rc = hip_check(aq::launch_fwd_lse(a, (int)pl.D, st), "forward pass 1"))) return rc;
+    if ((rc = hip_check(aq::launch_fwd_out(a, (int)pl.D, st), "forward pass 2"))) return rc;
+    return ok();
+}
+
+int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const void* v,
+                const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                void* workspace, size_t workspace_bytes, void* stream) {
+    Plan pl;
+    int rc = validate_problem(p, pl);
+    if (rc) return rc;
+    if ((rc = check_tensor("q", q, pl.q, pl.H, pl.Nq, pl.D))) return rc;
+    if ((rc = check_tensor("k", k, pl.k, pl.H, pl.Nk, pl.D))) return rc;
+    if ((rc = check_tensor("v", v, pl.v, pl.H, pl.Nk, pl.D))) return rc;
+    if ((rc = check_tensor("o", o, pl.o, pl.H, pl.Nq, pl.D))) return rc;
+    if ((rc = check_tensor("dout", dout, pl.dout, pl.H, pl.Nq, pl.D))) return rc;
+    if ((rc = check_tensor("dq", dq, pl.dq, pl.H, pl.Nq, pl.D))) return rc;
+    if ((rc = check_tensor("dk", dk, pl.dk, pl.H, pl.Nk, pl.D))) return rc;
+    if ((rc = check_tensor("dv", dv, pl.dv, pl.H, pl.Nk, pl.D))) return rc;
+    if (!lse) return fail(ATTNQAT_E_INVALID, "lse is NULL");
+    if (((uintptr_t)lse) % 4) return fail(ATTNQAT_E_MISALIGNED, "lse is not 4-byte aligned");
+    const Layout L = layout(pl, true);
+    if (!workspace || workspace_bytes < L.total)
+        return fail(ATTNQAT_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", L.total,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (((uintptr_t)workspace) % 256)
+        return fail(ATTNQAT_E_MISALIGNED, "workspace is not 256-byte aligned");
+    const Range outs[4] = {extent(dq, pl.dq, pl.B, pl.H, pl.Nq, pl.D, 2),
+                           extent(dk, pl.dk, pl.B, pl.H, pl.Nk, pl.D, 2),
+                           extent(dv, pl.dv, pl.B, pl.H, pl.Nk, pl.D, 2),
+                           {(uintptr_t)workspace, (uintptr_t)workspace + L.total}};
+    const Range ins[6] = {extent(q, pl.q, pl.B, pl.H, pl.Nq, pl.D, 2),
+                          extent(k, pl.k, pl.B, pl.H, pl.Nk, pl.D, 2),
+                          extent(v, pl.v, pl.B, pl.H, pl.Nk, pl.D, 2),
+                          extent(o, pl.o, pl.B, pl.H, pl.Nq, pl.D, 2),
+                          extent(dout, pl.dout, pl.B, pl.H, pl.Nq, pl.D, 2),
+                          {(uintptr_t)lse, (uintptr_t)lse + (uintptr_t)(pl.BH * pl.Nq * 4)}};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlaps(outs[i], ins[j]))
+                return fail(ATTNQAT_E_INVALID, "an output or the workspace overlaps an input");
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], outs[j]))
+                return fail(ATTNQAT_E_INVALID, "outputs overlap each other or the workspace");
+    }
+    if ((rc = check_device())) return rc;
+
+    hipStream_t st = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    if ((rc = prepare_operands(pl, p->quant_mask, q, k, v, ws, L, true, st))) return rc;
+    aq::PreArgs pa{};
+    pa.o = (const uint16_t*)o;
+    pa.osb = pl.o.b;
+    pa.osh = pl.o.h;
+    pa.osn = pl.o.n;
+    pa.dout = (const uint16_t*)dout;
+    pa.dsb = pl.dout.b;
+    pa.dsh = pl.dout.h;
+    pa.dsn = pl.dout.n;
+    pa.lse = lse;
+    pa.delta = (float*)(ws + L.delta);
+    pa.lse2 = (float*)(ws + L.lse2);
+    pa.dOw = (uint16_t*)(ws + L.dow);
+    pa.BH = pl.BH;
+    pa.H = pl.H;
+    pa.Nq = pl.Nq;
+    pa.Nq_pad = pl.Nq_pad;
+    pa.D = (int)pl.D;
+    if ((rc = hip_check(aq::launch_bwd_pre(pa, st), "backward preprocess"))) return rc;
+    if ((rc = hip_check(aq::launch_transpose_perm((const uint16_t*)(ws + L.dow),
+                                                  (uint16_t*)(ws + L.dot), pl.BH, (int)pl.Nq_pad,
+                                                  (int)pl.D, st),
+                        "transpose dO")))
+        return rc;
+    aq::AttnArgs a = attn_args(p, pl, ws, L);
+    a.Qt = (const uint16_t*)(ws + L.qt);
+    a.Kt = (const uint16_t*)(ws + L.kt);
+    a.dOw = (const uint16_t*)(ws + L.dow);
+    a.dOt = (const uint16_t*)(ws + L.dot);
+    a.lse2 = (const float*)(ws + L.lse2);
+    a.delta = (const float*)(ws + L.delta);
+    a.dq = (uint16_t*)dq;
+    a.dqsb = pl.dq.b;
+    a.dqsh = pl.dq.h;
+    a.dqsn = pl.dq.n;
+    a.dk = (uint16_t*)dk;
+    a.dksb = pl.dk.b;
+    a.dksh = pl.dk.h;
+    a.dksn = pl.dk.n;
+    a.dv = (uint16_t*)dv;
+    a.dvsb = pl.dv.b;
+    a.dvsh = pl.dv.h;
+    a.dvsn = pl.dv.n;
+    if (pl.sparse) {
+        a.q_list = (const int32_t*)(ws + L.qlist);
+        a.q_count = (const int32_t*)(ws + L.qcount);
+        if ((rc = hip_check(aq::launch_reverse_index(p->kv_block_idx, (int32_t*)(ws + L.qlist),
+                                                     (int32_t*)(ws + L.qcount), pl.BH, pl.nbq,
+                                                     pl.nbk, p->topk, st),
+                            "reverse block index")))
+            return rc;
+    }
+    if ((rc = hip_check(aq::launch_bwd_dkdv(a, (int)pl.D, st), "backward dK/dV"))) return rc;
+    if ((rc = hip_check(aq::launch_bwd_dq(a, (int)pl.D, st), "backward dQ"))) return rc;
+    return ok();
+}
+
+size_t attnqat_block_select_workspace_bytes(const attnqat_problem* p) {
+    if (!p || p->B < 1 || p->H < 1 || p->Nq < 1 || p->Nk < 1 || p->D < 1 || p->block_tokens < 1)
+        return 0;
+    const int64_t nbq = (p->Nq + p->block_tokens - 1) / p->block_tokens;
+    const int64_t nbk = (p->Nk + p->block_tokens - 1) / p->block_tokens;
+    const size_t a = (size_t)(p->B * p->H * nbq * p->D * 2 + 255) / 256 * 256;
+    const size_t b = (size_t)(p->B * p->H * nbk * p->D * 2 + 255) / 256 * 256;
+    return a + b;
+}
+
+int attnqat_block_select(const attnqat_problem* p, const void* q, const void* k,
+                         int32_t* kv_block_idx, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    if (!p) return fail(ATTNQAT_E_INVALID, "problem is NULL");
+    if (p->B < 1 || p->H < 1 || p->Nq < 1 || p->Nk < 1)
+        return fail(ATTNQAT_E_INVALID, "sizes must be >= 1");
+    if (p->D != 64 && p->D != 128)
+        return fail(ATTNQAT_E_UNSUPPORTED, "head dimension %lld (supported: 64, 128)",
+                    (long long)p->D);
+    if (p->block_tokens < 1 || p->block_tokens > 4096)
+        return fail(ATTNQAT_E_INVALID, "block_tokens %d outside [1, 4096]", p->block_tokens);
+    const int64_t nbq = (p->Nq + p->block_tokens - 1) / p->block_tokens;
+    const int64_t nbk = (p->Nk + p->block_tokens - 1) / p->block_tokens;
+    if (nbk > 1024) return fail(ATTNQAT_E_UNSUPPORTED, "more than 1024 key blocks");
+    if (p->topk < 1 || p->topk > nbk)
+        return fail(ATTNQAT_E_INVALID, "topk %d outside [1, %lld]", p->topk, (long long)nbk);
+    if (p->Nq > (1 << 30) || p->Nk > (1 << 30) || p->B * p->H > (1 << 30))
+        return fail(ATTNQAT_E_INVALID, "sizes too large");
+    const Strides sq = resolve(p->q, p->H, p->Nq, p->D), sk = resolve(p->k, p->H, p->Nk, p->D);
+    int rc;
+    if ((rc = check_tensor("q", q, sq, p->H, p->Nq, p->D))) return rc;
+    if ((rc = check_tensor("k", k, sk, p->H, p->Nk, p->D))) return rc;
+    if (!kv_block_idx) return fail(ATTNQAT_E_INVALID, "kv_block_idx is NULL");
+    if (((uintptr_t)kv_block_idx) % 4)
+        return fail(ATTNQAT_E_MISALIGNED, "kv_block_idx is not 4-byte aligned");
+    const size_t need = attnqat_block_select_workspace_bytes(p);
+    if (!workspace || workspace_bytes < need)
+        return fail(ATTNQAT_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (((uintptr_t)workspace) % 256)
+        return fail(ATTNQAT_E_MISALIGNED, "workspace is not 256-byte aligned");
+    const Range ri = {(uintptr_t)kv_block_idx,
+                      (uintptr_t)kv_block_idx + (uintptr_t)(p->B * p->H * nbq * p->topk * 4)};
+    const Range rw = {(uintptr_t)workspace, (uintptr_t)workspace + need};
+    const Range rq = extent(q, sq, p->B, p->H, p->Nq, p->D, 2);
+    const Range rk = extent(k, sk, p->B, p->H, p->Nk, p->D, 2);
+    if (overlaps(ri, rq) || overlaps(ri, rk) || overlaps(rw, rq) || overlaps(rw, rk) ||
+        overlaps(ri, rw))
+        return fail(ATTNQAT_E_INVALID, "kv_block_idx or the workspace overlaps an input");
+    if ((rc = check_device())) return rc;
+    aq::SelectArgs a{};
+    a.q = (const uint16_t*)q;
+    a.qsb = sq.b;
+    a.qsh = sq.h;
+    a.qsn = sq.n;
+    a.k = (const uint16_t*)k;
+    a.ksb = sk.b;
+    a.ksh = sk.h;
+    a.ksn = sk.n;
+    const size_t qbar_bytes = (size_t)(p->B * p->H * nbq * p->D * 2 + 255) / 256 * 256;
+    a.qbar = (uint16_t*)workspace;
+    a.kbar = (uint16_t*)((char*)workspace + qbar_bytes);
+    a.idx = kv_block_idx;
+    a.BH = p->B * p->H;
+    a.H = p->H;
+    a.Nq = (int)p->Nq;
+    a.Nk = (int)p->Nk;
+    a.bt = p->block_tokens;
+    a.nbq = (int)nbq;
+    a.nbk = (int)nbk;
+    a.topk = p->topk;
+    a.D = (int)p->D;
+    hipStream_t st = (hipStream_t)stream;
+    if ((rc = hip_check(aq::launch_block_pool(a, st), "block pooling"))) return rc;
+    if ((rc = hip_check(aq::launch_block_topk(a, st), "block top-k"))) return rc;
+    return ok();
+}
+
+}  // extern "C"

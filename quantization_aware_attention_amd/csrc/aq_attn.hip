@@ -1,0 +1,451 @@
+// Attn-QAT attention on MFMA: two-pass forward and split backward.
+//
+// What is computed (FastVideo VSA checkpoint metadata, attention.precision:
+// NVFP4 fake quantization of Q, K, V and P with BF16 matmuls and no global
+// scale; Attn-QAT training guide, FWD_EXACT_M row of the environment table, and
+// the fastvideo-kernel commit message on the SM100 route: softmax statistics
+// are saved by the forward and P is recomputed from them in the backward):
+//
+//   S = c0 Qq Kq^T, LSE = ln sum exp(S), P = exp(S - LSE), Pq = FQ_keys(P),
+//   O = Pq Vq;   dV = Pq^T dO, dS = P (dO Vq^T - rowsum(dO O)),
+//   dQ = c0 dS Kq, dK = c0 dS^T Qq.
+//
+// Quantizing the normalised P needs the final LSE before any P is formed, so
+// the forward runs in two passes over the keys: pass 1 accumulates the row
+// statistics, pass 2 recomputes S, quantizes P in registers and multiplies by
+// V. Q, K and V arrive already fake-quantized (see aq_prep.hip), contiguous and
+// zero-padded to multiples of 128 tokens.
+//
+// Scores are computed transposed, S^T = K Q^T, so one lane holds one query and
+// 16 keys of a 32 x 32 tile: a 16-key P group is 8 registers of lane l plus
+// 8 of lane l ^ 32, and its maximum takes one cross-lane swap.
+#include "aq_kernels.h"
+
+namespace aq {
+
+__device__ __forceinline__ uint16_t bf16_rne1(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Key index (within a 32-key block) of accumulator register r for lane half hh.
+__device__ __forceinline__ int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
+
+// NVFP4 fake quantization of one 16-key P group held as 8 registers in each of
+// lanes l and l ^ 32 (values >= 0). Decisions are taken in fp32 with a
+// reciprocal of the scale; a tie of the exact reals can only be missed by
+// values within 2^-22 relative of a rounding midpoint.
+__device__ __forceinline__ void quant_p_group(float* p) {
+    float am = fmaxf(fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])),
+                     fmaxf(fmaxf(p[4], p[5]), fmaxf(p[6], p[7])));
+    am = max_lane_pair(am);
+    const float s = e4m3_round(am * (1.0f / 6.0f));
+    const float inv = (s > 0.0f) ? __builtin_amdgcn_rcpf(s) : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = e2m1_round(p[j] * inv) * s;
+}
+
+// Stage rows [r0, r0 + R) of a [*, D] bf16 matrix into LDS with row pitch P.
+template <int R, int D, int P>
+__device__ __forceinline__ void stage_rows(uint16_t* lds, const uint16_t* g, int tid) {
+#pragma unroll
+    for (int i = tid; i < R * D / 8; i += 256) {
+        const int r = i / (D / 8), cc = i % (D / 8);
+        *(u32x4*)(lds + r * P + cc * 8) = *(const u32x4*)(g + (size_t)r * D + cc * 8);
+    }
+}
+
+// Stage columns [c0, c0 + C) of a [D][ld] bf16 matrix into LDS with row pitch P.
+template <int C, int D, int P>
+__device__ __forceinline__ void stage_cols(uint16_t* lds, const uint16_t* g, int ld, int tid) {
+#pragma unroll
+    for (int i = tid; i < D * C / 8; i += 256) {
+        const int r = i / (C / 8), cc = i % (C / 8);
+        *(u32x4*)(lds + r * P + cc * 8) = *(const u32x4*)(g + (size_t)r * ld + cc * 8);
+    }
+}
+
+// Store a transposed C tile (rows = head dim d, columns = token) as bf16 rows
+// of a [token][d] output: lane holds token `tok`, registers hold d.
+template <int D>
+__device__ __forceinline__ void store_rows_T(uint16_t* out_row, const f32x16* acc, float scale,
+                                             int hh) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            u32x2 w;
+            w[0] = pack_rne(acc[db][4 * rr + 0] * scale, acc[db][4 * rr + 1] * scale);
+            w[1] = pack_rne(acc[db][4 * rr + 2] * scale, acc[db][4 * rr + 3] * scale);
+            *(u32x2*)(out_row + db * 32 + rr * 8 + hh * 4) = w;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Forward pass 1: LSE per query row.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_lse_kernel(AttnArgs a) {
+    constexpr int BN = 64, KP = D + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KP];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int bh = blockIdx.y, qblk = blockIdx.x;
+    const int q0 = qblk * 128 + wave * 32;
+    const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
+    const uint16_t* Kb = a.Kw + (size_t)bh * a.Nk_pad * D;
+    u32x4 qf[D / 16];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+        qf[c] = *(const u32x4*)(Qb + (size_t)(q0 + l32) * D + c * 16 + hh * 8);
+    const int32_t* kvi = a.kv_idx ? a.kv_idx + ((size_t)bh * a.nbq + qblk) * a.topk : nullptr;
+    const int n_iter = kvi ? a.topk * 2 : a.Nk_pad / BN;
+    float m = kNegBig, l = 0.0f;
+    for (int it = 0; it < n_iter; ++it) {
+        const int kt = kvi ? kvi[it >> 1] * 128 + (it & 1) * BN : it * BN;
+        __syncthreads();
+        stage_rows<BN, D, KP>(sK, Kb + (size_t)kt * D, tid);
+        __syncthreads();
+        const bool tail = kt + BN > a.Nk;
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb) {
+            f32x16 acc = {};
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) {
+                const u32x4 kf = *(const u32x4*)(sK + (kb * 32 + l32) * KP + c * 16 + hh * 8);
+                acc = mfma(kf, qf[c], acc);
+            }
+            if (tail) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (kt + kb * 32 + acc_row(r, hh) >= a.Nk) acc[r] = -INFINITY;
+            }
+            float mx = m;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+            const float mc = mx * a.c;
+            float sum = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(acc[r], a.c, -mc));
+            l = l * __builtin_amdgcn_exp2f((m - mx) * a.c) + sum;
+            m = mx;
+        }
+    }
+    const float mp = partner_lane(m), lp = partner_lane(l);
+    const float mt = fmaxf(m, mp);
+    const float lt = l * __builtin_amdgcn_exp2f((m - mt) * a.c) +
+                     lp * __builtin_amdgcn_exp2f((mp - mt) * a.c);
+    const int q = q0 + l32;
+    if (hh == 0 && q < a.Nq) a.lse_out[(size_t)bh * a.Nq + q] = (mt * a.c + log2f(lt)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// Forward pass 2: O = FQ(P) Vq with P = exp(S - LSE).
+template <int D, bool QP>
+__global__ __launch_bounds__(256) void fwd_out_kernel(AttnArgs a) {
+    constexpr int BN = 64, KP = D + 8, VP = BN + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KP];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[D * VP];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int bh = blockIdx.y, qblk = blockIdx.x;
+    const int q0 = qblk * 128 + wave * 32;
+    const int q = q0 + l32;
+    const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
+    const uint16_t* Kb = a.Kw + (size_t)bh * a.Nk_pad * D;
+    const uint16_t* Vtb = a.Vt + (size_t)bh * D * a.Nk_pad;
+    u32x4 qf[D / 16];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+        qf[c] = *(const u32x4*)(Qb + (size_t)(q0 + l32) * D + c * 16 + hh * 8);
+    const float lse2 = (q < a.Nq) ? a.lse[(size_t)bh * a.Nq + q] * kLog2e : 0.0f;
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+    const int32_t* kvi = a.kv_idx ? a.kv_idx + ((size_t)bh * a.nbq + qblk) * a.topk : nullptr;
+    const int n_iter = kvi ? a.topk * 2 : a.Nk_pad / BN;
+    for (int it = 0; it < n_iter; ++it) {
+        const int kt = kvi ? kvi[it >> 1] * 128 + (it & 1) * BN : it * BN;
+        __syncthreads();
+        stage_rows<BN, D, KP>(sK, Kb + (size_t)kt * D, tid);
+        stage_cols<BN, D, VP>(sV, Vtb + kt, a.Nk_pad, tid);
+        __syncthreads();
+        const bool tail = kt + BN > a.Nk;
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb) {
+            f32x16 acc = {};
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) {
+                const u32x4 kf = *(const u32x4*)(sK + (kb * 32 + l32) * KP + c * 16 + hh * 8);
+                acc = mfma(kf, qf[c], acc);
+            }
+            float p[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], a.c, -lse2));
+            if (tail) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (kt + kb * 32 + acc_row(r, hh) >= a.Nk) p[r] = 0.0f;
+            }
+            u32x4 bfr[2];
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                float* pg = p + 8 * g;
+                if (QP) {
+                    quant_p_group(pg);
+                    bfr[g] = u32x4{pack_exact(pg[0], pg[1]), pack_exact(pg[2], pg[3]),
+                                   pack_exact(pg[4], pg[5]), pack_exact(pg[6], pg[7])};
+                } else {
+                    bfr[g] = u32x4{pack_rne(pg[0], pg[1]), pack_rne(pg[2], pg[3]),
+                                   pack_rne(pg[4], pg[5]), pack_rne(pg[6], pg[7])};
+                }
+            }
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    const u32x4 vf =
+                        *(const u32x4*)(sV + (db * 32 + l32) * VP + kb * 32 + g * 16 + hh * 8);
+                    o[db] = mfma(vf, bfr[g], o[db]);
+                }
+            }
+        }
+    }
+    if (q < a.Nq) {
+        const int64_t b = bh / a.H, h = bh % a.H;
+        store_rows_T<D>(a.o + b * a.osb + h * a.osh + (int64_t)q * a.osn, o, 1.0f, hh);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward dQ: grid over 128-query blocks, loop over key tiles.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dq_kernel(AttnArgs a) {
+    constexpr int BN = 64, KP = D + 8, VP = BN + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KP];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[BN * KP];
+    __shared__ __attribute__((aligned(16))) uint16_t sKt[D * VP];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int bh = blockIdx.y, qblk = blockIdx.x;
+    const int q0 = qblk * 128 + wave * 32;
+    const int q = q0 + l32;
+    const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
+    const uint16_t* dOb = a.dOw + (size_t)bh * a.Nq_pad * D;
+    const uint16_t* Kb = a.Kw + (size_t)bh * a.Nk_pad * D;
+    const uint16_t* Vb = a.Vw + (size_t)bh * a.Nk_pad * D;
+    const uint16_t* Ktb = a.Kt + (size_t)bh * D * a.Nk_pad;
+    u32x4 qf[D / 16], df[D / 16];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+        qf[c] = *(const u32x4*)(Qb + (size_t)q * D + c * 16 + hh * 8);
+        df[c] = *(const u32x4*)(dOb + (size_t)q * D + c * 16 + hh * 8);
+    }
+    const float lse2 = a.lse2[(size_t)bh * a.Nq_pad + q];
+    const float dl = a.delta[(size_t)bh * a.Nq_pad + q];
+    f32x16 dqa[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) dqa[db] = f32x16{};
+    const int32_t* kvi = a.kv_idx ? a.kv_idx + ((size_t)bh * a.nbq + qblk) * a.topk : nullptr;
+    const int n_iter = kvi ? a.topk * 2 : a.Nk_pad / BN;
+    for (int it = 0; it < n_iter; ++it) {
+        const int kt = kvi ? kvi[it >> 1] * 128 + (it & 1) * BN : it * BN;
+        __syncthreads();
+        stage_rows<BN, D, KP>(sK, Kb + (size_t)kt * D, tid);
+        stage_rows<BN, D, KP>(sV, Vb + (size_t)kt * D, tid);
+        stage_cols<BN, D, VP>(sKt, Ktb + kt, a.Nk_pad, tid);
+        __syncthreads();
+        const bool tail = kt + BN > a.Nk;
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb) {
+            f32x16 s = {}, dp = {};
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) {
+                const u32x4 kf = *(const u32x4*)(sK + (kb * 32 + l32) * KP + c * 16 + hh * 8);
+                s = mfma(kf, qf[c], s);
+                const u32x4 vf = *(const u32x4*)(sV + (kb * 32 + l32) * KP + c * 16 + hh * 8);
+                dp = mfma(vf, df[c], dp);
+            }
+            float ds[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float p = __builtin_amdgcn_exp2f(fmaf(s[r], a.c, -lse2));
+                if (tail && kt + kb * 32 + acc_row(r, hh) >= a.Nk) p = 0.0f;
+                ds[r] = p * (dp[r] - dl);
+            }
+            u32x4 bfr[2];
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+                bfr[g] = u32x4{pack_rne(ds[8 * g + 0], ds[8 * g + 1]),
+                               pack_rne(ds[8 * g + 2], ds[8 * g + 3]),
+                               pack_rne(ds[8 * g + 4], ds[8 * g + 5]),
+                               pack_rne(ds[8 * g + 6], ds[8 * g + 7])};
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    const u32x4 kt_f =
+                        *(const u32x4*)(sKt + (db * 32 + l32) * VP + kb * 32 + g * 16 + hh * 8);
+                    dqa[db] = mfma(kt_f, bfr[g], dqa[db]);
+                }
+            }
+        }
+    }
+    if (q < a.Nq) {
+        const int64_t b = bh / a.H, h = bh % a.H;
+        store_rows_T<D>(a.dq + b * a.dqsb + h * a.dqsh + (int64_t)q * a.dqsn, dqa, a.sm_scale, hh);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Backward dK, dV: grid over 128-key blocks (32 keys per wave), loop over
+// 64-query tiles. P^T-layout values are transposed through a per-wave LDS tile
+// so that queries become the contraction index.
+template <int D, bool QP>
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(AttnArgs a) {
+    constexpr int BM = 64, KP = D + 8, QTP = BM + 8, TP = 32 + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[BM * KP];
+    __shared__ __attribute__((aligned(16))) uint16_t sdO[BM * KP];
+    __shared__ __attribute__((aligned(16))) uint16_t sQt[D * QTP];
+    __shared__ __attribute__((aligned(16))) uint16_t sdOt[D * QTP];
+    __shared__ __attribute__((aligned(16))) uint16_t sT[4][2][32 * TP];
+    __shared__ float sL[BM], sDl[BM];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int bh = blockIdx.y, kblk = blockIdx.x;
+    const int k0 = kblk * 128 + wave * 32;
+    const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
+    const uint16_t* dOb = a.dOw + (size_t)bh * a.Nq_pad * D;
+    const uint16_t* Qtb = a.Qt + (size_t)bh * D * a.Nq_pad;
+    const uint16_t* dOtb = a.dOt + (size_t)bh * D * a.Nq_pad;
+    const float* Lb = a.lse2 + (size_t)bh * a.Nq_pad;
+    const float* Db = a.delta + (size_t)bh * a.Nq_pad;
+    u32x4 kf[D / 16], vf[D / 16];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+        kf[c] = *(const u32x4*)(a.Kw + ((size_t)bh * a.Nk_pad + k0 + l32) * D + c * 16 + hh * 8);
+        vf[c] = *(const u32x4*)(a.Vw + ((size_t)bh * a.Nk_pad + k0 + l32) * D + c * 16 + hh * 8);
+    }
+    f32x16 dka[D / 32], dva[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        dka[db] = f32x16{};
+        dva[db] = f32x16{};
+    }
+    const bool tailK = kblk * 128 + 128 > a.Nk;
+    const int32_t* ql = nullptr;
+    int n_iter = a.Nq_pad / BM;
+    if (a.q_list) {
+        ql = a.q_list + ((size_t)bh * a.nbk + kblk) * a.nbq;
+        n_iter = 2 * a.q_count[(size_t)bh * a.nbk + kblk];
+    }
+    uint16_t* Tp = sT[wave][0];
+    uint16_t* Td = sT[wave][1];
+    const int qpos = (l32 & ~15) + perm16(l32 & 15);
+    for (int it = 0; it < n_iter; ++it) {
+        const int qt = ql ? ql[it >> 1] * 128 + (it & 1) * BM : it * BM;
+        __syncthreads();
+        stage_rows<BM, D, KP>(sQ, Qb + (size_t)qt * D, tid);
+        stage_rows<BM, D, KP>(sdO, dOb + (size_t)qt * D, tid);
+        stage_cols<BM, D, QTP>(sQt, Qtb + qt, a.Nq_pad, tid);
+        stage_cols<BM, D, QTP>(sdOt, dOtb + qt, a.Nq_pad, tid);
+        if (tid < BM) {
+            sL[tid] = Lb[qt + tid];
+            sDl[tid] = Db[qt + tid];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int qb = 0; qb < BM / 32; ++qb) {
+            f32x16 s = {}, dp = {};
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) {
+                const u32x4 qv = *(const u32x4*)(sQ + (qb * 32 + l32) * KP + c * 16 + hh * 8);
+                s = mfma(kf[c], qv, s);
+                const u32x4 dv = *(const u32x4*)(sdO + (qb * 32 + l32) * KP + c * 16 + hh * 8);
+                dp = mfma(vf[c], dv, dp);
+            }
+            const float L = sL[qb * 32 + l32];
+            const float Dl = sDl[qb * 32 + l32];
+            float p[16], ds[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], a.c, -L));
+                if (tailK && k0 + acc_row(r, hh) >= a.Nk) p[r] = 0.0f;
+                ds[r] = p[r] * (dp[r] - Dl);
+            }
+            if (QP) {
+                quant_p_group(p);
+                quant_p_group(p + 8);
+            }
+            // transpose through LDS: T[key][position of query]
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = acc_row(r, hh);
+                Tp[key * TP + qpos] = QP ? (uint16_t)(__float_as_uint(p[r]) >> 16) : bf16_rne1(p[r]);
+                Td[key * TP + qpos] = bf16_rne1(ds[r]);
+            }
+            u32x4 pT[2], dT[2];
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                pT[g] = *(const u32x4*)(Tp + l32 * TP + g * 16 + hh * 8);
+                dT[g] = *(const u32x4*)(Td + l32 * TP + g * 16 + hh * 8);
+            }
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    const int off = (db * 32 + l32) * QTP + qb * 32 + g * 16 + hh * 8;
+                    dva[db] = mfma(*(const u32x4*)(sdOt + off), pT[g], dva[db]);
+                    dka[db] = mfma(*(const u32x4*)(sQt + off), dT[g], dka[db]);
+                }
+            }
+        }
+    }
+    const int key = k0 + l32;
+    if (key < a.Nk) {
+        const int64_t b = bh / a.H, h = bh % a.H;
+        store_rows_T<D>(a.dk + b * a.dksb + h * a.dksh + (int64_t)key * a.dksn, dka, a.sm_scale, hh);
+        store_rows_T<D>(a.dv + b * a.dvsb + h * a.dvsh + (int64_t)key * a.dvsn, dva, 1.0f, hh);
+    }
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_fwd_lse(const AttnArgs& a, int D, hipStream_t st) {
+    dim3 grid(a.Nq_pad / 128, a.BH);
+    if (D == 128) fwd_lse_kernel<128><<<grid, 256, 0, st>>>(a);
+    else fwd_lse_kernel<64><<<grid, 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_out(const AttnArgs& a, int D, hipStream_t st) {
+    dim3 grid(a.Nq_pad / 128, a.BH);
+    if (D == 128) {
+        if (a.quant_p) fwd_out_kernel<128, true><<<grid, 256, 0, st>>>(a);
+        else fwd_out_kernel<128, false><<<grid, 256, 0, st>>>(a);
+    } else {
+        if (a.quant_p) fwd_out_kernel<64, true><<<grid, 256, 0, st>>>(a);
+        else fwd_out_kernel<64, false><<<grid, 256, 0, st>>>(a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t st) {
+    dim3 grid(a.Nq_pad / 128, a.BH);
+    if (D == 128) bwd_dq_kernel<128><<<grid, 256, 0, st>>>(a);
+    else bwd_dq_kernel<64><<<grid, 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t st) {
+    dim3 grid(a.Nk_pad / 128, a.BH);
+    if (D == 128) {
+        if (a.quant_p) bwd_dkdv_kernel<128, true><<<grid, 256, 0, st>>>(a);
+        else bwd_dkdv_kernel<128, false><<<grid, 256, 0, st>>>(a);
+    } else {
+        if (a.quant_p) bwd_dkdv_kernel<64, true><<<grid, 256, 0, st>>>(a);
+        else bwd_dkdv_kernel<64, false><<<grid, 256, 0, st>>>(a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace aq

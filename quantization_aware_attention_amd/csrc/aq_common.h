@@ -1,0 +1,123 @@
+// Shared device helpers for the Attn-QAT HIP kernels (gfx950 / CDNA4).
+//
+// Layout conventions used by every kernel in this library:
+//  * bf16 values travel as raw uint16_t patterns.
+//  * Matrix products use v_mfma_f32_32x32x16_bf16 (wave64). For lane l,
+//    with h = l / 32 and c = l % 32:
+//      A operand (32 x 16):  A[c][8h + j], j = 0..7  (8 bf16 per lane)
+//      B operand (16 x 32):  B[8h + j][c]
+//      C/D (32 x 32, fp32):  C[row(r, h)][c], r = 0..15,
+//                            row(r, h) = 8 (r / 4) + 4 h + r % 4.
+//    The k index of A and B only has to agree between the two operands, so a
+//    C tile can feed the next product directly when its row index is the
+//    contraction index: registers r = 0..7 hold k-slots 8h + j of the first
+//    16-row half, r = 8..15 those of the second, with k-slot 8h + j holding
+//    row 8 (j / 4) + 4 h + j % 4 of that half.
+//  * Operands that must be read along the contraction index (K^T, V^T, Q^T,
+//    dO^T) are stored transposed ([D][N]) with the tokens of every 16-token
+//    group permuted so that this k-slot order becomes contiguous: position p
+//    holds token perm16(p), which swaps the 4-token chunks 1 and 2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace aq {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegBig = -1.0e30f;
+
+__host__ __device__ constexpr int perm16(int p) {
+    // swap chunk 1 (positions 4..7) with chunk 2 (positions 8..11); an involution
+    return ((p & 12) == 4) ? p + 4 : (((p & 12) == 8) ? p - 4 : p);
+}
+
+__device__ __forceinline__ f32x16 mfma(const u32x4& a, const u32x4& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Pack two floats whose values are exactly representable in bf16 (low 16 bits zero).
+__device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+}
+
+// Round two floats to bf16 (nearest even) and pack them.
+__device__ __forceinline__ uint32_t pack_rne(float lo, float hi) {
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Maximum of x over lanes l and l ^ 32.
+__device__ __forceinline__ float max_lane_pair(float x) {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+// Value of x held by lane l ^ 32.
+__device__ __forceinline__ float partner_lane(float x) {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return (__lane_id() < 32) ? __uint_as_float(sw[1]) : __uint_as_float(sw[0]);
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 scale: s = E4M3(v), v = amax / 6 >= 0, round to nearest even onto the
+// OCP E4M3FN grid, saturating at 448. Below 2^-6 the grid is m * 2^-9;
+// above, the fp32 significand is rounded to 3 fraction bits.
+__device__ __forceinline__ float e4m3_round(float v) {
+    float sub = __builtin_rintf(v * 512.0f) * (1.0f / 512.0f);
+    uint32_t b = __float_as_uint(v);
+    b = (b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u;
+    float nrm = __uint_as_float(b);
+    float s = (v < 0.015625f) ? sub : nrm;
+    return fminf(s, 448.0f);
+}
+
+// OCP E4M3FN code of a value produced by e4m3_round.
+__device__ __forceinline__ uint8_t e4m3_code(float s) {
+    if (s < 0.015625f) return (uint8_t)(int)(s * 512.0f);
+    const uint32_t b = __float_as_uint(s);
+    const int e = (int)((b >> 23) & 0xFFu) - 127;
+    return (uint8_t)(((e + 7) << 3) | ((b >> 20) & 7u));
+}
+
+// Exact NVFP4 element for bf16 inputs: returns sign(x) * E2M1(|x| / s) * s,
+// decided by comparing |x| with the rounding midpoints t * s (each product is
+// exact in fp32), so exact ties go to the even E2M1 code. s == 0 gives +-0.
+__device__ __forceinline__ float fq_elem_exact(float x, float s) {
+    float ax = fabsf(x);
+    float y = 0.0f;
+    y = (ax > 0.25f * s) ? 0.5f * s : y;
+    y = (ax >= 0.75f * s) ? 1.0f * s : y;
+    y = (ax > 1.25f * s) ? 1.5f * s : y;
+    y = (ax >= 1.75f * s) ? 2.0f * s : y;
+    y = (ax > 2.5f * s) ? 3.0f * s : y;
+    y = (ax >= 3.5f * s) ? 4.0f * s : y;
+    y = (ax > 5.0f * s) ? 6.0f * s : y;
+    return __builtin_copysignf(y, x);
+}
+
+// E2M1 rounding of r >= 0 (nearest even, saturating at 6), for P.
+// Adding and subtracting C = 2^22 * 2^max(e, 0) (e = binary exponent of r)
+// rounds r to the E2M1 spacing of its binade: 0.5 below 2, 1 in [2, 4),
+// 2 in [4, 8); the fp32 addition rounds to nearest even.
+__device__ __forceinline__ float e2m1_round(float r) {
+    float t = fminf(r, 6.0f);
+    float c = __uint_as_float((__float_as_uint(t) & 0xFF800000u) + (22u << 23));
+    c = fmaxf(c, 4194304.0f);
+    return (t + c) - c;
+}
+
+}  // namespace aq

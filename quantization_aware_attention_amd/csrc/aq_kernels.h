@@ -1,0 +1,103 @@
+// Kernel argument blocks and launchers (internal to the library).
+#pragma once
+
+#include "aq_common.h"
+
+namespace aq {
+
+// Tile sizes shared by the host planner and the kernels.
+constexpr int kTileN = 128;  // token padding granularity of every workspace operand
+
+struct FqArgs {
+    const uint16_t* x;
+    int64_t xsb, xsh, xsn;
+    uint16_t* y;
+    int64_t ysb, ysh, ysn;
+    uint8_t* codes;  // nullable
+    int64_t BH;
+    int64_t H;
+    int64_t N;     // valid tokens
+    int64_t Nout;  // rows written (>= N; rows >= N are zero)
+    int D;
+};
+
+struct PreArgs {
+    const uint16_t* o;
+    int64_t osb, osh, osn;
+    const uint16_t* dout;
+    int64_t dsb, dsh, dsn;
+    const float* lse;  // [BH][Nq]
+    float* delta;      // [BH][Nq_pad]
+    float* lse2;       // [BH][Nq_pad]
+    uint16_t* dOw;     // [BH][Nq_pad][D]
+    int64_t BH, H, Nq, Nq_pad;
+    int D;
+};
+
+// Attention problem as seen by the tiled kernels: operands live in the
+// workspace, contiguous and zero-padded to multiples of kTileN tokens.
+struct AttnArgs {
+    const uint16_t* Qw;   // [BH][Nq_pad][D]
+    const uint16_t* Kw;   // [BH][Nk_pad][D]
+    const uint16_t* Vw;   // [BH][Nk_pad][D]
+    const uint16_t* Qt;   // [BH][D][Nq_pad] permuted
+    const uint16_t* Kt;   // [BH][D][Nk_pad] permuted
+    const uint16_t* Vt;   // [BH][D][Nk_pad] permuted
+    const uint16_t* dOw;  // [BH][Nq_pad][D]
+    const uint16_t* dOt;  // [BH][D][Nq_pad] permuted
+    const float* lse;     // forward: natural-log LSE output/input [BH][Nq]
+    const float* lse2;    // backward: LSE * log2(e), [BH][Nq_pad]
+    const float* delta;   // backward: [BH][Nq_pad]
+    float* lse_out;       // forward pass 1 output [BH][Nq]
+    uint16_t* o;          // strided outputs
+    int64_t osb, osh, osn;
+    uint16_t* dq;
+    int64_t dqsb, dqsh, dqsn;
+    uint16_t* dk;
+    int64_t dksb, dksh, dksn;
+    uint16_t* dv;
+    int64_t dvsb, dvsh, dvsn;
+    // block sparsity (NULL = dense)
+    const int32_t* kv_idx;   // [BH][nbq][topk]
+    const int32_t* q_list;   // [BH][nbk][nbq] reverse index (query blocks per key block)
+    const int32_t* q_count;  // [BH][nbk]
+    int topk;
+    int nbq, nbk;
+    int64_t H;
+    int Nq, Nk, Nq_pad, Nk_pad;
+    int BH;
+    float c;        // sm_scale * log2(e)
+    float sm_scale;
+    int quant_p;
+};
+
+hipError_t launch_fq_axis_d(const FqArgs& a, bool quant, hipStream_t st);
+hipError_t launch_fq_axis_n(const FqArgs& a, bool quant, hipStream_t st);
+hipError_t launch_transpose_perm(const uint16_t* src, uint16_t* dst, int64_t BH, int Npad, int D,
+                                 hipStream_t st);
+hipError_t launch_bwd_pre(const PreArgs& a, hipStream_t st);
+
+hipError_t launch_fwd_lse(const AttnArgs& a, int D, hipStream_t st);
+hipError_t launch_fwd_out(const AttnArgs& a, int D, hipStream_t st);
+hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t st);
+hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t st);
+
+struct SelectArgs {
+    const uint16_t* q;
+    int64_t qsb, qsh, qsn;
+    const uint16_t* k;
+    int64_t ksb, ksh, ksn;
+    uint16_t* qbar;   // [BH][nbq][D] bf16
+    uint16_t* kbar;   // [BH][nbk][D] bf16
+    int32_t* idx;     // [BH][nbq][topk]
+    int32_t* q_list;  // nullable: reverse index [BH][nbk][nbq]
+    int32_t* q_count; // nullable: [BH][nbk]
+    int64_t BH, H;
+    int Nq, Nk, bt, nbq, nbk, topk, D;
+};
+hipError_t launch_block_pool(const SelectArgs& a, hipStream_t st);
+hipError_t launch_block_topk(const SelectArgs& a, hipStream_t st);
+hipError_t launch_reverse_index(const int32_t* idx, int32_t* q_list, int32_t* q_count, int64_t BH,
+                                int nbq, int nbk, int topk, hipStream_t st);
+
+}  // namespace aq

@@ -1,0 +1,50 @@
+"""Shared helpers for the GPU parity tests (bf16 transfer, error metrics)."""
+import numpy as np
+import torch
+
+from synthetic import f32_from_bf16_bits
+
+TOL_QUANT = 1e-2       # relative L2, O / dQ / dK / dV with any quantizer on
+TOL_PLAIN = 5e-3       # relative L2 with every quantizer off
+TOL_LSE = 1e-3         # max absolute error of LSE
+
+
+def to_dev(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    """uint16 bf16 patterns -> bf16 tensor on the device (bit-identical)."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def to_f64(bits: np.ndarray) -> np.ndarray:
+    return f32_from_bf16_bits(bits).astype(np.float64)
+
+
+def dev_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def dev_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+ZERO_GRAD_ABS = 1e-5   # max |dQ|, |dK| when the exact gradient vanishes by cancellation
+
+
+def rel_l2(got: np.ndarray, ref: np.ndarray, exact_zero: bool = True) -> float:
+    """Relative L2 error.
+
+    When the reference is exactly zero: with ``exact_zero`` (O and dV, which
+    vanish because every quantized probability is flushed to zero) the result
+    must be exactly zero too; otherwise (dQ and dK, which vanish by algebraic
+    cancellation of dP - D, e.g. a single key) the largest magnitude must stay
+    below ZERO_GRAD_ABS (the error is then reported as 0, else as inf).
+    """
+    n = np.linalg.norm(ref)
+    if n == 0:
+        if exact_zero:
+            return 0.0 if np.all(got == 0) else float("inf")
+        return 0.0 if float(np.abs(got).max()) <= ZERO_GRAD_ABS else float("inf")
+    return float(np.linalg.norm(got - ref) / n)
+
+
+def tol_for(mask: int) -> float:
+    return TOL_QUANT if mask else TOL_PLAIN

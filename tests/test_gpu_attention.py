@@ -1,0 +1,131 @@
+"""GPU parity of the Attn-QAT forward and backward against the fp64 oracle.
+
+Small sizes the oracle finishes in seconds, spanning several 128-token tiles
+and ragged tails; every quantization mask on the tiny workload; cross-attention
+with Nq != Nk; determinism, stream order, strided layouts and input
+immutability.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oatt
+from synthetic import WORKLOADS, make_inputs, random_bf16
+from tests.helpers import TOL_LSE, dev_bits, dev_f64, rel_l2, to_dev, to_f64, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_pair(gpu_lib, bits, mask, sc, do_bwd=True):
+    t = {k: to_dev(v) for k, v in bits.items()}
+    o, lse = gpu_lib.fwd(t["q"], t["k"], t["v"], sc, mask)
+    out = {"o": o, "lse": lse}
+    if do_bwd:
+        dq, dk, dv = gpu_lib.bwd(t["q"], t["k"], t["v"], o, lse, t["do"], sc, mask)
+        out.update(dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return {k: dev_f64(v) for k, v in out.items()}
+
+
+def _oracle(bits, mask, sc, do_bwd=True):
+    f = {k: to_f64(v) for k, v in bits.items()}
+    O, L = oatt.forward(f["q"], f["k"], f["v"], sc, mask)
+    res = {"o": O, "lse": L}
+    if do_bwd:
+        res["dq"], res["dk"], res["dv"] = oatt.backward(f["q"], f["k"], f["v"], f["do"], sc, mask,
+                                                        O, L)
+    return res
+
+
+def _compare(got, ref, mask, label):
+    tol = tol_for(mask)
+    errs = {k: rel_l2(got[k], ref[k], exact_zero=k in ("o", "dv")) for k in got if k != "lse"}
+    lse_err = float(np.abs(got["lse"] - ref["lse"]).max())
+    msg = f"{label} mask={mask} rel-L2 {errs} lse {lse_err:.2e}"
+    print(msg, flush=True)
+    assert lse_err <= TOL_LSE, msg
+    for k, e in errs.items():
+        assert e <= tol, msg
+
+
+@pytest.mark.parametrize("mask", list(range(16)))
+def test_tiny_all_masks(gpu_lib, mask):
+    w = WORKLOADS[1]
+    bits = make_inputs(1)
+    got = _run_pair(gpu_lib, bits, mask, w.sm_scale)
+    ref = _oracle(bits, mask, w.sm_scale)
+    _compare(got, ref, mask, "tiny")
+
+
+@pytest.mark.parametrize("Nq,Nk,D", [(200, 200, 64), (100, 333, 128), (333, 77, 64),
+                                     (1, 17, 128), (130, 1, 64), (384, 256, 128)])
+@pytest.mark.parametrize("mask", [15, 0])
+def test_ragged_and_cross(gpu_lib, Nq, Nk, D, mask):
+    bits = {"q": random_bf16(11, (2, 2, Nq, D)), "k": random_bf16(12, (2, 2, Nk, D)),
+            "v": random_bf16(13, (2, 2, Nk, D)), "do": random_bf16(14, (2, 2, Nq, D))}
+    sc = 1.0 / np.sqrt(D)
+    got = _run_pair(gpu_lib, bits, mask, sc)
+    ref = _oracle(bits, mask, sc)
+    _compare(got, ref, mask, f"Nq={Nq} Nk={Nk} D={D}")
+
+
+def test_sm_scale_is_honoured(gpu_lib):
+    bits = make_inputs(1)
+    for sc in (0.05, 0.3):
+        got = _run_pair(gpu_lib, bits, 15, sc)
+        ref = _oracle(bits, 15, sc)
+        _compare(got, ref, 15, f"sm_scale={sc}")
+
+
+def test_wide_scores_keep_p_groups(gpu_lib):
+    """Larger logits so that many P groups keep a non-zero scale at N = 640."""
+    bits = {"q": random_bf16(21, (1, 2, 640, 128), 2.0), "k": random_bf16(22, (1, 2, 640, 128), 2.0),
+            "v": random_bf16(23, (1, 2, 640, 128)), "do": random_bf16(24, (1, 2, 640, 128))}
+    got = _run_pair(gpu_lib, bits, 15, 1 / np.sqrt(128))
+    ref = _oracle(bits, 15, 1 / np.sqrt(128))
+    assert np.linalg.norm(ref["o"]) > 0
+    _compare(got, ref, 15, "wide")
+
+
+def test_deterministic_and_inputs_unchanged(gpu_lib):
+    bits = {"q": random_bf16(31, (1, 3, 300, 128)), "k": random_bf16(32, (1, 3, 300, 128)),
+            "v": random_bf16(33, (1, 3, 300, 128)), "do": random_bf16(34, (1, 3, 300, 128))}
+    t = {k: to_dev(v) for k, v in bits.items()}
+    outs = []
+    for _ in range(2):
+        o, lse = gpu_lib.fwd(t["q"], t["k"], t["v"], 0.1, 15)
+        dq, dk, dv = gpu_lib.bwd(t["q"], t["k"], t["v"], o, lse, t["do"], 0.1, 15)
+        torch.cuda.synchronize()
+        outs.append([dev_bits(x) if x.dtype == torch.bfloat16 else x.cpu().numpy()
+                     for x in (o, lse, dq, dk, dv)])
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
+    for k, v in bits.items():
+        np.testing.assert_array_equal(dev_bits(t[k]), v)
+
+
+def test_non_default_stream_and_strides(gpu_lib):
+    B, H, N, D = 1, 2, 260, 64
+    bits = {k: random_bf16(40 + i, (B, N, H, D)) for i, k in enumerate(("q", "k", "v", "do"))}
+    t = {k: to_dev(v).permute(0, 2, 1, 3) for k, v in bits.items()}   # BSHD memory, BHSD view
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, lse = gpu_lib.fwd(t["q"], t["k"], t["v"], 0.125, 15)
+        dq, dk, dv = gpu_lib.bwd(t["q"], t["k"], t["v"], o, lse, t["do"], 0.125, 15)
+    s.synchronize()
+    ref = _oracle({k: np.ascontiguousarray(v.transpose(0, 2, 1, 3)) for k, v in bits.items()},
+                  15, 0.125)
+    got = {"o": dev_f64(o), "lse": lse.cpu().numpy(), "dq": dev_f64(dq), "dk": dev_f64(dk),
+           "dv": dev_f64(dv)}
+    _compare(got, ref, 15, "strided+stream")
+
+
+def test_autograd_function(gpu_lib):
+    bits = make_inputs(1)
+    t = {k: to_dev(v).requires_grad_(k != "do") for k, v in bits.items()}
+    o = gpu_lib.attention(t["q"], t["k"], t["v"])
+    o.backward(t["do"])
+    ref = _oracle(bits, 15, WORKLOADS[1].sm_scale)
+    assert rel_l2(dev_f64(o), ref["o"]) <= 1e-2
+    for n in ("q", "k", "v"):
+        assert rel_l2(dev_f64(t[n].grad), ref["d" + n]) <= 1e-2
