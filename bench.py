@@ -1,0 +1,202 @@
+#!/usr/bin/env python3
+"""Attn-QAT forward + backward throughput on one MI355X.
+
+One step is the whole hot path on one batch of synthetic input already resident
+in HBM: attnqat_fwd (operand fake-quant, statistics pass, quantized-P output
+pass) followed by attnqat_bwd (operand preparation, rowsum(dO*O) preprocess,
+dK/dV kernel, dQ kernel). The default workload is the kernel-timing shape of
+the FastVideo kernel commit message: 6 heads x 31,200 tokens, head dim 128,
+B = 1, NVFP4 fake quantization of Q, K, V and P.
+
+Throughput is credited FLOPs (4 Nq Nk D B H forward, 2.5x that backward) per
+second. The JSON line also carries the roofline of the dominant kernel (its
+algorithmic FLOPs per launch over its mean launch time, timed with HIP events on
+the kernel's stream inside the timed region) and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense BF16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "Attn-QAT fwd+bwd ms & TFLOP/s (% BF16 MFMA peak), H=6 N=31200 d=128"
+
+# Algorithmic FLOPs per (query, key) pair and head dimension unit, per kernel:
+# products the method needs at least once. fwd_out: S and P V (4 d);
+# bwd_dkdv: S, dP, dV, dK (8 d); bwd_dq: dQ only (2 d), its S and dP are
+# recomputation; fwd_lse: none (it recomputes S for the statistics).
+ALGO_PER_PAIR = {"fwd_out": 4, "bwd_dkdv": 8, "bwd_dq": 2, "fwd_lse": 0}
+EXEC_PER_PAIR = {"fwd_out": 4, "bwd_dkdv": 8, "bwd_dq": 6, "fwd_lse": 2}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3,
+                    help="synthetic workload id (see synthetic.WORKLOADS)")
+    ap.add_argument("--quant", default="qkvp", help="quantized operands, e.g. qkvp or none")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=8192,
+                    help="query rows of head 0 in the CPU-oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(bits, w, rows, mask):
+    """Time the fp64 oracle on the sub-problem: `rows` query rows of head 0
+    against all keys, forward and backward."""
+    import numpy as np
+    from oracle import attention as oatt
+    from synthetic import f32_from_bf16_bits
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    q = f32_from_bf16_bits(bits["q"][0, 0, :rows]).astype(np.float64)
+    k = f32_from_bf16_bits(bits["k"][0, 0]).astype(np.float64)
+    v = f32_from_bf16_bits(bits["v"][0, 0]).astype(np.float64)
+    do = f32_from_bf16_bits(bits["do"][0, 0, :rows]).astype(np.float64)
+    t0 = time.perf_counter()
+    qq, kq, vq = oatt.quantize_operands(q, k, v, mask)
+    O, L = oatt.head_forward(qq, kq, vq, w.sm_scale, mask)
+    oatt.head_backward(qq, kq, vq, do, O, L, w.sm_scale, mask)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * rows * w.N * w.D * 3.5
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"fwd+bwd of {rows} query rows of head 0 against all {w.N} keys "
+                      f"(credited {flops / 1e9:.1f} GFLOP), fp64 numpy oracle"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the Attn-QAT "
+                                   "kernel is measured at one GPU's share of the workload; "
+                                   "multi-GPU runs are not supported", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import quantization_aware_attention_amd as qaa
+    from synthetic import WORKLOADS, make_inputs, sha256_hex
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    qaa.load()
+    w = WORKLOADS[args.workload]
+    mask = qaa.parse_mask(args.quant) if args.quant != "none" else 0
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    bits = make_inputs(args.workload)
+    hashes = {k: sha256_hex(v)[:16] for k, v in bits.items()}
+    t = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(dev) for k, v in bits.items()}
+    print(f"[bench] inputs {w.name} {w.shape} generated in {time.perf_counter() - t_gen:.1f}s",
+          file=sys.stderr, flush=True)
+    kv_idx = None
+    if w.topk:
+        kv_idx = qaa.block_select(t["q"], t["k"], w.topk, w.block_tokens)
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    B, H, N, D = w.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    p = qaa.make_problem(q, k, w.sm_scale, mask, v=v, o=o, do=do, dq=dq, dk=dk, dv=dv,
+                         kv_block_idx=kv_idx)
+    import ctypes
+    L = qaa.lib()
+    ws_f = torch.empty(L.attnqat_fwd_workspace_bytes(ctypes.byref(p)), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(L.attnqat_bwd_workspace_bytes(ctypes.byref(p)), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        qaa.fwd(q, k, v, w.sm_scale, mask, kv_idx, out=o, lse=lse, workspace=ws_f)
+        if ev:
+            ev[1].record()
+        qaa.bwd(q, k, v, o, lse, do, w.sm_scale, mask, kv_idx, dq=dq, dk=dk, dv=dv, workspace=ws_b)
+        if ev:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    qaa.profile_enable(True)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = qaa.profile_read()
+    qaa.profile_enable(False)
+    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in evs]))
+    bwd_ms = float(np.mean([b.elapsed_time(c) for _, b, c in evs]))
+    ms_step = wall * 1e3 / args.steps
+    f_fwd, f_bwd = w.credited_flops()
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+
+    pairs = float(B * H) * N * N * ((w.topk / (-(-N // w.block_tokens))) if w.topk else 1.0)
+    kernels = {}
+    for name, (tot, cnt) in kern.items():
+        avg = tot / cnt
+        e = {"ms_per_launch": round(avg, 4), "launches_per_step": cnt / args.steps,
+             "ms_per_step": round(tot / args.steps, 4)}
+        if name in EXEC_PER_PAIR:
+            e["exec_tflops"] = round(EXEC_PER_PAIR[name] * pairs * D / (avg * 1e-3) / 1e12, 1)
+            e["algo_tflops"] = round(ALGO_PER_PAIR[name] * pairs * D / (avg * 1e-3) / 1e12, 1)
+        kernels[name] = e
+    dom = max(kern.items(), key=lambda kv: kv[1][0])[0]
+    dom_avg = kern[dom][0] / kern[dom][1]
+    if dom in ALGO_PER_PAIR:
+        achieved = ALGO_PER_PAIR[dom] * pairs * D / (dom_avg * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "ms_per_launch": round(dom_avg, 4),
+                "algo_flops_per_launch": ALGO_PER_PAIR[dom] * pairs * D}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": None, "traffic": None, "ms_per_launch": round(dom_avg, 4)}
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "D": D,
+                   "quant": args.quant, "sm_scale": w.sm_scale,
+                   "topk": w.topk or None},
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 1),
+        "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 1),
+        "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": roof, "kernels": kernels, "input_sha256_16": hashes,
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(bits, w, args.cpu_rows, mask)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -32,8 +32,9 @@
  *    contiguous layout {H*N*D, N*D, D}. Pointers must be 16-byte aligned and
  *    every stride a multiple of 8 elements.
  *  - All pointers to tensor data, statistics and workspaces are device
- *    pointers. The caller owns every buffer; the library allocates no memory
- *    and keeps no state besides the device-architecture check below.
+ *    pointers. The caller owns every buffer; the library allocates no device
+ *    memory and keeps no state besides a per-device architecture check and
+ *    the optional per-thread kernel-timing record (attnqat_profile_enable).
  *  - All work is enqueued in order on `stream` (a hipStream_t; NULL is the
  *    default stream). No call synchronises the host; results are valid once
  *    the caller has synchronised the stream.
@@ -176,6 +177,20 @@ size_t attnqat_block_select_workspace_bytes(const attnqat_problem* p);
 int attnqat_block_select(const attnqat_problem* p, const void* q, const void* k,
                          int32_t* kv_block_idx, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/*
+ * Kernel timing (diagnostics). While enabled on the calling thread, every
+ * kernel the library enqueues from that thread is bracketed by a pair of HIP
+ * events recorded on the kernel's own stream (so only the kernel's execution is
+ * timed). attnqat_profile_read synchronises on the recorded events, writes for
+ * up to max_kinds kernel kinds their name (static string), total milliseconds
+ * and launch count, clears the record, and returns the number of kinds
+ * written (negative status on a HIP failure). Enabling or disabling clears the
+ * record. Event pairs are created on first use and reused; at most 65536
+ * launches are recorded between reads (later ones are not timed).
+ */
+int attnqat_profile_enable(int on);
+int attnqat_profile_read(const char** names, double* total_ms, int* launches, int max_kinds);
 
 #ifdef __cplusplus
 }

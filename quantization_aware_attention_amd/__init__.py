@@ -49,7 +49,7 @@ EXPORTS = [
     "attnqat_abi_version", "attnqat_status_string", "attnqat_last_error",
     "attnqat_fakequant_nvfp4", "attnqat_fwd_workspace_bytes", "attnqat_fwd",
     "attnqat_bwd_workspace_bytes", "attnqat_bwd", "attnqat_block_select_workspace_bytes",
-    "attnqat_block_select",
+    "attnqat_block_select", "attnqat_profile_enable", "attnqat_profile_read",
 ]
 
 _lib = None
@@ -103,6 +103,12 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.attnqat_block_select_workspace_bytes.argtypes = [pp]
     lib.attnqat_block_select.restype = ctypes.c_int
     lib.attnqat_block_select.argtypes = [pp, P, P, P, P, SZ, V]
+    lib.attnqat_profile_enable.restype = ctypes.c_int
+    lib.attnqat_profile_enable.argtypes = [ctypes.c_int]
+    lib.attnqat_profile_read.restype = ctypes.c_int
+    lib.attnqat_profile_read.argtypes = [ctypes.POINTER(ctypes.c_char_p),
+                                         ctypes.POINTER(ctypes.c_double),
+                                         ctypes.POINTER(ctypes.c_int), ctypes.c_int]
     rts = _hip_runtimes_mapped()
     if len(rts) > 1:
         raise AttnQatError(f"two HIP runtimes are mapped ({sorted(rts)}); streams would not "
@@ -255,6 +261,24 @@ def block_select(q, k, topk: int, block_tokens: int = 128, stream=None) -> torch
     check(L.attnqat_block_select(ctypes.byref(p), q.data_ptr(), k.data_ptr(), idx.data_ptr(),
                                  ws.data_ptr(), ws.numel(), _stream(stream)))
     return idx
+
+
+def profile_enable(on: bool = True) -> None:
+    """Time every kernel this thread enqueues with HIP events on its stream."""
+    check(load().attnqat_profile_enable(1 if on else 0))
+
+
+def profile_read() -> dict:
+    """{kernel kind: (total ms, launches)} since the last read; synchronises."""
+    L = load()
+    n = 32
+    names = (ctypes.c_char_p * n)()
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int * n)()
+    k = L.attnqat_profile_read(names, ms, cnt, n)
+    if k < 0:
+        check(-k)
+    return {names[i].decode(): (ms[i], cnt[i]) for i in range(k)}
 
 
 class AttnQatFunction(torch.autograd.Function):

@@ -8,6 +8,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/attnqat.h"
 #include "aq_kernels.h"
@@ -60,6 +61,103 @@ int check_device() {
 int hip_check(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(ATTNQAT_E_HIP, "%s: %s", what, hipGetErrorString(e));
     return ATTNQAT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// optional per-thread kernel timing
+enum Kind {
+    K_FQ_D, K_FQ_N, K_TRANSPOSE, K_FWD_LSE, K_FWD_OUT, K_BWD_PRE, K_BWD_DKDV, K_BWD_DQ,
+    K_BLOCK_POOL, K_BLOCK_TOPK, K_REVERSE_INDEX, K_NUM
+};
+const char* const kKindName[K_NUM] = {
+    "fq_axis_d", "fq_axis_n", "transpose_perm", "fwd_lse", "fwd_out", "bwd_pre", "bwd_dkdv",
+    "bwd_dq", "block_pool", "block_topk", "reverse_index"};
+
+constexpr int kMaxTimed = 65536;
+
+struct Profiler {
+    bool on = false;
+    std::vector<hipEvent_t> ev;  // pairs
+    std::vector<int> kind;       // kind of recorded pair i
+    int used = 0;
+};
+thread_local Profiler g_prof;
+
+int launch(Kind k, hipStream_t st, hipError_t (*fn)(const void*, hipStream_t), const void* args,
+           const char* what) {
+    Profiler& P = g_prof;
+    const bool timed = P.on && P.used < kMaxTimed;
+    if (timed) {
+        if ((int)P.kind.size() <= P.used) {
+            hipEvent_t a, b;
+            if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess)
+                return fail(ATTNQAT_E_HIP, "hipEventCreate failed");
+            P.ev.push_back(a);
+            P.ev.push_back(b);
+            P.kind.push_back(0);
+        }
+        P.kind[P.used] = k;
+        int rc = hip_check(hipEventRecord(P.ev[2 * P.used], st), "hipEventRecord");
+        if (rc) return rc;
+    }
+    int rc = hip_check(fn(args, st), what);
+    if (rc) return rc;
+    if (timed) {
+        rc = hip_check(hipEventRecord(P.ev[2 * P.used + 1], st), "hipEventRecord");
+        if (rc) return rc;
+        ++P.used;
+    }
+    return ATTNQAT_OK;
+}
+
+template <class A, hipError_t (*F)(const A&, hipStream_t)>
+hipError_t thunk(const void* a, hipStream_t st) {
+    return F(*(const A*)a, st);
+}
+
+struct TransposeArgs {
+    const uint16_t* src;
+    uint16_t* dst;
+    int64_t BH;
+    int Npad, D;
+};
+hipError_t do_transpose(const TransposeArgs& t, hipStream_t st) {
+    return aq::launch_transpose_perm(t.src, t.dst, t.BH, t.Npad, t.D, st);
+}
+struct DimArgs {
+    aq::AttnArgs a;
+    int D;
+};
+hipError_t do_fwd_lse(const DimArgs& d, hipStream_t st) { return aq::launch_fwd_lse(d.a, d.D, st); }
+hipError_t do_fwd_out(const DimArgs& d, hipStream_t st) { return aq::launch_fwd_out(d.a, d.D, st); }
+hipError_t do_bwd_dq(const DimArgs& d, hipStream_t st) { return aq::launch_bwd_dq(d.a, d.D, st); }
+hipError_t do_bwd_dkdv(const DimArgs& d, hipStream_t st) { return aq::launch_bwd_dkdv(d.a, d.D, st); }
+hipError_t do_fq_d_q(const aq::FqArgs& a, hipStream_t st) { return aq::launch_fq_axis_d(a, true, st); }
+hipError_t do_fq_d_c(const aq::FqArgs& a, hipStream_t st) { return aq::launch_fq_axis_d(a, false, st); }
+hipError_t do_fq_n_q(const aq::FqArgs& a, hipStream_t st) { return aq::launch_fq_axis_n(a, true, st); }
+hipError_t do_fq_n_c(const aq::FqArgs& a, hipStream_t st) { return aq::launch_fq_axis_n(a, false, st); }
+struct RevArgs {
+    const int32_t* idx;
+    int32_t *q_list, *q_count;
+    int64_t BH;
+    int nbq, nbk, topk;
+};
+hipError_t do_reverse(const RevArgs& r, hipStream_t st) {
+    return aq::launch_reverse_index(r.idx, r.q_list, r.q_count, r.BH, r.nbq, r.nbk, r.topk, st);
+}
+
+int run_fq(bool axis_d, bool quant, const aq::FqArgs& a, hipStream_t st, const char* what) {
+    if (axis_d)
+        return launch(K_FQ_D, st, quant ? thunk<aq::FqArgs, do_fq_d_q> : thunk<aq::FqArgs, do_fq_d_c>,
+                      &a, what);
+    return launch(K_FQ_N, st, quant ? thunk<aq::FqArgs, do_fq_n_q> : thunk<aq::FqArgs, do_fq_n_c>,
+                  &a, what);
+}
+
+int run_transpose(const uint16_t* src, uint16_t* dst, int64_t BH, int64_t Npad, int64_t D,
+                  hipStream_t st, const char* what) {
+    const TransposeArgs t{src, dst, BH, (int)Npad, (int)D};
+    return launch(K_TRANSPOSE, st, thunk<TransposeArgs, do_transpose>, &t, what);
 }
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -217,34 +315,26 @@ int prepare_operands(const Plan& pl, uint32_t mask, const void* q, const void* k
     const Strides wq{pl.H * pl.Nq_pad * pl.D, pl.Nq_pad * pl.D, pl.D};
     const Strides wk{pl.H * pl.Nk_pad * pl.D, pl.Nk_pad * pl.D, pl.D};
     int rc;
-    rc = hip_check(aq::launch_fq_axis_d(fq_args(q, pl.q, ws + L.qw, wq, nullptr, pl.BH, pl.H, pl.Nq,
-                                                pl.Nq_pad, pl.D),
-                                        mask & ATTNQAT_QUANT_Q, st),
-                   "fake-quant Q");
+    rc = run_fq(true, mask & ATTNQAT_QUANT_Q,
+                fq_args(q, pl.q, ws + L.qw, wq, nullptr, pl.BH, pl.H, pl.Nq, pl.Nq_pad, pl.D), st,
+                "fake-quant Q");
     if (rc) return rc;
-    rc = hip_check(aq::launch_fq_axis_d(fq_args(k, pl.k, ws + L.kw, wk, nullptr, pl.BH, pl.H, pl.Nk,
-                                                pl.Nk_pad, pl.D),
-                                        mask & ATTNQAT_QUANT_K, st),
-                   "fake-quant K");
+    rc = run_fq(true, mask & ATTNQAT_QUANT_K,
+                fq_args(k, pl.k, ws + L.kw, wk, nullptr, pl.BH, pl.H, pl.Nk, pl.Nk_pad, pl.D), st,
+                "fake-quant K");
     if (rc) return rc;
-    rc = hip_check(aq::launch_fq_axis_n(fq_args(v, pl.v, ws + L.vw, wk, nullptr, pl.BH, pl.H, pl.Nk,
-                                                pl.Nk_pad, pl.D),
-                                        mask & ATTNQAT_QUANT_V, st),
-                   "fake-quant V");
+    rc = run_fq(false, mask & ATTNQAT_QUANT_V,
+                fq_args(v, pl.v, ws + L.vw, wk, nullptr, pl.BH, pl.H, pl.Nk, pl.Nk_pad, pl.D), st,
+                "fake-quant V");
     if (rc) return rc;
-    if (!bwd) {
-        return hip_check(aq::launch_transpose_perm((const uint16_t*)(ws + L.vw),
-                                                   (uint16_t*)(ws + L.vt), pl.BH, (int)pl.Nk_pad,
-                                                   (int)pl.D, st),
-                         "transpose V");
-    }
-    rc = hip_check(aq::launch_transpose_perm((const uint16_t*)(ws + L.qw), (uint16_t*)(ws + L.qt),
-                                             pl.BH, (int)pl.Nq_pad, (int)pl.D, st),
-                   "transpose Q");
+    if (!bwd)
+        return run_transpose((const uint16_t*)(ws + L.vw), (uint16_t*)(ws + L.vt), pl.BH, pl.Nk_pad,
+                             pl.D, st, "transpose V");
+    rc = run_transpose((const uint16_t*)(ws + L.qw), (uint16_t*)(ws + L.qt), pl.BH, pl.Nq_pad, pl.D,
+                       st, "transpose Q");
     if (rc) return rc;
-    return hip_check(aq::launch_transpose_perm((const uint16_t*)(ws + L.kw), (uint16_t*)(ws + L.kt),
-                                               pl.BH, (int)pl.Nk_pad, (int)pl.D, st),
-                     "transpose K");
+    return run_transpose((const uint16_t*)(ws + L.kw), (uint16_t*)(ws + L.kt), pl.BH, pl.Nk_pad,
+                         pl.D, st, "transpose K");
 }
 
 aq::AttnArgs attn_args(const attnqat_problem* p, const Plan& pl, char* ws, const Layout& L) {
@@ -319,9 +409,7 @@ int attnqat_fakequant_nvfp4(const void* x, attnqat_strides xs, void* y, attnqat_
     if (rc) return rc;
     hipStream_t st = (hipStream_t)stream;
     const aq::FqArgs a = fq_args(x, sx, y, sy, scale_codes, B * H, H, N, N, D);
-    rc = hip_check(group_axis == ATTNQAT_AXIS_D ? aq::launch_fq_axis_d(a, true, st)
-                                                : aq::launch_fq_axis_n(a, true, st),
-                   "fake-quant launch");
+    rc = run_fq(group_axis == ATTNQAT_AXIS_D, true, a, st, "fake-quant launch");
     return rc ? rc : ok();
 }
 
@@ -378,8 +466,9 @@ int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const vo
     a.osb = pl.o.b;
     a.osh = pl.o.h;
     a.osn = pl.o.n;
-    if ((rc = hip_check(aq::launch_fwd_lse(a, (int)pl.D, st), "forward pass 1"))) return rc;
-    if ((rc = hip_check(aq::launch_fwd_out(a, (int)pl.D, st), "forward pass 2"))) return rc;
+    const DimArgs da{a, (int)pl.D};
+    if ((rc = launch(K_FWD_LSE, st, thunk<DimArgs, do_fwd_lse>, &da, "forward pass 1"))) return rc;
+    if ((rc = launch(K_FWD_OUT, st, thunk<DimArgs, do_fwd_out>, &da, "forward pass 2"))) return rc;
     return ok();
 }
 
@@ -446,11 +535,11 @@ int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const vo
     pa.Nq = pl.Nq;
     pa.Nq_pad = pl.Nq_pad;
     pa.D = (int)pl.D;
-    if ((rc = hip_check(aq::launch_bwd_pre(pa, st), "backward preprocess"))) return rc;
-    if ((rc = hip_check(aq::launch_transpose_perm((const uint16_t*)(ws + L.dow),
-                                                  (uint16_t*)(ws + L.dot), pl.BH, (int)pl.Nq_pad,
-                                                  (int)pl.D, st),
-                        "transpose dO")))
+    if ((rc = launch(K_BWD_PRE, st, thunk<aq::PreArgs, aq::launch_bwd_pre>, &pa,
+                     "backward preprocess")))
+        return rc;
+    if ((rc = run_transpose((const uint16_t*)(ws + L.dow), (uint16_t*)(ws + L.dot), pl.BH,
+                            pl.Nq_pad, pl.D, st, "transpose dO")))
         return rc;
     aq::AttnArgs a = attn_args(p, pl, ws, L);
     a.Qt = (const uint16_t*)(ws + L.qt);
@@ -474,14 +563,15 @@ int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const vo
     if (pl.sparse) {
         a.q_list = (const int32_t*)(ws + L.qlist);
         a.q_count = (const int32_t*)(ws + L.qcount);
-        if ((rc = hip_check(aq::launch_reverse_index(p->kv_block_idx, (int32_t*)(ws + L.qlist),
-                                                     (int32_t*)(ws + L.qcount), pl.BH, pl.nbq,
-                                                     pl.nbk, p->topk, st),
-                            "reverse block index")))
+        const RevArgs ra{p->kv_block_idx, (int32_t*)(ws + L.qlist), (int32_t*)(ws + L.qcount),
+                         pl.BH, pl.nbq, pl.nbk, p->topk};
+        if ((rc = launch(K_REVERSE_INDEX, st, thunk<RevArgs, do_reverse>, &ra,
+                         "reverse block index")))
             return rc;
     }
-    if ((rc = hip_check(aq::launch_bwd_dkdv(a, (int)pl.D, st), "backward dK/dV"))) return rc;
-    if ((rc = hip_check(aq::launch_bwd_dq(a, (int)pl.D, st), "backward dQ"))) return rc;
+    const DimArgs da{a, (int)pl.D};
+    if ((rc = launch(K_BWD_DKDV, st, thunk<DimArgs, do_bwd_dkdv>, &da, "backward dK/dV"))) return rc;
+    if ((rc = launch(K_BWD_DQ, st, thunk<DimArgs, do_bwd_dq>, &da, "backward dQ"))) return rc;
     return ok();
 }
 
@@ -558,9 +648,51 @@ int attnqat_block_select(const attnqat_problem* p, const void* q, const void* k,
     a.topk = p->topk;
     a.D = (int)p->D;
     hipStream_t st = (hipStream_t)stream;
-    if ((rc = hip_check(aq::launch_block_pool(a, st), "block pooling"))) return rc;
-    if ((rc = hip_check(aq::launch_block_topk(a, st), "block top-k"))) return rc;
+    if ((rc = launch(K_BLOCK_POOL, st, thunk<aq::SelectArgs, aq::launch_block_pool>, &a,
+                     "block pooling")))
+        return rc;
+    if ((rc = launch(K_BLOCK_TOPK, st, thunk<aq::SelectArgs, aq::launch_block_topk>, &a,
+                     "block top-k")))
+        return rc;
     return ok();
+}
+
+int attnqat_profile_enable(int on) {
+    g_prof.on = on != 0;
+    g_prof.used = 0;
+    return ok();
+}
+
+int attnqat_profile_read(const char** names, double* total_ms, int* launches, int max_kinds) {
+    double tot[K_NUM] = {0};
+    int cnt[K_NUM] = {0};
+    Profiler& P = g_prof;
+    for (int i = 0; i < P.used; ++i) {
+        hipError_t e = hipEventSynchronize(P.ev[2 * i + 1]);
+        if (e != hipSuccess) {
+            P.used = 0;
+            return -fail(ATTNQAT_E_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
+        }
+        float ms = 0.0f;
+        e = hipEventElapsedTime(&ms, P.ev[2 * i], P.ev[2 * i + 1]);
+        if (e != hipSuccess) {
+            P.used = 0;
+            return -fail(ATTNQAT_E_HIP, "hipEventElapsedTime: %s", hipGetErrorString(e));
+        }
+        tot[P.kind[i]] += ms;
+        cnt[P.kind[i]] += 1;
+    }
+    P.used = 0;
+    int n = 0;
+    for (int k = 0; k < K_NUM && n < max_kinds; ++k) {
+        if (!cnt[k]) continue;
+        if (names) names[n] = kKindName[k];
+        if (total_ms) total_ms[n] = tot[k];
+        if (launches) launches[n] = cnt[k];
+        ++n;
+    }
+    ok();
+    return n;
 }
 
 }  // extern "C"

@@ -10,6 +10,7 @@ import pytest
 import torch
 
 from oracle import attention as oatt
+from oracle.block_sparse import bf16_round
 from synthetic import WORKLOADS, make_inputs, random_bf16
 from tests.helpers import TOL_LSE, dev_bits, dev_f64, rel_l2, to_dev, to_f64, tol_for
 
@@ -28,12 +29,14 @@ def _run_pair(gpu_lib, bits, mask, sc, do_bwd=True):
 
 
 def _oracle(bits, mask, sc, do_bwd=True):
+    """Oracle forward; its backward takes D from the forward output as returned,
+    i.e. rounded to the bf16 output dtype (never from the GPU's output)."""
     f = {k: to_f64(v) for k, v in bits.items()}
     O, L = oatt.forward(f["q"], f["k"], f["v"], sc, mask)
     res = {"o": O, "lse": L}
     if do_bwd:
         res["dq"], res["dk"], res["dv"] = oatt.backward(f["q"], f["k"], f["v"], f["do"], sc, mask,
-                                                        O, L)
+                                                        bf16_round(O), L)
     return res
 
 
