@@ -82,6 +82,33 @@ def head_forward(qq, kq, vq, sm_scale: float, mask: int, rows=None, row_block: i
     return O, L
 
 
+def _forward_rows_task(args):
+    qq, kq, vq, sm_scale, mask, r0, r1 = args
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            return head_forward(qq[r0:r1], kq, vq, sm_scale, mask)
+    except ImportError:  # pragma: no cover
+        return head_forward(qq[r0:r1], kq, vq, sm_scale, mask)
+
+
+def head_forward_all(qq, kq, vq, sm_scale: float, mask: int, workers: int = 0,
+                     chunk: int = 1024):
+    """``head_forward`` over every query row, split into row chunks across
+    ``workers`` processes (0 or 1: in this process). Rows are independent in
+    the forward, so the result is identical to a single call."""
+    n = qq.shape[0]
+    spans = [(r0, min(n, r0 + chunk)) for r0 in range(0, n, chunk)]
+    if workers <= 1:
+        parts = [head_forward(qq[a:b], kq, vq, sm_scale, mask) for a, b in spans]
+    else:
+        import multiprocessing as mp
+        with mp.get_context("fork").Pool(workers) as pool:
+            parts = pool.map(_forward_rows_task,
+                             [(qq, kq, vq, sm_scale, mask, a, b) for a, b in spans])
+    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+
+
 def forward(q, k, v, sm_scale: float, mask: int = MASK_ALL, row_block: int = 512):
     """O [B,H,Nq,D] and LSE [B,H,Nq] for real-valued inputs q, k, v."""
     q = np.asarray(q, np.float64)

@@ -144,3 +144,56 @@ def backward(q, k, v, do, sm_scale: float, idx: np.ndarray, block_tokens: int,
                 dq[b, h, r0:r1] = sm_scale * (dS @ kq[b, h, keys])
                 dk[b, h, keys] += sm_scale * (dS.T @ qq[b, h, r0:r1])
     return dq, dk, dv
+
+
+def query_block_forward(qq, kq, vq, blocks, r0: int, r1: int, block_tokens: int,
+                        sm_scale: float, mask: int):
+    """One head, query rows [r0, r1) of one query block attending to ``blocks``.
+
+    Operands are already quantized ([N, D] arrays). Returns (keys, O, LSE, P, Pq)
+    where ``keys`` are the attended key indices in visiting order.
+    """
+    keys = _keys_of(blocks, block_tokens, kq.shape[0])
+    S = sm_scale * (qq[r0:r1] @ kq[keys].T)
+    lse = _lse(S)
+    P = np.exp(S - lse[:, None])
+    Pq = fake_quant(P, axis=-1) if mask & MASK_P else P
+    return keys, Pq @ vq[keys], lse, P, Pq
+
+
+def query_block_backward(qq, kq, vq, do, O, blocks, r0: int, r1: int, block_tokens: int,
+                         sm_scale: float, mask: int):
+    """dQ of query rows [r0, r1) of one head (one query block) attending to
+    ``blocks``; ``O`` is the forward output of those rows (D = rowsum(dO O))."""
+    keys, _, lse, P, Pq = query_block_forward(qq, kq, vq, blocks, r0, r1, block_tokens,
+                                              sm_scale, mask)
+    Dd = np.sum(do[r0:r1] * O, axis=-1)
+    dS = P * (do[r0:r1] @ vq[keys].T - Dd[:, None])
+    return sm_scale * (dS @ kq[keys])
+
+
+def key_block_backward(qq, kq, vq, do, idx_h, j: int, block_tokens: int, sm_scale: float,
+                       mask: int, o_round=None):
+    """dK, dV of key block ``j`` of one head: the sum over every query block
+    whose selection ``idx_h`` [nbq, topk] contains j. The forward output of
+    those query blocks is recomputed here; ``o_round`` (optional) maps it to
+    the stored output dtype before it enters D = rowsum(dO O)."""
+    Nq, Nk = qq.shape[0], kq.shape[0]
+    k0, k1 = j * block_tokens, min(Nk, (j + 1) * block_tokens)
+    dk = np.zeros((k1 - k0, kq.shape[1]))
+    dv = np.zeros((k1 - k0, vq.shape[1]))
+    for i in range(idx_h.shape[0]):
+        if j not in set(int(x) for x in idx_h[i]):
+            continue
+        r0, r1 = i * block_tokens, min(Nq, (i + 1) * block_tokens)
+        keys, O, lse, P, Pq = query_block_forward(qq, kq, vq, idx_h[i], r0, r1, block_tokens,
+                                                  sm_scale, mask)
+        if o_round is not None:
+            O = o_round(O)
+        sel = np.nonzero((keys >= k0) & (keys < k1))[0]
+        Dd = np.sum(do[r0:r1] * O, axis=-1)
+        dP = do[r0:r1] @ vq[keys[sel]].T
+        dS = P[:, sel] * (dP - Dd[:, None])
+        dv += Pq[:, sel].T @ do[r0:r1]
+        dk += sm_scale * (dS.T @ qq[r0:r1])
+    return dk, dv

@@ -1,0 +1,176 @@
+"""C-ABI contract checks that need no GPU.
+
+The library loads, exports every function declared in include/attnqat.h, and
+rejects every malformed call with the documented status before any HIP call
+(so these calls use fake device addresses that are never dereferenced).
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import quantization_aware_attention_amd as qaa
+from quantization_aware_attention_amd import build as qbuild
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "attnqat.h")
+OK, E_INVALID, E_UNSUPPORTED, E_MISALIGNED, E_WORKSPACE, E_HIP = 0, 1, 2, 3, 4, 5
+A = 1 << 20          # fake, 16-byte (and 256-byte) aligned device addresses, never dereferenced
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(qbuild.LIB_PATH):
+        qbuild.build()
+    return qaa.load()
+
+
+def _prob(**kw):
+    p = qaa.Problem()
+    p.B, p.H, p.Nq, p.Nk, p.D = 1, 2, 100, 120, 64
+    p.sm_scale = 0.125
+    p.quant_mask = 15
+    p.block_tokens = 128
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def _fwd(L, p, q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, ws=6 * A, wsb=1 << 40):
+    return L.attnqat_fwd(ctypes.byref(p), q, k, v, o, lse, ws, wsb, None)
+
+
+def _bwd(L, p, ws=20 * A, wsb=1 << 40, **ptrs):
+    d = dict(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, do=6 * A, dq=7 * A, dk=8 * A, dv=9 * A)
+    d.update(ptrs)
+    return L.attnqat_bwd(ctypes.byref(p), d["q"], d["k"], d["v"], d["o"], d["lse"], d["do"],
+                         d["dq"], d["dk"], d["dv"], ws, wsb, None)
+
+
+def test_exports_every_declared_function(L):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(attnqat_\w+)\s*\(", text, re.M))
+    assert declared == set(qaa.EXPORTS), declared ^ set(qaa.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.attnqat_abi_version() == 1
+
+
+def test_status_strings(L):
+    for code in range(6):
+        assert L.attnqat_status_string(code)
+    assert L.attnqat_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("D", 96, E_UNSUPPORTED), ("D", 256, E_UNSUPPORTED), ("B", 0, E_INVALID),
+    ("Nq", 0, E_INVALID), ("Nk", 0, E_INVALID), ("H", -1, E_INVALID),
+    ("sm_scale", 0.0, E_INVALID), ("sm_scale", -1.0, E_INVALID),
+    ("sm_scale", float("nan"), E_INVALID), ("sm_scale", float("inf"), E_INVALID),
+    ("quant_mask", 16, E_INVALID), ("quant_mask", 0x80000000, E_INVALID),
+])
+def test_forward_rejects_bad_problem(L, field, value, code):
+    p = _prob(**{field: value})
+    assert _fwd(L, p) == code
+    assert L.attnqat_last_error()
+    assert L.attnqat_fwd_workspace_bytes(ctypes.byref(p)) == 0
+
+
+def test_forward_pointer_checks(L):
+    p = _prob()
+    assert _fwd(L, p, q=0) == E_INVALID
+    assert _fwd(L, p, lse=0) == E_INVALID
+    assert _fwd(L, p, k=2 * A + 8) == E_MISALIGNED
+    assert _fwd(L, p, ws=6 * A + 16) == E_MISALIGNED
+    assert _fwd(L, p, lse=5 * A + 2) == E_MISALIGNED
+    assert _fwd(L, p, ws=0) == E_WORKSPACE
+    need = L.attnqat_fwd_workspace_bytes(ctypes.byref(p))
+    assert need > 0
+    assert _fwd(L, p, wsb=need - 1) == E_WORKSPACE
+    assert _fwd(L, p, o=A) == E_INVALID                 # output aliases q
+    assert _fwd(L, p, ws=A) == E_INVALID                # workspace overlaps q
+    assert b"overlap" in L.attnqat_last_error()
+
+
+def test_forward_stride_checks(L):
+    p = _prob()
+    p.q = qaa.Strides(2 * 100 * 64, 100 * 64, 60)       # row stride < D and not a multiple of 8
+    assert _fwd(L, p) == E_MISALIGNED
+    p.q = qaa.Strides(2 * 100 * 64, 100 * 64, 32)       # rows overlap
+    assert _fwd(L, p) == E_INVALID
+    p.q = qaa.Strides(-8, 100 * 64, 64)
+    assert _fwd(L, p) == E_INVALID
+
+
+def test_backward_checks(L):
+    p = _prob()
+    need = L.attnqat_bwd_workspace_bytes(ctypes.byref(p))
+    assert need > L.attnqat_fwd_workspace_bytes(ctypes.byref(p))
+    assert _bwd(L, p, dq=0) == E_INVALID
+    assert _bwd(L, p, wsb=need - 1) == E_WORKSPACE
+    assert _bwd(L, p, dk=7 * A) == E_INVALID            # dk overlaps dq
+    assert _bwd(L, p, dv=A) == E_INVALID                # dv overlaps q
+    assert _bwd(L, p, do=6 * A + 4) == E_MISALIGNED
+
+
+def test_sparse_problem_checks(L):
+    p = _prob(Nq=1024, Nk=1024, block_tokens=64)
+    p.kv_block_idx = 30 * A
+    p.topk = 2
+    assert _fwd(L, p) == E_UNSUPPORTED                  # block_tokens must be 128
+    p.block_tokens = 128
+    p.topk = 9
+    assert _fwd(L, p) == E_INVALID                      # 8 key blocks
+    p.topk = 0
+    assert _fwd(L, p) == E_INVALID
+    p.topk = 3
+    dense = _prob(Nq=1024, Nk=1024)
+    assert (L.attnqat_bwd_workspace_bytes(ctypes.byref(p)) >
+            L.attnqat_bwd_workspace_bytes(ctypes.byref(dense)))
+
+
+def test_block_select_checks(L):
+    p = _prob(Nq=1024, Nk=1024)
+    p.topk = 3
+    need = L.attnqat_block_select_workspace_bytes(ctypes.byref(p))
+    assert need > 0
+    sel = L.attnqat_block_select
+    assert sel(ctypes.byref(p), A, 2 * A, 0, 6 * A, need, None) == E_INVALID
+    assert sel(ctypes.byref(p), A, 2 * A, 3 * A, 6 * A, need - 1, None) == E_WORKSPACE
+    assert sel(ctypes.byref(p), A, 2 * A, 3 * A + 2, 6 * A, need, None) == E_MISALIGNED
+    p.topk = 9
+    assert sel(ctypes.byref(p), A, 2 * A, 3 * A, 6 * A, need, None) == E_INVALID
+    p.topk = 3
+    p.D = 80
+    assert sel(ctypes.byref(p), A, 2 * A, 3 * A, 6 * A, need, None) == E_UNSUPPORTED
+
+
+def test_fakequant_checks(L):
+    s0 = qaa.Strides(0, 0, 0)
+    fq = L.attnqat_fakequant_nvfp4
+    assert fq(A, s0, 2 * A, s0, None, 1, 1, 16, 64, 2, None) == E_INVALID       # axis
+    assert fq(A, s0, 2 * A, s0, None, 1, 1, 16, 40, 0, None) == E_UNSUPPORTED   # D % 16
+    assert fq(A, s0, 2 * A, s0, None, 1, 1, 16, 12, 1, None) == E_UNSUPPORTED   # D % 8
+    assert fq(0, s0, 2 * A, s0, None, 1, 1, 16, 64, 0, None) == E_INVALID
+    assert fq(A, s0, A + 64, s0, None, 1, 1, 16, 64, 0, None) == E_INVALID      # overlap
+    assert fq(A + 8, s0, 2 * A, s0, None, 1, 1, 16, 64, 0, None) == E_MISALIGNED
+    assert fq(A, s0, 2 * A, s0, None, 0, 1, 16, 64, 0, None) == E_INVALID
+    assert fq(A, s0, 2 * A, s0, A + 16, 1, 1, 16, 64, 0, None) == E_INVALID     # codes overlap
+
+
+def test_profile_read_empty(L):
+    assert L.attnqat_profile_enable(1) == OK
+    assert L.attnqat_profile_read(None, None, None, 8) == 0
+    assert L.attnqat_profile_enable(0) == OK
+
+
+def test_workspace_sizes_scale_with_problem(L):
+    a = L.attnqat_fwd_workspace_bytes(ctypes.byref(_prob(Nq=128, Nk=128)))
+    b = L.attnqat_fwd_workspace_bytes(ctypes.byref(_prob(Nq=256, Nk=256)))
+    assert b > a > 0 and a % 256 == 0 and b % 256 == 0
+
+
+def test_mask_parsing():
+    assert qaa.parse_mask("qkvp") == 15 and qaa.parse_mask("p") == 8 and qaa.parse_mask(5) == 5
+    assert math.isclose(1 / math.sqrt(128), 0.08838834764831845)

@@ -1,0 +1,121 @@
+"""Parity at the workloads' full sizes, in the launch configuration bench.py times.
+
+The GPU computes every output; the oracle checks samples it can afford:
+query rows of three heads (O, LSE, dQ), every row of one head (O, LSE), and
+whole 16-key groups of that head (dK, dV, which need that head's full forward).
+With every quantizer off, sum_j dK_j = 0 is checked over every head.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as oatt
+from oracle.block_sparse import bf16_round
+from synthetic import WORKLOADS, make_inputs
+from tests.helpers import TOL_LSE, dev_f64, rel_l2, to_dev, to_f64, tol_for
+
+pytestmark = pytest.mark.gpu
+
+WORKERS = min(16, os.cpu_count() or 1)
+
+
+def _check(label, errs, lse_err, tol):
+    msg = f"{label} rel-L2 {errs} lse {lse_err:.2e}"
+    print(msg, flush=True)
+    assert lse_err <= TOL_LSE, msg
+    for k, e in errs.items():
+        assert e <= tol, msg
+
+
+@pytest.mark.parametrize("cid,mask", [(2, 15), (3, 15), (4, 15), (4, 0)])
+def test_full_size(gpu_lib, cid, mask):
+    w = WORKLOADS[cid]
+    print(f"workload {w.name} {w.shape} mask={mask}", flush=True)
+    bits = make_inputs(cid)
+    t = {k: to_dev(v) for k, v in bits.items()}
+    sc = w.sm_scale
+    o, lse = gpu_lib.fwd(t["q"], t["k"], t["v"], sc, mask)
+    dq, dk, dv = gpu_lib.bwd(t["q"], t["k"], t["v"], o, lse, t["do"], sc, mask)
+    torch.cuda.synchronize()
+    B, H, N, D = w.shape
+    tol = tol_for(mask)
+    rs = np.random.RandomState(cid * 10 + mask)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(N - 8, N),
+                                     rs.choice(N, 8, replace=False)]))
+    heads = [(0, 0), (B - 1, H // 2), (B - 1, H - 1)]
+    for b, h in heads:
+        f = {k: to_f64(bits[k][b, h]) for k in bits}
+        qq, kq, vq = oatt.quantize_operands(f["q"], f["k"], f["v"], mask)
+        Or, Lr = oatt.head_forward(qq, kq, vq, sc, mask, rows=rows)
+        dqr = oatt.head_backward_rows(qq, kq, vq, f["do"][rows], bf16_round(Or), Lr, rows, sc,
+                                      mask)
+        errs = {"o": rel_l2(dev_f64(o[b, h, rows]), Or),
+                "dq": rel_l2(dev_f64(dq[b, h, rows]), dqr, exact_zero=False)}
+        lse_err = float(np.abs(lse[b, h, rows].cpu().numpy() - Lr).max())
+        _check(f"{w.name} b={b} h={h} rows", errs, lse_err, tol)
+
+    # one head in full: O and LSE of every row, dK/dV of whole key groups
+    b, h = 0, 0
+    f = {k: to_f64(bits[k][b, h]) for k in bits}
+    qq, kq, vq = oatt.quantize_operands(f["q"], f["k"], f["v"], mask)
+    Of, Lf = oatt.head_forward_all(qq, kq, vq, sc, mask, workers=WORKERS)
+    errs = {"o_head": rel_l2(dev_f64(o[b, h]), Of)}
+    lse_err = float(np.abs(lse[b, h].cpu().numpy() - Lf).max())
+    ng = (N + 15) // 16
+    groups = [0, ng // 2, ng - 1]
+    keys = np.concatenate([np.arange(g * 16, min(N, g * 16 + 16)) for g in groups])
+    dkr, dvr = oatt.head_backward_keys(qq, kq, vq, f["do"], bf16_round(Of), Lf, sc, mask, keys)
+    errs["dk_keys"] = rel_l2(dev_f64(dk[b, h, keys]), dkr, exact_zero=False)
+    errs["dv_keys"] = rel_l2(dev_f64(dv[b, h, keys]), dvr)
+    _check(f"{w.name} b={b} h={h} full head", errs, lse_err, tol)
+    if np.linalg.norm(Of) == 0:
+        # every quantized probability of this head flushed to zero
+        assert torch.count_nonzero(o[b, h]) == 0 and torch.count_nonzero(dv[b, h]) == 0
+    if mask == 0:
+        # Shift invariance: sum_j dK_j = 0 exactly. Each stored dK_j carries a
+        # bf16 rounding error of at most 2^-8 relative, so the column sums are
+        # compared with the standard deviation of that rounding noise.
+        g = dk.double()
+        s = g.sum(dim=2).abs()
+        noise = g.pow(2).sum(dim=2).sqrt() * (2.0 ** -8 / 3 ** 0.5)
+        ratio = (s / noise.clamp_min(1e-30)).max().item()
+        print(f"max |sum_j dK_j| / rounding-noise sigma = {ratio:.2f}", flush=True)
+        assert ratio <= 6.0
+
+
+def test_sparse_full_size(gpu_lib):
+    from oracle import block_sparse as bsp
+    w = WORKLOADS[5]
+    bits = make_inputs(5)
+    t = {k: to_dev(v) for k, v in bits.items()}
+    B, H, N, D = w.shape
+    sc, bt = w.sm_scale, w.block_tokens
+    print(f"workload {w.name} {w.shape} topk={w.topk}", flush=True)
+    idx_g = gpu_lib.block_select(t["q"], t["k"], w.topk, bt)
+    idx_r = bsp.select_blocks(to_f64(bits["q"]), to_f64(bits["k"]), bt, w.topk)
+    np.testing.assert_array_equal(idx_g.cpu().numpy(), idx_r)
+    idx_t = torch.from_numpy(idx_r).to("cuda")
+    o, lse = gpu_lib.fwd(t["q"], t["k"], t["v"], sc, 15, idx_t)
+    dq, dk, dv = gpu_lib.bwd(t["q"], t["k"], t["v"], o, lse, t["do"], sc, 15, idx_t)
+    torch.cuda.synchronize()
+    nb = N // bt
+    for h in (0, H - 1):
+        f = {k: to_f64(bits[k][0, h]) for k in bits}
+        qq, kq, vq = oatt.quantize_operands(f["q"], f["k"], f["v"], 15)
+        for i in (0, nb // 3, nb - 1):
+            r0, r1 = i * bt, (i + 1) * bt
+            _, Oi, Li, _, _ = bsp.query_block_forward(qq, kq, vq, idx_r[0, h, i], r0, r1, bt, sc, 15)
+            dqi = bsp.query_block_backward(qq, kq, vq, f["do"], bf16_round(Oi), idx_r[0, h, i],
+                                           r0, r1, bt, sc, 15)
+            errs = {"o": rel_l2(dev_f64(o[0, h, r0:r1]), Oi),
+                    "dq": rel_l2(dev_f64(dq[0, h, r0:r1]), dqi, exact_zero=False)}
+            lse_err = float(np.abs(lse[0, h, r0:r1].cpu().numpy() - Li).max())
+            _check(f"sparse h={h} qblock={i}", errs, lse_err, 1e-2)
+        for j in (1, nb - 2):
+            dkj, dvj = bsp.key_block_backward(qq, kq, vq, f["do"], idx_r[0, h], j, bt, sc, 15,
+                                              o_round=bf16_round)
+            errs = {"dk": rel_l2(dev_f64(dk[0, h, j * bt:(j + 1) * bt]), dkj, exact_zero=False),
+                    "dv": rel_l2(dev_f64(dv[0, h, j * bt:(j + 1) * bt]), dvj)}
+            _check(f"sparse h={h} kblock={j}", errs, 0.0, 1e-2)

@@ -323,3 +323,39 @@ def test_block_sparse_equals_masked_dense(mask):
         O2, _ = bsp.forward(q, k, v, 0.25, idx_all, bt, 0)
         Or2, _ = _sdpa_fp64(q, k, v, 0.25)
         np.testing.assert_allclose(O2, Or2, rtol=1e-12, atol=1e-13)
+
+
+def test_block_helpers_match_full_sparse_oracle():
+    bt, nb, topk = 32, 5, 2
+    N = bt * nb - 7                       # ragged last block
+    q = _bf16(60, (1, 1, N, 16), 2.0)
+    k = _bf16(61, (1, 1, N, 16), 2.0)
+    v = _bf16(62, (1, 1, N, 16))
+    do = _bf16(63, (1, 1, N, 16))
+    idx = bsp.select_blocks(q, k, bt, topk)
+    O, L = bsp.forward(q, k, v, 0.3, idx, bt, 15)
+    dq, dk, dv = bsp.backward(q, k, v, do, 0.3, idx, bt, 15, O, L)
+    qq, kq, vq = att.quantize_operands(q[0, 0], k[0, 0], v[0, 0], 15)
+    for i in range(nb):
+        r0, r1 = i * bt, min(N, (i + 1) * bt)
+        _, Oi, Li, _, _ = bsp.query_block_forward(qq, kq, vq, idx[0, 0, i], r0, r1, bt, 0.3, 15)
+        np.testing.assert_allclose(Oi, O[0, 0, r0:r1], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(Li, L[0, 0, r0:r1], rtol=1e-13)
+        dqi = bsp.query_block_backward(qq, kq, vq, do[0, 0], Oi, idx[0, 0, i], r0, r1, bt, 0.3, 15)
+        np.testing.assert_allclose(dqi, dq[0, 0, r0:r1], rtol=1e-11, atol=1e-14)
+    for j in range(nb):
+        dkj, dvj = bsp.key_block_backward(qq, kq, vq, do[0, 0], idx[0, 0], j, bt, 0.3, 15)
+        k0, k1 = j * bt, min(N, (j + 1) * bt)
+        np.testing.assert_allclose(dkj, dk[0, 0, k0:k1], rtol=1e-11, atol=1e-14)
+        np.testing.assert_allclose(dvj, dv[0, 0, k0:k1], rtol=1e-11, atol=1e-14)
+
+
+def test_parallel_full_head_forward_matches():
+    q = _bf16(70, (1, 1, 300, 32), 2.0)
+    k = _bf16(71, (1, 1, 250, 32), 2.0)
+    v = _bf16(72, (1, 1, 250, 32))
+    qq, kq, vq = att.quantize_operands(q[0, 0], k[0, 0], v[0, 0], 15)
+    O1, L1 = att.head_forward(qq, kq, vq, 0.2, 15)
+    O2, L2 = att.head_forward_all(qq, kq, vq, 0.2, 15, workers=2, chunk=64)
+    np.testing.assert_array_equal(O1, O2)
+    np.testing.assert_array_equal(L1, L2)
