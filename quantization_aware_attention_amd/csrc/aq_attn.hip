@@ -45,23 +45,37 @@ __device__ __forceinline__ void quant_p_group(float* p) {
     for (int j = 0; j < 8; ++j) p[j] = e2m1_round(p[j] * inv) * s;
 }
 
-// Stage rows [r0, r0 + R) of a [*, D] bf16 matrix into LDS with row pitch P.
-template <int R, int D, int P>
-__device__ __forceinline__ void stage_rows(uint16_t* lds, const uint16_t* g, int tid) {
+// Tile staging through registers. A tile is R rows of W bf16 (16-byte
+// chunks); each of the 256 threads owns R * W / 8 / 256 chunks. Loads for the
+// next tile are issued before the current tile is computed on, so global
+// latency overlaps the MFMA work; the register copy is written to LDS after
+// the next barrier.
+template <int R, int W>
+struct TileRegs {
+    static constexpr int N = R * W / 8 / 256;
+    static_assert(R * W / 8 % 256 == 0, "tile must split evenly over 256 threads");
+    u32x4 v[N];
+};
+
+// Load rows [0, R) of a row-major matrix with leading dimension ld (elements).
+template <int R, int W>
+__device__ __forceinline__ void tile_load(TileRegs<R, W>& t, const uint16_t* g, int ld, int tid) {
 #pragma unroll
-    for (int i = tid; i < R * D / 8; i += 256) {
-        const int r = i / (D / 8), cc = i % (D / 8);
-        *(u32x4*)(lds + r * P + cc * 8) = *(const u32x4*)(g + (size_t)r * D + cc * 8);
+    for (int j = 0; j < TileRegs<R, W>::N; ++j) {
+        const int i = tid + 256 * j;
+        const int r = i / (W / 8), cc = i % (W / 8);
+        t.v[j] = *(const u32x4*)(g + (size_t)r * ld + cc * 8);
     }
 }
 
-// Stage columns [c0, c0 + C) of a [D][ld] bf16 matrix into LDS with row pitch P.
-template <int C, int D, int P>
-__device__ __forceinline__ void stage_cols(uint16_t* lds, const uint16_t* g, int ld, int tid) {
+// Write the tile to LDS with row pitch P (elements).
+template <int R, int W, int P>
+__device__ __forceinline__ void tile_store(uint16_t* lds, const TileRegs<R, W>& t, int tid) {
 #pragma unroll
-    for (int i = tid; i < D * C / 8; i += 256) {
-        const int r = i / (C / 8), cc = i % (C / 8);
-        *(u32x4*)(lds + r * P + cc * 8) = *(const u32x4*)(g + (size_t)r * ld + cc * 8);
+    for (int j = 0; j < TileRegs<R, W>::N; ++j) {
+        const int i = tid + 256 * j;
+        const int r = i / (W / 8), cc = i % (W / 8);
+        *(u32x4*)(lds + r * P + cc * 8) = t.v[j];
     }
 }
 
@@ -100,12 +114,16 @@ __global__ __launch_bounds__(256) void fwd_lse_kernel(AttnArgs a) {
         qf[c] = *(const u32x4*)(Qb + (size_t)(q0 + l32) * D + c * 16 + hh * 8);
     const int32_t* kvi = a.kv_idx ? a.kv_idx + ((size_t)bh * a.nbq + qblk) * a.topk : nullptr;
     const int n_iter = kvi ? a.topk * 2 : a.Nk_pad / BN;
+    auto tile_at = [&](int it) { return kvi ? kvi[it >> 1] * 128 + (it & 1) * BN : it * BN; };
     float m = kNegBig, l = 0.0f;
+    TileRegs<BN, D> rk;
+    tile_load(rk, Kb + (size_t)tile_at(0) * D, D, tid);
     for (int it = 0; it < n_iter; ++it) {
-        const int kt = kvi ? kvi[it >> 1] * 128 + (it & 1) * BN : it * BN;
+        const int kt = tile_at(it);
         __syncthreads();
-        stage_rows<BN, D, KP>(sK, Kb + (size_t)kt * D, tid);
+        tile_store<BN, D, KP>(sK, rk, tid);
         __syncthreads();
+        if (it + 1 < n_iter) tile_load(rk, Kb + (size_t)tile_at(it + 1) * D, D, tid);
         const bool tail = kt + BN > a.Nk;
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb) {
@@ -164,12 +182,22 @@ __global__ __launch_bounds__(256) void fwd_out_kernel(AttnArgs a) {
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
     const int32_t* kvi = a.kv_idx ? a.kv_idx + ((size_t)bh * a.nbq + qblk) * a.topk : nullptr;
     const int n_iter = kvi ? a.topk * 2 : a.Nk_pad / BN;
+    auto tile_at = [&](int it) { return kvi ? kvi[it >> 1] * 128 + (it & 1) * BN : it * BN; };
+    TileRegs<BN, D> rk;
+    TileRegs<D, BN> rv;
+    tile_load(rk, Kb + (size_t)tile_at(0) * D, D, tid);
+    tile_load(rv, Vtb + tile_at(0), a.Nk_pad, tid);
     for (int it = 0; it < n_iter; ++it) {
-        const int kt = kvi ? kvi[it >> 1] * 128 + (it & 1) * BN : it * BN;
+        const int kt = tile_at(it);
         __syncthreads();
-        stage_rows<BN, D, KP>(sK, Kb + (size_t)kt * D, tid);
-        stage_cols<BN, D, VP>(sV, Vtb + kt, a.Nk_pad, tid);
+        tile_store<BN, D, KP>(sK, rk, tid);
+        tile_store<D, BN, VP>(sV, rv, tid);
         __syncthreads();
+        if (it + 1 < n_iter) {
+            const int kn = tile_at(it + 1);
+            tile_load(rk, Kb + (size_t)kn * D, D, tid);
+            tile_load(rv, Vtb + kn, a.Nk_pad, tid);
+        }
         const bool tail = kt + BN > a.Nk;
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb) {
@@ -248,13 +276,28 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(AttnArgs a) {
     for (int db = 0; db < D / 32; ++db) dqa[db] = f32x16{};
     const int32_t* kvi = a.kv_idx ? a.kv_idx + ((size_t)bh * a.nbq + qblk) * a.topk : nullptr;
     const int n_iter = kvi ? a.topk * 2 : a.Nk_pad / BN;
+    auto tile_at = [&](int it) { return kvi ? kvi[it >> 1] * 128 + (it & 1) * BN : it * BN; };
+    TileRegs<BN, D> rk, rv;
+    TileRegs<D, BN> rkt;
+    {
+        const int k0 = tile_at(0);
+        tile_load(rk, Kb + (size_t)k0 * D, D, tid);
+        tile_load(rv, Vb + (size_t)k0 * D, D, tid);
+        tile_load(rkt, Ktb + k0, a.Nk_pad, tid);
+    }
     for (int it = 0; it < n_iter; ++it) {
-        const int kt = kvi ? kvi[it >> 1] * 128 + (it & 1) * BN : it * BN;
+        const int kt = tile_at(it);
         __syncthreads();
-        stage_rows<BN, D, KP>(sK, Kb + (size_t)kt * D, tid);
-        stage_rows<BN, D, KP>(sV, Vb + (size_t)kt * D, tid);
-        stage_cols<BN, D, VP>(sKt, Ktb + kt, a.Nk_pad, tid);
+        tile_store<BN, D, KP>(sK, rk, tid);
+        tile_store<BN, D, KP>(sV, rv, tid);
+        tile_store<D, BN, VP>(sKt, rkt, tid);
         __syncthreads();
+        if (it + 1 < n_iter) {
+            const int kn = tile_at(it + 1);
+            tile_load(rk, Kb + (size_t)kn * D, D, tid);
+            tile_load(rv, Vb + (size_t)kn * D, D, tid);
+            tile_load(rkt, Ktb + kn, a.Nk_pad, tid);
+        }
         const bool tail = kt + BN > a.Nk;
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb) {
@@ -342,18 +385,33 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(AttnArgs a) {
     uint16_t* Tp = sT[wave][0];
     uint16_t* Td = sT[wave][1];
     const int qpos = (l32 & ~15) + perm16(l32 & 15);
-    for (int it = 0; it < n_iter; ++it) {
-        const int qt = ql ? ql[it >> 1] * 128 + (it & 1) * BM : it * BM;
-        __syncthreads();
-        stage_rows<BM, D, KP>(sQ, Qb + (size_t)qt * D, tid);
-        stage_rows<BM, D, KP>(sdO, dOb + (size_t)qt * D, tid);
-        stage_cols<BM, D, QTP>(sQt, Qtb + qt, a.Nq_pad, tid);
-        stage_cols<BM, D, QTP>(sdOt, dOtb + qt, a.Nq_pad, tid);
+    auto tile_at = [&](int it) { return ql ? ql[it >> 1] * 128 + (it & 1) * BM : it * BM; };
+    TileRegs<BM, D> rq, rdo;
+    TileRegs<D, BM> rqt, rdot;
+    float rl = 0.0f, rdl = 0.0f;
+    auto load_all = [&](int qt) {
+        tile_load(rq, Qb + (size_t)qt * D, D, tid);
+        tile_load(rdo, dOb + (size_t)qt * D, D, tid);
+        tile_load(rqt, Qtb + qt, a.Nq_pad, tid);
+        tile_load(rdot, dOtb + qt, a.Nq_pad, tid);
         if (tid < BM) {
-            sL[tid] = Lb[qt + tid];
-            sDl[tid] = Db[qt + tid];
+            rl = Lb[qt + tid];
+            rdl = Db[qt + tid];
+        }
+    };
+    if (n_iter > 0) load_all(tile_at(0));
+    for (int it = 0; it < n_iter; ++it) {
+        __syncthreads();
+        tile_store<BM, D, KP>(sQ, rq, tid);
+        tile_store<BM, D, KP>(sdO, rdo, tid);
+        tile_store<D, BM, QTP>(sQt, rqt, tid);
+        tile_store<D, BM, QTP>(sdOt, rdot, tid);
+        if (tid < BM) {
+            sL[tid] = rl;
+            sDl[tid] = rdl;
         }
         __syncthreads();
+        if (it + 1 < n_iter) load_all(tile_at(it + 1));
 #pragma unroll
         for (int qb = 0; qb < BM / 32; ++qb) {
             f32x16 s = {}, dp = {};
