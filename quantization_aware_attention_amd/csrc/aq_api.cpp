@@ -120,9 +120,10 @@ struct TransposeArgs {
     uint16_t* dst;
     int64_t BH;
     int Npad, D;
+    bool perm;
 };
 hipError_t do_transpose(const TransposeArgs& t, hipStream_t st) {
-    return aq::launch_transpose_perm(t.src, t.dst, t.BH, t.Npad, t.D, st);
+    return aq::launch_transpose_perm(t.src, t.dst, t.BH, t.Npad, t.D, t.perm, st);
 }
 struct DimArgs {
     aq::AttnArgs a;
@@ -155,8 +156,8 @@ int run_fq(bool axis_d, bool quant, const aq::FqArgs& a, hipStream_t st, const c
 }
 
 int run_transpose(const uint16_t* src, uint16_t* dst, int64_t BH, int64_t Npad, int64_t D,
-                  hipStream_t st, const char* what) {
-    const TransposeArgs t{src, dst, BH, (int)Npad, (int)D};
+                  bool perm, hipStream_t st, const char* what) {
+    const TransposeArgs t{src, dst, BH, (int)Npad, (int)D, perm};
     return launch(K_TRANSPOSE, st, thunk<TransposeArgs, do_transpose>, &t, what);
 }
 
@@ -329,12 +330,12 @@ int prepare_operands(const Plan& pl, uint32_t mask, const void* q, const void* k
     if (rc) return rc;
     if (!bwd)
         return run_transpose((const uint16_t*)(ws + L.vw), (uint16_t*)(ws + L.vt), pl.BH, pl.Nk_pad,
-                             pl.D, st, "transpose V");
+                             pl.D, true, st, "transpose V");
     rc = run_transpose((const uint16_t*)(ws + L.qw), (uint16_t*)(ws + L.qt), pl.BH, pl.Nq_pad, pl.D,
-                       st, "transpose Q");
+                       false, st, "transpose Q");
     if (rc) return rc;
     return run_transpose((const uint16_t*)(ws + L.kw), (uint16_t*)(ws + L.kt), pl.BH, pl.Nk_pad,
-                         pl.D, st, "transpose K");
+                         pl.D, true, st, "transpose K");
 }
 
 aq::AttnArgs attn_args(const attnqat_problem* p, const Plan& pl, char* ws, const Layout& L) {
@@ -539,7 +540,7 @@ int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const vo
                      "backward preprocess")))
         return rc;
     if ((rc = run_transpose((const uint16_t*)(ws + L.dow), (uint16_t*)(ws + L.dot), pl.BH,
-                            pl.Nq_pad, pl.D, st, "transpose dO")))
+                            pl.Nq_pad, pl.D, false, st, "transpose dO")))
         return rc;
     aq::AttnArgs a = attn_args(p, pl, ws, L);
     a.Qt = (const uint16_t*)(ws + L.qt);

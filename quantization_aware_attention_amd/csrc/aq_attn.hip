@@ -31,20 +31,6 @@ __device__ __forceinline__ uint16_t bf16_rne1(float x) {
 // Key index (within a 32-key block) of accumulator register r for lane half hh.
 __device__ __forceinline__ int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
 
-// NVFP4 fake quantization of one 16-key P group held as 8 registers in each of
-// lanes l and l ^ 32 (values >= 0). Decisions are taken in fp32 with a
-// reciprocal of the scale; a tie of the exact reals can only be missed by
-// values within 2^-22 relative of a rounding midpoint.
-__device__ __forceinline__ void quant_p_group(float* p) {
-    float am = fmaxf(fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])),
-                     fmaxf(fmaxf(p[4], p[5]), fmaxf(p[6], p[7])));
-    am = max_lane_pair(am);
-    const float s = e4m3_round(am * (1.0f / 6.0f));
-    const float inv = (s > 0.0f) ? __builtin_amdgcn_rcpf(s) : 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = e2m1_round(p[j] * inv) * s;
-}
-
 // Tile staging through registers. A tile is R rows of W bf16 (16-byte
 // chunks); each of the 256 threads owns R * W / 8 / 256 chunks. Loads for the
 // next tile are issued before the current tile is computed on, so global
@@ -220,7 +206,7 @@ __global__ __launch_bounds__(256) void fwd_out_kernel(AttnArgs a) {
             for (int g = 0; g < 2; ++g) {
                 float* pg = p + 8 * g;
                 if (QP) {
-                    quant_p_group(pg);
+                    quant_group8_hw(pg);
                     bfr[g] = u32x4{pack_exact(pg[0], pg[1]), pack_exact(pg[2], pg[3]),
                                    pack_exact(pg[4], pg[5]), pack_exact(pg[6], pg[7])};
                 } else {
@@ -346,12 +332,12 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(AttnArgs a) {
 // so that queries become the contraction index.
 template <int D, bool QP>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(AttnArgs a) {
-    constexpr int BM = 64, KP = D + 8, QTP = BM + 8, TP = 32 + 8;
+    constexpr int BM = 64, KP = D + 8, QTP = BM + 8;
     __shared__ __attribute__((aligned(16))) uint16_t sQ[BM * KP];
     __shared__ __attribute__((aligned(16))) uint16_t sdO[BM * KP];
     __shared__ __attribute__((aligned(16))) uint16_t sQt[D * QTP];
     __shared__ __attribute__((aligned(16))) uint16_t sdOt[D * QTP];
-    __shared__ __attribute__((aligned(16))) uint16_t sT[4][2][32 * TP];
+    __shared__ __attribute__((aligned(16))) uint16_t sT[4][2][32 * 32];
     __shared__ float sL[BM], sDl[BM];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -382,9 +368,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(AttnArgs a) {
         ql = a.q_list + ((size_t)bh * a.nbk + kblk) * a.nbq;
         n_iter = 2 * a.q_count[(size_t)bh * a.nbk + kblk];
     }
+    // Per-wave 32 x 32 transpose tiles, row = query, 64 bytes per row, 8-byte
+    // column chunks XOR-swizzled by (row / 4) % 8 so that both the row writes
+    // and the transposing reads are free of bank conflicts.
     uint16_t* Tp = sT[wave][0];
     uint16_t* Td = sT[wave][1];
-    const int qpos = (l32 & ~15) + perm16(l32 & 15);
+    const int wsw = (l32 >> 2) & 7;
+    const int grp = lane >> 4, i16 = lane & 15;
     auto tile_at = [&](int it) { return ql ? ql[it >> 1] * 128 + (it & 1) * BM : it * BM; };
     TileRegs<BM, D> rq, rdo;
     TileRegs<D, BM> rqt, rdot;
@@ -432,21 +422,43 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(AttnArgs a) {
                 ds[r] = p[r] * (dp[r] - Dl);
             }
             if (QP) {
-                quant_p_group(p);
-                quant_p_group(p + 8);
+                quant_group8_hw(p);
+                quant_group8_hw(p + 8);
             }
-            // transpose through LDS: T[key][position of query]
+            // transpose through LDS: write rows (query = l32; keys 8a + 4hh ..
+            // + 3 from registers 4a .. 4a + 3), read columns with the
+            // transposing load so that lane (key, hh) gets queries 16g + 8hh + j
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = acc_row(r, hh);
-                Tp[key * TP + qpos] = QP ? (uint16_t)(__float_as_uint(p[r]) >> 16) : bf16_rne1(p[r]);
-                Td[key * TP + qpos] = bf16_rne1(ds[r]);
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int off = l32 * 32 + ((((2 * a4 + hh) ^ wsw)) << 2);
+                u32x2 wp, wd;
+                if (QP) {
+                    wp[0] = pack_exact(p[4 * a4], p[4 * a4 + 1]);
+                    wp[1] = pack_exact(p[4 * a4 + 2], p[4 * a4 + 3]);
+                } else {
+                    wp[0] = pack_rne(p[4 * a4], p[4 * a4 + 1]);
+                    wp[1] = pack_rne(p[4 * a4 + 2], p[4 * a4 + 3]);
+                }
+                wd[0] = pack_rne(ds[4 * a4], ds[4 * a4 + 1]);
+                wd[1] = pack_rne(ds[4 * a4 + 2], ds[4 * a4 + 3]);
+                *(u32x2*)(Tp + off) = wp;
+                *(u32x2*)(Td + off) = wd;
             }
             u32x4 pT[2], dT[2];
 #pragma unroll
             for (int g = 0; g < 2; ++g) {
-                pT[g] = *(const u32x4*)(Tp + l32 * TP + g * 16 + hh * 8);
-                dT[g] = *(const u32x4*)(Td + l32 * TP + g * 16 + hh * 8);
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int row = 16 * g + 8 * hh + 4 * half + (i16 >> 2);
+                    const int col8 = 4 * (grp & 1) + (i16 & 3);
+                    const int off = row * 32 + ((col8 ^ ((row >> 2) & 7)) << 2);
+                    const u32x2 vp = lds_read_tr16(Tp + off);
+                    const u32x2 vd = lds_read_tr16(Td + off);
+                    pT[g][2 * half] = vp[0];
+                    pT[g][2 * half + 1] = vp[1];
+                    dT[g][2 * half] = vd[0];
+                    dT[g][2 * half + 1] = vd[1];
+                }
             }
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {

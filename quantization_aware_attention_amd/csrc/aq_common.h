@@ -30,6 +30,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -118,6 +121,50 @@ __device__ __forceinline__ float e2m1_round(float r) {
     float c = __uint_as_float((__float_as_uint(t) & 0xFF800000u) + (22u << 23));
     c = fmaxf(c, 4194304.0f);
     return (t + c) - c;
+}
+
+// NVFP4 fake quantization of one 16-element group of non-negative fp32 values
+// held as 8 registers in each of lanes l and l ^ 32 (the probabilities P),
+// using the CDNA4 conversion units: the group maximum / 6 is rounded to E4M3
+// by an FP8 round trip (nearest even; values here are <= 1/6, far below the
+// 448 saturation point), p / s is rounded to E2M1 by an FP4 round trip (nearest
+// even, saturating at 6, unit scale), and the result is multiplied back by s.
+// The division is a multiplication by a reciprocal, so a tie of the exact reals
+// can be missed only by values within 2^-22 relative of a rounding midpoint.
+__device__ __forceinline__ void quant_group8_hw(float* p) {
+    float am = fmaxf(fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])),
+                     fmaxf(fmaxf(p[4], p[5]), fmaxf(p[6], p[7])));
+    am = max_lane_pair(am);
+    const i16x2 z = {0, 0};
+    const i16x2 c8 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, am * (1.0f / 6.0f), 0.0f, 1.0f,
+                                                              false);
+    const float s = __builtin_amdgcn_cvt_scalef32_f32_fp8(__builtin_bit_cast(int, c8), 1.0f, 0);
+    const float inv = (s > 0.0f) ? __builtin_amdgcn_rcpf(s) : 0.0f;
+    uint32_t codes = 0u;
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, p[0] * inv, p[1] * inv, 1.0f, 0);
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, p[2] * inv, p[3] * inv, 1.0f, 1);
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, p[4] * inv, p[5] * inv, 1.0f, 2);
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, p[6] * inv, p[7] * inv, 1.0f, 3);
+    const f32x2 q0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+    const f32x2 q1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+    const f32x2 q2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+    const f32x2 q3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+    p[0] = q0[0] * s;
+    p[1] = q0[1] * s;
+    p[2] = q1[0] * s;
+    p[3] = q1[1] * s;
+    p[4] = q2[0] * s;
+    p[5] = q2[1] * s;
+    p[6] = q3[0] * s;
+    p[7] = q3[1] * s;
+}
+
+// 16-bit transposing LDS read (ds_read_b64_tr_b16). Within each group of 16
+// lanes, lane m supplies the address of 4 consecutive 16-bit elements M[m][0..3];
+// lane i receives M[4 j + i / 4][i % 4] for j = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+    const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+    return __builtin_bit_cast(u32x2, r);
 }
 
 }  // namespace aq

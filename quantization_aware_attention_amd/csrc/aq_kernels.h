@@ -40,11 +40,11 @@ struct AttnArgs {
     const uint16_t* Qw;   // [BH][Nq_pad][D]
     const uint16_t* Kw;   // [BH][Nk_pad][D]
     const uint16_t* Vw;   // [BH][Nk_pad][D]
-    const uint16_t* Qt;   // [BH][D][Nq_pad] permuted
+    const uint16_t* Qt;   // [BH][D][Nq_pad] natural token order
     const uint16_t* Kt;   // [BH][D][Nk_pad] permuted
     const uint16_t* Vt;   // [BH][D][Nk_pad] permuted
     const uint16_t* dOw;  // [BH][Nq_pad][D]
-    const uint16_t* dOt;  // [BH][D][Nq_pad] permuted
+    const uint16_t* dOt;  // [BH][D][Nq_pad] natural token order
     const float* lse;     // forward: natural-log LSE output/input [BH][Nq]
     const float* lse2;    // backward: LSE * log2(e), [BH][Nq_pad]
     const float* delta;   // backward: [BH][Nq_pad]
@@ -74,7 +74,7 @@ struct AttnArgs {
 hipError_t launch_fq_axis_d(const FqArgs& a, bool quant, hipStream_t st);
 hipError_t launch_fq_axis_n(const FqArgs& a, bool quant, hipStream_t st);
 hipError_t launch_transpose_perm(const uint16_t* src, uint16_t* dst, int64_t BH, int Npad, int D,
-                                 hipStream_t st);
+                                 bool perm, hipStream_t st);
 hipError_t launch_bwd_pre(const PreArgs& a, hipStream_t st);
 
 hipError_t launch_fwd_lse(const AttnArgs& a, int D, hipStream_t st);

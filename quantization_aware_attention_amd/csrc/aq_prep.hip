@@ -110,9 +110,11 @@ __global__ __launch_bounds__(256) void fq_axis_n_kernel(FqArgs a) {
     }
 }
 
-// Transposed, permuted copy: dst[bh][d][p] = src[bh][tok(p)][d] for a
-// contiguous padded [BH][Npad][D] source, with tok(p) = 16 (p / 16) +
-// perm16(p % 16). Tile: 64 tokens x 64 columns per block.
+// Transposed copy: dst[bh][d][p] = src[bh][tok(p)][d] for a contiguous padded
+// [BH][Npad][D] source, with tok(p) = 16 (p / 16) + perm16(p % 16) when PERM
+// (operands read by MFMA k-slots in accumulator-row order) and tok(p) = p
+// otherwise. Tile: 64 tokens x 64 columns per block.
+template <bool PERM>
 __global__ __launch_bounds__(256) void transpose_perm_kernel(const uint16_t* __restrict__ src,
                                                              uint16_t* __restrict__ dst,
                                                              int Npad, int D) {
@@ -139,7 +141,8 @@ __global__ __launch_bounds__(256) void transpose_perm_kernel(const uint16_t* __r
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int p0 = pc * 8 + 2 * j, p1 = p0 + 1;
-            const int t0 = (p0 & ~15) + perm16(p0 & 15), t1 = (p1 & ~15) + perm16(p1 & 15);
+            const int t0 = PERM ? (p0 & ~15) + perm16(p0 & 15) : p0;
+            const int t1 = PERM ? (p1 & ~15) + perm16(p1 & 15) : p1;
             w[j] = (uint32_t)tile[t0][dr] | ((uint32_t)tile[t1][dr] << 16);
         }
         u32x4 v = {w[0], w[1], w[2], w[3]};
@@ -206,9 +209,10 @@ hipError_t launch_fq_axis_n(const FqArgs& a, bool quant, hipStream_t st) {
 }
 
 hipError_t launch_transpose_perm(const uint16_t* src, uint16_t* dst, int64_t BH, int Npad, int D,
-                                 hipStream_t st) {
+                                 bool perm, hipStream_t st) {
     dim3 grid(Npad / 64, D / 64, (unsigned)BH);
-    transpose_perm_kernel<<<grid, 256, 0, st>>>(src, dst, Npad, D);
+    if (perm) transpose_perm_kernel<true><<<grid, 256, 0, st>>>(src, dst, Npad, D);
+    else transpose_perm_kernel<false><<<grid, 256, 0, st>>>(src, dst, Npad, D);
     return hipGetLastError();
 }
 
