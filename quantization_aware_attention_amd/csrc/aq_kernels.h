@@ -6,7 +6,7 @@
 namespace aq {
 
 // Tile sizes shared by the host planner and the kernels.
-constexpr int kTileN = 128;  // token padding granularity of every workspace operand
+constexpr int kTileN = 256;  // token padding granularity of every workspace operand
 
 struct FqArgs {
     const uint16_t* x;
