@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="query rows of head 0 in the CPU-oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run one plain 1 GiB device copy (a kernel "
+                         "of known traffic for scaling HBM byte counters)")
     return ap.parse_args()
 
 
@@ -190,6 +193,14 @@ def main():
         "roofline": roof, "kernels": kernels, "input_sha256_16": hashes,
         "device": torch.cuda.get_device_name(0),
     }
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = 1 << 30
+        del src, dst
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(bits, w, args.cpu_rows, mask)

@@ -94,7 +94,8 @@ typedef struct {
      * the listed key blocks; LSE and P are taken over those keys only. */
     const int32_t* kv_block_idx;
     int32_t topk;         /* entries per row of kv_block_idx (ignored when dense) */
-    int32_t block_tokens; /* tokens per block; must be 128 when kv_block_idx != NULL */
+    int32_t block_tokens; /* tokens per block; must be 128 when kv_block_idx != NULL;
+                           * block-sparse problems have at most 1024 blocks per sequence */
 } attnqat_problem;
 
 /* ABI version of the loaded library (ATTNQAT_ABI_VERSION it was built with). */

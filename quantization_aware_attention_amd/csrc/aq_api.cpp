@@ -247,6 +247,9 @@ int validate_problem(const attnqat_problem* p, Plan& pl) {
         pl.nbk = (int)((p->Nk + 127) / 128);
         if (p->topk < 1 || p->topk > pl.nbk)
             return fail(ATTNQAT_E_INVALID, "topk %d outside [1, %d]", p->topk, pl.nbk);
+        if (pl.nbq > 1024 || pl.nbk > 1024)
+            return fail(ATTNQAT_E_UNSUPPORTED, "block-sparse attention supports at most 1024 "
+                        "blocks of 128 tokens per sequence");
         if (((uintptr_t)p->kv_block_idx) % 4)
             return fail(ATTNQAT_E_MISALIGNED, "kv_block_idx is not 4-byte aligned");
     }
