@@ -420,228 +420,253 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Backward dK, dV: 4 waves x 32 keys, loop over 64-query tiles. Pq and dS
-// (queries on lanes) are transposed through a per-wave LDS tile so that
-// queries become the contraction index of dV^T = dO^T Pq and dK^T = Q^T dS.
-//
-// One wave per SIMD fits (the dK and dV accumulators alone take 128
-// registers), so the two 32-query halves of a tile are software-pipelined
-// inside the wave: the S/dP products of half 1 run on the matrix cores while
-// the vector units turn half 0's S/dP into P, Pq and dS and transpose them,
-// and the dV/dK products of half 0 run while half 1 is processed.
-// sched_group_barrier lays the two instruction streams out interleaved.
+// Backward dV and dK: NW waves x 32 keys per workgroup, loop over 64-query
+// tiles. Scores are computed with keys on registers (S^T = K Q^T, the layout
+// in which P's 16-key groups are quantized), so P, Pq and dS have queries on
+// lanes; a per-wave LDS transpose turns them into B operands with queries as
+// the contraction index of dV^T = dO^T Pq and dK^T = Q^T dS. dV and dK run as
+// two kernels: together their per-key accumulators, K and V operands and S/dP
+// tiles do not fit two waves per SIMD, and the vector work (exp, quantization,
+// transposes) only overlaps the matrix work when two waves share a SIMD.
 
-// MFMA issue pattern for a region: N x {1 MFMA, R LDS reads, V VALU}.
-template <int N, int R, int V>
-__device__ __forceinline__ void interleave_mfma() {
+// Transpose a 32 x 32 tile held as accumulator-layout values (lane = query
+// l32, registers r -> key acc_row(r, hh)) into two B operands with keys on
+// lanes and queries 16 g + 8 hh + j on the k-slots. Row = query, 64 bytes per
+// row; 8-byte column chunks are XOR-swizzled by (row / 4) % 8 so that the
+// row writes and the transposing column reads avoid bank conflicts.
+__device__ __forceinline__ void transpose_tile(const float* v, uint16_t* T, u32x4* out, int lane) {
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int wsw = (l32 >> 2) & 7;
+    const int grp = lane >> 4, i16 = lane & 15;
 #pragma unroll
-    for (int i = 0; i < N; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (R) __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+    for (int a4 = 0; a4 < 4; ++a4) {
+        const int off = l32 * 32 + (((2 * a4 + hh) ^ wsw) << 2);
+        u32x2 w;
+        w[0] = pack_rne(v[4 * a4], v[4 * a4 + 1]);
+        w[1] = pack_rne(v[4 * a4 + 2], v[4 * a4 + 3]);
+        *(u32x2*)(T + off) = w;
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int trow = 16 * g + 8 * hh + 4 * half + (i16 >> 2);
+            const int col8 = 4 * (grp & 1) + (i16 & 3);
+            const int off = trow * 32 + ((col8 ^ ((trow >> 2) & 7)) << 2);
+            const u32x2 r = lds_read_tr16(T + off);
+            out[g][2 * half] = r[0];
+            out[g][2 * half + 1] = r[1];
+        }
     }
 }
 
-template <int D, bool QP, bool TAILK>
-struct BwdDkdv {
+template <int D, bool QP>
+struct BwdDv {
     static constexpr int BM = 64;
-
-    // S^T and dP^T for the 32 queries of half qb (16 MFMAs).
-    __device__ static void sdp(const uint16_t* sQ, const uint16_t* sdO, int qb, const u32x4* kf,
-                               const u32x4* vf, f32x16& s, f32x16& dp, int l32, int hh) {
-        s = f32x16{};
-        dp = f32x16{};
-        const int row = qb * 32 + l32;
-#pragma unroll
-        for (int cc = 0; cc < D / 16; ++cc) {
-            const u32x4 qv = *(const u32x4*)(sQ + toff<D>(row, 2 * cc + hh));
-            s = mfma(kf[cc], qv, s);
-            const u32x4 dv = *(const u32x4*)(sdO + toff<D>(row, 2 * cc + hh));
-            dp = mfma(vf[cc], dv, dp);
-        }
-        // the vector units read S and dP next: accumulate them in vector registers
-        asm volatile("" : "+v"(s));
-        asm volatile("" : "+v"(dp));
-    }
-
-    // P, Pq, dS of half qb and their transposes (keys on lanes) as B operands.
-    __device__ static void valu(const f32x16& s, const f32x16& dp, const float* sL,
-                                const float* sDl, int qb, uint16_t* Tp, uint16_t* Td, int k0,
-                                int Nk, float c, u32x4* pT, u32x4* dT, int lane) {
+    template <bool TAILK>
+    __device__ static void block(const uint16_t* sQ, const uint16_t* sdOt, const float* sL,
+                                 uint16_t* T, int k0, int Nk, const u32x4* kf, float c, f32x16* dva,
+                                 int lane) {
         const int l32 = lane & 31, hh = lane >> 5;
-        const int wsw = (l32 >> 2) & 7;
-        const int grp = lane >> 4, i16 = lane & 15;
-        const int row = qb * 32 + l32;
-        const float L = sL[row];
-        const float Dl = sDl[row];
-        float p[16], ds[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -L));
-            if (TAILK && k0 + acc_row(r, hh) >= Nk) p[r] = 0.0f;
-            ds[r] = p[r] * (dp[r] - Dl);
-        }
-        if (QP) {
-            quant_group8_hw(p);
-            quant_group8_hw(p + 8);
-        }
-        // Transpose through LDS: row = query (l32), keys 8a + 4hh .. + 3 from
-        // registers 4a .. 4a + 3; 8-byte column chunks XOR-swizzled by
-        // (row / 4) % 8 so that the row writes and the transposing column
-        // reads avoid bank conflicts.
+        for (int qb = 0; qb < BM / 32; ++qb) {
+            const int row = qb * 32 + l32;
+            f32x16 s = {};
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-            const int off = l32 * 32 + (((2 * a4 + hh) ^ wsw) << 2);
-            u32x2 wp, wd;
-            wp[0] = pack_rne(p[4 * a4], p[4 * a4 + 1]);
-            wp[1] = pack_rne(p[4 * a4 + 2], p[4 * a4 + 3]);
-            wd[0] = pack_rne(ds[4 * a4], ds[4 * a4 + 1]);
-            wd[1] = pack_rne(ds[4 * a4 + 2], ds[4 * a4 + 3]);
-            *(u32x2*)(Tp + off) = wp;
-            *(u32x2*)(Td + off) = wd;
-        }
+            for (int cc = 0; cc < D / 16; ++cc)
+                s = mfma(kf[cc], *(const u32x4*)(sQ + toff<D>(row, 2 * cc + hh)), s);
+            const float L = sL[row];
+            float p[16];
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
+            for (int r = 0; r < 16; ++r) {
+                p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -L));
+                if (TAILK && k0 + acc_row(r, hh) >= Nk) p[r] = 0.0f;
+            }
+            if (QP) {
+                quant_group8_hw(p);
+                quant_group8_hw(p + 8);
+            }
+            u32x4 pT[2];
+            transpose_tile(p, T, pT, lane);
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int trow = 16 * g + 8 * hh + 4 * half + (i16 >> 2);
-                const int col8 = 4 * (grp & 1) + (i16 & 3);
-                const int off = trow * 32 + ((col8 ^ ((trow >> 2) & 7)) << 2);
-                const u32x2 vp = lds_read_tr16(Tp + off);
-                const u32x2 vd = lds_read_tr16(Td + off);
-                pT[g][2 * half] = vp[0];
-                pT[g][2 * half + 1] = vp[1];
-                dT[g][2 * half] = vd[0];
-                dT[g][2 * half + 1] = vd[1];
+            for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    const int off = toff<BM>(db * 32 + l32, 4 * qb + 2 * g + hh);
+                    dva[db] = mfma(*(const u32x4*)(sdOt + off), pT[g], dva[db]);
+                }
             }
         }
-    }
-
-    // dV^T += dO^T Pq and dK^T += Q^T dS for half qb (16 MFMAs).
-    __device__ static void dvdk(const uint16_t* sQt, const uint16_t* sdOt, int qb,
-                                const u32x4* pT, const u32x4* dT, f32x16* dka, f32x16* dva,
-                                int l32, int hh) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-            for (int g = 0; g < 2; ++g) {
-                const int off = toff<BM>(db * 32 + l32, 4 * qb + 2 * g + hh);
-                dva[db] = mfma(*(const u32x4*)(sdOt + off), pT[g], dva[db]);
-                dka[db] = mfma(*(const u32x4*)(sQt + off), dT[g], dka[db]);
-            }
-        }
-    }
-
-    __device__ static void block(const uint16_t* sQ, const uint16_t* sdO, const uint16_t* sQt,
-                                 const uint16_t* sdOt, const float* sL, const float* sDl,
-                                 uint16_t* Tp, uint16_t* Td, int k0, int Nk, const u32x4* kf,
-                                 const u32x4* vf, float c, f32x16* dka, f32x16* dva, int lane) {
-        const int l32 = lane & 31, hh = lane >> 5;
-        f32x16 s0, dp0, s1, dp1;
-        u32x4 pT0[2], dT0[2], pT1[2], dT1[2];
-        sdp(sQ, sdO, 0, kf, vf, s0, dp0, l32, hh);
-        __builtin_amdgcn_sched_barrier(0);
-        sdp(sQ, sdO, 1, kf, vf, s1, dp1, l32, hh);
-        valu(s0, dp0, sL, sDl, 0, Tp, Td, k0, Nk, c, pT0, dT0, lane);
-        interleave_mfma<2 * D / 16, 0, 8>();
-        __builtin_amdgcn_sched_barrier(0);
-        dvdk(sQt, sdOt, 0, pT0, dT0, dka, dva, l32, hh);
-        valu(s1, dp1, sL, sDl, 1, Tp, Td, k0, Nk, c, pT1, dT1, lane);
-        interleave_mfma<D / 8, 0, 8>();
-        __builtin_amdgcn_sched_barrier(0);
-        dvdk(sQt, sdOt, 1, pT1, dT1, dka, dva, l32, hh);
-        __builtin_amdgcn_sched_barrier(0);
     }
 };
 
-// LDS of the dK/dV kernel: double-buffered Q, dO, Q^T, dO^T tiles, the two
-// statistics rows, and the per-wave transpose tiles.
 template <int D>
-struct DkdvLds {
+struct BwdDk {
     static constexpr int BM = 64;
-    uint16_t q[2][BM * D], o[2][BM * D], qt[2][D * BM], ot[2][D * BM];
-    uint16_t t[4 * 2 * 32 * 32];
-    float l[2][BM], d[2][BM];
-    int lst[kMaxBlockList];
+    template <bool TAILK>
+    __device__ static void block(const uint16_t* sQ, const uint16_t* sdO, const uint16_t* sQt,
+                                 const float* sL, const float* sDl, uint16_t* T, int k0, int Nk,
+                                 const u32x4* kf, const u32x4* vf, float c, f32x16* dka,
+                                 int lane) {
+        const int l32 = lane & 31, hh = lane >> 5;
+#pragma unroll
+        for (int qb = 0; qb < BM / 32; ++qb) {
+            const int row = qb * 32 + l32;
+            f32x16 s = {}, dp = {};
+#pragma unroll
+            for (int cc = 0; cc < D / 16; ++cc) {
+                s = mfma(kf[cc], *(const u32x4*)(sQ + toff<D>(row, 2 * cc + hh)), s);
+                dp = mfma(vf[cc], *(const u32x4*)(sdO + toff<D>(row, 2 * cc + hh)), dp);
+            }
+            const float L = sL[row];
+            const float Dl = sDl[row];
+            float ds[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -L));
+                if (TAILK && k0 + acc_row(r, hh) >= Nk) p = 0.0f;
+                ds[r] = p * (dp[r] - Dl);
+            }
+            u32x4 dT[2];
+            transpose_tile(ds, T, dT, lane);
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    const int off = toff<BM>(db * 32 + l32, 4 * qb + 2 * g + hh);
+                    dka[db] = mfma(*(const u32x4*)(sQt + off), dT[g], dka[db]);
+                }
+            }
+        }
+    }
 };
 
-template <int D, bool QP, bool TAILK, bool SPARSE>
-__device__ __forceinline__ void dkdv_loop(const AttnArgs& a, DkdvLds<D>& S, int bh, int kblk,
-                                          f32x16* dka, f32x16* dva) {
-    constexpr int BM = DkdvLds<D>::BM;
+// Per-lane K (and V) A-operand fragments of this wave's 32 keys.
+template <int D>
+__device__ __forceinline__ void load_key_frags(const uint16_t* X, int bh, int Nk_pad, int k0, int l32,
+                                               int hh, u32x4* f) {
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+        f[c] = *(const u32x4*)(X + ((size_t)bh * Nk_pad + k0 + l32) * D + c * 16 + hh * 8);
+}
+
+// Query-tile visiting order of a key workgroup: every 64-query tile (dense) or
+// the tiles of the query blocks that selected this key block (sparse, staged).
+template <bool SPARSE>
+__device__ __forceinline__ int query_tiles(const AttnArgs& a, int bh, int kblk, int* lst) {
+    if (!SPARSE) return (a.Nq + 63) / 64;
+    const int cnt = a.q_count[(size_t)bh * a.nbk + kblk];
+    stage_list(lst, a.q_list + ((size_t)bh * a.nbk + kblk) * a.nbq, cnt);
+    return 2 * cnt;
+}
+
+template <int D, bool QP, int NW, bool SPARSE>
+__global__ __launch_bounds__(NW * 64) void bwd_dv_kernel(AttnArgs a) {
+    constexpr int BM = 64, NT = NW * 64, KW = NW * 32;
+    static_assert(!SPARSE || NW == 4, "sparse key workgroups cover one key block");
+    __shared__ __attribute__((aligned(1024))) uint16_t sQ[2][BM * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t sOt[2][D * BM];
+    __shared__ __attribute__((aligned(1024))) uint16_t sT[NW][32 * 32];
+    __shared__ __attribute__((aligned(256))) float sL[2][BM];
+    __shared__ int lst[SPARSE ? kMaxBlockList : 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
-    const int k0 = kblk * 128 + wave * 32;
+    const int bh = blockIdx.y, kblk = blockIdx.x;
+    const int k0 = kblk * KW + wave * 32;
+    const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
+    const uint16_t* dOtb = a.dOt + (size_t)bh * D * a.Nq_pad;
+    const float* Lb = a.lse2 + (size_t)bh * a.Nq_pad;
+    u32x4 kf[D / 16];
+    load_key_frags<D>(a.Kw, bh, a.Nk_pad, k0, l32, hh, kf);
+    f32x16 dva[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) dva[db] = f32x16{};
+    const int n_iter = query_tiles<SPARSE>(a, bh, kblk, lst);
+    if (n_iter > 0) {
+        AsyncTile<BM, D, NT> tr;
+        AsyncTile<D, BM, NT> tc;
+        tr.init(D, tid);
+        tc.init(a.Nq_pad, tid);
+        auto issue = [&](int buf, int it) {
+            const int qt = tile_start<SPARSE, BM>(lst, it);
+            tr.issue(sQ[buf], Qb + (size_t)qt * D);
+            tc.issue(sOt[buf], dOtb + qt);
+            if (wave == 0) async_f32x64(sL[buf], Lb + qt, lane);
+        };
+        // keys beyond Nk exist only in the last key workgroup: mask them there only
+        if (kblk * KW + KW > a.Nk)
+            tile_pipeline(n_iter, false, issue, [&](int buf, int, auto) {
+                BwdDv<D, QP>::template block<true>(sQ[buf], sOt[buf], sL[buf], sT[wave], k0, a.Nk, kf,
+                                                   a.c, dva, lane);
+            });
+        else
+            tile_pipeline(n_iter, false, issue, [&](int buf, int, auto) {
+                BwdDv<D, QP>::template block<false>(sQ[buf], sOt[buf], sL[buf], sT[wave], k0, a.Nk,
+                                                    kf, a.c, dva, lane);
+            });
+    }
+    const int key = k0 + l32;
+    if (key < a.Nk) {
+        const int64_t b = bh / a.H, h = bh % a.H;
+        store_rows_T<D>(a.dv + b * a.dvsb + h * a.dvsh + (int64_t)key * a.dvsn, dva, 1.0f, hh);
+    }
+}
+
+template <int D, int NW, bool SPARSE>
+__global__ __launch_bounds__(NW * 64) void bwd_dk_kernel(AttnArgs a) {
+    constexpr int BM = 64, NT = NW * 64, KW = NW * 32;
+    static_assert(!SPARSE || NW == 4, "sparse key workgroups cover one key block");
+    __shared__ __attribute__((aligned(1024))) uint16_t sQ[2][BM * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t sO[2][BM * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t sQt[2][D * BM];
+    __shared__ __attribute__((aligned(1024))) uint16_t sT[NW][32 * 32];
+    __shared__ __attribute__((aligned(256))) float sL[2][BM], sD[2][BM];
+    __shared__ int lst[SPARSE ? kMaxBlockList : 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int bh = blockIdx.y, kblk = blockIdx.x;
+    const int k0 = kblk * KW + wave * 32;
     const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
     const uint16_t* dOb = a.dOw + (size_t)bh * a.Nq_pad * D;
     const uint16_t* Qtb = a.Qt + (size_t)bh * D * a.Nq_pad;
-    const uint16_t* dOtb = a.dOt + (size_t)bh * D * a.Nq_pad;
     const float* Lb = a.lse2 + (size_t)bh * a.Nq_pad;
     const float* Db = a.delta + (size_t)bh * a.Nq_pad;
     u32x4 kf[D / 16], vf[D / 16];
+    load_key_frags<D>(a.Kw, bh, a.Nk_pad, k0, l32, hh, kf);
+    load_key_frags<D>(a.Vw, bh, a.Nk_pad, k0, l32, hh, vf);
+    f32x16 dka[D / 32];
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-        kf[c] = *(const u32x4*)(a.Kw + ((size_t)bh * a.Nk_pad + k0 + l32) * D + c * 16 + hh * 8);
-        vf[c] = *(const u32x4*)(a.Vw + ((size_t)bh * a.Nk_pad + k0 + l32) * D + c * 16 + hh * 8);
-        // Keep the K/V operands in accumulation registers (MFMA reads its A
-        // operand from there) so that the vector registers stay free for the
-        // S, dP, P and dS values the vector units work on.
-        asm volatile("" : "+a"(kf[c]));
-        asm volatile("" : "+a"(vf[c]));
+    for (int db = 0; db < D / 32; ++db) dka[db] = f32x16{};
+    const int n_iter = query_tiles<SPARSE>(a, bh, kblk, lst);
+    if (n_iter > 0) {
+        AsyncTile<BM, D, NT> tr;
+        AsyncTile<D, BM, NT> tc;
+        tr.init(D, tid);
+        tc.init(a.Nq_pad, tid);
+        auto issue = [&](int buf, int it) {
+            const int qt = tile_start<SPARSE, BM>(lst, it);
+            tr.issue(sQ[buf], Qb + (size_t)qt * D);
+            tr.issue(sO[buf], dOb + (size_t)qt * D);
+            tc.issue(sQt[buf], Qtb + qt);
+            if (wave == 0) async_f32x64(sL[buf], Lb + qt, lane);
+            if (wave == 1) async_f32x64(sD[buf], Db + qt, lane);
+        };
+        if (kblk * KW + KW > a.Nk)
+            tile_pipeline(n_iter, false, issue, [&](int buf, int, auto) {
+                BwdDk<D>::template block<true>(sQ[buf], sO[buf], sQt[buf], sL[buf], sD[buf],
+                                               sT[wave], k0, a.Nk, kf, vf, a.c, dka, lane);
+            });
+        else
+            tile_pipeline(n_iter, false, issue, [&](int buf, int, auto) {
+                BwdDk<D>::template block<false>(sQ[buf], sO[buf], sQt[buf], sL[buf], sD[buf],
+                                                sT[wave], k0, a.Nk, kf, vf, a.c, dka, lane);
+            });
     }
-    int n_iter = (a.Nq + BM - 1) / BM;
-    if (SPARSE) {
-        const int cnt = a.q_count[(size_t)bh * a.nbk + kblk];
-        stage_list(S.lst, a.q_list + ((size_t)bh * a.nbk + kblk) * a.nbq, cnt);
-        n_iter = 2 * cnt;
-    }
-    if (n_iter == 0) return;
-    auto tile_at = [&](int it) { return tile_start<SPARSE, BM>(S.lst, it); };
-    AsyncTile<BM, D, 256> tr;
-    AsyncTile<D, BM, 256> tc;
-    tr.init(D, tid);
-    tc.init(a.Nq_pad, tid);
-    auto issue = [&](int buf, int qt) {
-        tr.issue(S.q[buf], Qb + (size_t)qt * D);
-        tr.issue(S.o[buf], dOb + (size_t)qt * D);
-        tc.issue(S.qt[buf], Qtb + qt);
-        tc.issue(S.ot[buf], dOtb + qt);
-        if (wave == 0) async_f32x64(S.l[buf], Lb + qt, lane);
-        if (wave == 1) async_f32x64(S.d[buf], Db + qt, lane);
-    };
-    uint16_t* Tp = S.t + wave * 2048;
-    uint16_t* Td = Tp + 1024;
-    issue(0, tile_at(0));
-    for (int it = 0; it < n_iter; ++it) {
-        const int cur = it & 1;
-        wait_async();
-        __syncthreads();
-        if (it + 1 < n_iter) issue(cur ^ 1, tile_at(it + 1));
-        BwdDkdv<D, QP, TAILK>::block(S.q[cur], S.o[cur], S.qt[cur], S.ot[cur], S.l[cur],
-                                     S.d[cur], Tp, Td, k0, a.Nk, kf, vf, a.c, dka, dva, lane);
-    }
-}
-
-template <int D, bool QP, bool SPARSE>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(1024))) DkdvLds<D> S;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int hh = lane >> 5, l32 = lane & 31;
-    const int bh = blockIdx.y, kblk = blockIdx.x;
-    f32x16 dka[D / 32], dva[D / 32];
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-        dka[db] = f32x16{};
-        dva[db] = f32x16{};
-    }
-    // keys beyond Nk exist only in the last key block: mask them there only
-    if (kblk * 128 + 128 > a.Nk) dkdv_loop<D, QP, true, SPARSE>(a, S, bh, kblk, dka, dva);
-    else dkdv_loop<D, QP, false, SPARSE>(a, S, bh, kblk, dka, dva);
-    const int key = kblk * 128 + wave * 32 + l32;
+    const int key = k0 + l32;
     if (key < a.Nk) {
         const int64_t b = bh / a.H, h = bh % a.H;
-        store_rows_T<D>(a.dk + b * a.dksb + h * a.dksh + (int64_t)key * a.dksn, dka, a.sm_scale, hh);
-        store_rows_T<D>(a.dv + b * a.dvsb + h * a.dvsh + (int64_t)key * a.dvsn, dva, 1.0f, hh);
+        store_rows_T<D>(a.dk + b * a.dksb + h * a.dksh + (int64_t)key * a.dksn, dka, a.sm_scale,
+                        hh);
     }
 }
 
@@ -691,22 +716,36 @@ hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int D, bool QP, bool SP>
-static void dkdv_go(const AttnArgs& a, dim3 g, hipStream_t st) {
-    bwd_dkdv_kernel<D, QP, SP><<<g, 256, 0, st>>>(a);
+template <int D>
+static void dv_d(const AttnArgs& a, bool sp, hipStream_t st) {
+    if (sp) {
+        dim3 g(a.nbk, a.BH);
+        if (a.quant_p) bwd_dv_kernel<D, true, 4, true><<<g, 256, 0, st>>>(a);
+        else bwd_dv_kernel<D, false, 4, true><<<g, 256, 0, st>>>(a);
+    } else {
+        dim3 g((a.Nk + 255) / 256, a.BH);
+        if (a.quant_p) bwd_dv_kernel<D, true, 8, false><<<g, 512, 0, st>>>(a);
+        else bwd_dv_kernel<D, false, 8, false><<<g, 512, 0, st>>>(a);
+    }
 }
 
 template <int D>
-static void dkdv_d(const AttnArgs& a, dim3 g, bool sp, hipStream_t st) {
-    if (a.quant_p) sp ? dkdv_go<D, true, true>(a, g, st) : dkdv_go<D, true, false>(a, g, st);
-    else sp ? dkdv_go<D, false, true>(a, g, st) : dkdv_go<D, false, false>(a, g, st);
+static void dk_d(const AttnArgs& a, bool sp, hipStream_t st) {
+    if (sp) bwd_dk_kernel<D, 4, true><<<dim3(a.nbk, a.BH), 256, 0, st>>>(a);
+    else bwd_dk_kernel<D, 8, false><<<dim3((a.Nk + 255) / 256, a.BH), 512, 0, st>>>(a);
 }
 
-hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t st) {
-    dim3 grid((a.Nk + 127) / 128, a.BH);
+hipError_t launch_bwd_dv(const AttnArgs& a, int D, hipStream_t st) {
     const bool sp = a.q_list != nullptr;
-    if (D == 128) dkdv_d<128>(a, grid, sp, st);
-    else dkdv_d<64>(a, grid, sp, st);
+    if (D == 128) dv_d<128>(a, sp, st);
+    else dv_d<64>(a, sp, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dk(const AttnArgs& a, int D, hipStream_t st) {
+    const bool sp = a.q_list != nullptr;
+    if (D == 128) dk_d<128>(a, sp, st);
+    else dk_d<64>(a, sp, st);
     return hipGetLastError();
 }
 

@@ -166,8 +166,8 @@ def test_profile_read_empty(L):
 
 
 def test_workspace_sizes_scale_with_problem(L):
-    a = L.attnqat_fwd_workspace_bytes(ctypes.byref(_prob(Nq=128, Nk=128)))
-    b = L.attnqat_fwd_workspace_bytes(ctypes.byref(_prob(Nq=256, Nk=256)))
+    a = L.attnqat_fwd_workspace_bytes(ctypes.byref(_prob(Nq=256, Nk=256)))
+    b = L.attnqat_fwd_workspace_bytes(ctypes.byref(_prob(Nq=512, Nk=512)))
     assert b > a > 0 and a % 256 == 0 and b % 256 == 0
 
 
