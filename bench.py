@@ -17,6 +17,7 @@ bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -38,6 +39,49 @@ METRIC = "Attn-QAT fwd+bwd ms & TFLOP/s (% BF16 MFMA peak), H=6 N=31200 d=128"
 # recomputes S for the statistics). EXEC counts the products each kernel runs.
 ALGO_PER_PAIR = {"fwd_out": 4, "bwd_dv": 4, "bwd_dk": 4, "bwd_dq": 2, "fwd_lse": 0}
 EXEC_PER_PAIR = {"fwd_out": 4, "bwd_dv": 4, "bwd_dk": 6, "bwd_dq": 6, "fwd_lse": 2}
+# Algorithmic HBM bytes per launch of the memory-bound kernels (square
+# problems): fake quantization and the transposed copies read and write each
+# bf16 element once (4 B); the preprocess reads O and dO and writes D (4 d + 4
+# B per query row).
+ALGO_BYTES = {
+    "fq_axis_d": lambda bh, n, d: 4 * bh * n * d,
+    "fq_axis_n": lambda bh, n, d: 4 * bh * n * d,
+    "transpose_perm": lambda bh, n, d: 4 * bh * n * d,
+    "bwd_pre": lambda bh, n, d: (4 * d + 4) * bh * n,
+}
+
+
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash():
+    """Hash of the kernel and library sources, to tie counter summaries to the
+    code they were taken from."""
+    d = os.path.join(ROOT, "quantization_aware_attention_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(name.encode())
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, quant, kernel, src_hash):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE/WRITE_SIZE
+    summary of this workload, or None when there is none or the sources have
+    changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"attn_step_{workload}_hbm_bytes.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = [json.loads(line[6:]) for line in f if line.startswith("json: ")]
+    if not rec:
+        return None
+    rec = rec[-1]
+    if rec.get("kernel_source_sha256_16") != src_hash or rec.get("quant") != quant:
+        return None
+    return rec.get("bytes_per_launch", {}).get(kernel)
 
 
 def parse():
@@ -162,22 +206,27 @@ def main():
         avg = tot / cnt
         e = {"ms_per_launch": round(avg, 4), "launches_per_step": cnt / args.steps,
              "ms_per_step": round(tot / args.steps, 4)}
+        if name in ALGO_BYTES:
+            nbytes = ALGO_BYTES[name](B * H, N, D)
+            e["algo_gbs"] = round(nbytes / (avg * 1e-3) / 1e9, 1)
         if name in EXEC_PER_PAIR:
             e["exec_tflops"] = round(EXEC_PER_PAIR[name] * pairs * D / (avg * 1e-3) / 1e12, 1)
             e["algo_tflops"] = round(ALGO_PER_PAIR[name] * pairs * D / (avg * 1e-3) / 1e12, 1)
         kernels[name] = e
     dom = max(kern.items(), key=lambda kv: kv[1][0])[0]
     dom_avg = kern[dom][0] / kern[dom][1]
+    src_hash = kernel_source_hash()
+    traffic = measured_traffic(w.name, args.quant, dom, src_hash)
     if dom in ALGO_PER_PAIR:
         achieved = ALGO_PER_PAIR[dom] * pairs * D / (dom_avg * 1e-3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "ms_per_launch": round(dom_avg, 4),
                 "algo_flops_per_launch": ALGO_PER_PAIR[dom] * pairs * D}
     else:
         roof = {"kernel": dom, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": None, "traffic": None, "ms_per_launch": round(dom_avg, 4)}
+                "unit": "GB/s", "frac": None, "traffic": traffic, "ms_per_launch": round(dom_avg, 4)}
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -192,8 +241,28 @@ def main():
         "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 1),
         "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": roof, "kernels": kernels, "input_sha256_16": hashes,
+        "kernel_source_sha256_16": src_hash,
         "device": torch.cuda.get_device_name(0),
     }
+    # Standalone fake quantization of one input (HBM-bound): 4 bytes per
+    # element (2 read, 2 written), along d (Q's layout) and along tokens (V's).
+    fq_out = torch.empty_like(q)
+    fq = {}
+    for axis, x in (("d", q), ("n", v)):
+        for _ in range(2):
+            qaa.fakequant(x, axis, out=fq_out)
+        torch.cuda.synchronize()
+        qaa.profile_enable(True)
+        for _ in range(20):
+            qaa.fakequant(x, axis, out=fq_out)
+        torch.cuda.synchronize()
+        (tot, cnt), = qaa.profile_read().values()
+        qaa.profile_enable(False)
+        ms = tot / cnt
+        gbs = 4.0 * x.numel() / (ms * 1e-3) / 1e9
+        fq[f"axis_{axis}"] = {"ms_per_launch": round(ms, 4), "algo_gbs": round(gbs, 1),
+                              "frac_hbm": round(gbs / PEAK_HBM_GBS, 3)}
+    out["fakequant_standalone"] = fq
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)

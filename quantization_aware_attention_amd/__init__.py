@@ -176,13 +176,18 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
-def fakequant(x: torch.Tensor, axis: str = "d", return_scale_codes: bool = False, stream=None):
+def fakequant(x: torch.Tensor, axis: str = "d", return_scale_codes: bool = False, stream=None,
+              out=None):
     """NVFP4 fake quantization of a bf16 [B,H,N,D] tensor along 'd' or 'n'."""
     L = load()
     _check4("x", x)
     B, H, N, D = x.shape
     ax = AXIS_D if axis == "d" else AXIS_N
-    y = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=x.device)
+    y = out if out is not None else torch.empty((B, H, N, D), dtype=torch.bfloat16,
+                                                device=x.device)
+    _check4("out", y)
+    if tuple(y.shape) != (B, H, N, D):
+        raise ValueError("out must have the shape of x")
     codes = None
     if return_scale_codes:
         shp = (B, H, N, D // 16) if ax == AXIS_D else (B, H, (N + 15) // 16, D)

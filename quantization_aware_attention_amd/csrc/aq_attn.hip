@@ -165,6 +165,37 @@ __device__ __forceinline__ f32x16 scores_T(const uint16_t* sK, int kr0, const u3
     return acc;
 }
 
+// Issue order for a chain of N MFMAs that each take one operand from LDS:
+// PRE reads first, then one MFMA per further read, so every operand is
+// requested PRE MFMAs (PRE x 32 cycles) before its use. Ends the scheduling
+// region.
+template <int N, int PRE>
+__device__ __forceinline__ void lds_mfma_chain() {
+    __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
+#pragma unroll
+    for (int i = 0; i < N - PRE; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, PRE, 0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// As lds_mfma_chain, with V vector instructions issued after each MFMA, so
+// that independent vector work fills the matrix core's busy cycles.
+constexpr int kValuPerMfma = 8;
+template <int N, int PRE, int V>
+__device__ __forceinline__ void mfma_valu_chain() {
+    __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < N - PRE) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---------------------------------------------------------------------------
 // Forward pass 1: LSE per query row. 4 waves x 32 queries, 64-key tiles.
 template <int D>
@@ -194,14 +225,15 @@ struct FwdLse {
     }
 };
 
-template <int D, bool SPARSE>
-__global__ __launch_bounds__(256) void fwd_lse_kernel(AttnArgs a) {
+template <int D, int NW, bool SPARSE>
+__global__ __launch_bounds__(NW * 64) void fwd_lse_kernel(AttnArgs a) {
     constexpr int BN = FwdLse<D>::BN;
+    static_assert(!SPARSE || NW == 4, "sparse workgroups cover one 128-query block");
     __shared__ __attribute__((aligned(1024))) uint16_t sK[2][BN * D];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
     const int bh = blockIdx.y, qblk = blockIdx.x;
-    const int q0 = qblk * 128 + wave * 32;
+    const int q0 = qblk * (NW * 32) + wave * 32;
     const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
     const uint16_t* Kb = a.Kw + (size_t)bh * a.Nk_pad * D;
     u32x4 qf[D / 16];
@@ -213,7 +245,7 @@ __global__ __launch_bounds__(256) void fwd_lse_kernel(AttnArgs a) {
     const int n_iter = SPARSE ? a.topk * 2 : (a.Nk + BN - 1) / BN;
     auto tile_at = [&](int it) { return tile_start<SPARSE, BN>(lst, it); };
     float m = kNegBig, l = 0.0f;
-    AsyncTile<BN, D, 256> tk;
+    AsyncTile<BN, D, NW * 64> tk;
     tk.init(D, tid);
     tile_pipeline(
         n_iter, tile_at(n_iter - 1) + BN > a.Nk,
@@ -235,50 +267,72 @@ __global__ __launch_bounds__(256) void fwd_lse_kernel(AttnArgs a) {
 template <int D, bool QP>
 struct FwdOut {
     static constexpr int BN = 64;
+
+    // P (or its quantization) of one 32-key score block as two B operands.
     template <bool tail>
-    __device__ static void block(const uint16_t* sK, const uint16_t* sV, int kt, int Nk,
-                                 const u32x4* qf, float c, float lse2, f32x16* o, int l32, int hh) {
+    __device__ static void probs(const f32x16& acc, int k0, int Nk, float c, float lse2, int hh,
+                                 u32x4* bfr) {
+        float p[16];
 #pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
-            const f32x16 acc = scores_T<D>(sK, kb * 32, qf, l32, hh);
-            float p[16];
+        for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], c, -lse2));
+        if (tail) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], c, -lse2));
-            if (tail) {
+            for (int r = 0; r < 16; ++r)
+                if (k0 + acc_row(r, hh) >= Nk) p[r] = 0.0f;
+        }
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (kt + kb * 32 + acc_row(r, hh) >= Nk) p[r] = 0.0f;
-            }
-            u32x4 bfr[2];
+        for (int g = 0; g < 2; ++g) {
+            float* pg = p + 8 * g;
+            if (QP) quant_group8_hw(pg);
+            bfr[g] = u32x4{pack_rne(pg[0], pg[1]), pack_rne(pg[2], pg[3]), pack_rne(pg[4], pg[5]),
+                           pack_rne(pg[6], pg[7])};
+        }
+    }
+
+    // O^T += V^T P^T for key block kb (D / 16 MFMAs, one LDS read each).
+    __device__ static void pv(const uint16_t* sV, int kb, const u32x4* bfr, f32x16* o, int l32,
+                              int hh) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
             for (int g = 0; g < 2; ++g) {
-                float* pg = p + 8 * g;
-                if (QP) quant_group8_hw(pg);
-                bfr[g] = u32x4{pack_rne(pg[0], pg[1]), pack_rne(pg[2], pg[3]),
-                               pack_rne(pg[4], pg[5]), pack_rne(pg[6], pg[7])};
-            }
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    const u32x4 vf =
-                        *(const u32x4*)(sV + toff<BN>(db * 32 + l32, 4 * kb + 2 * g + hh));
-                    o[db] = mfma(vf, bfr[g], o[db]);
-                }
+                const u32x4 vf = *(const u32x4*)(sV + toff<BN>(db * 32 + l32, 4 * kb + 2 * g + hh));
+                o[db] = mfma(vf, bfr[g], o[db]);
             }
         }
     }
+
+    // Two 32-key blocks, software-pipelined so that the vector work on one
+    // block (exp, quantization, packing) is issued between the matrix
+    // products of the other:
+    //   S0 | S1 + P(S0) | PV0 + P(S1) | PV1.
+    template <bool tail>
+    __device__ static void block(const uint16_t* sK, const uint16_t* sV, int kt, int Nk,
+                                 const u32x4* qf, float c, float lse2, f32x16* o, int l32, int hh) {
+        const f32x16 s0 = scores_T<D>(sK, 0, qf, l32, hh);
+        lds_mfma_chain<D / 16, 4>();
+        const f32x16 s1 = scores_T<D>(sK, 32, qf, l32, hh);
+        u32x4 b0[2], b1[2];
+        probs<tail>(s0, kt, Nk, c, lse2, hh, b0);
+        mfma_valu_chain<D / 16, 4, kValuPerMfma>();
+        pv(sV, 0, b0, o, l32, hh);
+        probs<tail>(s1, kt + 32, Nk, c, lse2, hh, b1);
+        mfma_valu_chain<D / 16, 4, kValuPerMfma>();
+        pv(sV, 1, b1, o, l32, hh);
+        lds_mfma_chain<D / 16, 4>();
+    }
 };
 
-template <int D, bool QP, bool SPARSE>
-__global__ __launch_bounds__(256, 2) void fwd_out_kernel(AttnArgs a) {
+template <int D, bool QP, int NW, bool SPARSE>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_out_kernel(AttnArgs a) {
     constexpr int BN = FwdOut<D, QP>::BN;
+    static_assert(!SPARSE || NW == 4, "sparse workgroups cover one 128-query block");
     __shared__ __attribute__((aligned(1024))) uint16_t sK[2][BN * D];
     __shared__ __attribute__((aligned(1024))) uint16_t sV[2][D * BN];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
     const int bh = blockIdx.y, qblk = blockIdx.x;
-    const int q0 = qblk * 128 + wave * 32;
+    const int q0 = qblk * (NW * 32) + wave * 32;
     const int q = q0 + l32;
     const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
     const uint16_t* Kb = a.Kw + (size_t)bh * a.Nk_pad * D;
@@ -295,8 +349,8 @@ __global__ __launch_bounds__(256, 2) void fwd_out_kernel(AttnArgs a) {
     if (SPARSE) stage_list(lst, a.kv_idx + ((size_t)bh * a.nbq + qblk) * a.topk, a.topk);
     const int n_iter = SPARSE ? a.topk * 2 : (a.Nk + BN - 1) / BN;
     auto tile_at = [&](int it) { return tile_start<SPARSE, BN>(lst, it); };
-    AsyncTile<BN, D, 256> tk;
-    AsyncTile<D, BN, 256> tv;
+    AsyncTile<BN, D, NW * 64> tk;
+    AsyncTile<D, BN, NW * 64> tv;
     tk.init(D, tid);
     tv.init(a.Nk_pad, tid);
     tile_pipeline(
@@ -336,6 +390,7 @@ struct BwdDq {
                 const u32x4 vf = *(const u32x4*)(sV + toff<D>(row, 2 * cc + hh));
                 dp = mfma(vf, df[cc], dp);
             }
+            lds_mfma_chain<D / 8, 4>();
             float ds[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -359,6 +414,7 @@ struct BwdDq {
                     dqa[db] = mfma(ktf, bfr[g], dqa[db]);
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 };
@@ -475,6 +531,7 @@ struct BwdDv {
 #pragma unroll
             for (int cc = 0; cc < D / 16; ++cc)
                 s = mfma(kf[cc], *(const u32x4*)(sQ + toff<D>(row, 2 * cc + hh)), s);
+            lds_mfma_chain<D / 16, 4>();
             const float L = sL[row];
             float p[16];
 #pragma unroll
@@ -496,6 +553,7 @@ struct BwdDv {
                     dva[db] = mfma(*(const u32x4*)(sdOt + off), pT[g], dva[db]);
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 };
@@ -518,6 +576,7 @@ struct BwdDk {
                 s = mfma(kf[cc], *(const u32x4*)(sQ + toff<D>(row, 2 * cc + hh)), s);
                 dp = mfma(vf[cc], *(const u32x4*)(sdO + toff<D>(row, 2 * cc + hh)), dp);
             }
+            lds_mfma_chain<D / 8, 4>();
             const float L = sL[row];
             const float Dl = sDl[row];
             float ds[16];
@@ -537,6 +596,7 @@ struct BwdDk {
                     dka[db] = mfma(*(const u32x4*)(sQt + off), dT[g], dka[db]);
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 };
@@ -671,35 +731,45 @@ __global__ __launch_bounds__(NW * 64) void bwd_dk_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-template <int D, bool SP>
-static void fwd_lse_go(const AttnArgs& a, dim3 g, hipStream_t st) {
-    fwd_lse_kernel<D, SP><<<g, 256, 0, st>>>(a);
+// Dense forward workgroups are 8 waves (256 queries) so that each K/V tile
+// brought into LDS serves twice the queries; sparse ones are one 128-query
+// block (4 waves).
+constexpr int kFwdDenseWaves = 8;
+constexpr int kFwdOutDenseWaves = 4;
+
+template <int D>
+static void fwd_lse_d(const AttnArgs& a, bool sp, hipStream_t st) {
+    if (sp) {
+        fwd_lse_kernel<D, 4, true><<<dim3(a.nbq, a.BH), 256, 0, st>>>(a);
+    } else {
+        constexpr int NW = kFwdDenseWaves;
+        fwd_lse_kernel<D, NW, false><<<dim3((a.Nq + NW * 32 - 1) / (NW * 32), a.BH), NW * 64, 0,
+                                       st>>>(a);
+    }
 }
 
 hipError_t launch_fwd_lse(const AttnArgs& a, int D, hipStream_t st) {
     const bool sp = a.kv_idx != nullptr;
-    dim3 grid(sp ? a.nbq : (a.Nq + 127) / 128, a.BH);
-    if (D == 128) sp ? fwd_lse_go<128, true>(a, grid, st) : fwd_lse_go<128, false>(a, grid, st);
-    else sp ? fwd_lse_go<64, true>(a, grid, st) : fwd_lse_go<64, false>(a, grid, st);
+    if (D == 128) fwd_lse_d<128>(a, sp, st);
+    else fwd_lse_d<64>(a, sp, st);
     return hipGetLastError();
 }
 
-template <int D, bool QP, bool SP>
-static void fwd_out_go(const AttnArgs& a, dim3 g, hipStream_t st) {
-    fwd_out_kernel<D, QP, SP><<<g, 256, 0, st>>>(a);
-}
-
-template <int D>
-static void fwd_out_d(const AttnArgs& a, dim3 g, bool sp, hipStream_t st) {
-    if (a.quant_p) sp ? fwd_out_go<D, true, true>(a, g, st) : fwd_out_go<D, true, false>(a, g, st);
-    else sp ? fwd_out_go<D, false, true>(a, g, st) : fwd_out_go<D, false, false>(a, g, st);
+template <int D, bool QP>
+static void fwd_out_go(const AttnArgs& a, bool sp, hipStream_t st) {
+    if (sp) {
+        fwd_out_kernel<D, QP, 4, true><<<dim3(a.nbq, a.BH), 256, 0, st>>>(a);
+    } else {
+        constexpr int NW = kFwdOutDenseWaves;
+        fwd_out_kernel<D, QP, NW, false><<<dim3((a.Nq + NW * 32 - 1) / (NW * 32), a.BH), NW * 64,
+                                           0, st>>>(a);
+    }
 }
 
 hipError_t launch_fwd_out(const AttnArgs& a, int D, hipStream_t st) {
     const bool sp = a.kv_idx != nullptr;
-    dim3 grid(sp ? a.nbq : (a.Nq + 127) / 128, a.BH);
-    if (D == 128) fwd_out_d<128>(a, grid, sp, st);
-    else fwd_out_d<64>(a, grid, sp, st);
+    if (D == 128) a.quant_p ? fwd_out_go<128, true>(a, sp, st) : fwd_out_go<128, false>(a, sp, st);
+    else a.quant_p ? fwd_out_go<64, true>(a, sp, st) : fwd_out_go<64, false>(a, sp, st);
     return hipGetLastError();
 }
 
