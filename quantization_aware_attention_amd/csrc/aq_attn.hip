@@ -78,15 +78,23 @@ struct AsyncTile {
     }
     __device__ __forceinline__ void issue(uint16_t* lds, const uint16_t* g) const {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-            __builtin_amdgcn_global_load_lds((glb_void_t*)((const char*)g + goff[j]),
+        for (int j = 0; j < NJ; ++j) {
+            // Opaque copy: keeps the 32-bit offset from being widened outside
+            // the loop, so the load takes the wave-uniform base in SGPRs and
+            // the offset in one VGPR.
+            uint32_t o = goff[j];
+            asm volatile("" : "+v"(o));
+            __builtin_amdgcn_global_load_lds((glb_void_t*)((const char*)g + o),
                                              (lds_void_t*)(lds + (j * NW + wave) * 512), 16, 0, 0);
+        }
     }
 };
 
 // Asynchronous copy of 64 consecutive floats into LDS by one wave.
 __device__ __forceinline__ void async_f32x64(float* lds, const float* g, int lane) {
-    __builtin_amdgcn_global_load_lds((glb_void_t*)(g + lane), (lds_void_t*)lds, 4, 0, 0);
+    uint32_t o = 4u * (uint32_t)lane;
+    asm volatile("" : "+v"(o));
+    __builtin_amdgcn_global_load_lds((glb_void_t*)((const char*)g + o), (lds_void_t*)lds, 4, 0, 0);
 }
 
 // Wait until this wave's direct-to-LDS loads have landed (vmcnt = 0).
@@ -111,26 +119,51 @@ __device__ __forceinline__ void stage_list(int* lst, const int32_t* g, int n) {
     __syncthreads();
 }
 
+// Buffer b (std::integral_constant 0 or 1) of a pair of LDS buffers. The two
+// buffers are separate variables and every access names one of them at
+// compile time, so the compiler can tell reads of one buffer from the
+// direct-to-LDS loads into the other and does not make them wait for those
+// loads to land.
+template <class B, class T>
+__device__ __forceinline__ T* sel(B, T* b0, T* b1) {
+    return B::value ? b1 : b0;
+}
+
 // Double-buffered tile loop. issue(buf, it) starts the asynchronous copy of
-// tile it into buffer buf; body(buf, it, tail) consumes it. Full tiles run the
+// tile it into buffer buf; body(buf, it, tail) consumes it; buf is a
+// compile-time 0 or 1 (the loop is unrolled by two). Full tiles run the
 // unmasked body; a partial last tile (last_partial) runs the masked body once,
-// after the loop, so that only one body is live inside the loop.
+// after the loop, so that only the unmasked body is live inside the loop.
 template <class Issue, class Body>
 __device__ __forceinline__ void tile_pipeline(int n_iter, bool last_partial, Issue issue,
                                               Body body) {
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
     const int n_main = n_iter - (last_partial ? 1 : 0);
-    issue(0, 0);
+    issue(B0{}, 0);
     int it = 0;
-    for (; it < n_main; ++it) {
+    for (; it + 1 < n_main; it += 2) {
         wait_async();
         __syncthreads();
-        if (it + 1 < n_iter) issue((it + 1) & 1, it + 1);
-        body(it & 1, it, std::false_type{});
+        issue(B1{}, it + 1);
+        body(B0{}, it, std::false_type{});
+        wait_async();
+        __syncthreads();
+        if (it + 2 < n_iter) issue(B0{}, it + 2);
+        body(B1{}, it + 1, std::false_type{});
+    }
+    if (it < n_main) {
+        wait_async();
+        __syncthreads();
+        if (it + 1 < n_iter) issue(B1{}, it + 1);
+        body(B0{}, it, std::false_type{});
+        ++it;
     }
     if (last_partial) {
         wait_async();
         __syncthreads();
-        body(it & 1, it, std::true_type{});
+        if (it & 1) body(B1{}, it, std::true_type{});
+        else body(B0{}, it, std::true_type{});
     }
 }
 
@@ -229,7 +262,7 @@ template <int D, int NW, bool SPARSE>
 __global__ __launch_bounds__(NW * 64) void fwd_lse_kernel(AttnArgs a) {
     constexpr int BN = FwdLse<D>::BN;
     static_assert(!SPARSE || NW == 4, "sparse workgroups cover one 128-query block");
-    __shared__ __attribute__((aligned(1024))) uint16_t sK[2][BN * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t sK0[BN * D], sK1[BN * D];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
     const int bh = blockIdx.y, qblk = blockIdx.x;
@@ -249,10 +282,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_lse_kernel(AttnArgs a) {
     tk.init(D, tid);
     tile_pipeline(
         n_iter, tile_at(n_iter - 1) + BN > a.Nk,
-        [&](int buf, int it) { tk.issue(sK[buf], Kb + (size_t)tile_at(it) * D); },
-        [&](int buf, int it, auto tail) {
-            FwdLse<D>::template block<decltype(tail)::value>(sK[buf], tile_at(it), a.Nk, qf, a.c,
-                                                             m, l, l32, hh);
+        [&](auto b, int it) { tk.issue(sel(b, sK0, sK1), Kb + (size_t)tile_at(it) * D); },
+        [&](auto b, int it, auto tail) {
+            FwdLse<D>::template block<decltype(tail)::value>(sel(b, sK0, sK1), tile_at(it), a.Nk, qf,
+                                                             a.c, m, l, l32, hh);
         });
     const float mp = partner_lane(m), lp = partner_lane(l);
     const float mt = fmaxf(m, mp);
@@ -327,8 +360,11 @@ template <int D, bool QP, int NW, bool SPARSE>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_out_kernel(AttnArgs a) {
     constexpr int BN = FwdOut<D, QP>::BN;
     static_assert(!SPARSE || NW == 4, "sparse workgroups cover one 128-query block");
-    __shared__ __attribute__((aligned(1024))) uint16_t sK[2][BN * D];
-    __shared__ __attribute__((aligned(1024))) uint16_t sV[2][D * BN];
+    struct Buf {
+        uint16_t k[BN * D];
+        uint16_t v[D * BN];
+    };
+    __shared__ __attribute__((aligned(1024))) Buf s0, s1;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
     const int bh = blockIdx.y, qblk = blockIdx.x;
@@ -355,14 +391,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_out_kernel(AttnA
     tv.init(a.Nk_pad, tid);
     tile_pipeline(
         n_iter, tile_at(n_iter - 1) + BN > a.Nk,
-        [&](int buf, int it) {
+        [&](auto b, int it) {
             const int kt = tile_at(it);
-            tk.issue(sK[buf], Kb + (size_t)kt * D);
-            tv.issue(sV[buf], Vtb + kt);
+            tk.issue(sel(b, &s0, &s1)->k, Kb + (size_t)kt * D);
+            tv.issue(sel(b, &s0, &s1)->v, Vtb + kt);
         },
-        [&](int buf, int it, auto tail) {
-            FwdOut<D, QP>::template block<decltype(tail)::value>(sK[buf], sV[buf], tile_at(it), a.Nk,
-                                                                 qf, a.c, lse2, o, l32, hh);
+        [&](auto b, int it, auto tail) {
+            FwdOut<D, QP>::template block<decltype(tail)::value>(sel(b, &s0, &s1)->k, sel(b, &s0, &s1)->v,
+                                                                 tile_at(it), a.Nk, qf, a.c, lse2, o,
+                                                                 l32, hh);
         });
     if (q < a.Nq) {
         const int64_t b = bh / a.H, h = bh % a.H;
@@ -422,9 +459,12 @@ struct BwdDq {
 template <int D, int NW, bool SPARSE>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
     constexpr int BN = BwdDq<D>::BN, NT = NW * 64;
-    __shared__ __attribute__((aligned(1024))) uint16_t sK[2][BN * D];
-    __shared__ __attribute__((aligned(1024))) uint16_t sV[2][BN * D];
-    __shared__ __attribute__((aligned(1024))) uint16_t sT[2][D * BN];
+    struct Buf {
+        uint16_t k[BN * D];
+        uint16_t v[BN * D];
+        uint16_t kt[D * BN];
+    };
+    __shared__ __attribute__((aligned(1024))) Buf s0, s1;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
     const int bh = blockIdx.y, qblk = blockIdx.x;
@@ -458,16 +498,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
     tt.init(a.Nk_pad, tid);
     tile_pipeline(
         n_iter, tile_at(n_iter - 1) + BN > a.Nk,
-        [&](int buf, int it) {
+        [&](auto b, int it) {
             const int kt = tile_at(it);
-            tk.issue(sK[buf], Kb + (size_t)kt * D);
-            tk.issue(sV[buf], Vb + (size_t)kt * D);
-            tt.issue(sT[buf], Ktb + kt);
+            Buf* t = sel(b, &s0, &s1);
+            tk.issue(t->k, Kb + (size_t)kt * D);
+            tk.issue(t->v, Vb + (size_t)kt * D);
+            tt.issue(t->kt, Ktb + kt);
         },
-        [&](int buf, int it, auto tail) {
-            BwdDq<D>::template block<decltype(tail)::value>(sK[buf], sV[buf], sT[buf], tile_at(it),
-                                                            a.Nk, qf, df, a.c, lse2, dl, dqa, l32,
-                                                            hh);
+        [&](auto b, int it, auto tail) {
+            Buf* t = sel(b, &s0, &s1);
+            BwdDq<D>::template block<decltype(tail)::value>(t->k, t->v, t->kt, tile_at(it), a.Nk, qf,
+                                                            df, a.c, lse2, dl, dqa, l32, hh);
         });
     if (q < a.Nq) {
         const int64_t b = bh / a.H, h = bh % a.H;
@@ -561,11 +602,9 @@ struct BwdDv {
 template <int D>
 struct BwdDk {
     static constexpr int BM = 64;
-    template <bool TAILK>
     __device__ static void block(const uint16_t* sQ, const uint16_t* sdO, const uint16_t* sQt,
-                                 const float* sL, const float* sDl, uint16_t* T, int k0, int Nk,
-                                 const u32x4* kf, const u32x4* vf, float c, f32x16* dka,
-                                 int lane) {
+                                 const float* sL, const float* sDl, uint16_t* T, const u32x4* kf,
+                                 const u32x4* vf, float c, f32x16* dka, int lane) {
         const int l32 = lane & 31, hh = lane >> 5;
 #pragma unroll
         for (int qb = 0; qb < BM / 32; ++qb) {
@@ -582,8 +621,7 @@ struct BwdDk {
             float ds[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -L));
-                if (TAILK && k0 + acc_row(r, hh) >= Nk) p = 0.0f;
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -L));
                 ds[r] = p * (dp[r] - Dl);
             }
             u32x4 dT[2];
@@ -624,10 +662,13 @@ template <int D, bool QP, int NW, bool SPARSE>
 __global__ __launch_bounds__(NW * 64) void bwd_dv_kernel(AttnArgs a) {
     constexpr int BM = 64, NT = NW * 64, KW = NW * 32;
     static_assert(!SPARSE || NW == 4, "sparse key workgroups cover one key block");
-    __shared__ __attribute__((aligned(1024))) uint16_t sQ[2][BM * D];
-    __shared__ __attribute__((aligned(1024))) uint16_t sOt[2][D * BM];
+    struct Buf {
+        uint16_t q[BM * D];
+        uint16_t ot[D * BM];
+        float l[BM];
+    };
+    __shared__ __attribute__((aligned(1024))) Buf s0, s1;
     __shared__ __attribute__((aligned(1024))) uint16_t sT[NW][32 * 32];
-    __shared__ __attribute__((aligned(256))) float sL[2][BM];
     __shared__ int lst[SPARSE ? kMaxBlockList : 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -647,22 +688,26 @@ __global__ __launch_bounds__(NW * 64) void bwd_dv_kernel(AttnArgs a) {
         AsyncTile<D, BM, NT> tc;
         tr.init(D, tid);
         tc.init(a.Nq_pad, tid);
-        auto issue = [&](int buf, int it) {
+        auto issue = [&](auto b, int it) {
             const int qt = tile_start<SPARSE, BM>(lst, it);
-            tr.issue(sQ[buf], Qb + (size_t)qt * D);
-            tc.issue(sOt[buf], dOtb + qt);
-            if (wave == 0) async_f32x64(sL[buf], Lb + qt, lane);
+            Buf* t = sel(b, &s0, &s1);
+            tr.issue(t->q, Qb + (size_t)qt * D);
+            tc.issue(t->ot, dOtb + qt);
+            if (wave == 0) async_f32x64(t->l, Lb + qt, lane);
         };
-        // keys beyond Nk exist only in the last key workgroup: mask them there only
+        // keys beyond Nk exist only in the last key workgroup: mask them there
+        // only (they would enter the maxima of the last P groups)
         if (kblk * KW + KW > a.Nk)
-            tile_pipeline(n_iter, false, issue, [&](int buf, int, auto) {
-                BwdDv<D, QP>::template block<true>(sQ[buf], sOt[buf], sL[buf], sT[wave], k0, a.Nk, kf,
-                                                   a.c, dva, lane);
+            tile_pipeline(n_iter, false, issue, [&](auto b, int, auto) {
+                Buf* t = sel(b, &s0, &s1);
+                BwdDv<D, QP>::template block<true>(t->q, t->ot, t->l, sT[wave], k0, a.Nk, kf, a.c,
+                                                   dva, lane);
             });
         else
-            tile_pipeline(n_iter, false, issue, [&](int buf, int, auto) {
-                BwdDv<D, QP>::template block<false>(sQ[buf], sOt[buf], sL[buf], sT[wave], k0, a.Nk,
-                                                    kf, a.c, dva, lane);
+            tile_pipeline(n_iter, false, issue, [&](auto b, int, auto) {
+                Buf* t = sel(b, &s0, &s1);
+                BwdDv<D, QP>::template block<false>(t->q, t->ot, t->l, sT[wave], k0, a.Nk, kf, a.c,
+                                                    dva, lane);
             });
     }
     const int key = k0 + l32;
@@ -676,11 +721,15 @@ template <int D, int NW, bool SPARSE>
 __global__ __launch_bounds__(NW * 64) void bwd_dk_kernel(AttnArgs a) {
     constexpr int BM = 64, NT = NW * 64, KW = NW * 32;
     static_assert(!SPARSE || NW == 4, "sparse key workgroups cover one key block");
-    __shared__ __attribute__((aligned(1024))) uint16_t sQ[2][BM * D];
-    __shared__ __attribute__((aligned(1024))) uint16_t sO[2][BM * D];
-    __shared__ __attribute__((aligned(1024))) uint16_t sQt[2][D * BM];
+    struct Buf {
+        uint16_t q[BM * D];
+        uint16_t o[BM * D];
+        uint16_t qt[D * BM];
+        float l[BM];
+        float d[BM];
+    };
+    __shared__ __attribute__((aligned(1024))) Buf s0, s1;
     __shared__ __attribute__((aligned(1024))) uint16_t sT[NW][32 * 32];
-    __shared__ __attribute__((aligned(256))) float sL[2][BM], sD[2][BM];
     __shared__ int lst[SPARSE ? kMaxBlockList : 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -703,24 +752,21 @@ __global__ __launch_bounds__(NW * 64) void bwd_dk_kernel(AttnArgs a) {
         AsyncTile<D, BM, NT> tc;
         tr.init(D, tid);
         tc.init(a.Nq_pad, tid);
-        auto issue = [&](int buf, int it) {
+        auto issue = [&](auto b, int it) {
             const int qt = tile_start<SPARSE, BM>(lst, it);
-            tr.issue(sQ[buf], Qb + (size_t)qt * D);
-            tr.issue(sO[buf], dOb + (size_t)qt * D);
-            tc.issue(sQt[buf], Qtb + qt);
-            if (wave == 0) async_f32x64(sL[buf], Lb + qt, lane);
-            if (wave == 1) async_f32x64(sD[buf], Db + qt, lane);
+            Buf* t = sel(b, &s0, &s1);
+            tr.issue(t->q, Qb + (size_t)qt * D);
+            tr.issue(t->o, dOb + (size_t)qt * D);
+            tc.issue(t->qt, Qtb + qt);
+            if (wave == 0) async_f32x64(t->l, Lb + qt, lane);
+            if (wave == 1) async_f32x64(t->d, Db + qt, lane);
         };
-        if (kblk * KW + KW > a.Nk)
-            tile_pipeline(n_iter, false, issue, [&](int buf, int, auto) {
-                BwdDk<D>::template block<true>(sQ[buf], sO[buf], sQt[buf], sL[buf], sD[buf],
-                                               sT[wave], k0, a.Nk, kf, vf, a.c, dka, lane);
-            });
-        else
-            tile_pipeline(n_iter, false, issue, [&](int buf, int, auto) {
-                BwdDk<D>::template block<false>(sQ[buf], sO[buf], sQt[buf], sL[buf], sD[buf],
-                                                sT[wave], k0, a.Nk, kf, vf, a.c, dka, lane);
-            });
+        // No key mask: dK of key j depends on column j of P only, and the
+        // rows of keys beyond Nk (zero-padded operands) are never stored.
+        tile_pipeline(n_iter, false, issue, [&](auto b, int, auto) {
+            Buf* t = sel(b, &s0, &s1);
+            BwdDk<D>::block(t->q, t->o, t->qt, t->l, t->d, sT[wave], kf, vf, a.c, dka, lane);
+        });
     }
     const int key = k0 + l32;
     if (key < a.Nk) {
