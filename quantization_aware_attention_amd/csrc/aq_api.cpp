@@ -120,10 +120,10 @@ struct TransposeArgs {
     uint16_t* dst;
     int64_t BH;
     int Npad, D;
-    bool perm;
+    bool perm, to_f16;
 };
 hipError_t do_transpose(const TransposeArgs& t, hipStream_t st) {
-    return aq::launch_transpose_perm(t.src, t.dst, t.BH, t.Npad, t.D, t.perm, st);
+    return aq::launch_transpose_perm(t.src, t.dst, t.BH, t.Npad, t.D, t.perm, t.to_f16, st);
 }
 struct DimArgs {
     aq::AttnArgs a;
@@ -157,8 +157,8 @@ int run_fq(bool axis_d, bool quant, const aq::FqArgs& a, hipStream_t st, const c
 }
 
 int run_transpose(const uint16_t* src, uint16_t* dst, int64_t BH, int64_t Npad, int64_t D,
-                  bool perm, hipStream_t st, const char* what) {
-    const TransposeArgs t{src, dst, BH, (int)Npad, (int)D, perm};
+                  bool perm, hipStream_t st, const char* what, bool to_f16 = false) {
+    const TransposeArgs t{src, dst, BH, (int)Npad, (int)D, perm, to_f16};
     return launch(K_TRANSPOSE, st, thunk<TransposeArgs, do_transpose>, &t, what);
 }
 
@@ -314,6 +314,12 @@ aq::FqArgs fq_args(const void* x, const Strides& xs, void* y, const Strides& ys,
     return a;
 }
 
+// The forward's P V product runs on fp16 operands when both P and V are
+// NVFP4 values (fp16 holds them exactly); V^T is then stored as fp16.
+bool pv_f16(uint32_t mask) {
+    return (mask & ATTNQAT_QUANT_P) && (mask & ATTNQAT_QUANT_V);
+}
+
 // Quantize (or copy) q, k, v into the padded workspace operands.
 int prepare_operands(const Plan& pl, uint32_t mask, const void* q, const void* k, const void* v,
                      char* ws, const Layout& L, bool bwd, hipStream_t st) {
@@ -334,7 +340,7 @@ int prepare_operands(const Plan& pl, uint32_t mask, const void* q, const void* k
     if (rc) return rc;
     if (!bwd)
         return run_transpose((const uint16_t*)(ws + L.vw), (uint16_t*)(ws + L.vt), pl.BH, pl.Nk_pad,
-                             pl.D, true, st, "transpose V");
+                             pl.D, false, st, "transpose V", pv_f16(mask));
     rc = run_transpose((const uint16_t*)(ws + L.qw), (uint16_t*)(ws + L.qt), pl.BH, pl.Nq_pad, pl.D,
                        false, st, "transpose Q");
     if (rc) return rc;
@@ -356,6 +362,7 @@ aq::AttnArgs attn_args(const attnqat_problem* p, const Plan& pl, char* ws, const
     a.sm_scale = p->sm_scale;
     a.c = p->sm_scale * aq::kLog2e;
     a.quant_p = (p->quant_mask & ATTNQAT_QUANT_P) ? 1 : 0;
+    a.pv_f16 = pv_f16(p->quant_mask) ? 1 : 0;
     if (pl.sparse) {
         a.kv_idx = p->kv_block_idx;
         a.topk = p->topk;

@@ -60,10 +60,13 @@ __device__ __forceinline__ int toff(int row, int c) {
 // each lane fetches the global chunk that the swizzle maps to that slot. The
 // per-lane source offsets depend only on the tile shape, so they are computed
 // once; each issue adds them to a wave-uniform tile base.
-template <int R, int W, int NT>
+// With PERM32, tile row `row` receives source row perm32 of its position in
+// its 32-row block (the key order of score tiles, see perm32).
+template <int R, int W, int NT, bool PERM32 = false>
 struct AsyncTile {
     static constexpr int CH = W / 8, NB = R * CH / 64, NW = NT / 64, NJ = NB / NW;
     static_assert(NB % NW == 0, "tile must split evenly over the waves");
+    static_assert(!PERM32 || R % 32 == 0, "permuted tiles hold whole 32-row blocks");
     uint32_t goff[NJ];  // byte offsets of this lane's chunks in the source tile
     int wave;           // wave index (uniform)
     __device__ __forceinline__ void init(int ld, int tid) {
@@ -73,7 +76,8 @@ struct AsyncTile {
         for (int j = 0; j < NJ; ++j) {
             const int L = (j * NW + wave) * 64 + lane;
             const int row = L / CH, pch = L % CH;
-            goff[j] = (uint32_t)(row * ld + ((pch ^ swz<W>(row)) << 3)) * 2u;
+            const int src = PERM32 ? (row & ~31) | perm32(row & 31) : row;
+            goff[j] = (uint32_t)(src * ld + ((pch ^ swz<W>(row)) << 3)) * 2u;
         }
     }
     __device__ __forceinline__ void issue(uint16_t* lds, const uint16_t* g) const {
@@ -297,28 +301,38 @@ __global__ __launch_bounds__(NW * 64) void fwd_lse_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // Forward pass 2: O = FQ(P) Vq with P = exp(S - LSE). 4 waves x 32 queries.
-template <int D, bool QP>
+// K tiles are loaded in perm32 row order, so lane half hh of a 32-key score
+// block holds keys 16 hh .. 16 hh + 15 for its query: one whole P group.
+// With F16 (P and V both quantized) the P V product runs on fp16 operands,
+// which hold NVFP4 values exactly, and V^T is stored as fp16.
+template <int D, bool QP, bool F16>
 struct FwdOut {
     static constexpr int BN = 64;
+    static_assert(!F16 || QP, "fp16 P operands are NVFP4 values");
 
-    // P (or its quantization) of one 32-key score block as two B operands.
+    // P (or its quantization) of one 32-key score block as two B operands
+    // (k-slot 8 hh + j of operand g is key 16 hh + 8 g + j).
     template <bool tail>
-    __device__ static void probs(const f32x16& acc, int k0, int Nk, float c, float lse2, int hh,
+    __device__ static void probs(f32x16 acc, int k0, int Nk, float c, float lse2, int hh,
                                  u32x4* bfr) {
-        float p[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], c, -lse2));
         if (tail) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                if (k0 + acc_row(r, hh) >= Nk) p[r] = 0.0f;
+                if (k0 + 16 * hh + r >= Nk) acc[r] = -INFINITY;
         }
+        float x[16];
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            float* pg = p + 8 * g;
-            if (QP) quant_group8_hw(pg);
-            bfr[g] = u32x4{pack_rne(pg[0], pg[1]), pack_rne(pg[2], pg[3]), pack_rne(pg[4], pg[5]),
-                           pack_rne(pg[6], pg[7])};
+        for (int r = 0; r < 16; ++r) x[r] = acc[r];
+        if (QP) {
+            quant_p_group16<F16>(x, c, lse2, bfr);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = __builtin_amdgcn_exp2f(fmaf(x[r], c, -lse2));
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+                bfr[g] = u32x4{pack_rne(x[8 * g], x[8 * g + 1]), pack_rne(x[8 * g + 2], x[8 * g + 3]),
+                               pack_rne(x[8 * g + 4], x[8 * g + 5]),
+                               pack_rne(x[8 * g + 6], x[8 * g + 7])};
         }
     }
 
@@ -329,8 +343,8 @@ struct FwdOut {
         for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
             for (int g = 0; g < 2; ++g) {
-                const u32x4 vf = *(const u32x4*)(sV + toff<BN>(db * 32 + l32, 4 * kb + 2 * g + hh));
-                o[db] = mfma(vf, bfr[g], o[db]);
+                const u32x4 vf = *(const u32x4*)(sV + toff<BN>(db * 32 + l32, 4 * kb + 2 * hh + g));
+                o[db] = F16 ? mfma_f16(vf, bfr[g], o[db]) : mfma(vf, bfr[g], o[db]);
             }
         }
     }
@@ -356,9 +370,10 @@ struct FwdOut {
     }
 };
 
-template <int D, bool QP, int NW, bool SPARSE>
+template <int D, bool QP, bool F16, int NW, bool SPARSE>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_out_kernel(AttnArgs a) {
-    constexpr int BN = FwdOut<D, QP>::BN;
+    using F = FwdOut<D, QP, F16>;
+    constexpr int BN = F::BN;
     static_assert(!SPARSE || NW == 4, "sparse workgroups cover one 128-query block");
     struct Buf {
         uint16_t k[BN * D];
@@ -385,7 +400,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_out_kernel(AttnA
     if (SPARSE) stage_list(lst, a.kv_idx + ((size_t)bh * a.nbq + qblk) * a.topk, a.topk);
     const int n_iter = SPARSE ? a.topk * 2 : (a.Nk + BN - 1) / BN;
     auto tile_at = [&](int it) { return tile_start<SPARSE, BN>(lst, it); };
-    AsyncTile<BN, D, NW * 64> tk;
+    AsyncTile<BN, D, NW * 64, true> tk;
     AsyncTile<D, BN, NW * 64> tv;
     tk.init(D, tid);
     tv.init(a.Nk_pad, tid);
@@ -397,9 +412,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_out_kernel(AttnA
             tv.issue(sel(b, &s0, &s1)->v, Vtb + kt);
         },
         [&](auto b, int it, auto tail) {
-            FwdOut<D, QP>::template block<decltype(tail)::value>(sel(b, &s0, &s1)->k, sel(b, &s0, &s1)->v,
-                                                                 tile_at(it), a.Nk, qf, a.c, lse2, o,
-                                                                 l32, hh);
+            F::template block<decltype(tail)::value>(sel(b, &s0, &s1)->k, sel(b, &s0, &s1)->v,
+                                                     tile_at(it), a.Nk, qf, a.c, lse2, o, l32, hh);
         });
     if (q < a.Nq) {
         const int64_t b = bh / a.H, h = bh % a.H;
@@ -801,21 +815,28 @@ hipError_t launch_fwd_lse(const AttnArgs& a, int D, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int D, bool QP>
+template <int D, bool QP, bool F16>
 static void fwd_out_go(const AttnArgs& a, bool sp, hipStream_t st) {
     if (sp) {
-        fwd_out_kernel<D, QP, 4, true><<<dim3(a.nbq, a.BH), 256, 0, st>>>(a);
+        fwd_out_kernel<D, QP, F16, 4, true><<<dim3(a.nbq, a.BH), 256, 0, st>>>(a);
     } else {
         constexpr int NW = kFwdOutDenseWaves;
-        fwd_out_kernel<D, QP, NW, false><<<dim3((a.Nq + NW * 32 - 1) / (NW * 32), a.BH), NW * 64,
-                                           0, st>>>(a);
+        fwd_out_kernel<D, QP, F16, NW, false>
+            <<<dim3((a.Nq + NW * 32 - 1) / (NW * 32), a.BH), NW * 64, 0, st>>>(a);
     }
+}
+
+template <int D>
+static void fwd_out_d(const AttnArgs& a, bool sp, hipStream_t st) {
+    if (a.quant_p && a.pv_f16) fwd_out_go<D, true, true>(a, sp, st);
+    else if (a.quant_p) fwd_out_go<D, true, false>(a, sp, st);
+    else fwd_out_go<D, false, false>(a, sp, st);
 }
 
 hipError_t launch_fwd_out(const AttnArgs& a, int D, hipStream_t st) {
     const bool sp = a.kv_idx != nullptr;
-    if (D == 128) a.quant_p ? fwd_out_go<128, true>(a, sp, st) : fwd_out_go<128, false>(a, sp, st);
-    else a.quant_p ? fwd_out_go<64, true>(a, sp, st) : fwd_out_go<64, false>(a, sp, st);
+    if (D == 128) fwd_out_d<128>(a, sp, st);
+    else fwd_out_d<64>(a, sp, st);
     return hipGetLastError();
 }
 

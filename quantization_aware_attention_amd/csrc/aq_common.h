@@ -25,6 +25,8 @@
 namespace aq {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -46,6 +48,13 @@ __host__ __device__ constexpr int perm16(int p) {
 __device__ __forceinline__ f32x16 mfma(const u32x4& a, const u32x4& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Same product with fp16 operands (used where both operands are NVFP4 values,
+// which fp16 represents exactly).
+__device__ __forceinline__ f32x16 mfma_f16(const u32x4& a, const u32x4& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
@@ -157,6 +166,74 @@ __device__ __forceinline__ void quant_group8_hw(float* p) {
     p[5] = q2[1] * s;
     p[6] = q3[0] * s;
     p[7] = q3[1] * s;
+}
+
+// Key order inside a 32-key block of a score tile S^T = K Q^T. The MFMA
+// accumulator puts tile row 8 (r / 4) + 4 h + r % 4 in register r of lane
+// half h; loading key 16 h + r into that row gives each lane one whole
+// 16-key group (keys 16 h .. 16 h + 15) in registers 0..15. perm32(row) is the
+// key stored at tile row `row`.
+__host__ __device__ constexpr int perm32(int p) {
+    return 16 * ((p >> 2) & 1) + 4 * (p >> 3) + (p & 3);
+}
+
+// NVFP4 fake quantization of P for one 16-key group held in one lane:
+// P_j = 2^(x_j c - lse2) with x_j the raw scores (masked keys at -inf).
+// The scale s = E4M3(max_j P_j / 6) comes from an FP8 round trip (nearest
+// even). The division by s is folded into the exponent,
+// P_j / s = 2^(x_j c - lse2 - log2 s), and the E2M1 rounding of that ratio
+// (nearest even, saturating at 6) is the FP4 conversion unit's. An all-zero
+// group (s = 0) multiplies every code by 0. Outputs: the 16 values
+// q_j * s in key order as 8 packed pairs, fp16 (F16, exact: q * s has at
+// most 6 significant bits and lies in [2^-10, 6]) or bf16 (also exact).
+template <bool F16>
+__device__ __forceinline__ void quant_p_group16(const float* x, float c, float lse2, u32x4* out) {
+    float mx = x[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) mx = __builtin_fmaxf(mx, x[j]);
+    const float pmax = __builtin_amdgcn_exp2f(__builtin_fmaf(mx, c, -lse2));
+    const float a6 = pmax * (1.0f / 6.0f);
+    const i16x2 z = {0, 0};
+    const i16x2 c8 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, a6, a6, 1.0f, false);
+    const int code2 = __builtin_bit_cast(int, c8);  // the scale code in bytes 0 and 1
+    const float s = __builtin_amdgcn_cvt_scalef32_f32_fp8(code2, 1.0f, 0);
+    const float t = lse2 + __builtin_fmaxf(__builtin_amdgcn_logf(s), -64.0f);
+    float r[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) r[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], c, -t));
+    uint32_t codes[2];
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        const float* rw = r + 8 * w;
+        uint32_t cw = 0u;
+        cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, rw[0], rw[1], 1.0f, 0);
+        cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, rw[2], rw[3], 1.0f, 1);
+        cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, rw[4], rw[5], 1.0f, 2);
+        cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, rw[6], rw[7], 1.0f, 3);
+        codes[w] = cw;
+    }
+    if (F16) {
+        const f16x2 s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((short)code2, 1.0f, false);
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const f16x2 q0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes[w], 1.0f, 0);
+            const f16x2 q1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes[w], 1.0f, 1);
+            const f16x2 q2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes[w], 1.0f, 2);
+            const f16x2 q3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes[w], 1.0f, 3);
+            out[w] = u32x4{__builtin_bit_cast(uint32_t, q0 * s2), __builtin_bit_cast(uint32_t, q1 * s2),
+                           __builtin_bit_cast(uint32_t, q2 * s2), __builtin_bit_cast(uint32_t, q3 * s2)};
+        }
+    } else {
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const f32x2 q0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes[w], 1.0f, 0);
+            const f32x2 q1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes[w], 1.0f, 1);
+            const f32x2 q2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes[w], 1.0f, 2);
+            const f32x2 q3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes[w], 1.0f, 3);
+            out[w] = u32x4{pack_rne(q0[0] * s, q0[1] * s), pack_rne(q1[0] * s, q1[1] * s),
+                           pack_rne(q2[0] * s, q2[1] * s), pack_rne(q3[0] * s, q3[1] * s)};
+        }
+    }
 }
 
 // 16-bit transposing LDS read (ds_read_b64_tr_b16). Within each group of 16

@@ -42,7 +42,7 @@ struct AttnArgs {
     const uint16_t* Vw;   // [BH][Nk_pad][D]
     const uint16_t* Qt;   // [BH][D][Nq_pad] natural token order
     const uint16_t* Kt;   // [BH][D][Nk_pad] permuted
-    const uint16_t* Vt;   // [BH][D][Nk_pad] permuted
+    const uint16_t* Vt;   // [BH][D][Nk_pad] natural token order; fp16 when pv_f16
     const uint16_t* dOw;  // [BH][Nq_pad][D]
     const uint16_t* dOt;  // [BH][D][Nq_pad] natural token order
     const float* lse;     // forward: natural-log LSE output/input [BH][Nq]
@@ -69,12 +69,13 @@ struct AttnArgs {
     float c;        // sm_scale * log2(e)
     float sm_scale;
     int quant_p;
+    int pv_f16;  // forward: P and V both quantized, P V runs on fp16 operands
 };
 
 hipError_t launch_fq_axis_d(const FqArgs& a, bool quant, hipStream_t st);
 hipError_t launch_fq_axis_n(const FqArgs& a, bool quant, hipStream_t st);
 hipError_t launch_transpose_perm(const uint16_t* src, uint16_t* dst, int64_t BH, int Npad, int D,
-                                 bool perm, hipStream_t st);
+                                 bool perm, bool to_f16, hipStream_t st);
 hipError_t launch_bwd_pre(const PreArgs& a, hipStream_t st);
 
 hipError_t launch_fwd_lse(const AttnArgs& a, int D, hipStream_t st);

@@ -113,8 +113,9 @@ __global__ __launch_bounds__(256) void fq_axis_n_kernel(FqArgs a) {
 // Transposed copy: dst[bh][d][p] = src[bh][tok(p)][d] for a contiguous padded
 // [BH][Npad][D] source, with tok(p) = 16 (p / 16) + perm16(p % 16) when PERM
 // (operands read by MFMA k-slots in accumulator-row order) and tok(p) = p
-// otherwise. Tile: 64 tokens x 64 columns per block.
-template <bool PERM>
+// otherwise. With F16 the bf16 values are converted to fp16 (nearest even;
+// exact for NVFP4 values). Tile: 64 tokens x 64 columns per block.
+template <bool PERM, bool F16>
 __global__ __launch_bounds__(256) void transpose_perm_kernel(const uint16_t* __restrict__ src,
                                                              uint16_t* __restrict__ dst,
                                                              int Npad, int D) {
@@ -130,6 +131,10 @@ __global__ __launch_bounds__(256) void transpose_perm_kernel(const uint16_t* __r
         u32x4 w = *(const u32x4*)(s + (size_t)(n0 + r) * D + d0 + cc * 8);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+            if (F16) {
+                const f32x2 f = {bf_lo(w[j]), bf_hi(w[j])};
+                w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+            }
             tile[r][cc * 8 + 2 * j] = (uint16_t)(w[j] & 0xFFFFu);
             tile[r][cc * 8 + 2 * j + 1] = (uint16_t)(w[j] >> 16);
         }
@@ -209,10 +214,11 @@ hipError_t launch_fq_axis_n(const FqArgs& a, bool quant, hipStream_t st) {
 }
 
 hipError_t launch_transpose_perm(const uint16_t* src, uint16_t* dst, int64_t BH, int Npad, int D,
-                                 bool perm, hipStream_t st) {
+                                 bool perm, bool to_f16, hipStream_t st) {
     dim3 grid(Npad / 64, D / 64, (unsigned)BH);
-    if (perm) transpose_perm_kernel<true><<<grid, 256, 0, st>>>(src, dst, Npad, D);
-    else transpose_perm_kernel<false><<<grid, 256, 0, st>>>(src, dst, Npad, D);
+    if (perm) transpose_perm_kernel<true, false><<<grid, 256, 0, st>>>(src, dst, Npad, D);
+    else if (to_f16) transpose_perm_kernel<false, true><<<grid, 256, 0, st>>>(src, dst, Npad, D);
+    else transpose_perm_kernel<false, false><<<grid, 256, 0, st>>>(src, dst, Npad, D);
     return hipGetLastError();
 }
 
