@@ -571,6 +571,38 @@ __device__ __forceinline__ void transpose_tile(const float* v, uint16_t* T, u32x
     }
 }
 
+// As transpose_tile, for a score tile whose rows are in perm32 key order
+// (lane half hh holds keys 16 hh + r) and whose values arrive packed as bf16
+// pairs: w[g][k] holds keys 16 hh + 8 g + 2 k and + 1.
+__device__ __forceinline__ void transpose_tile_p32(const u32x4* w, uint16_t* T, u32x4* out,
+                                                   int lane) {
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int wsw = (l32 >> 2) & 7;
+    const int grp = lane >> 4, i16 = lane & 15;
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+        const int off = l32 * 32 + (((4 * hh + a4) ^ wsw) << 2);
+        u32x2 v;
+        v[0] = w[a4 >> 1][2 * (a4 & 1)];
+        v[1] = w[a4 >> 1][2 * (a4 & 1) + 1];
+        *(u32x2*)(T + off) = v;
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int trow = 16 * g + 8 * hh + 4 * half + (i16 >> 2);
+            const int col8 = 4 * (grp & 1) + (i16 & 3);
+            const int off = trow * 32 + ((col8 ^ ((trow >> 2) & 7)) << 2);
+            const u32x2 r = lds_read_tr16(T + off);
+            out[g][2 * half] = r[0];
+            out[g][2 * half + 1] = r[1];
+        }
+    }
+}
+
+// dV kernel: the wave's key fragments are loaded in perm32 order, so each
+// lane's score registers hold one whole 16-key P group.
 template <int D, bool QP>
 struct BwdDv {
     static constexpr int BM = 64;
@@ -588,18 +620,26 @@ struct BwdDv {
                 s = mfma(kf[cc], *(const u32x4*)(sQ + toff<D>(row, 2 * cc + hh)), s);
             lds_mfma_chain<D / 16, 4>();
             const float L = sL[row];
-            float p[16];
+            float x[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], c, -L));
-                if (TAILK && k0 + acc_row(r, hh) >= Nk) p[r] = 0.0f;
+                x[r] = s[r];
+                if (TAILK && k0 + 16 * hh + r >= Nk) x[r] = -INFINITY;
             }
+            u32x4 pw[2];
             if (QP) {
-                quant_group8_hw(p);
-                quant_group8_hw(p + 8);
+                quant_p_group16<false>(x, c, L, pw);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) x[r] = __builtin_amdgcn_exp2f(fmaf(x[r], c, -L));
+#pragma unroll
+                for (int g = 0; g < 2; ++g)
+                    pw[g] = u32x4{pack_rne(x[8 * g], x[8 * g + 1]), pack_rne(x[8 * g + 2], x[8 * g + 3]),
+                                  pack_rne(x[8 * g + 4], x[8 * g + 5]),
+                                  pack_rne(x[8 * g + 6], x[8 * g + 7])};
             }
             u32x4 pT[2];
-            transpose_tile(p, T, pT, lane);
+            transpose_tile_p32(pw, T, pT, lane);
 #pragma unroll
             for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
@@ -653,13 +693,15 @@ struct BwdDk {
     }
 };
 
-// Per-lane K (and V) A-operand fragments of this wave's 32 keys.
-template <int D>
+// Per-lane K (and V) A-operand fragments of this wave's 32 keys (row l32 of
+// the score tile holds key k0 + perm32(l32) with PERM32).
+template <int D, bool PERM32 = false>
 __device__ __forceinline__ void load_key_frags(const uint16_t* X, int bh, int Nk_pad, int k0, int l32,
                                                int hh, u32x4* f) {
+    const int row = k0 + (PERM32 ? perm32(l32) : l32);
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
-        f[c] = *(const u32x4*)(X + ((size_t)bh * Nk_pad + k0 + l32) * D + c * 16 + hh * 8);
+        f[c] = *(const u32x4*)(X + ((size_t)bh * Nk_pad + row) * D + c * 16 + hh * 8);
 }
 
 // Query-tile visiting order of a key workgroup: every 64-query tile (dense) or
@@ -692,7 +734,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dv_kernel(AttnArgs a) {
     const uint16_t* dOtb = a.dOt + (size_t)bh * D * a.Nq_pad;
     const float* Lb = a.lse2 + (size_t)bh * a.Nq_pad;
     u32x4 kf[D / 16];
-    load_key_frags<D>(a.Kw, bh, a.Nk_pad, k0, l32, hh, kf);
+    load_key_frags<D, true>(a.Kw, bh, a.Nk_pad, k0, l32, hh, kf);
     f32x16 dva[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) dva[db] = f32x16{};
