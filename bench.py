@@ -34,11 +34,11 @@ METRIC = "Attn-QAT fwd+bwd ms & TFLOP/s (% BF16 MFMA peak), H=6 N=31200 d=128"
 
 # Algorithmic FLOPs per (query, key) pair and head dimension unit, per kernel:
 # products the method needs at least once. fwd_out: S and P V (4 d);
-# bwd_dv: S, dV (4 d); bwd_dk: dP, dK (4 d), its S is recomputation;
-# bwd_dq: dQ only (2 d), its S and dP are recomputation; fwd_lse: none (it
-# recomputes S for the statistics). EXEC counts the products each kernel runs.
-ALGO_PER_PAIR = {"fwd_out": 4, "bwd_dv": 4, "bwd_dk": 4, "bwd_dq": 2, "fwd_lse": 0}
-EXEC_PER_PAIR = {"fwd_out": 4, "bwd_dv": 4, "bwd_dk": 6, "bwd_dq": 6, "fwd_lse": 2}
+# bwd_dkdv: S, dV, dP, dK (8 d); bwd_dq: dQ only (2 d), its S and dP are
+# recomputation; fwd_lse: none (it recomputes S for the statistics). EXEC
+# counts the products each kernel runs.
+ALGO_PER_PAIR = {"fwd_out": 4, "bwd_dkdv": 8, "bwd_dq": 2, "fwd_lse": 0}
+EXEC_PER_PAIR = {"fwd_out": 4, "bwd_dkdv": 8, "bwd_dq": 6, "fwd_lse": 2}
 # Algorithmic HBM bytes per launch of the memory-bound kernels (square
 # problems): fake quantization and the transposed copies read and write each
 # bf16 element once (4 B); the preprocess reads O and dO and writes D (4 d + 4

@@ -66,12 +66,12 @@ int hip_check(hipError_t e, const char* what) {
 // ---------------------------------------------------------------------------
 // optional per-thread kernel timing
 enum Kind {
-    K_FQ_D, K_FQ_N, K_TRANSPOSE, K_FWD_LSE, K_FWD_OUT, K_BWD_PRE, K_BWD_DV, K_BWD_DK, K_BWD_DQ,
+    K_FQ_D, K_FQ_N, K_TRANSPOSE, K_FWD_LSE, K_FWD_OUT, K_BWD_PRE, K_BWD_DKDV, K_BWD_DQ,
     K_BLOCK_POOL, K_BLOCK_TOPK, K_REVERSE_INDEX, K_NUM
 };
 const char* const kKindName[K_NUM] = {
-    "fq_axis_d", "fq_axis_n", "transpose_perm", "fwd_lse", "fwd_out", "bwd_pre", "bwd_dv",
-    "bwd_dk", "bwd_dq", "block_pool", "block_topk", "reverse_index"};
+    "fq_axis_d", "fq_axis_n", "transpose_perm", "fwd_lse", "fwd_out", "bwd_pre", "bwd_dkdv",
+    "bwd_dq", "block_pool", "block_topk", "reverse_index"};
 
 constexpr int kMaxTimed = 65536;
 
@@ -132,8 +132,9 @@ struct DimArgs {
 hipError_t do_fwd_lse(const DimArgs& d, hipStream_t st) { return aq::launch_fwd_lse(d.a, d.D, st); }
 hipError_t do_fwd_out(const DimArgs& d, hipStream_t st) { return aq::launch_fwd_out(d.a, d.D, st); }
 hipError_t do_bwd_dq(const DimArgs& d, hipStream_t st) { return aq::launch_bwd_dq(d.a, d.D, st); }
-hipError_t do_bwd_dv(const DimArgs& d, hipStream_t st) { return aq::launch_bwd_dv(d.a, d.D, st); }
-hipError_t do_bwd_dk(const DimArgs& d, hipStream_t st) { return aq::launch_bwd_dk(d.a, d.D, st); }
+hipError_t do_bwd_dkdv(const DimArgs& d, hipStream_t st) {
+    return aq::launch_bwd_dkdv(d.a, d.D, st);
+}
 hipError_t do_fq_d_q(const aq::FqArgs& a, hipStream_t st) { return aq::launch_fq_axis_d(a, true, st); }
 hipError_t do_fq_d_c(const aq::FqArgs& a, hipStream_t st) { return aq::launch_fq_axis_d(a, false, st); }
 hipError_t do_fq_n_q(const aq::FqArgs& a, hipStream_t st) { return aq::launch_fq_axis_n(a, true, st); }
@@ -582,8 +583,8 @@ int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const vo
             return rc;
     }
     const DimArgs da{a, (int)pl.D};
-    if ((rc = launch(K_BWD_DV, st, thunk<DimArgs, do_bwd_dv>, &da, "backward dV"))) return rc;
-    if ((rc = launch(K_BWD_DK, st, thunk<DimArgs, do_bwd_dk>, &da, "backward dK"))) return rc;
+    if ((rc = launch(K_BWD_DKDV, st, thunk<DimArgs, do_bwd_dkdv>, &da, "backward dK/dV")))
+        return rc;
     if ((rc = launch(K_BWD_DQ, st, thunk<DimArgs, do_bwd_dq>, &da, "backward dQ"))) return rc;
     return ok();
 }

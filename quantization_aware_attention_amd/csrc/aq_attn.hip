@@ -94,11 +94,11 @@ struct AsyncTile {
     }
 };
 
-// Asynchronous copy of 64 consecutive floats into LDS by one wave.
-__device__ __forceinline__ void async_f32x64(float* lds, const float* g, int lane) {
-    uint32_t o = 4u * (uint32_t)lane;
-    asm volatile("" : "+v"(o));
-    __builtin_amdgcn_global_load_lds((glb_void_t*)((const char*)g + o), (lds_void_t*)lds, 4, 0, 0);
+// Wait until at most N of this wave's vector memory operations are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
 // Wait until this wave's direct-to-LDS loads have landed (vmcnt = 0).
@@ -531,49 +531,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Backward dV and dK: NW waves x 32 keys per workgroup, loop over 64-query
-// tiles. Scores are computed with keys on registers (S^T = K Q^T, the layout
-// in which P's 16-key groups are quantized), so P, Pq and dS have queries on
-// lanes; a per-wave LDS transpose turns them into B operands with queries as
-// the contraction index of dV^T = dO^T Pq and dK^T = Q^T dS. dV and dK run as
-// two kernels: together their per-key accumulators, K and V operands and S/dP
-// tiles do not fit two waves per SIMD, and the vector work (exp, quantization,
-// transposes) only overlaps the matrix work when two waves share a SIMD.
-
-// Transpose a 32 x 32 tile held as accumulator-layout values (lane = query
-// l32, registers r -> key acc_row(r, hh)) into two B operands with keys on
+// Backward helpers. Scores are computed with keys on the accumulator rows
+// (S^T = K Q^T, perm32 key order: lane half hh holds keys 16 hh + r), the
+// layout in which P's 16-key groups are quantized, so P, Pq and dS have
+// queries on lanes; a per-wave LDS transpose turns them into B operands with
+// queries as the contraction index of dV^T = dO^T Pq and dK^T = Q^T dS.
+//
+// Transpose a 32 x 32 score tile packed as bf16 pairs (w[g][k] holds keys
+// 16 hh + 8 g + 2 k and + 1 of query l32) into two B operands with keys on
 // lanes and queries 16 g + 8 hh + j on the k-slots. Row = query, 64 bytes per
 // row; 8-byte column chunks are XOR-swizzled by (row / 4) % 8 so that the
 // row writes and the transposing column reads avoid bank conflicts.
-__device__ __forceinline__ void transpose_tile(const float* v, uint16_t* T, u32x4* out, int lane) {
-    const int l32 = lane & 31, hh = lane >> 5;
-    const int wsw = (l32 >> 2) & 7;
-    const int grp = lane >> 4, i16 = lane & 15;
-#pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-        const int off = l32 * 32 + (((2 * a4 + hh) ^ wsw) << 2);
-        u32x2 w;
-        w[0] = pack_rne(v[4 * a4], v[4 * a4 + 1]);
-        w[1] = pack_rne(v[4 * a4 + 2], v[4 * a4 + 3]);
-        *(u32x2*)(T + off) = w;
-    }
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int trow = 16 * g + 8 * hh + 4 * half + (i16 >> 2);
-            const int col8 = 4 * (grp & 1) + (i16 & 3);
-            const int off = trow * 32 + ((col8 ^ ((trow >> 2) & 7)) << 2);
-            const u32x2 r = lds_read_tr16(T + off);
-            out[g][2 * half] = r[0];
-            out[g][2 * half + 1] = r[1];
-        }
-    }
-}
-
-// As transpose_tile, for a score tile whose rows are in perm32 key order
-// (lane half hh holds keys 16 hh + r) and whose values arrive packed as bf16
-// pairs: w[g][k] holds keys 16 hh + 8 g + 2 k and + 1.
 __device__ __forceinline__ void transpose_tile_p32(const u32x4* w, uint16_t* T, u32x4* out,
                                                    int lane) {
     const int l32 = lane & 31, hh = lane >> 5;
@@ -601,98 +569,6 @@ __device__ __forceinline__ void transpose_tile_p32(const u32x4* w, uint16_t* T, 
     }
 }
 
-// dV kernel: the wave's key fragments are loaded in perm32 order, so each
-// lane's score registers hold one whole 16-key P group.
-template <int D, bool QP>
-struct BwdDv {
-    static constexpr int BM = 64;
-    template <bool TAILK>
-    __device__ static void block(const uint16_t* sQ, const uint16_t* sdOt, const float* sL,
-                                 uint16_t* T, int k0, int Nk, const u32x4* kf, float c, f32x16* dva,
-                                 int lane) {
-        const int l32 = lane & 31, hh = lane >> 5;
-#pragma unroll
-        for (int qb = 0; qb < BM / 32; ++qb) {
-            const int row = qb * 32 + l32;
-            f32x16 s = {};
-#pragma unroll
-            for (int cc = 0; cc < D / 16; ++cc)
-                s = mfma(kf[cc], *(const u32x4*)(sQ + toff<D>(row, 2 * cc + hh)), s);
-            lds_mfma_chain<D / 16, 4>();
-            const float L = sL[row];
-            float x[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                x[r] = s[r];
-                if (TAILK && k0 + 16 * hh + r >= Nk) x[r] = -INFINITY;
-            }
-            u32x4 pw[2];
-            if (QP) {
-                quant_p_group16<false>(x, c, L, pw);
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) x[r] = __builtin_amdgcn_exp2f(fmaf(x[r], c, -L));
-#pragma unroll
-                for (int g = 0; g < 2; ++g)
-                    pw[g] = u32x4{pack_rne(x[8 * g], x[8 * g + 1]), pack_rne(x[8 * g + 2], x[8 * g + 3]),
-                                  pack_rne(x[8 * g + 4], x[8 * g + 5]),
-                                  pack_rne(x[8 * g + 6], x[8 * g + 7])};
-            }
-            u32x4 pT[2];
-            transpose_tile_p32(pw, T, pT, lane);
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    const int off = toff<BM>(db * 32 + l32, 4 * qb + 2 * g + hh);
-                    dva[db] = mfma(*(const u32x4*)(sdOt + off), pT[g], dva[db]);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-};
-
-template <int D>
-struct BwdDk {
-    static constexpr int BM = 64;
-    __device__ static void block(const uint16_t* sQ, const uint16_t* sdO, const uint16_t* sQt,
-                                 const float* sL, const float* sDl, uint16_t* T, const u32x4* kf,
-                                 const u32x4* vf, float c, f32x16* dka, int lane) {
-        const int l32 = lane & 31, hh = lane >> 5;
-#pragma unroll
-        for (int qb = 0; qb < BM / 32; ++qb) {
-            const int row = qb * 32 + l32;
-            f32x16 s = {}, dp = {};
-#pragma unroll
-            for (int cc = 0; cc < D / 16; ++cc) {
-                s = mfma(kf[cc], *(const u32x4*)(sQ + toff<D>(row, 2 * cc + hh)), s);
-                dp = mfma(vf[cc], *(const u32x4*)(sdO + toff<D>(row, 2 * cc + hh)), dp);
-            }
-            lds_mfma_chain<D / 8, 4>();
-            const float L = sL[row];
-            const float Dl = sDl[row];
-            float ds[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -L));
-                ds[r] = p * (dp[r] - Dl);
-            }
-            u32x4 dT[2];
-            transpose_tile(ds, T, dT, lane);
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    const int off = toff<BM>(db * 32 + l32, 4 * qb + 2 * g + hh);
-                    dka[db] = mfma(*(const u32x4*)(sQt + off), dT[g], dka[db]);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-};
-
 // Per-lane K (and V) A-operand fragments of this wave's 32 keys (row l32 of
 // the score tile holds key k0 + perm32(l32) with PERM32).
 template <int D, bool PERM32 = false>
@@ -714,121 +590,272 @@ __device__ __forceinline__ int query_tiles(const AttnArgs& a, int bh, int kblk, 
     return 2 * cnt;
 }
 
-template <int D, bool QP, int NW, bool SPARSE>
-__global__ __launch_bounds__(NW * 64) void bwd_dv_kernel(AttnArgs a) {
-    constexpr int BM = 64, NT = NW * 64, KW = NW * 32;
-    static_assert(!SPARSE || NW == 4, "sparse key workgroups cover one key block");
-    struct Buf {
-        uint16_t q[BM * D];
-        uint16_t ot[D * BM];
-        float l[BM];
-    };
-    __shared__ __attribute__((aligned(1024))) Buf s0, s1;
-    __shared__ __attribute__((aligned(1024))) uint16_t sT[NW][32 * 32];
-    __shared__ int lst[SPARSE ? kMaxBlockList : 1];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int l32 = lane & 31, hh = lane >> 5;
-    const int bh = blockIdx.y, kblk = blockIdx.x;
-    const int k0 = kblk * KW + wave * 32;
-    const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
-    const uint16_t* dOtb = a.dOt + (size_t)bh * D * a.Nq_pad;
-    const float* Lb = a.lse2 + (size_t)bh * a.Nq_pad;
-    u32x4 kf[D / 16];
-    load_key_frags<D, true>(a.Kw, bh, a.Nk_pad, k0, l32, hh, kf);
-    f32x16 dva[D / 32];
+// ---------------------------------------------------------------------------
+// Backward dK and dV in one kernel. A workgroup owns 128 keys and runs 8
+// waves, two per SIMD: "P" wave w (waves 0..3) and "dS" wave w + 4 share the
+// same 32 keys (perm32 order, so that a lane's score registers hold one whole
+// P group) and the same SIMD.
+//   P wave:  S^T = K Q^T; P = exp(S - LSE), Pq = FQ(P); P to the dS wave
+//            through LDS; dV^T += dO^T Pq          (K fragments, dV^T in registers)
+//   dS wave: dP^T = V dO^T; dS = P (dP - Dl); dK^T += Q^T dS
+//                                                 (V fragments, dK^T in registers)
+// Each wave needs under 256 registers, so the two share a SIMD and the
+// hardware interleaves one wave's vector work (exp, quantization) with the
+// other's matrix products; S is computed once.
+//
+// Only the transposed query tiles are staged: Q^T, dO^T ([D][64], swizzled)
+// and the row statistics. The Q and dO operands of S^T and dP^T are read
+// from them with transposing LDS reads. Tiles live in a ring of three
+// buffers. The P wave runs one 32-query sub-block ahead of the dS wave: step
+// u computes sub-block u in the P wave and sub-block u - 1 in the dS wave,
+// so P crosses between them through a double-buffered exchange with a single
+// barrier per step. Tile t is read in steps 2t .. 2t + 2; its buffer is
+// refilled with tile t + 3 right after step 2t + 2, three steps before use.
+// The tile loads are LDS-DMA instructions issued in inline assembly, which
+// keeps them out of the compiler's wait-count tracking: the kernel waits for
+// them itself, and only where a tile is first needed.
+template <int D>
+struct KVTile {
+    static constexpr int BM = 64;
+    uint16_t qt[D * BM];
+    uint16_t ot[D * BM];
+    float st[2 * BM];  // LSE * log2(e) for the BM queries, then Dl
+};
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16-byte (and 4-byte) LDS-DMA copies: lane i's global bytes land at LDS
+// byte address lds + 16 i (+ 4 i). lds and g are wave-uniform.
+__device__ __forceinline__ const void* uniform_ptr(const void* g) {
+    const uint64_t v = (uint64_t)g;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void*)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void dma16(uint32_t lds, const void* g, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_ptr(g))
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(uint32_t lds, const void* g, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_ptr(g))
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+
+// B operand of S^T = K Q^T (or dP^T = V dO^T) for d-chunk cc of a 32-query
+// sub-block, read from a [D][64] transposed tile: lane (hh, c) gets the 8
+// values at d = 16 cc + 8 hh + 0..7 of query c. Lanes 4 j .. 4 j + 3 of each
+// 16-lane group point at row 16 cc + 8 hh + j (and + 4), 4 queries apart,
+// so the transposing read hands every lane its query's column.
+template <int D>
+__device__ __forceinline__ u32x4 bop_tr(const uint16_t* t, int sb, int cc, int lane) {
+    const int G = lane >> 4, i = lane & 15;
+    const int hh = G >> 1, j = i >> 2, q = i & 3;
+    const int col = sb * 32 + 16 * (G & 1) + 4 * q;
+    const int row = 16 * cc + 8 * hh + j;
+    const u32x2 lo = lds_read_tr16(t + toff<64>(row, col >> 3) + (col & 7));
+    const u32x2 hi = lds_read_tr16(t + toff<64>(row + 4, col >> 3) + (col & 7));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// S^T (or dP^T) of sub-block sb: A = the wave's key fragments.
+template <int D>
+__device__ __forceinline__ f32x16 scores_tr(const uint16_t* t, int sb, const u32x4* f, int lane) {
+    f32x16 a = {};
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) dva[db] = f32x16{};
-    const int n_iter = query_tiles<SPARSE>(a, bh, kblk, lst);
-    if (n_iter > 0) {
-        AsyncTile<BM, D, NT> tr;
-        AsyncTile<D, BM, NT> tc;
-        tr.init(D, tid);
-        tc.init(a.Nq_pad, tid);
-        auto issue = [&](auto b, int it) {
-            const int qt = tile_start<SPARSE, BM>(lst, it);
-            Buf* t = sel(b, &s0, &s1);
-            tr.issue(t->q, Qb + (size_t)qt * D);
-            tc.issue(t->ot, dOtb + qt);
-            if (wave == 0) async_f32x64(t->l, Lb + qt, lane);
-        };
-        // keys beyond Nk exist only in the last key workgroup: mask them there
-        // only (they would enter the maxima of the last P groups)
-        if (kblk * KW + KW > a.Nk)
-            tile_pipeline(n_iter, false, issue, [&](auto b, int, auto) {
-                Buf* t = sel(b, &s0, &s1);
-                BwdDv<D, QP>::template block<true>(t->q, t->ot, t->l, sT[wave], k0, a.Nk, kf, a.c,
-                                                   dva, lane);
-            });
-        else
-            tile_pipeline(n_iter, false, issue, [&](auto b, int, auto) {
-                Buf* t = sel(b, &s0, &s1);
-                BwdDv<D, QP>::template block<false>(t->q, t->ot, t->l, sT[wave], k0, a.Nk, kf, a.c,
-                                                    dva, lane);
-            });
-    }
-    const int key = k0 + l32;
-    if (key < a.Nk) {
-        const int64_t b = bh / a.H, h = bh % a.H;
-        store_rows_T<D>(a.dv + b * a.dvsb + h * a.dvsh + (int64_t)key * a.dvsn, dva, 1.0f, hh);
+    for (int cc = 0; cc < D / 16; ++cc) a = mfma(f[cc], bop_tr<D>(t, sb, cc, lane), a);
+    return a;
+}
+
+// X^T += A^T B for sub-block sb: A^T rows from a [D][64] tile, B transposed.
+template <int D>
+__device__ __forceinline__ void accum_T(const uint16_t* t, int sb, const u32x4* bT, f32x16* acc,
+                                        int l32, int hh) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const int off = toff<64>(db * 32 + l32, 4 * sb + 2 * g + hh);
+            acc[db] = mfma(*(const u32x4*)(t + off), bT[g], acc[db]);
+        }
     }
 }
 
-template <int D, int NW, bool SPARSE>
-__global__ __launch_bounds__(NW * 64) void bwd_dk_kernel(AttnArgs a) {
-    constexpr int BM = 64, NT = NW * 64, KW = NW * 32;
-    static_assert(!SPARSE || NW == 4, "sparse key workgroups cover one key block");
-    struct Buf {
-        uint16_t q[BM * D];
-        uint16_t o[BM * D];
-        uint16_t qt[D * BM];
-        float l[BM];
-        float d[BM];
-    };
-    __shared__ __attribute__((aligned(1024))) Buf s0, s1;
-    __shared__ __attribute__((aligned(1024))) uint16_t sT[NW][32 * 32];
+// P exchange slot of one wave pair: 16 floats per lane, stored as four
+// 16-byte chunks with lanes contiguous inside each chunk row.
+__device__ __forceinline__ void put_p(float* X, const float* p, int lane) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        *(f32x4_t*)(X + (j * 64 + lane) * 4) = f32x4_t{p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]};
+}
+__device__ __forceinline__ void get_p(const float* X, float* p, int lane) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const f32x4_t v = *(const f32x4_t*)(X + (j * 64 + lane) * 4);
+        p[4 * j] = v[0];
+        p[4 * j + 1] = v[1];
+        p[4 * j + 2] = v[2];
+        p[4 * j + 3] = v[3];
+    }
+}
+
+template <int D, bool QP, bool SPARSE>
+__global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnArgs a) {
+    using Tile = KVTile<D>;
+    constexpr int BM = Tile::BM, KW = 128;
+    // loads per wave per tile: Q^T and dO^T (D * BM * 2 bytes each, in 1 KB
+    // DMA blocks over 8 waves) and one 64-byte slice of the statistics
+    constexpr int NJ = 2 * D * BM * 2 / 1024 / 8;
+    constexpr int NL = NJ + 1;
+    static_assert(2 * D * BM * 2 % 8192 == 0, "tile splits into whole DMA blocks per wave");
+    __shared__ __attribute__((aligned(1024))) Tile ring[3];
+    __shared__ __attribute__((aligned(1024))) float sX[2][4][16 * 64];  // P exchange
+    __shared__ __attribute__((aligned(1024))) uint16_t sTa[4][32 * 32];  // P waves' transposes
     __shared__ int lst[SPARSE ? kMaxBlockList : 1];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pair = wave & 3;
+    const bool pw_role = wave < 4;  // P wave (else dS wave); wave-uniform
     const int l32 = lane & 31, hh = lane >> 5;
     const int bh = blockIdx.y, kblk = blockIdx.x;
-    const int k0 = kblk * KW + wave * 32;
-    const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
-    const uint16_t* dOb = a.dOw + (size_t)bh * a.Nq_pad * D;
+    const int k0 = kblk * KW + pair * 32;
     const uint16_t* Qtb = a.Qt + (size_t)bh * D * a.Nq_pad;
-    const float* Lb = a.lse2 + (size_t)bh * a.Nq_pad;
-    const float* Db = a.delta + (size_t)bh * a.Nq_pad;
-    u32x4 kf[D / 16], vf[D / 16];
-    load_key_frags<D>(a.Kw, bh, a.Nk_pad, k0, l32, hh, kf);
-    load_key_frags<D>(a.Vw, bh, a.Nk_pad, k0, l32, hh, vf);
-    f32x16 dka[D / 32];
+    const uint16_t* dOtb = a.dOt + (size_t)bh * D * a.Nq_pad;
+    // statistics slice of this wave: waves 0..3 LSE2, 4..7 Dl, 16 queries each
+    const float* Sb = (pw_role ? a.lse2 : a.delta) + (size_t)bh * a.Nq_pad + pair * 16;
+    // K fragments (P wave) or V fragments (dS wave)
+    u32x4 f[D / 16];
+    load_key_frags<D, true>(pw_role ? a.Kw : a.Vw, bh, a.Nk_pad, k0, l32, hh, f);
+    // let the fragments land before any tile copy is issued: the copies are
+    // invisible to the compiler, whose waits for these loads would otherwise
+    // also wait for the copies in flight
+    wait_vm<0>();
+    f32x16 acc[D / 32];  // dV^T (P wave) or dK^T (dS wave)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) dka[db] = f32x16{};
-    const int n_iter = query_tiles<SPARSE>(a, bh, kblk, lst);
-    if (n_iter > 0) {
-        AsyncTile<BM, D, NT> tr;
-        AsyncTile<D, BM, NT> tc;
-        tr.init(D, tid);
-        tc.init(a.Nq_pad, tid);
-        auto issue = [&](auto b, int it) {
-            const int qt = tile_start<SPARSE, BM>(lst, it);
-            Buf* t = sel(b, &s0, &s1);
-            tr.issue(t->q, Qb + (size_t)qt * D);
-            tr.issue(t->o, dOb + (size_t)qt * D);
-            tc.issue(t->qt, Qtb + qt);
-            if (wave == 0) async_f32x64(t->l, Lb + qt, lane);
-            if (wave == 1) async_f32x64(t->d, Db + qt, lane);
-        };
-        // No key mask: dK of key j depends on column j of P only, and the
-        // rows of keys beyond Nk (zero-padded operands) are never stored.
-        tile_pipeline(n_iter, false, issue, [&](auto b, int, auto) {
-            Buf* t = sel(b, &s0, &s1);
-            BwdDk<D>::block(t->q, t->o, t->qt, t->l, t->d, sT[wave], kf, vf, a.c, dka, lane);
-        });
+    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+    const int n = query_tiles<SPARSE>(a, bh, kblk, lst);
+    const bool tailk = kblk * KW + KW > a.Nk;
+    // Per-lane source offsets of this wave's DMA blocks in a [D][Nq_pad] tile:
+    // block b = j * 8 + wave covers tile rows 8 b .. 8 b + 7 (64 columns =
+    // 128 bytes each); lane i fills LDS slot 16 i of the block, which holds
+    // logical chunk (i % 8) ^ swz(row) of row 8 b + i / 8.
+    uint32_t goff[NJ / 2];
+#pragma unroll
+    for (int j = 0; j < NJ / 2; ++j) {
+        const int row = (j * 8 + wave) * 8 + (lane >> 3);
+        goff[j] = (uint32_t)(row * a.Nq_pad + (((lane & 7) ^ swz<64>(row)) << 3)) * 2u;
+    }
+    auto issue = [&](int t) {
+        Tile* T = ring + t % 3;
+        const int qt = tile_start<SPARSE, BM>(lst, t);
+#pragma unroll
+        for (int j = 0; j < NJ / 2; ++j) {
+            const uint32_t blk = (uint32_t)((j * 8 + wave) * 512);  // elements
+            dma16(lds_addr(T->qt + blk), Qtb + qt, goff[j]);
+            dma16(lds_addr(T->ot + blk), dOtb + qt, goff[j]);
+        }
+        if (lane < 16) dma4(lds_addr(T->st + wave * 16), Sb + qt, 4u * (uint32_t)lane);
+    };
+    // The whole step loop is instantiated once per role, so that each
+    // wave's accumulators stay in fixed registers. Both instances execute
+    // the same barriers (one per step).
+    auto run = [&](auto role, auto tail) {
+        constexpr bool PW = decltype(role)::value;
+        constexpr bool TK = decltype(tail)::value;
+        issue(0);
+        if (n > 1) issue(1);
+        if (n > 1) wait_vm<NL>();
+        else wait_vm<0>();
+        for (int u = 0; u <= 2 * n; ++u) {
+            // before step u: tile u / 2 must be resident (first needed by the
+            // P wave at even u); tile (u - 1) / 2 + 2 refills the buffer freed
+            // by step u - 1 (odd u)
+            if (u > 0 && !(u & 1)) {
+                if (u / 2 + 1 < n) wait_vm<NL>();
+                else wait_vm<0>();
+            }
+            __syncthreads();
+            if ((u & 1) && (u - 1) / 2 + 2 < n) issue((u - 1) / 2 + 2);
+            if (PW) {
+                if (u < 2 * n) {
+                    const Tile* T = ring + (u >> 1) % 3;
+                    const int sb = u & 1;
+                    const f32x16 sd = scores_tr<D>(T->qt, sb, f, lane);
+                    float x[16], p[16];
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        x[j] = sd[j];
+                        if (TK && k0 + 16 * hh + j >= a.Nk) x[j] = -INFINITY;
+                    }
+                    const float L = T->st[sb * 32 + l32];
+                    u32x4 pw[2];
+                    if (QP) {
+                        quant_p_group16_bwd(x, a.c, L, pw, p);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 16; ++j)
+                            p[j] = __builtin_amdgcn_exp2f(fmaf(x[j], a.c, -L));
+#pragma unroll
+                        for (int g = 0; g < 2; ++g)
+                            pw[g] = u32x4{pack_rne(p[8 * g], p[8 * g + 1]),
+                                          pack_rne(p[8 * g + 2], p[8 * g + 3]),
+                                          pack_rne(p[8 * g + 4], p[8 * g + 5]),
+                                          pack_rne(p[8 * g + 6], p[8 * g + 7])};
+                    }
+                    put_p(sX[u & 1][pair], p, lane);
+                    u32x4 bT[2];
+                    transpose_tile_p32(pw, sTa[pair], bT, lane);
+                    accum_T<D>(T->ot, sb, bT, acc, l32, hh);
+                }
+            } else if (u > 0) {
+                const int v = u - 1;
+                const Tile* T = ring + (v >> 1) % 3;
+                const int sb = v & 1;
+                const f32x16 dp = scores_tr<D>(T->ot, sb, f, lane);
+                float* X = sX[v & 1][pair];
+                float p[16];
+                get_p(X, p, lane);
+                const float Dl = T->st[BM + sb * 32 + l32];
+                u32x4 dw[2];
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int j = 8 * g + 2 * k;
+                        w[k] = pack_rne(p[j] * (dp[j] - Dl), p[j + 1] * (dp[j + 1] - Dl));
+                    }
+                    dw[g] = u32x4{w[0], w[1], w[2], w[3]};
+                }
+                u32x4 bT[2];
+                transpose_tile_p32(dw, (uint16_t*)X, bT, lane);
+                accum_T<D>(T->qt, sb, bT, acc, l32, hh);
+            }
+        }
+    };
+    if (n > 0) {
+        // keys beyond Nk exist only in the last key workgroup: mask them there
+        // only (they would enter the maxima of the last P groups)
+        if (pw_role) {
+            if (tailk) run(std::true_type{}, std::true_type{});
+            else run(std::true_type{}, std::false_type{});
+        } else {
+            run(std::false_type{}, std::false_type{});
+        }
     }
     const int key = k0 + l32;
     if (key < a.Nk) {
         const int64_t b = bh / a.H, h = bh % a.H;
-        store_rows_T<D>(a.dk + b * a.dksb + h * a.dksh + (int64_t)key * a.dksn, dka, a.sm_scale,
-                        hh);
+        if (pw_role)
+            store_rows_T<D>(a.dv + b * a.dvsb + h * a.dvsh + (int64_t)key * a.dvsn, acc, 1.0f, hh);
+        else
+            store_rows_T<D>(a.dk + b * a.dksb + h * a.dksh + (int64_t)key * a.dksn, acc, a.sm_scale,
+                            hh);
     }
 }
 
@@ -896,36 +923,23 @@ hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t st) {
 }
 
 template <int D>
-static void dv_d(const AttnArgs& a, bool sp, hipStream_t st) {
+static void dkdv_d(const AttnArgs& a, bool sp, hipStream_t st) {
+    const dim3 g(sp ? a.nbk : (a.Nk + 127) / 128, a.BH);
     if (sp) {
-        dim3 g(a.nbk, a.BH);
-        if (a.quant_p) bwd_dv_kernel<D, true, 4, true><<<g, 256, 0, st>>>(a);
-        else bwd_dv_kernel<D, false, 4, true><<<g, 256, 0, st>>>(a);
+        if (a.quant_p) bwd_dkdv_kernel<D, true, true><<<g, 512, 0, st>>>(a);
+        else bwd_dkdv_kernel<D, false, true><<<g, 512, 0, st>>>(a);
     } else {
-        dim3 g((a.Nk + 255) / 256, a.BH);
-        if (a.quant_p) bwd_dv_kernel<D, true, 8, false><<<g, 512, 0, st>>>(a);
-        else bwd_dv_kernel<D, false, 8, false><<<g, 512, 0, st>>>(a);
+        if (a.quant_p) bwd_dkdv_kernel<D, true, false><<<g, 512, 0, st>>>(a);
+        else bwd_dkdv_kernel<D, false, false><<<g, 512, 0, st>>>(a);
     }
 }
 
-template <int D>
-static void dk_d(const AttnArgs& a, bool sp, hipStream_t st) {
-    if (sp) bwd_dk_kernel<D, 4, true><<<dim3(a.nbk, a.BH), 256, 0, st>>>(a);
-    else bwd_dk_kernel<D, 8, false><<<dim3((a.Nk + 255) / 256, a.BH), 512, 0, st>>>(a);
-}
-
-hipError_t launch_bwd_dv(const AttnArgs& a, int D, hipStream_t st) {
+hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t st) {
     const bool sp = a.q_list != nullptr;
-    if (D == 128) dv_d<128>(a, sp, st);
-    else dv_d<64>(a, sp, st);
+    if (D == 128) dkdv_d<128>(a, sp, st);
+    else dkdv_d<64>(a, sp, st);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_dk(const AttnArgs& a, int D, hipStream_t st) {
-    const bool sp = a.q_list != nullptr;
-    if (D == 128) dk_d<128>(a, sp, st);
-    else dk_d<64>(a, sp, st);
-    return hipGetLastError();
-}
 
 }  // namespace aq

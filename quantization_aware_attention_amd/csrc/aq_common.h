@@ -13,10 +13,12 @@
 //    contraction index: registers r = 0..7 hold k-slots 8h + j of the first
 //    16-row half, r = 8..15 those of the second, with k-slot 8h + j holding
 //    row 8 (j / 4) + 4 h + j % 4 of that half.
-//  * Operands that must be read along the contraction index (K^T, V^T, Q^T,
-//    dO^T) are stored transposed ([D][N]) with the tokens of every 16-token
-//    group permuted so that this k-slot order becomes contiguous: position p
-//    holds token perm16(p), which swaps the 4-token chunks 1 and 2.
+//  * Operands that must be read along the contraction index are stored
+//    transposed ([D][N]). K^T, which multiplies a score tile held in this
+//    accumulator order, has the tokens of every 16-token group permuted so
+//    that the k-slot order becomes contiguous: position p holds token
+//    perm16(p), which swaps the 4-token chunks 1 and 2. Score tiles whose
+//    keys are loaded in perm32 order (below) need no such permutation.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -31,6 +33,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
@@ -70,12 +73,6 @@ __device__ __forceinline__ uint32_t pack_exact(float lo, float hi) {
 __device__ __forceinline__ uint32_t pack_rne(float lo, float hi) {
     f32x2 v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-
-// Maximum of x over lanes l and l ^ 32.
-__device__ __forceinline__ float max_lane_pair(float x) {
-    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
 }
 
 // Value of x held by lane l ^ 32.
@@ -119,53 +116,6 @@ __device__ __forceinline__ float fq_elem_exact(float x, float s) {
     y = (ax >= 3.5f * s) ? 4.0f * s : y;
     y = (ax > 5.0f * s) ? 6.0f * s : y;
     return __builtin_copysignf(y, x);
-}
-
-// E2M1 rounding of r >= 0 (nearest even, saturating at 6), for P.
-// Adding and subtracting C = 2^22 * 2^max(e, 0) (e = binary exponent of r)
-// rounds r to the E2M1 spacing of its binade: 0.5 below 2, 1 in [2, 4),
-// 2 in [4, 8); the fp32 addition rounds to nearest even.
-__device__ __forceinline__ float e2m1_round(float r) {
-    float t = fminf(r, 6.0f);
-    float c = __uint_as_float((__float_as_uint(t) & 0xFF800000u) + (22u << 23));
-    c = fmaxf(c, 4194304.0f);
-    return (t + c) - c;
-}
-
-// NVFP4 fake quantization of one 16-element group of non-negative fp32 values
-// held as 8 registers in each of lanes l and l ^ 32 (the probabilities P),
-// using the CDNA4 conversion units: the group maximum / 6 is rounded to E4M3
-// by an FP8 round trip (nearest even; values here are <= 1/6, far below the
-// 448 saturation point), p / s is rounded to E2M1 by an FP4 round trip (nearest
-// even, saturating at 6, unit scale), and the result is multiplied back by s.
-// The division is a multiplication by a reciprocal, so a tie of the exact reals
-// can be missed only by values within 2^-22 relative of a rounding midpoint.
-__device__ __forceinline__ void quant_group8_hw(float* p) {
-    float am = fmaxf(fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3])),
-                     fmaxf(fmaxf(p[4], p[5]), fmaxf(p[6], p[7])));
-    am = max_lane_pair(am);
-    const i16x2 z = {0, 0};
-    const i16x2 c8 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, am * (1.0f / 6.0f), 0.0f, 1.0f,
-                                                              false);
-    const float s = __builtin_amdgcn_cvt_scalef32_f32_fp8(__builtin_bit_cast(int, c8), 1.0f, 0);
-    const float inv = (s > 0.0f) ? __builtin_amdgcn_rcpf(s) : 0.0f;
-    uint32_t codes = 0u;
-    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, p[0] * inv, p[1] * inv, 1.0f, 0);
-    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, p[2] * inv, p[3] * inv, 1.0f, 1);
-    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, p[4] * inv, p[5] * inv, 1.0f, 2);
-    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, p[6] * inv, p[7] * inv, 1.0f, 3);
-    const f32x2 q0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
-    const f32x2 q1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
-    const f32x2 q2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
-    const f32x2 q3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
-    p[0] = q0[0] * s;
-    p[1] = q0[1] * s;
-    p[2] = q1[0] * s;
-    p[3] = q1[1] * s;
-    p[4] = q2[0] * s;
-    p[5] = q2[1] * s;
-    p[6] = q3[0] * s;
-    p[7] = q3[1] * s;
 }
 
 // Key order inside a 32-key block of a score tile S^T = K Q^T. The MFMA
@@ -233,6 +183,44 @@ __device__ __forceinline__ void quant_p_group16(const float* x, float c, float l
             out[w] = u32x4{pack_rne(q0[0] * s, q0[1] * s), pack_rne(q1[0] * s, q1[1] * s),
                            pack_rne(q2[0] * s, q2[1] * s), pack_rne(q3[0] * s, q3[1] * s)};
         }
+    }
+}
+
+// Backward form of quant_p_group16 (bf16 output): also returns the
+// unquantized probabilities P_j (for dS), recovered as (P_j / s') * s' with
+// s' = s, or 2^-64 for an all-zero group (an exact power-of-two rescaling).
+__device__ __forceinline__ void quant_p_group16_bwd(const float* x, float c, float lse2, u32x4* out,
+                                                    float* p) {
+    float mx = x[0];
+#pragma unroll
+    for (int j = 1; j < 16; ++j) mx = __builtin_fmaxf(mx, x[j]);
+    const float pmax = __builtin_amdgcn_exp2f(__builtin_fmaf(mx, c, -lse2));
+    const float a6 = pmax * (1.0f / 6.0f);
+    const i16x2 z = {0, 0};
+    const i16x2 c8 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, a6, a6, 1.0f, false);
+    const float s = __builtin_amdgcn_cvt_scalef32_f32_fp8(__builtin_bit_cast(int, c8), 1.0f, 0);
+    const float sp = (s > 0.0f) ? s : 0x1p-64f;
+    const float t = lse2 + __builtin_amdgcn_logf(sp);
+    float r[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        r[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], c, -t));
+        p[j] = r[j] * sp;
+    }
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        const float* rw = r + 8 * w;
+        uint32_t cw = 0u;
+        cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, rw[0], rw[1], 1.0f, 0);
+        cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, rw[2], rw[3], 1.0f, 1);
+        cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, rw[4], rw[5], 1.0f, 2);
+        cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, rw[6], rw[7], 1.0f, 3);
+        const f32x2 q0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0);
+        const f32x2 q1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1);
+        const f32x2 q2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 2);
+        const f32x2 q3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 3);
+        out[w] = u32x4{pack_rne(q0[0] * s, q0[1] * s), pack_rne(q1[0] * s, q1[1] * s),
+                       pack_rne(q2[0] * s, q2[1] * s), pack_rne(q3[0] * s, q3[1] * s)};
     }
 }
 

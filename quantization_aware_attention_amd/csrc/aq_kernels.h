@@ -81,8 +81,7 @@ hipError_t launch_bwd_pre(const PreArgs& a, hipStream_t st);
 hipError_t launch_fwd_lse(const AttnArgs& a, int D, hipStream_t st);
 hipError_t launch_fwd_out(const AttnArgs& a, int D, hipStream_t st);
 hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t st);
-hipError_t launch_bwd_dv(const AttnArgs& a, int D, hipStream_t st);
-hipError_t launch_bwd_dk(const AttnArgs& a, int D, hipStream_t st);
+hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t st);
 
 struct SelectArgs {
     const uint16_t* q;
