@@ -39,13 +39,17 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 __device__ __forceinline__ int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
 
 // Swizzle of 16-byte chunks for tiles with W bf16 per row: 256-byte rows XOR
-// the chunk with row % 16, 128-byte rows with (row / 2) % 8. Sixteen
-// consecutive rows read at the same logical chunk then hit 16 distinct bank
-// quads.
+// the chunk with row % 16, 128-byte rows with f((row / 2) % 8), where
+// f(x) = x ^ ((x & 2) << 1) permutes 0..7. Sixteen consecutive rows read at
+// the same logical chunk then hit 16 distinct bank quads; for 128-byte rows
+// f also separates rows 4 apart (f(x) and f(x + 2) differ in bit 2), which
+// keeps the transposing operand reads of the backward conflict-free.
 template <int W>
 __device__ __forceinline__ int swz(int row) {
     static_assert(W == 64 || W == 128, "tile width");
-    return W == 128 ? (row & 15) : ((row >> 1) & 7);
+    if (W == 128) return row & 15;
+    const int x = (row >> 1) & 7;
+    return x ^ ((x & 2) << 1);
 }
 
 // Element offset of logical 16-byte chunk c of row `row` in a swizzled tile.
@@ -648,18 +652,20 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // B operand of S^T = K Q^T (or dP^T = V dO^T) for d-chunk cc of a 32-query
-// sub-block, read from a [D][64] transposed tile: lane (hh, c) gets the 8
-// values at d = 16 cc + 8 hh + 0..7 of query c. Lanes 4 j .. 4 j + 3 of each
-// 16-lane group point at row 16 cc + 8 hh + j (and + 4), 4 queries apart,
-// so the transposing read hands every lane its query's column.
+// sub-block, read from a [D][64] transposed tile: lane (hh, c) gets 8 values
+// of query c at d = 16 cc + 8 hh + {0, 1, 4, 5, 2, 3, 6, 7} (the k-slot
+// order; the A fragments are loaded in the same order). Lanes 4 j .. 4 j + 3
+// of each 16-lane group point at one row, 4 queries apart, so the
+// transposing read hands every lane its query's column; rows {0, 1, 4, 5}
+// and then {2, 3, 6, 7} make the two reads free of bank conflicts.
 template <int D>
 __device__ __forceinline__ u32x4 bop_tr(const uint16_t* t, int sb, int cc, int lane) {
     const int G = lane >> 4, i = lane & 15;
     const int hh = G >> 1, j = i >> 2, q = i & 3;
     const int col = sb * 32 + 16 * (G & 1) + 4 * q;
-    const int row = 16 * cc + 8 * hh + j;
+    const int row = 16 * cc + 8 * hh + (j & 1) + 4 * (j >> 1);
     const u32x2 lo = lds_read_tr16(t + toff<64>(row, col >> 3) + (col & 7));
-    const u32x2 hi = lds_read_tr16(t + toff<64>(row + 4, col >> 3) + (col & 7));
+    const u32x2 hi = lds_read_tr16(t + toff<64>(row + 2, col >> 3) + (col & 7));
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
@@ -731,6 +737,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnArgs a) {
     // K fragments (P wave) or V fragments (dS wave)
     u32x4 f[D / 16];
     load_key_frags<D, true>(pw_role ? a.Kw : a.Vw, bh, a.Nk_pad, k0, l32, hh, f);
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) f[cc] = u32x4{f[cc][0], f[cc][2], f[cc][1], f[cc][3]};
     // let the fragments land before any tile copy is issued: the copies are
     // invisible to the compiler, whose waits for these loads would otherwise
     // also wait for the copies in flight
