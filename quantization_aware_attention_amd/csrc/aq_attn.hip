@@ -237,6 +237,22 @@ __device__ __forceinline__ void mfma_valu_chain() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Issue order for N MFMAs fed by N / M LDS reads (M products per operand):
+// PRE reads first, then after every M MFMAs the next read, with V vector
+// instructions after each MFMA. Ends the scheduling region.
+template <int N, int M, int PRE, int V>
+__device__ __forceinline__ void mfma_chain_m() {
+    constexpr int NR = N / M;
+    __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i % M == M - 1 && i / M < NR - PRE) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (V > 0) __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---------------------------------------------------------------------------
 // Forward pass 1: LSE per query row. 4 waves x 32 queries, 64-key tiles.
 template <int D>
@@ -427,56 +443,91 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_out_kernel(AttnA
 
 // ---------------------------------------------------------------------------
 // Backward dQ: NW waves x 32 queries, loop over 64-key tiles.
-template <int D>
+// Backward dQ: NW waves x 32 QB queries, loop over 64-key tiles. A wave
+// keeps the Q and dO B operands of its QB 32-query blocks in registers; each
+// K, V or K^T operand read from LDS feeds QB products.
+template <int D, int QB>
 struct BwdDq {
     static constexpr int BN = 64;
+
+    // S^T and dP^T of 32-key block kb for the wave's query blocks.
+    __device__ static void sdp(const uint16_t* sK, const uint16_t* sV, int kb, const u32x4 (*qf)[D / 16],
+                               const u32x4 (*df)[D / 16], f32x16* s, f32x16* dp, int l32, int hh) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb] = dp[qb] = f32x16{};
+#pragma unroll
+        for (int cc = 0; cc < D / 16; ++cc) {
+            const int row = kb * 32 + l32;
+            const u32x4 ka = *(const u32x4*)(sK + toff<D>(row, 2 * cc + hh));
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) s[qb] = mfma(ka, qf[qb][cc], s[qb]);
+            const u32x4 va = *(const u32x4*)(sV + toff<D>(row, 2 * cc + hh));
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) dp[qb] = mfma(va, df[qb][cc], dp[qb]);
+        }
+    }
+
+    // dS = P (dP - Dl) of one block as two bf16 B operands.
+    template <bool tail>
+    __device__ static void dsop(const f32x16& s, const f32x16& dp, int k0, int Nk, float c,
+                                float lse2, float dl, int hh, u32x4* bfr) {
+        float ds[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
+            if (tail && k0 + acc_row(r, hh) >= Nk) p = 0.0f;
+            ds[r] = p * (dp[r] - dl);
+        }
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+            bfr[g] = u32x4{pack_rne(ds[8 * g + 0], ds[8 * g + 1]), pack_rne(ds[8 * g + 2], ds[8 * g + 3]),
+                           pack_rne(ds[8 * g + 4], ds[8 * g + 5]), pack_rne(ds[8 * g + 6], ds[8 * g + 7])};
+    }
+
+    // dQ^T += Kt dS^T for block kb.
+    __device__ static void dq(const uint16_t* sKt, int kb, const u32x4 (*bfr)[2], f32x16 (*dqa)[D / 32],
+                              int l32, int hh) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const u32x4 ktf = *(const u32x4*)(sKt + toff<BN>(db * 32 + l32, 4 * kb + 2 * g + hh));
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb) dqa[qb][db] = mfma(ktf, bfr[qb][g], dqa[qb][db]);
+            }
+        }
+    }
+
+    // Two 32-key blocks, software-pipelined so that the vector work of one
+    // (exp, dS, packing) is issued between the matrix products of the other:
+    //   S/dP 0 | S/dP 1 + dS 0 | dQ 0 + dS 1 | dQ 1.
     template <bool tail>
     __device__ static void block(const uint16_t* sK, const uint16_t* sV, const uint16_t* sKt,
-                                 int kt, int Nk, const u32x4* qf, const u32x4* df, float c,
-                                 float lse2, float dl, f32x16* dqa, int l32, int hh) {
+                                 int kt, int Nk, const u32x4 (*qf)[D / 16], const u32x4 (*df)[D / 16],
+                                 float c, const float* lse2, const float* dl, f32x16 (*dqa)[D / 32],
+                                 int l32, int hh) {
+        f32x16 s0[QB], dp0[QB], s1[QB], dp1[QB];
+        u32x4 b0[QB][2], b1[QB][2];
+        sdp(sK, sV, 0, qf, df, s0, dp0, l32, hh);
+        mfma_chain_m<QB * D / 8, QB, 4, 0>();
+        sdp(sK, sV, 1, qf, df, s1, dp1, l32, hh);
 #pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
-            f32x16 s = {}, dp = {};
+        for (int qb = 0; qb < QB; ++qb) dsop<tail>(s0[qb], dp0[qb], kt, Nk, c, lse2[qb], dl[qb], hh, b0[qb]);
+        mfma_chain_m<QB * D / 8, QB, 4, 5 / QB>();
+        dq(sKt, 0, b0, dqa, l32, hh);
 #pragma unroll
-            for (int cc = 0; cc < D / 16; ++cc) {
-                const int row = kb * 32 + l32;
-                const u32x4 kf = *(const u32x4*)(sK + toff<D>(row, 2 * cc + hh));
-                s = mfma(kf, qf[cc], s);
-                const u32x4 vf = *(const u32x4*)(sV + toff<D>(row, 2 * cc + hh));
-                dp = mfma(vf, df[cc], dp);
-            }
-            lds_mfma_chain<D / 8, 4>();
-            float ds[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
-                if (tail && kt + kb * 32 + acc_row(r, hh) >= Nk) p = 0.0f;
-                ds[r] = p * (dp[r] - dl);
-            }
-            u32x4 bfr[2];
-#pragma unroll
-            for (int g = 0; g < 2; ++g)
-                bfr[g] = u32x4{pack_rne(ds[8 * g + 0], ds[8 * g + 1]),
-                               pack_rne(ds[8 * g + 2], ds[8 * g + 3]),
-                               pack_rne(ds[8 * g + 4], ds[8 * g + 5]),
-                               pack_rne(ds[8 * g + 6], ds[8 * g + 7])};
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    const u32x4 ktf =
-                        *(const u32x4*)(sKt + toff<BN>(db * 32 + l32, 4 * kb + 2 * g + hh));
-                    dqa[db] = mfma(ktf, bfr[g], dqa[db]);
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int qb = 0; qb < QB; ++qb)
+            dsop<tail>(s1[qb], dp1[qb], kt + 32, Nk, c, lse2[qb], dl[qb], hh, b1[qb]);
+        mfma_chain_m<QB * D / 16, QB, 4, kValuPerMfma>();
+        dq(sKt, 1, b1, dqa, l32, hh);
+        mfma_chain_m<QB * D / 16, QB, 4, 0>();
     }
 };
 
-template <int D, int NW, bool SPARSE>
+template <int D, int NW, int QB, bool SPARSE>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
-    constexpr int BN = BwdDq<D>::BN, NT = NW * 64;
+    using DQ = BwdDq<D, QB>;
+    constexpr int BN = DQ::BN, NT = NW * 64;
     struct Buf {
         uint16_t k[BN * D];
         uint16_t v[BN * D];
@@ -486,26 +537,32 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
     const int bh = blockIdx.y, qblk = blockIdx.x;
-    const int q0 = qblk * (NW * 32) + wave * 32;
-    const int q = q0 + l32;
+    const int q0 = qblk * (NW * 32 * QB) + wave * 32 * QB;
     const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
     const uint16_t* dOb = a.dOw + (size_t)bh * a.Nq_pad * D;
     const uint16_t* Kb = a.Kw + (size_t)bh * a.Nk_pad * D;
     const uint16_t* Vb = a.Vw + (size_t)bh * a.Nk_pad * D;
     const uint16_t* Ktb = a.Kt + (size_t)bh * D * a.Nk_pad;
-    u32x4 qf[D / 16], df[D / 16];
+    u32x4 qf[QB][D / 16], df[QB][D / 16];
+    float lse2[QB], dl[QB];
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-        qf[c] = *(const u32x4*)(Qb + (size_t)q * D + c * 16 + hh * 8);
-        df[c] = *(const u32x4*)(dOb + (size_t)q * D + c * 16 + hh * 8);
+    for (int qb = 0; qb < QB; ++qb) {
+        const int q = q0 + qb * 32 + l32;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) {
+            qf[qb][c] = *(const u32x4*)(Qb + (size_t)q * D + c * 16 + hh * 8);
+            df[qb][c] = *(const u32x4*)(dOb + (size_t)q * D + c * 16 + hh * 8);
+        }
+        lse2[qb] = a.lse2[(size_t)bh * a.Nq_pad + q];
+        dl[qb] = a.delta[(size_t)bh * a.Nq_pad + q];
     }
-    const float lse2 = a.lse2[(size_t)bh * a.Nq_pad + q];
-    const float dl = a.delta[(size_t)bh * a.Nq_pad + q];
-    f32x16 dqa[D / 32];
+    f32x16 dqa[QB][D / 32];
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) dqa[db] = f32x16{};
-    // sparse launches use NW = 4 so that a workgroup is one 128-query block
-    static_assert(!SPARSE || NW == 4, "sparse dQ workgroups cover one query block");
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) dqa[qb][db] = f32x16{};
+    // sparse launches use NW = 4, QB = 1 so that a workgroup is one 128-query block
+    static_assert(!SPARSE || (NW == 4 && QB == 1), "sparse dQ workgroups cover one query block");
     __shared__ int lst[SPARSE ? kMaxBlockList : 1];
     if (SPARSE) stage_list(lst, a.kv_idx + ((size_t)bh * a.nbq + qblk) * a.topk, a.topk);
     const int n_iter = SPARSE ? a.topk * 2 : (a.Nk + BN - 1) / BN;
@@ -525,12 +582,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
         },
         [&](auto b, int it, auto tail) {
             Buf* t = sel(b, &s0, &s1);
-            BwdDq<D>::template block<decltype(tail)::value>(t->k, t->v, t->kt, tile_at(it), a.Nk, qf,
-                                                            df, a.c, lse2, dl, dqa, l32, hh);
+            DQ::template block<decltype(tail)::value>(t->k, t->v, t->kt, tile_at(it), a.Nk, qf, df,
+                                                      a.c, lse2, dl, dqa, l32, hh);
         });
-    if (q < a.Nq) {
-        const int64_t b = bh / a.H, h = bh % a.H;
-        store_rows_T<D>(a.dq + b * a.dqsb + h * a.dqsh + (int64_t)q * a.dqsn, dqa, a.sm_scale, hh);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int q = q0 + qb * 32 + l32;
+        if (q < a.Nq) {
+            const int64_t b = bh / a.H, h = bh % a.H;
+            store_rows_T<D>(a.dq + b * a.dqsb + h * a.dqsh + (int64_t)q * a.dqsn, dqa[qb], a.sm_scale,
+                            hh);
+        }
     }
 }
 
@@ -920,12 +982,12 @@ hipError_t launch_fwd_out(const AttnArgs& a, int D, hipStream_t st) {
 hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t st) {
     if (a.kv_idx) {
         dim3 grid(a.nbq, a.BH);
-        if (D == 128) bwd_dq_kernel<128, 4, true><<<grid, 256, 0, st>>>(a);
-        else bwd_dq_kernel<64, 4, true><<<grid, 256, 0, st>>>(a);
+        if (D == 128) bwd_dq_kernel<128, 4, 1, true><<<grid, 256, 0, st>>>(a);
+        else bwd_dq_kernel<64, 4, 1, true><<<grid, 256, 0, st>>>(a);
     } else {
         dim3 grid((a.Nq + 255) / 256, a.BH);
-        if (D == 128) bwd_dq_kernel<128, 8, false><<<grid, 512, 0, st>>>(a);
-        else bwd_dq_kernel<64, 8, false><<<grid, 512, 0, st>>>(a);
+        if (D == 128) bwd_dq_kernel<128, 8, 1, false><<<grid, 512, 0, st>>>(a);
+        else bwd_dq_kernel<64, 8, 1, false><<<grid, 512, 0, st>>>(a);
     }
     return hipGetLastError();
 }
