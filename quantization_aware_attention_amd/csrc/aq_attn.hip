@@ -603,16 +603,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
 // queries on lanes; a per-wave LDS transpose turns them into B operands with
 // queries as the contraction index of dV^T = dO^T Pq and dK^T = Q^T dS.
 //
-// Transpose a 32 x 32 score tile packed as bf16 pairs (w[g][k] holds keys
-// 16 hh + 8 g + 2 k and + 1 of query l32) into two B operands with keys on
-// lanes and queries 16 g + 8 hh + j on the k-slots. Row = query, 64 bytes per
-// row; 8-byte column chunks are XOR-swizzled by (row / 4) % 8 so that the
-// row writes and the transposing column reads avoid bank conflicts.
-__device__ __forceinline__ void transpose_tile_p32(const u32x4* w, uint16_t* T, u32x4* out,
-                                                   int lane) {
+// Transpose of a 32 x 32 score tile packed as bf16 pairs (w[g][k] holds keys
+// 16 hh + 8 g + 2 k and + 1 of query l32) through LDS: transpose_write stores
+// it with row = query (64 bytes per row, 8-byte chunks XOR-swizzled by
+// (row / 4) % 8 so that the row writes and the transposing column reads
+// avoid bank conflicts); transpose_read returns two B operands with keys on
+// lanes and queries 16 g + 8 hh + j on the k-slots.
+__device__ __forceinline__ void transpose_write(const u32x4* w, uint16_t* T, int lane) {
     const int l32 = lane & 31, hh = lane >> 5;
     const int wsw = (l32 >> 2) & 7;
-    const int grp = lane >> 4, i16 = lane & 15;
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
         const int off = l32 * 32 + (((4 * hh + a4) ^ wsw) << 2);
@@ -621,6 +620,10 @@ __device__ __forceinline__ void transpose_tile_p32(const u32x4* w, uint16_t* T, 
         v[1] = w[a4 >> 1][2 * (a4 & 1) + 1];
         *(u32x2*)(T + off) = v;
     }
+}
+__device__ __forceinline__ void transpose_read(const uint16_t* T, u32x4* out, int lane) {
+    const int hh = lane >> 5;
+    const int grp = lane >> 4, i16 = lane & 15;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
 #pragma unroll
@@ -658,28 +661,29 @@ __device__ __forceinline__ int query_tiles(const AttnArgs& a, int bh, int kblk, 
 
 // ---------------------------------------------------------------------------
 // Backward dK and dV in one kernel. A workgroup owns 128 keys and runs 8
-// waves, two per SIMD: "P" wave w (waves 0..3) and "dS" wave w + 4 share the
-// same 32 keys (perm32 order, so that a lane's score registers hold one whole
-// P group) and the same SIMD.
-//   P wave:  S^T = K Q^T; P = exp(S - LSE), Pq = FQ(P); P to the dS wave
-//            through LDS; dV^T += dO^T Pq          (K fragments, dV^T in registers)
-//   dS wave: dP^T = V dO^T; dS = P (dP - Dl); dK^T += Q^T dS
-//                                                 (V fragments, dK^T in registers)
-// Each wave needs under 256 registers, so the two share a SIMD and the
-// hardware interleaves one wave's vector work (exp, quantization) with the
-// other's matrix products; S is computed once.
+// waves, two per SIMD: producer wave w (waves 0..3) and consumer wave w + 4
+// share the same 32 keys (perm32 order, so that a lane's score registers
+// hold one whole P group) and the same SIMD.
+//   producer: S^T = K Q^T and dP^T = V dO^T (K and V fragments in
+//             registers); P = exp(S - LSE), Pq = FQ(P), dS = P (dP - Dl);
+//             Pq and dS written transposed (bf16) to an LDS exchange slot
+//   consumer: dV^T += dO^T Pq and dK^T += Q^T dS, B operands read from the
+//             exchange slot (dV^T and dK^T in registers)
+// Each role issues 16 of the 32 products per 32-query sub-block; the
+// producer also carries all the vector work, which the hardware overlaps
+// with the consumer's products on the shared SIMD. S is computed once.
 //
 // Only the transposed query tiles are staged: Q^T, dO^T ([D][64], swizzled)
 // and the row statistics. The Q and dO operands of S^T and dP^T are read
 // from them with transposing LDS reads. Tiles live in a ring of three
-// buffers. The P wave runs one 32-query sub-block ahead of the dS wave: step
-// u computes sub-block u in the P wave and sub-block u - 1 in the dS wave,
-// so P crosses between them through a double-buffered exchange with a single
-// barrier per step. Tile t is read in steps 2t .. 2t + 2; its buffer is
-// refilled with tile t + 3 right after step 2t + 2, three steps before use.
-// The tile loads are LDS-DMA instructions issued in inline assembly, which
-// keeps them out of the compiler's wait-count tracking: the kernel waits for
-// them itself, and only where a tile is first needed.
+// buffers. The producer runs one 32-query sub-block ahead of the consumer:
+// step u computes sub-block u in the producer and sub-block u - 1 in the
+// consumer, through a double-buffered exchange with a single barrier per
+// step. Tile t is read in steps 2t .. 2t + 2; its buffer is refilled with
+// tile t + 3 right after step 2t + 2, three steps before use. The tile loads
+// are LDS-DMA instructions issued in inline assembly, which keeps them out of
+// the compiler's wait-count tracking: the kernel waits for them itself, and
+// only where a tile is first needed.
 template <int D>
 struct KVTile {
     static constexpr int BM = 64;
@@ -754,24 +758,6 @@ __device__ __forceinline__ void accum_T(const uint16_t* t, int sb, const u32x4* 
     }
 }
 
-// P exchange slot of one wave pair: 16 floats per lane, stored as four
-// 16-byte chunks with lanes contiguous inside each chunk row.
-__device__ __forceinline__ void put_p(float* X, const float* p, int lane) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        *(f32x4_t*)(X + (j * 64 + lane) * 4) = f32x4_t{p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]};
-}
-__device__ __forceinline__ void get_p(const float* X, float* p, int lane) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const f32x4_t v = *(const f32x4_t*)(X + (j * 64 + lane) * 4);
-        p[4 * j] = v[0];
-        p[4 * j + 1] = v[1];
-        p[4 * j + 2] = v[2];
-        p[4 * j + 3] = v[3];
-    }
-}
-
 template <int D, bool QP, bool SPARSE>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnArgs a) {
     using Tile = KVTile<D>;
@@ -782,32 +768,20 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnArgs a) {
     constexpr int NL = NJ + 1;
     static_assert(2 * D * BM * 2 % 8192 == 0, "tile splits into whole DMA blocks per wave");
     __shared__ __attribute__((aligned(1024))) Tile ring[3];
-    __shared__ __attribute__((aligned(1024))) float sX[2][4][16 * 64];  // P exchange
-    __shared__ __attribute__((aligned(1024))) uint16_t sTa[4][32 * 32];  // P waves' transposes
+    // exchange slots per step parity and wave pair: transposed Pq, then dS
+    __shared__ __attribute__((aligned(1024))) uint16_t sX[2][4][2 * 32 * 32];
     __shared__ int lst[SPARSE ? kMaxBlockList : 1];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int pair = wave & 3;
-    const bool pw_role = wave < 4;  // P wave (else dS wave); wave-uniform
+    const bool producer = wave < 4;  // wave-uniform
     const int l32 = lane & 31, hh = lane >> 5;
     const int bh = blockIdx.y, kblk = blockIdx.x;
     const int k0 = kblk * KW + pair * 32;
     const uint16_t* Qtb = a.Qt + (size_t)bh * D * a.Nq_pad;
     const uint16_t* dOtb = a.dOt + (size_t)bh * D * a.Nq_pad;
     // statistics slice of this wave: waves 0..3 LSE2, 4..7 Dl, 16 queries each
-    const float* Sb = (pw_role ? a.lse2 : a.delta) + (size_t)bh * a.Nq_pad + pair * 16;
-    // K fragments (P wave) or V fragments (dS wave)
-    u32x4 f[D / 16];
-    load_key_frags<D, true>(pw_role ? a.Kw : a.Vw, bh, a.Nk_pad, k0, l32, hh, f);
-#pragma unroll
-    for (int cc = 0; cc < D / 16; ++cc) f[cc] = u32x4{f[cc][0], f[cc][2], f[cc][1], f[cc][3]};
-    // let the fragments land before any tile copy is issued: the copies are
-    // invisible to the compiler, whose waits for these loads would otherwise
-    // also wait for the copies in flight
-    wait_vm<0>();
-    f32x16 acc[D / 32];  // dV^T (P wave) or dK^T (dS wave)
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) acc[db] = f32x16{};
+    const float* Sb = (wave < 4 ? a.lse2 : a.delta) + (size_t)bh * a.Nq_pad + pair * 16;
     const int n = query_tiles<SPARSE>(a, bh, kblk, lst);
     const bool tailk = kblk * KW + KW > a.Nk;
     // Per-lane source offsets of this wave's DMA blocks in a [D][Nq_pad] tile:
@@ -831,101 +805,107 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnArgs a) {
         }
         if (lane < 16) dma4(lds_addr(T->st + wave * 16), Sb + qt, 4u * (uint32_t)lane);
     };
-    // The whole step loop is instantiated once per role, so that each
-    // wave's accumulators stay in fixed registers. Both instances execute
-    // the same barriers (one per step).
-    auto run = [&](auto role, auto tail) {
-        constexpr bool PW = decltype(role)::value;
-        constexpr bool TK = decltype(tail)::value;
+    // Both roles execute the same barriers (one per step). A key block that
+    // no query block selected (sparse) has no steps.
+    auto steps = [&](auto body) {
+        if (n == 0) return;
         issue(0);
         if (n > 1) issue(1);
         if (n > 1) wait_vm<NL>();
         else wait_vm<0>();
         for (int u = 0; u <= 2 * n; ++u) {
-            // before step u: tile u / 2 must be resident (first needed by the
-            // P wave at even u); tile (u - 1) / 2 + 2 refills the buffer freed
-            // by step u - 1 (odd u)
+            // before step u: tile u / 2 must be resident (first needed at
+            // even u); tile (u - 1) / 2 + 2 refills the buffer freed by step
+            // u - 1 (odd u)
             if (u > 0 && !(u & 1)) {
                 if (u / 2 + 1 < n) wait_vm<NL>();
                 else wait_vm<0>();
             }
             __syncthreads();
             if ((u & 1) && (u - 1) / 2 + 2 < n) issue((u - 1) / 2 + 2);
-            if (PW) {
-                if (u < 2 * n) {
-                    const Tile* T = ring + (u >> 1) % 3;
-                    const int sb = u & 1;
-                    const f32x16 sd = scores_tr<D>(T->qt, sb, f, lane);
-                    float x[16], p[16];
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        x[j] = sd[j];
-                        if (TK && k0 + 16 * hh + j >= a.Nk) x[j] = -INFINITY;
-                    }
-                    const float L = T->st[sb * 32 + l32];
-                    u32x4 pw[2];
-                    if (QP) {
-                        quant_p_group16_bwd(x, a.c, L, pw, p);
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < 16; ++j)
-                            p[j] = __builtin_amdgcn_exp2f(fmaf(x[j], a.c, -L));
-#pragma unroll
-                        for (int g = 0; g < 2; ++g)
-                            pw[g] = u32x4{pack_rne(p[8 * g], p[8 * g + 1]),
-                                          pack_rne(p[8 * g + 2], p[8 * g + 3]),
-                                          pack_rne(p[8 * g + 4], p[8 * g + 5]),
-                                          pack_rne(p[8 * g + 6], p[8 * g + 7])};
-                    }
-                    put_p(sX[u & 1][pair], p, lane);
-                    u32x4 bT[2];
-                    transpose_tile_p32(pw, sTa[pair], bT, lane);
-                    accum_T<D>(T->ot, sb, bT, acc, l32, hh);
-                }
-            } else if (u > 0) {
-                const int v = u - 1;
-                const Tile* T = ring + (v >> 1) % 3;
-                const int sb = v & 1;
-                const f32x16 dp = scores_tr<D>(T->ot, sb, f, lane);
-                float* X = sX[v & 1][pair];
-                float p[16];
-                get_p(X, p, lane);
-                const float Dl = T->st[BM + sb * 32 + l32];
-                u32x4 dw[2];
-#pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    uint32_t w[4];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const int j = 8 * g + 2 * k;
-                        w[k] = pack_rne(p[j] * (dp[j] - Dl), p[j + 1] * (dp[j + 1] - Dl));
-                    }
-                    dw[g] = u32x4{w[0], w[1], w[2], w[3]};
-                }
-                u32x4 bT[2];
-                transpose_tile_p32(dw, (uint16_t*)X, bT, lane);
-                accum_T<D>(T->qt, sb, bT, acc, l32, hh);
-            }
+            body(u);
         }
     };
-    if (n > 0) {
+    if (producer) {
+        u32x4 fk[D / 16], fv[D / 16];
+        load_key_frags<D, true>(a.Kw, bh, a.Nk_pad, k0, l32, hh, fk);
+        load_key_frags<D, true>(a.Vw, bh, a.Nk_pad, k0, l32, hh, fv);
+#pragma unroll
+        for (int cc = 0; cc < D / 16; ++cc) {
+            fk[cc] = u32x4{fk[cc][0], fk[cc][2], fk[cc][1], fk[cc][3]};
+            fv[cc] = u32x4{fv[cc][0], fv[cc][2], fv[cc][1], fv[cc][3]};
+        }
+        // let the fragments land before any tile copy is issued: the copies
+        // are invisible to the compiler, whose waits for these loads would
+        // otherwise also wait for the copies in flight
+        wait_vm<0>();
+        auto body = [&](int u, auto tail) {
+            constexpr bool TK = decltype(tail)::value;
+            if (u >= 2 * n) return;
+            const Tile* T = ring + (u >> 1) % 3;
+            const int sb = u & 1;
+            const f32x16 sd = scores_tr<D>(T->qt, sb, fk, lane);
+            const f32x16 dp = scores_tr<D>(T->ot, sb, fv, lane);
+            float x[16], p[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                x[j] = sd[j];
+                if (TK && k0 + 16 * hh + j >= a.Nk) x[j] = -INFINITY;
+            }
+            const float L = T->st[sb * 32 + l32], Dl = T->st[BM + sb * 32 + l32];
+            u32x4 pw[2], dw[2];
+            if (QP) {
+                quant_p_group16_bwd(x, a.c, L, pw, p);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(x[j], a.c, -L));
+#pragma unroll
+                for (int g = 0; g < 2; ++g)
+                    pw[g] = u32x4{pack_rne(p[8 * g], p[8 * g + 1]), pack_rne(p[8 * g + 2], p[8 * g + 3]),
+                                  pack_rne(p[8 * g + 4], p[8 * g + 5]),
+                                  pack_rne(p[8 * g + 6], p[8 * g + 7])};
+            }
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                uint32_t w[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int j = 8 * g + 2 * k;
+                    w[k] = pack_rne(p[j] * (dp[j] - Dl), p[j + 1] * (dp[j + 1] - Dl));
+                }
+                dw[g] = u32x4{w[0], w[1], w[2], w[3]};
+            }
+            uint16_t* X = sX[u & 1][pair];
+            transpose_write(pw, X, lane);
+            transpose_write(dw, X + 32 * 32, lane);
+        };
         // keys beyond Nk exist only in the last key workgroup: mask them there
         // only (they would enter the maxima of the last P groups)
-        if (pw_role) {
-            if (tailk) run(std::true_type{}, std::true_type{});
-            else run(std::true_type{}, std::false_type{});
-        } else {
-            run(std::false_type{}, std::false_type{});
-        }
-    }
-    const int key = k0 + l32;
-    if (key < a.Nk) {
-        const int64_t b = bh / a.H, h = bh % a.H;
-        if (pw_role)
-            store_rows_T<D>(a.dv + b * a.dvsb + h * a.dvsh + (int64_t)key * a.dvsn, acc, 1.0f, hh);
-        else
-            store_rows_T<D>(a.dk + b * a.dksb + h * a.dksh + (int64_t)key * a.dksn, acc, a.sm_scale,
+        if (tailk) steps([&](int u) { body(u, std::true_type{}); });
+        else steps([&](int u) { body(u, std::false_type{}); });
+    } else {
+        f32x16 dva[D / 32], dka[D / 32];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) dva[db] = dka[db] = f32x16{};
+        steps([&](int u) {
+            if (u == 0) return;
+            const int v = u - 1;
+            const Tile* T = ring + (v >> 1) % 3;
+            const int sb = v & 1;
+            const uint16_t* X = sX[v & 1][pair];
+            u32x4 pT[2], dT[2];
+            transpose_read(X, pT, lane);
+            transpose_read(X + 32 * 32, dT, lane);
+            accum_T<D>(T->ot, sb, pT, dva, l32, hh);
+            accum_T<D>(T->qt, sb, dT, dka, l32, hh);
+        });
+        const int key = k0 + l32;
+        if (key < a.Nk) {
+            const int64_t b = bh / a.H, h = bh % a.H;
+            store_rows_T<D>(a.dv + b * a.dvsb + h * a.dvsh + (int64_t)key * a.dvsn, dva, 1.0f, hh);
+            store_rows_T<D>(a.dk + b * a.dksb + h * a.dksh + (int64_t)key * a.dksn, dka, a.sm_scale,
                             hh);
+        }
     }
 }
 
