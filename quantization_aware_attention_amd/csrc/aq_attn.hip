@@ -844,8 +844,14 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnArgs a) {
             if (u >= 2 * n) return;
             const Tile* T = ring + (u >> 1) % 3;
             const int sb = u & 1;
+            // the producer's products go first on the shared SIMD; the
+            // consumer's fill the matrix unit during its vector work
+            __builtin_amdgcn_s_setprio(2);
+            __builtin_amdgcn_sched_barrier(0);
             const f32x16 sd = scores_tr<D>(T->qt, sb, fk, lane);
             const f32x16 dp = scores_tr<D>(T->ot, sb, fv, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
             float x[16], p[16];
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
