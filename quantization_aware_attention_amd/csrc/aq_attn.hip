@@ -916,11 +916,11 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Dense forward workgroups are 8 waves (256 queries) so that each K/V tile
-// brought into LDS serves twice the queries; sparse ones are one 128-query
-// block (4 waves).
+// Dense forward workgroups are 8 waves (256 queries), so that each K/V tile
+// brought into LDS serves 256 queries; sparse ones are one 128-query block
+// (4 waves).
 constexpr int kFwdDenseWaves = 8;
-constexpr int kFwdOutDenseWaves = 4;
+constexpr int kFwdOutDenseWaves = 8;
 
 template <int D>
 static void fwd_lse_d(const AttnArgs& a, bool sp, hipStream_t st) {
