@@ -916,6 +916,135 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Dense forward pass 2 with producer/consumer wave pairs. A workgroup owns
+// 256 queries and runs 16 waves, four per SIMD: producer wave w (waves 0..7)
+// and consumer wave w + 8 share 32 queries and a SIMD.
+//   producer: S^T = K Q^T (Q fragments in registers), P = exp(S - LSE) and
+//             its quantization, packed as the B operands of P V and written
+//             to an LDS exchange slot (no transpose: the accumulator rows are
+//             the keys, the contraction index of P V)
+//   consumer: O^T += V^T Pq^T from the exchange slot (O^T in registers)
+// Each takes 8 of the 16 products per 32-key block; the producer also
+// carries the vector work. Step t computes key tile t in the producers and
+// key tile t - 1 in the consumers, so K tiles run one tile ahead of V^T
+// tiles; both are double-buffered, the exchange by step parity, with one
+// barrier per 64-key step. Tile copies are LDS-DMA in inline assembly,
+// issued right after the barrier that frees their buffer and waited for at
+// the next barrier.
+template <int D, bool QP, bool F16>
+__global__ __launch_bounds__(1024) void fwd_out_pc_kernel(AttnArgs a) {
+    using F = FwdOut<D, QP, F16>;
+    constexpr int BN = F::BN, NP = 8;
+    constexpr int KBLK = BN * D * 2 / 1024, VBLK = D * BN * 2 / 1024;  // 1 KB DMA blocks per tile
+    __shared__ __attribute__((aligned(1024))) uint16_t sK[2][BN * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t sV[2][D * BN];
+    // exchange: [parity][pair][32-key block][chunk j][lane][4 dwords]
+    __shared__ __attribute__((aligned(1024))) uint32_t sX[2][NP][2][2][64 * 4];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pair = wave & 7;
+    const bool producer = wave < 8;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int bh = blockIdx.y, qblk = blockIdx.x;
+    const int q0 = qblk * 256 + pair * 32;
+    const int q = q0 + l32;
+    const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
+    const uint16_t* Kb = a.Kw + (size_t)bh * a.Nk_pad * D;
+    const uint16_t* Vtb = a.Vt + (size_t)bh * D * a.Nk_pad;
+    const int nt = (a.Nk + BN - 1) / BN;
+    const bool last_partial = nt * BN > a.Nk;
+    // this wave's DMA blocks: block `wave` of the K tile (rows 4 b .. 4 b + 3
+    // for D = 128, each 16 chunks; perm32 source rows) and of the V^T tile
+    // (rows 8 b .. 8 b + 7, 8 chunks each); lane i fills slot 16 i
+    uint32_t koff = 0, voff = 0;
+    {
+        constexpr int CH = D / 8;  // 16-byte chunks per K row
+        const int kr = wave * (64 / CH) + lane / CH, kc = lane % CH;
+        const int src = (kr & ~31) | perm32(kr & 31);
+        koff = (uint32_t)(src * D + ((kc ^ swz<D>(kr)) << 3)) * 2u;
+        const int vr = wave * 8 + (lane >> 3), vc = lane & 7;
+        voff = (uint32_t)(vr * a.Nk_pad + ((vc ^ swz<BN>(vr)) << 3)) * 2u;
+    }
+    auto issue_k = [&](int t) {
+        if (wave < KBLK) dma16(lds_addr(sK[t & 1] + wave * 512), Kb + (size_t)t * BN * D, koff);
+    };
+    auto issue_v = [&](int t) {
+        if (wave < VBLK) dma16(lds_addr(sV[t & 1] + wave * 512), Vtb + t * BN, voff);
+    };
+    if (producer) {
+        u32x4 qf[D / 16];
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+            qf[c] = *(const u32x4*)(Qb + (size_t)q * D + c * 16 + hh * 8);
+        const float lse2 = (q < a.Nq) ? a.lse[(size_t)bh * a.Nq + q] * kLog2e : 0.0f;
+        // let these loads land before any tile copy is issued (the copies
+        // are invisible to the compiler's wait counts)
+        wait_vm<0>();
+        issue_k(0);
+        wait_vm<0>();
+        __syncthreads();
+        for (int t = 0; t <= nt; ++t) {
+            if (t > 0) {
+                wait_vm<0>();
+                __syncthreads();
+            }
+            if (t + 1 < nt) issue_k(t + 1);
+            if (t < nt) issue_v(t);
+            if (t >= nt) continue;
+            const uint16_t* K = sK[t & 1];
+            uint32_t* X = &sX[t & 1][pair][0][0][0];
+            auto run = [&](auto tail) {
+                constexpr bool TL = decltype(tail)::value;
+                const f32x16 s0 = scores_T<D>(K, 0, qf, l32, hh);
+                lds_mfma_chain<D / 16, 4>();
+                const f32x16 s1 = scores_T<D>(K, 32, qf, l32, hh);
+                u32x4 b0[2], b1[2];
+                F::template probs<TL>(s0, t * BN, a.Nk, a.c, lse2, hh, b0);
+                mfma_valu_chain<D / 16, 4, kValuPerMfma>();
+                F::template probs<TL>(s1, t * BN + 32, a.Nk, a.c, lse2, hh, b1);
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    *(u32x4*)(X + ((0 * 2 + g) * 64 + lane) * 4) = b0[g];
+                    *(u32x4*)(X + ((1 * 2 + g) * 64 + lane) * 4) = b1[g];
+                }
+            };
+            if (last_partial && t == nt - 1) run(std::true_type{});
+            else run(std::false_type{});
+        }
+    } else {
+        f32x16 o[D / 32];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+        issue_k(0);
+        wait_vm<0>();
+        __syncthreads();
+        for (int t = 0; t <= nt; ++t) {
+            if (t > 0) {
+                wait_vm<0>();
+                __syncthreads();
+            }
+            if (t + 1 < nt) issue_k(t + 1);
+            if (t < nt) issue_v(t);
+            if (t == 0) continue;
+            const uint16_t* V = sV[(t - 1) & 1];
+            const uint32_t* X = &sX[(t - 1) & 1][pair][0][0][0];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                u32x4 bfr[2];
+#pragma unroll
+                for (int g = 0; g < 2; ++g) bfr[g] = *(const u32x4*)(X + ((kb * 2 + g) * 64 + lane) * 4);
+                F::pv(V, kb, bfr, o, l32, hh);
+            }
+            lds_mfma_chain<D / 8, 4>();
+        }
+        if (q < a.Nq) {
+            const int64_t b = bh / a.H, h = bh % a.H;
+            store_rows_T<D>(a.o + b * a.osb + h * a.osh + (int64_t)q * a.osn, o, 1.0f, hh);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Dense forward workgroups are 8 waves (256 queries), so that each K/V tile
 // brought into LDS serves 256 queries; sparse ones are one 128-query block
 // (4 waves).
@@ -945,9 +1074,7 @@ static void fwd_out_go(const AttnArgs& a, bool sp, hipStream_t st) {
     if (sp) {
         fwd_out_kernel<D, QP, F16, 4, true><<<dim3(a.nbq, a.BH), 256, 0, st>>>(a);
     } else {
-        constexpr int NW = kFwdOutDenseWaves;
-        fwd_out_kernel<D, QP, F16, NW, false>
-            <<<dim3((a.Nq + NW * 32 - 1) / (NW * 32), a.BH), NW * 64, 0, st>>>(a);
+        fwd_out_pc_kernel<D, QP, F16><<<dim3((a.Nq + 255) / 256, a.BH), 1024, 0, st>>>(a);
     }
 }
 
