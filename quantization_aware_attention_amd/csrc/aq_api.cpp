@@ -260,7 +260,7 @@ int validate_problem(const attnqat_problem* p, Plan& pl) {
 
 // Workspace layout (bytes, each region 256-byte aligned).
 struct Layout {
-    size_t qw, kw, vw, qt, kt, vt, dow, dot, lse2, delta, qlist, qcount, total;
+    size_t qw, kw, vw, kt, vt, dow, lse2, delta, qlist, qcount, total;
 };
 
 Layout layout(const Plan& pl, bool bwd) {
@@ -277,10 +277,8 @@ Layout layout(const Plan& pl, bool bwd) {
     L.kw = take(kb);
     if (bwd) {
         L.vw = take(kb);
-        L.qt = take(qb);
         L.kt = take(kb);
         L.dow = take(qb);
-        L.dot = take(qb);
         L.lse2 = take((size_t)pl.BH * pl.Nq_pad * 4);
         L.delta = take((size_t)pl.BH * pl.Nq_pad * 4);
         if (pl.sparse) {
@@ -342,9 +340,6 @@ int prepare_operands(const Plan& pl, uint32_t mask, const void* q, const void* k
     if (!bwd)
         return run_transpose((const uint16_t*)(ws + L.vw), (uint16_t*)(ws + L.vt), pl.BH, pl.Nk_pad,
                              pl.D, false, st, "transpose V", pv_f16(mask));
-    rc = run_transpose((const uint16_t*)(ws + L.qw), (uint16_t*)(ws + L.qt), pl.BH, pl.Nq_pad, pl.D,
-                       false, st, "transpose Q");
-    if (rc) return rc;
     return run_transpose((const uint16_t*)(ws + L.kw), (uint16_t*)(ws + L.kt), pl.BH, pl.Nk_pad,
                          pl.D, true, st, "transpose K");
 }
@@ -551,14 +546,9 @@ int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const vo
     if ((rc = launch(K_BWD_PRE, st, thunk<aq::PreArgs, aq::launch_bwd_pre>, &pa,
                      "backward preprocess")))
         return rc;
-    if ((rc = run_transpose((const uint16_t*)(ws + L.dow), (uint16_t*)(ws + L.dot), pl.BH,
-                            pl.Nq_pad, pl.D, false, st, "transpose dO")))
-        return rc;
     aq::AttnArgs a = attn_args(p, pl, ws, L);
-    a.Qt = (const uint16_t*)(ws + L.qt);
     a.Kt = (const uint16_t*)(ws + L.kt);
     a.dOw = (const uint16_t*)(ws + L.dow);
-    a.dOt = (const uint16_t*)(ws + L.dot);
     a.lse2 = (const float*)(ws + L.lse2);
     a.delta = (const float*)(ws + L.delta);
     a.dq = (uint16_t*)dq;

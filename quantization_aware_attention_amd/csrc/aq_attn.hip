@@ -673,10 +673,13 @@ __device__ __forceinline__ int query_tiles(const AttnArgs& a, int bh, int kblk, 
 // producer also carries all the vector work, which the hardware overlaps
 // with the consumer's products on the shared SIMD. S is computed once.
 //
-// Only the transposed query tiles are staged: Q^T, dO^T ([D][64], swizzled)
-// and the row statistics. The Q and dO operands of S^T and dP^T are read
-// from them with transposing LDS reads. Tiles live in a ring of three
-// buffers. The producer runs one 32-query sub-block ahead of the consumer:
+// Query tiles are staged in natural layout (Qq and dO rows, swizzled) with
+// the row statistics. The producer reads its B operands with plain 16-byte
+// reads, all issued before its first product; the consumer reads its A
+// operands (columns of Qq and dO) with transposing reads at the end of the
+// previous step, while it waits at the barrier, so that the slower
+// transposing reads stay off the producer's path. Tiles live in a ring of
+// three buffers. The producer runs one 32-query sub-block ahead of the consumer:
 // step u computes sub-block u in the producer and sub-block u - 1 in the
 // consumer, through a double-buffered exchange with a single barrier per
 // step. Tile t is read in steps 2t .. 2t + 2; its buffer is refilled with
@@ -687,9 +690,9 @@ __device__ __forceinline__ int query_tiles(const AttnArgs& a, int bh, int kblk, 
 template <int D>
 struct KVTile {
     static constexpr int BM = 64;
-    uint16_t qt[D * BM];
-    uint16_t ot[D * BM];
-    float st[2 * BM];  // LSE * log2(e) for the BM queries, then Dl
+    uint16_t q[BM * D];  // Qq rows, natural layout (noff)
+    uint16_t o[BM * D];  // dO rows, natural layout (noff)
+    float st[2 * BM];    // LSE * log2(e) for the BM queries, then Dl
 };
 
 #pragma clang diagnostic push
@@ -717,52 +720,58 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const lds_void_t*)p;
 }
 
-// B operand of S^T = K Q^T (or dP^T = V dO^T) for d-chunk cc of a 32-query
-// sub-block, read from a [D][64] transposed tile: lane (hh, c) gets 8 values
-// of query c at d = 16 cc + 8 hh + {0, 1, 4, 5, 2, 3, 6, 7} (the k-slot
-// order; the A fragments are loaded in the same order). Lanes 4 j .. 4 j + 3
-// of each 16-lane group point at one row, 4 queries apart, so the
-// transposing read hands every lane its query's column; rows {0, 1, 4, 5}
-// and then {2, 3, 6, 7} make the two reads free of bank conflicts.
+// Natural-layout [64][D] query tile (row = query): logical 16-byte chunk c of
+// row r sits at chunk c ^ nswz(r). Both reads of the fused backward are then
+// free of bank conflicts: 16-byte reads of one chunk in 16 consecutive rows
+// (the B operands of S^T and dP^T) and transposing reads that cover 4
+// consecutive rows x 4 consecutive chunks per 32 lanes (the A operands of
+// dV^T and dK^T).
 template <int D>
-__device__ __forceinline__ u32x4 bop_tr(const uint16_t* t, int sb, int cc, int lane) {
+__device__ __forceinline__ int nswz(int row) {
+    static_assert(D == 64 || D == 128, "head dim");
+    if (D == 128) return 4 * (row & 3) + ((row >> 2) & 3);
+    return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+}
+template <int D>
+__device__ __forceinline__ int noff(int row, int c) {
+    return row * D + ((c ^ nswz<D>(row)) << 3);
+}
+
+// B operand of S^T = K Q^T (or dP^T = V dO^T) for d-chunk cc of 32-query
+// sub-block sb: lane (hh, c) holds d = 16 cc + 8 hh .. + 7 of query 32 sb + c.
+template <int D>
+__device__ __forceinline__ u32x4 bop_nat(const uint16_t* t, int sb, int cc, int l32, int hh) {
+    return *(const u32x4*)(t + noff<D>(sb * 32 + l32, 2 * cc + hh));
+}
+
+// A operand of X^T += A^T B (rows of A^T = d) for d-block db and query group g
+// of sub-block sb, read transposed from the natural tile: lane (hh, r) holds
+// d = 32 db + r of queries 32 sb + 16 g + 8 hh .. + 7. Each transposing read
+// covers 4 queries: in a 16-lane group, lane 4 j + q points at query j and
+// d columns 4 q .. 4 q + 3, and every lane receives the column of the d equal
+// to its index in the group. The swizzle depends on the row only through
+// row % 16, so the per-lane part of the address depends on db and on which
+// 4 of the 8 queries are read (aop_lane); sb and g add whole rows.
+template <int D>
+__device__ __forceinline__ int aop_lane(int db, int t, int lane) {
     const int G = lane >> 4, i = lane & 15;
     const int hh = G >> 1, j = i >> 2, q = i & 3;
-    const int col = sb * 32 + 16 * (G & 1) + 4 * q;
-    const int row = 16 * cc + 8 * hh + (j & 1) + 4 * (j >> 1);
-    const u32x2 lo = lds_read_tr16(t + toff<64>(row, col >> 3) + (col & 7));
-    const u32x2 hi = lds_read_tr16(t + toff<64>(row + 2, col >> 3) + (col & 7));
-    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    const int d = 32 * db + 16 * (G & 1) + 4 * q;
+    return noff<D>(8 * hh + 4 * t + j, d >> 3) + (d & 7);
 }
-
-// S^T (or dP^T) of sub-block sb: A = the wave's key fragments.
 template <int D>
-__device__ __forceinline__ f32x16 scores_tr(const uint16_t* t, int sb, const u32x4* f, int lane) {
-    f32x16 a = {};
-#pragma unroll
-    for (int cc = 0; cc < D / 16; ++cc) a = mfma(f[cc], bop_tr<D>(t, sb, cc, lane), a);
-    return a;
-}
-
-// X^T += A^T B for sub-block sb: A^T rows from a [D][64] tile, B transposed.
-template <int D>
-__device__ __forceinline__ void accum_T(const uint16_t* t, int sb, const u32x4* bT, f32x16* acc,
-                                        int l32, int hh) {
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-            const int off = toff<64>(db * 32 + l32, 4 * sb + 2 * g + hh);
-            acc[db] = mfma(*(const u32x4*)(t + off), bT[g], acc[db]);
-        }
-    }
+__device__ __forceinline__ u32x4 aop_tr(const uint16_t* t, int sb, int g, const int* lo) {
+    const uint16_t* b = t + (32 * sb + 16 * g) * D;
+    const u32x2 r0 = lds_read_tr16(b + lo[0]);
+    const u32x2 r1 = lds_read_tr16(b + lo[1]);
+    return u32x4{r0[0], r0[1], r1[0], r1[1]};
 }
 
 template <int D, bool QP, bool SPARSE>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnArgs a) {
     using Tile = KVTile<D>;
     constexpr int BM = Tile::BM, KW = 128;
-    // loads per wave per tile: Q^T and dO^T (D * BM * 2 bytes each, in 1 KB
+    // loads per wave per tile: Qq and dO rows (BM * D * 2 bytes each, in 1 KB
     // DMA blocks over 8 waves) and one 64-byte slice of the statistics
     constexpr int NJ = 2 * D * BM * 2 / 1024 / 8;
     constexpr int NL = NJ + 1;
@@ -778,21 +787,22 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnArgs a) {
     const int l32 = lane & 31, hh = lane >> 5;
     const int bh = blockIdx.y, kblk = blockIdx.x;
     const int k0 = kblk * KW + pair * 32;
-    const uint16_t* Qtb = a.Qt + (size_t)bh * D * a.Nq_pad;
-    const uint16_t* dOtb = a.dOt + (size_t)bh * D * a.Nq_pad;
+    const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
+    const uint16_t* dOb = a.dOw + (size_t)bh * a.Nq_pad * D;
     // statistics slice of this wave: waves 0..3 LSE2, 4..7 Dl, 16 queries each
     const float* Sb = (wave < 4 ? a.lse2 : a.delta) + (size_t)bh * a.Nq_pad + pair * 16;
     const int n = query_tiles<SPARSE>(a, bh, kblk, lst);
     const bool tailk = kblk * KW + KW > a.Nk;
-    // Per-lane source offsets of this wave's DMA blocks in a [D][Nq_pad] tile:
-    // block b = j * 8 + wave covers tile rows 8 b .. 8 b + 7 (64 columns =
-    // 128 bytes each); lane i fills LDS slot 16 i of the block, which holds
-    // logical chunk (i % 8) ^ swz(row) of row 8 b + i / 8.
+    // Per-lane source offsets of this wave's DMA blocks in a [BM][D] tile:
+    // block b = j * 8 + wave covers tile rows RB b .. RB b + RB - 1 (RB rows of
+    // CR 16-byte chunks make 1 KB); lane i fills LDS slot 16 i of the block,
+    // which holds logical chunk (i % CR) ^ nswz(row) of row RB b + i / CR.
+    constexpr int CR = D / 8, RB = 64 / CR;
     uint32_t goff[NJ / 2];
 #pragma unroll
     for (int j = 0; j < NJ / 2; ++j) {
-        const int row = (j * 8 + wave) * 8 + (lane >> 3);
-        goff[j] = (uint32_t)(row * a.Nq_pad + (((lane & 7) ^ swz<64>(row)) << 3)) * 2u;
+        const int row = (j * 8 + wave) * RB + lane / CR;
+        goff[j] = (uint32_t)(row * D + (((lane % CR) ^ nswz<D>(row)) << 3)) * 2u;
     }
     auto issue = [&](int t) {
         Tile* T = ring + t % 3;
@@ -800,111 +810,180 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnArgs a) {
 #pragma unroll
         for (int j = 0; j < NJ / 2; ++j) {
             const uint32_t blk = (uint32_t)((j * 8 + wave) * 512);  // elements
-            dma16(lds_addr(T->qt + blk), Qtb + qt, goff[j]);
-            dma16(lds_addr(T->ot + blk), dOtb + qt, goff[j]);
+            dma16(lds_addr(T->q + blk), Qb + (size_t)qt * D, goff[j]);
+            dma16(lds_addr(T->o + blk), dOb + (size_t)qt * D, goff[j]);
         }
         if (lane < 16) dma4(lds_addr(T->st + wave * 16), Sb + qt, 4u * (uint32_t)lane);
     };
     // Both roles execute the same barriers (one per step). A key block that
-    // no query block selected (sparse) has no steps.
-    auto steps = [&](auto body) {
+    // no query block selected (sparse) has no steps. With UNROLL the step
+    // loop is unrolled by two and body(u, odd) sees the parity of u at
+    // compile time (std::bool_constant); otherwise odd is a plain bool.
+    auto steps = [&](auto body, auto unroll) {
         if (n == 0) return;
         issue(0);
         if (n > 1) issue(1);
         if (n > 1) wait_vm<NL>();
         else wait_vm<0>();
-        for (int u = 0; u <= 2 * n; ++u) {
-            // before step u: tile u / 2 must be resident (first needed at
-            // even u); tile (u - 1) / 2 + 2 refills the buffer freed by step
-            // u - 1 (odd u)
-            if (u > 0 && !(u & 1)) {
-                if (u / 2 + 1 < n) wait_vm<NL>();
-                else wait_vm<0>();
-            }
+        auto one = [&](int u, auto odd) {
+            // before barrier u (odd u): tile (u + 1) / 2, the newest one
+            // issued, must be resident, as the producer reads its first
+            // operands during step u; after the barrier tile (u - 1) / 2 + 2
+            // refills the buffer freed by step u - 1
+            if (odd) wait_vm<0>();
             __syncthreads();
-            if ((u & 1) && (u - 1) / 2 + 2 < n) issue((u - 1) / 2 + 2);
-            body(u);
+            if (odd && (u - 1) / 2 + 2 < n) issue((u - 1) / 2 + 2);
+            body(u, odd);
+        };
+        if constexpr (decltype(unroll)::value) {
+            for (int u = 0; u <= 2 * n; u += 2) {
+                one(u, std::false_type{});
+                if (u < 2 * n) one(u + 1, std::true_type{});
+            }
+        } else {
+            for (int u = 0; u <= 2 * n; ++u) one(u, (u & 1) != 0);
         }
     };
     if (producer) {
         u32x4 fk[D / 16], fv[D / 16];
         load_key_frags<D, true>(a.Kw, bh, a.Nk_pad, k0, l32, hh, fk);
         load_key_frags<D, true>(a.Vw, bh, a.Nk_pad, k0, l32, hh, fv);
-#pragma unroll
-        for (int cc = 0; cc < D / 16; ++cc) {
-            fk[cc] = u32x4{fk[cc][0], fk[cc][2], fk[cc][1], fk[cc][3]};
-            fv[cc] = u32x4{fv[cc][0], fv[cc][2], fv[cc][1], fv[cc][3]};
-        }
         // let the fragments land before any tile copy is issued: the copies
         // are invisible to the compiler, whose waits for these loads would
         // otherwise also wait for the copies in flight
         wait_vm<0>();
-        auto body = [&](int u, auto tail) {
+        // B operands of sub-block v (Qq and dO rows of its 32 queries)
+        u32x4 bq[D / 16], bo[D / 16];
+        auto fetch = [&](int v) {
+            const Tile* T = ring + (v >> 1) % 3;
+#pragma unroll
+            for (int cc = 0; cc < D / 16; ++cc) {
+                bq[cc] = bop_nat<D>(T->q, v & 1, cc, l32, hh);
+                bo[cc] = bop_nat<D>(T->o, v & 1, cc, l32, hh);
+            }
+        };
+        // S^T and dP^T of even (A) and odd (B) sub-blocks
+        f32x16 sdA, dpA, sdB, dpB;
+        auto products = [&](f32x16& sd, f32x16& dp) {
+            sd = dp = f32x16{};
+#pragma unroll
+            for (int cc = 0; cc < D / 16; ++cc) {
+                sd = mfma(fk[cc], bq[cc], sd);
+                dp = mfma(fv[cc], bo[cc], dp);
+            }
+        };
+        // Step u: the vector work of sub-block u (whose S^T and dP^T are
+        // ready) with the products of sub-block u + 1 interleaved, so that
+        // this wave's own products fill the matrix unit during its vector
+        // work. At u = 2 n - 1 the products read a stale buffer and are
+        // discarded. The loop is unrolled by two so that the two score sets
+        // alternate without copies.
+        auto body = [&](int u, auto odd, auto tail) {
+            constexpr bool ODD = decltype(odd)::value;
             constexpr bool TK = decltype(tail)::value;
             if (u >= 2 * n) return;
+            f32x16& sd = ODD ? sdB : sdA;
+            f32x16& dp = ODD ? dpB : dpA;
             const Tile* T = ring + (u >> 1) % 3;
-            const int sb = u & 1;
-            // the producer's products go first on the shared SIMD; the
-            // consumer's fill the matrix unit during its vector work
-            __builtin_amdgcn_s_setprio(2);
+            constexpr int sb = ODD ? 1 : 0;
+            if (!ODD && u == 0) {
+                fetch(0);
+                products(sd, dp);
+            }
+            const float L = T->st[sb * 32 + l32], Dl = T->st[BM + sb * 32 + l32];
             __builtin_amdgcn_sched_barrier(0);
-            const f32x16 sd = scores_tr<D>(T->qt, sb, fk, lane);
-            const f32x16 dp = scores_tr<D>(T->ot, sb, fv, lane);
-            __builtin_amdgcn_sched_barrier(0);
-            __builtin_amdgcn_s_setprio(0);
-            float x[16], p[16];
+            fetch(u + 1);
+            float x[16], r[16], sp = 1.0f;
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 x[j] = sd[j];
                 if (TK && k0 + 16 * hh + j >= a.Nk) x[j] = -INFINITY;
             }
-            const float L = T->st[sb * 32 + l32], Dl = T->st[BM + sb * 32 + l32];
             u32x4 pw[2], dw[2];
             if (QP) {
-                quant_p_group16_bwd(x, a.c, L, pw, p);
+                quant_p_group16_bwd(x, a.c, L, pw, r, sp);
             } else {
 #pragma unroll
-                for (int j = 0; j < 16; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(x[j], a.c, -L));
+                for (int j = 0; j < 16; ++j) r[j] = __builtin_amdgcn_exp2f(fmaf(x[j], a.c, -L));
 #pragma unroll
                 for (int g = 0; g < 2; ++g)
-                    pw[g] = u32x4{pack_rne(p[8 * g], p[8 * g + 1]), pack_rne(p[8 * g + 2], p[8 * g + 3]),
-                                  pack_rne(p[8 * g + 4], p[8 * g + 5]),
-                                  pack_rne(p[8 * g + 6], p[8 * g + 7])};
+                    pw[g] = u32x4{pack_rne(r[8 * g], r[8 * g + 1]), pack_rne(r[8 * g + 2], r[8 * g + 3]),
+                                  pack_rne(r[8 * g + 4], r[8 * g + 5]),
+                                  pack_rne(r[8 * g + 6], r[8 * g + 7])};
             }
+            // dS = P (dP - Dl) with P = r s': r (dP s' - Dl s')
+            const float sdl = sp * Dl;
 #pragma unroll
             for (int g = 0; g < 2; ++g) {
                 uint32_t w[4];
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int j = 8 * g + 2 * k;
-                    w[k] = pack_rne(p[j] * (dp[j] - Dl), p[j + 1] * (dp[j + 1] - Dl));
+                    w[k] = pack_rne(r[j] * fmaf(dp[j], sp, -sdl), r[j + 1] * fmaf(dp[j + 1], sp, -sdl));
                 }
                 dw[g] = u32x4{w[0], w[1], w[2], w[3]};
             }
-            uint16_t* X = sX[u & 1][pair];
+            products(ODD ? sdA : sdB, ODD ? dpA : dpB);
+            // issue order: the operand reads, some vector work while they
+            // land, then one product after every 8 vector instructions
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 16), 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
+#pragma unroll
+            for (int i = 0; i < 2 * (D / 16); ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            uint16_t* X = sX[sb][pair];
             transpose_write(pw, X, lane);
             transpose_write(dw, X + 32 * 32, lane);
         };
         // keys beyond Nk exist only in the last key workgroup: mask them there
         // only (they would enter the maxima of the last P groups)
-        if (tailk) steps([&](int u) { body(u, std::true_type{}); });
-        else steps([&](int u) { body(u, std::false_type{}); });
+        if (tailk) steps([&](int u, auto odd) { body(u, odd, std::true_type{}); }, std::true_type{});
+        else steps([&](int u, auto odd) { body(u, odd, std::false_type{}); }, std::true_type{});
     } else {
         f32x16 dva[D / 32], dka[D / 32];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) dva[db] = dka[db] = f32x16{};
-        steps([&](int u) {
-            if (u == 0) return;
-            const int v = u - 1;
+        // A operands (dO^T and Q^T rows) of the next sub-block, read at the
+        // end of the previous step, while this wave waits for the barrier
+        // (the tile is resident: the producer passed a barrier with it)
+        u32x4 ao[D / 32][2], aq[D / 32][2];
+        int alo[D / 32][2];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) alo[db][t] = aop_lane<D>(db, t, lane);
+        auto prefetch = [&](int v) {
             const Tile* T = ring + (v >> 1) % 3;
-            const int sb = v & 1;
-            const uint16_t* X = sX[v & 1][pair];
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    ao[db][g] = aop_tr<D>(T->o, v & 1, g, alo[db]);
+                    aq[db][g] = aop_tr<D>(T->q, v & 1, g, alo[db]);
+                }
+        };
+        steps([&](int u, bool odd) {
+            if (u == 0) {
+                prefetch(0);
+                return;
+            }
+            const uint16_t* X = sX[odd ? 0 : 1][pair];
             u32x4 pT[2], dT[2];
             transpose_read(X, pT, lane);
             transpose_read(X + 32 * 32, dT, lane);
-            accum_T<D>(T->ot, sb, pT, dva, l32, hh);
-            accum_T<D>(T->qt, sb, dT, dka, l32, hh);
-        });
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    dva[db] = mfma(ao[db][g], pT[g], dva[db]);
+                    dka[db] = mfma(aq[db][g], dT[g], dka[db]);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+            if (u < 2 * n) prefetch(u);
+        }, std::false_type{});
         const int key = k0 + l32;
         if (key < a.Nk) {
             const int64_t b = bh / a.H, h = bh % a.H;

@@ -186,11 +186,12 @@ __device__ __forceinline__ void quant_p_group16(const float* x, float c, float l
     }
 }
 
-// Backward form of quant_p_group16 (bf16 output): also returns the
-// unquantized probabilities P_j (for dS), recovered as (P_j / s') * s' with
-// s' = s, or 2^-64 for an all-zero group (an exact power-of-two rescaling).
+// Backward form of quant_p_group16 (bf16 output): also returns r_j = P_j / s'
+// and s', so that the unquantized P_j = r_j s' (for dS) can be folded into
+// later products; s' = s, or 2^-64 for an all-zero group (an exact
+// power-of-two rescaling).
 __device__ __forceinline__ void quant_p_group16_bwd(const float* x, float c, float lse2, u32x4* out,
-                                                    float* p) {
+                                                    float* r, float& sp_out) {
     float mx = x[0];
 #pragma unroll
     for (int j = 1; j < 16; ++j) mx = __builtin_fmaxf(mx, x[j]);
@@ -201,12 +202,9 @@ __device__ __forceinline__ void quant_p_group16_bwd(const float* x, float c, flo
     const float s = __builtin_amdgcn_cvt_scalef32_f32_fp8(__builtin_bit_cast(int, c8), 1.0f, 0);
     const float sp = (s > 0.0f) ? s : 0x1p-64f;
     const float t = lse2 + __builtin_amdgcn_logf(sp);
-    float r[16];
+    sp_out = sp;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        r[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], c, -t));
-        p[j] = r[j] * sp;
-    }
+    for (int j = 0; j < 16; ++j) r[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], c, -t));
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
         const float* rw = r + 8 * w;

@@ -40,11 +40,9 @@ struct AttnArgs {
     const uint16_t* Qw;   // [BH][Nq_pad][D]
     const uint16_t* Kw;   // [BH][Nk_pad][D]
     const uint16_t* Vw;   // [BH][Nk_pad][D]
-    const uint16_t* Qt;   // [BH][D][Nq_pad] natural token order
     const uint16_t* Kt;   // [BH][D][Nk_pad] permuted
     const uint16_t* Vt;   // [BH][D][Nk_pad] natural token order; fp16 when pv_f16
     const uint16_t* dOw;  // [BH][Nq_pad][D]
-    const uint16_t* dOt;  // [BH][D][Nq_pad] natural token order
     const float* lse;     // forward: natural-log LSE output/input [BH][Nq]
     const float* lse2;    // backward: LSE * log2(e), [BH][Nq_pad]
     const float* delta;   // backward: [BH][Nq_pad]
