@@ -58,12 +58,40 @@ __device__ __forceinline__ int toff(int row, int c) {
     return row * W + ((c ^ swz<W>(row)) << 3);
 }
 
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16-byte (and 4-byte) LDS-DMA copies: lane i's global bytes land at LDS
+// byte address lds + 16 i (+ 4 i). lds and g are wave-uniform.
+__device__ __forceinline__ const void* uniform_ptr(const void* g) {
+    const uint64_t v = (uint64_t)g;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void*)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void dma16(uint32_t lds, const void* g, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_ptr(g))
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(uint32_t lds, const void* g, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_ptr(g))
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+
 // Asynchronous copy of an R x W bf16 tile (row-major source with leading
 // dimension ld) into a swizzled LDS tile. Each wave-wide direct-to-LDS load
 // fills one contiguous 1 KB block; lane i's 16 bytes land at block + 16 i, so
 // each lane fetches the global chunk that the swizzle maps to that slot. The
 // per-lane source offsets depend only on the tile shape, so they are computed
-// once; each issue adds them to a wave-uniform tile base.
+// once; each issue adds them to a wave-uniform tile base. The copies are
+// issued in inline assembly (dma16): the compiler does not track them, so
+// its own LDS waits stay partial, and the kernel waits for the copies itself
+// (wait_async) before the barrier that publishes a tile.
 // With PERM32, tile row `row` receives source row perm32 of its position in
 // its 32-row block (the key order of score tiles, see perm32).
 template <int R, int W, int NT, bool PERM32 = false>
@@ -86,15 +114,7 @@ struct AsyncTile {
     }
     __device__ __forceinline__ void issue(uint16_t* lds, const uint16_t* g) const {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            // Opaque copy: keeps the 32-bit offset from being widened outside
-            // the loop, so the load takes the wave-uniform base in SGPRs and
-            // the offset in one VGPR.
-            uint32_t o = goff[j];
-            asm volatile("" : "+v"(o));
-            __builtin_amdgcn_global_load_lds((glb_void_t*)((const char*)g + o),
-                                             (lds_void_t*)(lds + (j * NW + wave) * 512), 16, 0, 0);
-        }
+        for (int j = 0; j < NJ; ++j) dma16(lds_addr(lds + (j * NW + wave) * 512), g, goff[j]);
     }
 };
 
@@ -695,30 +715,6 @@ struct KVTile {
     float st[2 * BM];    // LSE * log2(e) for the BM queries, then Dl
 };
 
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-// 16-byte (and 4-byte) LDS-DMA copies: lane i's global bytes land at LDS
-// byte address lds + 16 i (+ 4 i). lds and g are wave-uniform.
-__device__ __forceinline__ const void* uniform_ptr(const void* g) {
-    const uint64_t v = (uint64_t)g;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return (const void*)(((uint64_t)hi << 32) | lo);
-}
-__device__ __forceinline__ void dma16(uint32_t lds, const void* g, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_ptr(g))
-                 : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(uint32_t lds, const void* g, uint32_t voff) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-                 :: "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(uniform_ptr(g))
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const lds_void_t*)p;
-}
 
 // Natural-layout [64][D] query tile (row = query): logical 16-byte chunk c of
 // row r sits at chunk c ^ nswz(r). Both reads of the fused backward are then
