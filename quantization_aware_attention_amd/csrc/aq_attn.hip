@@ -623,37 +623,31 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
 // queries on lanes; a per-wave LDS transpose turns them into B operands with
 // queries as the contraction index of dV^T = dO^T Pq and dK^T = Q^T dS.
 //
-// Transpose of a 32 x 32 score tile packed as bf16 pairs (w[g][k] holds keys
-// 16 hh + 8 g + 2 k and + 1 of query l32) through LDS: transpose_write stores
-// it with row = query (64 bytes per row, 8-byte chunks XOR-swizzled by
-// (row / 4) % 8 so that the row writes and the transposing column reads
-// avoid bank conflicts); transpose_read returns two B operands with keys on
-// lanes and queries 16 g + 8 hh + j on the k-slots.
+// Transpose of a 32 x 32 score tile packed as bf16 pairs (w[g] holds keys
+// 16 hh + 8 g .. + 7 of query l32) through LDS: transpose_write stores it
+// with row = query (64 bytes per row, two 16-byte writes per lane; 16-byte
+// chunk c of row q sits at c ^ ((q / 4) % 4), so that the row writes and the
+// transposing column reads avoid bank conflicts); transpose_read returns two
+// B operands with keys on lanes and queries 16 g + 8 hh + j on the k-slots.
+__device__ __forceinline__ int xoff(int q, int c) { return q * 32 + ((c ^ ((q >> 2) & 3)) << 3); }
 __device__ __forceinline__ void transpose_write(const u32x4* w, uint16_t* T, int lane) {
     const int l32 = lane & 31, hh = lane >> 5;
-    const int wsw = (l32 >> 2) & 7;
 #pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-        const int off = l32 * 32 + (((4 * hh + a4) ^ wsw) << 2);
-        u32x2 v;
-        v[0] = w[a4 >> 1][2 * (a4 & 1)];
-        v[1] = w[a4 >> 1][2 * (a4 & 1) + 1];
-        *(u32x2*)(T + off) = v;
-    }
+    for (int g = 0; g < 2; ++g) *(u32x4*)(T + xoff(l32, 2 * hh + g)) = w[g];
 }
 __device__ __forceinline__ void transpose_read(const uint16_t* T, u32x4* out, int lane) {
-    const int hh = lane >> 5;
-    const int grp = lane >> 4, i16 = lane & 15;
+    const int hh = lane >> 5, G = lane >> 4, i16 = lane & 15;
+    const int j = i16 >> 2, q = i16 & 3;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int trow = 16 * g + 8 * hh + 4 * half + (i16 >> 2);
-            const int col8 = 4 * (grp & 1) + (i16 & 3);
-            const int off = trow * 32 + ((col8 ^ ((trow >> 2) & 7)) << 2);
-            const u32x2 r = lds_read_tr16(T + off);
-            out[g][2 * half] = r[0];
-            out[g][2 * half + 1] = r[1];
+        for (int t = 0; t < 2; ++t) {
+            // lane 4 j + q of the group reads query j of these 4 and keys
+            // 16 (G % 2) + 4 q .. + 3; every lane receives its key's column
+            const int row = 16 * g + 8 * hh + 4 * t + j;
+            const u32x2 r = lds_read_tr16(T + xoff(row, 2 * (G & 1) + (q >> 1)) + 4 * (q & 1));
+            out[g][2 * t] = r[0];
+            out[g][2 * t + 1] = r[1];
         }
     }
 }
