@@ -36,6 +36,18 @@ the identity; the softmax Jacobian uses the unquantized P)::
     dQ = sm_scale * dS Kq
     dK = sm_scale * dS^T Qq
 
+Row-max-relative variant (``p_mode=P_ROWMAX``; the first of the pages'
+alternative readings of which P is quantized). The quantized quantity is the
+probability relative to the row maximum rather than the normalised one::
+
+    m_i = max_j S_ij,  l_i = sum_j exp(S_ij - m_i)      (LSE = m + ln l)
+    Pq  = FQ_keys(exp(S - m)) / l                      (values in (0, 1] before FQ)
+
+Everything else is unchanged: O = Pq Vq, and the backward uses this Pq in dV
+and the unquantized P = exp(S - LSE) in the softmax Jacobian. With the p bit
+clear both modes give Pq = P. Because exp(S - m) has maximum 1, the group
+scales do not flush to zero on long rows as those of the normalised P do.
+
 Everything is float64; S and P are materialised in row blocks.
 """
 from __future__ import annotations
@@ -46,6 +58,7 @@ from .nvfp4 import fake_quant
 
 MASK_Q, MASK_K, MASK_V, MASK_P = 1, 2, 4, 8
 MASK_ALL = 15
+P_NORMALISED, P_ROWMAX = 0, 1
 
 
 def quantize_operands(q, k, v, mask: int):
@@ -61,70 +74,94 @@ def _lse(S: np.ndarray) -> np.ndarray:
     return (m + np.log(np.sum(np.exp(S - m), axis=-1, keepdims=True)))[..., 0]
 
 
-def head_forward(qq, kq, vq, sm_scale: float, mask: int, rows=None, row_block: int = 512):
+def probabilities(S: np.ndarray, lse: np.ndarray, mask: int, p_mode: int = P_NORMALISED,
+                  row_max=None):
+    """(P, Pq) for whole score rows S [n, Nk] with their LSE [n].
+
+    P = exp(S - LSE). Pq = FQ_keys(P) (normalised mode) or
+    FQ_keys(exp(S - m)) / l with m the row maximum (``row_max`` if given, for
+    rows whose S holds only some of the keys) and l = exp(LSE - m).
+    """
+    P = np.exp(S - lse[:, None])
+    if not mask & MASK_P:
+        return P, P
+    if p_mode == P_ROWMAX:
+        m = (np.max(S, axis=-1) if row_max is None else np.asarray(row_max, np.float64))[:, None]
+        return P, fake_quant(np.exp(S - m), axis=-1) / np.exp(lse[:, None] - m)
+    return P, fake_quant(P, axis=-1)
+
+
+def head_forward(qq, kq, vq, sm_scale: float, mask: int, rows=None, row_block: int = 512,
+                 p_mode: int = P_NORMALISED, with_max: bool = False):
     """Forward for one head on already-quantized operands.
 
     ``rows`` (optional index array) restricts the query rows computed; the
-    result then has len(rows) rows. Returns (O [n, D], LSE [n]).
+    result then has len(rows) rows. Returns (O [n, D], LSE [n]), and the row
+    maxima of S [n] as a third value with ``with_max``.
     """
     qsel = qq if rows is None else qq[rows]
     n = qsel.shape[0]
     O = np.empty((n, vq.shape[1]))
     L = np.empty(n)
+    M = np.empty(n)
     for r0 in range(0, n, row_block):
         r1 = min(n, r0 + row_block)
         S = sm_scale * (qsel[r0:r1] @ kq.T)
         lse = _lse(S)
-        P = np.exp(S - lse[:, None])
-        Pq = fake_quant(P, axis=-1) if mask & MASK_P else P
+        _, Pq = probabilities(S, lse, mask, p_mode)
         O[r0:r1] = Pq @ vq
         L[r0:r1] = lse
-    return O, L
+        M[r0:r1] = np.max(S, axis=-1)
+    return (O, L, M) if with_max else (O, L)
 
 
 def _forward_rows_task(args):
-    qq, kq, vq, sm_scale, mask, r0, r1 = args
+    qq, kq, vq, sm_scale, mask, r0, r1, p_mode = args
     try:
         from threadpoolctl import threadpool_limits
         with threadpool_limits(1):
-            return head_forward(qq[r0:r1], kq, vq, sm_scale, mask)
+            return head_forward(qq[r0:r1], kq, vq, sm_scale, mask, p_mode=p_mode)
     except ImportError:  # pragma: no cover
-        return head_forward(qq[r0:r1], kq, vq, sm_scale, mask)
+        return head_forward(qq[r0:r1], kq, vq, sm_scale, mask, p_mode=p_mode)
 
 
 def head_forward_all(qq, kq, vq, sm_scale: float, mask: int, workers: int = 0,
-                     chunk: int = 1024):
+                     chunk: int = 1024, p_mode: int = P_NORMALISED):
     """``head_forward`` over every query row, split into row chunks across
     ``workers`` processes (0 or 1: in this process). Rows are independent in
     the forward, so the result is identical to a single call."""
     n = qq.shape[0]
     spans = [(r0, min(n, r0 + chunk)) for r0 in range(0, n, chunk)]
     if workers <= 1:
-        parts = [head_forward(qq[a:b], kq, vq, sm_scale, mask) for a, b in spans]
+        parts = [head_forward(qq[a:b], kq, vq, sm_scale, mask, p_mode=p_mode) for a, b in spans]
     else:
         import multiprocessing as mp
         with mp.get_context("fork").Pool(workers) as pool:
             parts = pool.map(_forward_rows_task,
-                             [(qq, kq, vq, sm_scale, mask, a, b) for a, b in spans])
+                             [(qq, kq, vq, sm_scale, mask, a, b, p_mode) for a, b in spans])
     return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
 
 
-def forward(q, k, v, sm_scale: float, mask: int = MASK_ALL, row_block: int = 512):
-    """O [B,H,Nq,D] and LSE [B,H,Nq] for real-valued inputs q, k, v."""
+def forward(q, k, v, sm_scale: float, mask: int = MASK_ALL, row_block: int = 512,
+            p_mode: int = P_NORMALISED, with_max: bool = False):
+    """O [B,H,Nq,D] and LSE [B,H,Nq] for real-valued inputs q, k, v (and the
+    row maxima of S [B,H,Nq] as a third value with ``with_max``)."""
     q = np.asarray(q, np.float64)
     B, H, Nq, D = q.shape
     qq, kq, vq = quantize_operands(q, k, v, mask)
     O = np.empty((B, H, Nq, vq.shape[-1]))
     L = np.empty((B, H, Nq))
+    M = np.empty((B, H, Nq))
     for b in range(B):
         for h in range(H):
-            O[b, h], L[b, h] = head_forward(qq[b, h], kq[b, h], vq[b, h], sm_scale,
-                                            mask, row_block=row_block)
-    return O, L
+            O[b, h], L[b, h], M[b, h] = head_forward(qq[b, h], kq[b, h], vq[b, h], sm_scale,
+                                                     mask, row_block=row_block, p_mode=p_mode,
+                                                     with_max=True)
+    return (O, L, M) if with_max else (O, L)
 
 
 def head_backward(qq, kq, vq, do, O, lse, sm_scale: float, mask: int,
-                  row_block: int = 512):
+                  row_block: int = 512, p_mode: int = P_NORMALISED):
     """dQ, dK, dV for one head on quantized operands (STE through quantizers).
 
     ``O`` and ``lse`` are this head's forward output and statistics (all rows).
@@ -137,8 +174,7 @@ def head_backward(qq, kq, vq, do, O, lse, sm_scale: float, mask: int,
     for r0 in range(0, Nq, row_block):
         r1 = min(Nq, r0 + row_block)
         S = sm_scale * (qq[r0:r1] @ kq.T)
-        P = np.exp(S - lse[r0:r1, None])
-        Pq = fake_quant(P, axis=-1) if mask & MASK_P else P
+        P, Pq = probabilities(S, lse[r0:r1], mask, p_mode)
         dv += Pq.T @ do[r0:r1]
         dP = do[r0:r1] @ vq.T
         dS = P * (dP - Dd[r0:r1, None])
@@ -148,14 +184,14 @@ def head_backward(qq, kq, vq, do, O, lse, sm_scale: float, mask: int,
 
 
 def backward(q, k, v, do, sm_scale: float, mask: int = MASK_ALL, O=None, lse=None,
-             row_block: int = 512):
+             row_block: int = 512, p_mode: int = P_NORMALISED):
     """dQ, dK, dV [B,H,N,D]. O / LSE default to this oracle's own forward."""
     q = np.asarray(q, np.float64)
     do = np.asarray(do, np.float64)
     B, H, Nq, D = q.shape
     qq, kq, vq = quantize_operands(q, k, v, mask)
     if O is None or lse is None:
-        O, lse = forward(q, k, v, sm_scale, mask, row_block)
+        O, lse = forward(q, k, v, sm_scale, mask, row_block, p_mode=p_mode)
     dq = np.empty_like(qq)
     dk = np.empty_like(kq)
     dv = np.empty_like(vq)
@@ -163,17 +199,18 @@ def backward(q, k, v, do, sm_scale: float, mask: int = MASK_ALL, O=None, lse=Non
         for h in range(H):
             dq[b, h], dk[b, h], dv[b, h] = head_backward(
                 qq[b, h], kq[b, h], vq[b, h], do[b, h], O[b, h], lse[b, h],
-                sm_scale, mask, row_block)
+                sm_scale, mask, row_block, p_mode)
     return dq, dk, dv
 
 
 def head_backward_keys(qq, kq, vq, do, O, lse, sm_scale: float, mask: int, keys,
-                       row_block: int = 2048):
+                       row_block: int = 2048, p_mode: int = P_NORMALISED, row_max=None):
     """dK and dV of one head restricted to the key rows ``keys``.
 
-    Needs this head's O and LSE for all query rows. P is quantized per
-    16-key group, so every group that contains a requested key is evaluated
-    whole. Returns (dK[keys], dV[keys]).
+    Needs this head's O and LSE for all query rows (and, for the row-max
+    variant, the row maxima of S over all keys, ``row_max``). P is quantized
+    per 16-key group, so every group that contains a requested key is
+    evaluated whole. Returns (dK[keys], dV[keys]).
     """
     keys = np.asarray(keys)
     Nk = kq.shape[0]
@@ -193,10 +230,15 @@ def head_backward_keys(qq, kq, vq, do, O, lse, sm_scale: float, mask: int, keys,
         S = sm_scale * (qq[r0:r1] @ kq[cols].T)
         P = np.exp(S - lse[r0:r1, None])
         if mask & MASK_P:
+            if p_mode == P_ROWMAX:
+                m = np.asarray(row_max, np.float64)[r0:r1, None]
+                X, post = np.exp(S - m), 1.0 / np.exp(lse[r0:r1, None] - m)
+            else:
+                X, post = P, 1.0
             Pq = np.empty_like(P)
             for gi, st in enumerate(starts):
                 en = starts[gi + 1] if gi + 1 < len(starts) else len(cols)
-                Pq[:, st:en] = fake_quant(P[:, st:en], axis=-1)
+                Pq[:, st:en] = fake_quant(X[:, st:en], axis=-1) * post
         else:
             Pq = P
         dv += Pq.T @ do[r0:r1]

@@ -90,6 +90,54 @@ def test_uniform_attention_p_quant_closed_forms():
                                    rtol=1e-12, atol=1e-15)
 
 
+ROWMAX_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "rowmax_p_quant.json")
+
+
+def test_rowmax_uniform_attention_closed_form():
+    """Row-max-relative P quantization on identical keys: O = 1.03125 mean(Vq)
+    for every Nk, including lengths where the normalised P flushes to zero."""
+    with open(ROWMAX_GOLDEN) as f:
+        cases = json.load(f)["uniform"]["cases"]
+    for c in cases:
+        Nk = c["Nk"]
+        q = _bf16(31, (1, 1, 4, 16))
+        k = np.repeat(_bf16(32, (1, 1, 1, 16)), Nk, axis=2)
+        v = _bf16(33, (1, 1, Nk, 16))
+        O, _ = att.forward(q, k, v, 0.25, mask=att.MASK_P, p_mode=att.P_ROWMAX)
+        expect = c["c"] * np.mean(v[0, 0], axis=0)
+        np.testing.assert_allclose(O[0, 0], np.broadcast_to(expect, O[0, 0].shape),
+                                   rtol=1e-12, atol=1e-15)
+
+
+def test_rowmax_worked_row():
+    """exp(S - m) = 2^-j over keys 0..15 and 1 over keys 16..31: the
+    hand-derived codes at s = 0.171875, divided by l; the normalised reading
+    gives a different result on the same row."""
+    with open(ROWMAX_GOLDEN) as f:
+        g = json.load(f)["worked_row"]
+    sm = 0.5
+    q = np.zeros((1, 1, 1, 32))
+    q[0, 0, 0, 0] = 1.0
+    k = np.zeros((1, 1, 32, 32))
+    k[0, 0, :16, 0] = -np.arange(16) * math.log(2.0) / sm   # S_j = -j ln 2, then S_j = 0
+    v = np.eye(32)[None, None]                               # O row = Pq row
+    O, L = att.forward(q, k, v, sm, mask=att.MASK_P, p_mode=att.P_ROWMAX)
+    expect = np.array(g["codes"]) * g["s"] / g["l"]
+    np.testing.assert_allclose(O[0, 0, 0], expect, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(L[0, 0, 0], math.log(g["l"]), rtol=0, atol=1e-14)
+    On, _ = att.forward(q, k, v, sm, mask=att.MASK_P)
+    assert np.abs(On[0, 0, 0] - expect).max() > 1e-3
+
+
+def test_rowmax_equals_normalised_without_p_quant():
+    q, k, v = _bf16(34, (1, 2, 24, 16)), _bf16(35, (1, 2, 40, 16)), _bf16(36, (1, 2, 40, 16))
+    for mask in (0, att.MASK_Q | att.MASK_K | att.MASK_V):
+        O0, L0 = att.forward(q, k, v, 0.3, mask=mask)
+        O1, L1 = att.forward(q, k, v, 0.3, mask=mask, p_mode=att.P_ROWMAX)
+        np.testing.assert_allclose(O1, O0, rtol=1e-13, atol=1e-15)
+        np.testing.assert_array_equal(L1, L0)
+
+
 def _fq_exact_vec(xs):
     fr = [Fraction(float(x)) for x in xs]
     grid4 = [Fraction(float(g)) for g in nvfp4.E4M3_GRID]
@@ -148,8 +196,9 @@ def _surrogate_loss(Q, K, V, W, rQ, rK, rV, lse0, R, scale):
     return float(np.sum(W * (Pt @ (V + rV))))
 
 
-@pytest.mark.parametrize("N,D,seed", [(32, 16, 0), (40, 32, 1)])
-def test_backward_quant_on_finite_differences(N, D, seed):
+@pytest.mark.parametrize("N,D,seed,p_mode", [(32, 16, 0, 0), (40, 32, 1, 0), (32, 16, 2, 1),
+                                           (40, 32, 3, 1)])
+def test_backward_quant_on_finite_differences(N, D, seed, p_mode):
     """Central differences of the straight-through surrogate loss.
 
     Residuals r = FQ(x0) - x0 are frozen at the base point and the quantized P
@@ -170,13 +219,20 @@ def test_backward_quant_on_finite_differences(N, D, seed):
     S0 = scale * Qq @ Kq.T
     lse0 = np.log(np.exp(S0).sum(axis=1))
     P0 = np.exp(S0 - lse0[:, None])
-    R = nvfp4.fake_quant(P0, -1) - P0
-    assert np.count_nonzero(nvfp4.fake_quant(P0, -1)) > N  # P quantization is active
+    if p_mode == att.P_ROWMAX:
+        # exp(S - m) quantized, divided by l = exp(LSE - m)
+        m0 = S0.max(axis=1, keepdims=True)
+        Pq0 = nvfp4.fake_quant(np.exp(S0 - m0), -1) / np.exp(lse0[:, None] - m0)
+    else:
+        Pq0 = nvfp4.fake_quant(P0, -1)
+    R = Pq0 - P0
+    assert np.count_nonzero(Pq0) > N  # P quantization is active
 
-    O, L = att.forward(Q[None, None], K[None, None], V[None, None], scale, att.MASK_ALL)
+    O, L = att.forward(Q[None, None], K[None, None], V[None, None], scale, att.MASK_ALL,
+                       p_mode=p_mode)
     np.testing.assert_allclose(O[0, 0], (P0 + R) @ Vq, rtol=1e-12, atol=1e-14)
     dq, dk, dv = att.backward(Q[None, None], K[None, None], V[None, None], W[None, None],
-                              scale, att.MASK_ALL)
+                              scale, att.MASK_ALL, p_mode=p_mode)
     h = 1e-6
     for X, G in ((Q, dq[0, 0]), (K, dk[0, 0]), (V, dv[0, 0])):
         num = np.zeros_like(X)
