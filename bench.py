@@ -263,6 +263,43 @@ def main():
         fq[f"axis_{axis}"] = {"ms_per_launch": round(ms, 4), "algo_gbs": round(gbs, 1),
                               "frac_hbm": round(gbs / PEAK_HBM_GBS, 3)}
     out["fakequant_standalone"] = fq
+    # Row-max-relative P quantization variant on the same inputs (reported
+    # beside the metric, which is the normalised reading): same credited FLOPs.
+    if mask & qaa.QUANT_P:
+        rm = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+        pr = qaa.make_problem(q, k, w.sm_scale, mask, v=v, o=o, do=do, dq=dq, dk=dk, dv=dv,
+                              kv_block_idx=kv_idx, p_mode=qaa.P_ROWMAX, row_max=rm)
+        ws_bv = torch.empty(L.attnqat_bwd_workspace_bytes(ctypes.byref(pr)), dtype=torch.uint8,
+                            device=dev)
+
+        def step_rowmax(ev=None):
+            if ev:
+                ev[0].record()
+            qaa.fwd(q, k, v, w.sm_scale, mask, kv_idx, out=o, lse=lse, workspace=ws_f,
+                    p_mode=qaa.P_ROWMAX, row_max=rm)
+            if ev:
+                ev[1].record()
+            qaa.bwd(q, k, v, o, lse, do, w.sm_scale, mask, kv_idx, dq=dq, dk=dk, dv=dv,
+                    workspace=ws_bv, p_mode=qaa.P_ROWMAX, row_max=rm)
+            if ev:
+                ev[2].record()
+
+        for _ in range(2):
+            step_rowmax()
+        nv = max(1, min(args.steps, 5))
+        evv = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nv)]
+        torch.cuda.synchronize()
+        for i in range(nv):
+            step_rowmax(evv[i])
+        torch.cuda.synchronize()
+        vf = float(np.mean([a.elapsed_time(b) for a, b, _ in evv]))
+        vb = float(np.mean([b.elapsed_time(c) for _, b, c in evv]))
+        out["variants"] = {"p_rowmax": {
+            "steps": nv, "fwd_ms": round(vf, 4), "bwd_ms": round(vb, 4),
+            "ms_per_step": round(vf + vb, 4),
+            "tflops": round((f_fwd + f_bwd) / ((vf + vb) * 1e-3) / 1e12, 1),
+            "frac_peak": round((f_fwd + f_bwd) / ((vf + vb) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}}
+        del ws_bv
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define ATTNQAT_ABI_VERSION 1
+#define ATTNQAT_ABI_VERSION 2
 
 /* status codes */
 #define ATTNQAT_OK 0
@@ -71,6 +71,10 @@ extern "C" {
 #define ATTNQAT_QUANT_V 4u
 #define ATTNQAT_QUANT_P 8u
 #define ATTNQAT_QUANT_ALL 15u
+
+/* which probabilities the P quantizer sees (attnqat_problem.p_mode) */
+#define ATTNQAT_P_NORMALISED 0u /* P = exp(S - LSE), quantized per 16-key group (default) */
+#define ATTNQAT_P_ROWMAX 1u     /* exp(S - m), m = row maximum, quantized, then divided by l */
 
 /* group axis of the standalone fake quantizer */
 #define ATTNQAT_AXIS_D 0 /* 16 consecutive elements of the last (head) dimension: Q, K */
@@ -96,6 +100,19 @@ typedef struct {
     int32_t topk;         /* entries per row of kv_block_idx (ignored when dense) */
     int32_t block_tokens; /* tokens per block; must be 128 when kv_block_idx != NULL;
                            * block-sparse problems have at most 1024 blocks per sequence */
+    /* Row-max-relative P quantization (an alternative reading of which P the
+     * pages quantize: the inference-backend pull request's FP4 attention call
+     * takes a single_level_p_quant option). With p_mode == ATTNQAT_P_ROWMAX
+     * and the P bit set, the quantized quantity is exp(S - m), m_i = max_j
+     * S_ij (over the keys the row attends to), and O = FQ(exp(S - m)) V / l
+     * with l_i = exp(LSE_i - m_i); the backward uses the same Pq. Zero
+     * (ATTNQAT_P_NORMALISED) keeps the normalised P. */
+    uint32_t p_mode;
+    /* Row maxima m of S, device fp32 [B,H,Nq] contiguous, 4-byte aligned:
+     * written by attnqat_fwd and read by attnqat_bwd when p_mode is
+     * ATTNQAT_P_ROWMAX (required then, and must not overlap any other
+     * argument); ignored otherwise. */
+    float* row_max;
 } attnqat_problem;
 
 /* ABI version of the loaded library (ATTNQAT_ABI_VERSION it was built with). */
@@ -137,7 +154,9 @@ size_t attnqat_fwd_workspace_bytes(const attnqat_problem* p);
  * with S = sm_scale FQ_d(Q) FQ_d(K)^T and P = exp(S - LSE) (normalised); each
  * quantizer applies only if its mask bit is set. P is quantized per 16-key
  * group of each query row, groups aligned at key 0; there is no
- * renormalisation after quantization.
+ * renormalisation after quantization. With p_mode == ATTNQAT_P_ROWMAX (and
+ * the P bit set) O = FQ_keys(exp(S - m)) FQ_tokens(V) / l instead, and the row
+ * maxima m are also written to p->row_max.
  * `workspace` (device, 256-byte aligned) of at least
  * attnqat_fwd_workspace_bytes(p) bytes is scratch owned by the caller; its
  * contents are undefined afterwards.
@@ -154,7 +173,8 @@ size_t attnqat_bwd_workspace_bytes(const attnqat_problem* p);
  * the output gradient `dout`, writes bf16 dq, dk, dv:
  *   Dl = rowsum(dout * o)
  *   dP = dout FQ_tokens(V)^T,  dS = P * (dP - Dl)   (P unquantized, from lse)
- *   dV = FQ_keys(P)^T dout
+ *   dV = FQ_keys(P)^T dout    (FQ_keys(exp(S - m))^T dout / l with ATTNQAT_P_ROWMAX,
+ *                              m read from p->row_max as written by attnqat_fwd)
  *   dQ = sm_scale dS FQ_d(K),  dK = sm_scale dS^T FQ_d(Q)
  * Outputs must not overlap each other or any input.
  */

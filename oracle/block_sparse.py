@@ -32,7 +32,7 @@ import math
 
 import numpy as np
 
-from .attention import MASK_ALL, MASK_P, quantize_operands, _lse
+from .attention import MASK_ALL, MASK_P, P_NORMALISED, probabilities, quantize_operands, _lse
 from .nvfp4 import fake_quant
 
 
@@ -92,8 +92,10 @@ def _keys_of(blocks, block_tokens: int, Nk: int) -> np.ndarray:
 
 
 def forward(q, k, v, sm_scale: float, idx: np.ndarray, block_tokens: int,
-            mask: int = MASK_ALL):
-    """Block-sparse O [B,H,Nq,D] and LSE [B,H,Nq] for the selection ``idx``."""
+            mask: int = MASK_ALL, p_mode: int = P_NORMALISED):
+    """Block-sparse O [B,H,Nq,D] and LSE [B,H,Nq] for the selection ``idx``
+    (``p_mode`` as in ``oracle.attention``: the row maximum is taken over the
+    selected keys)."""
     q = np.asarray(q, np.float64)
     B, H, Nq, D = q.shape
     Nk = np.asarray(k).shape[2]
@@ -108,22 +110,21 @@ def forward(q, k, v, sm_scale: float, idx: np.ndarray, block_tokens: int,
                 keys = _keys_of(idx[b, h, i], block_tokens, Nk)
                 S = sm_scale * (qq[b, h, r0:r1] @ kq[b, h, keys].T)
                 lse = _lse(S)
-                P = np.exp(S - lse[:, None])
-                Pq = fake_quant(P, axis=-1) if mask & MASK_P else P
+                _, Pq = probabilities(S, lse, mask, p_mode)
                 O[b, h, r0:r1] = Pq @ vq[b, h, keys]
                 L[b, h, r0:r1] = lse
     return O, L
 
 
 def backward(q, k, v, do, sm_scale: float, idx: np.ndarray, block_tokens: int,
-             mask: int = MASK_ALL, O=None, lse=None):
+             mask: int = MASK_ALL, O=None, lse=None, p_mode: int = P_NORMALISED):
     """Block-sparse STE backward: dQ, dK, dV (same formulas as the dense path)."""
     q = np.asarray(q, np.float64)
     do = np.asarray(do, np.float64)
     B, H, Nq, D = q.shape
     Nk = np.asarray(k).shape[2]
     if O is None or lse is None:
-        O, lse = forward(q, k, v, sm_scale, idx, block_tokens, mask)
+        O, lse = forward(q, k, v, sm_scale, idx, block_tokens, mask, p_mode)
     qq, kq, vq = quantize_operands(q, k, v, mask)
     dq = np.zeros_like(qq)
     dk = np.zeros_like(kq)
@@ -136,8 +137,7 @@ def backward(q, k, v, do, sm_scale: float, idx: np.ndarray, block_tokens: int,
                 r0, r1 = i * block_tokens, min(Nq, (i + 1) * block_tokens)
                 keys = _keys_of(idx[b, h, i], block_tokens, Nk)
                 S = sm_scale * (qq[b, h, r0:r1] @ kq[b, h, keys].T)
-                P = np.exp(S - lse[b, h, r0:r1, None])
-                Pq = fake_quant(P, axis=-1) if mask & MASK_P else P
+                P, Pq = probabilities(S, lse[b, h, r0:r1], mask, p_mode)
                 dv[b, h, keys] += Pq.T @ do[b, h, r0:r1]
                 dP = do[b, h, r0:r1] @ vq[b, h, keys].T
                 dS = P * (dP - Dd[r0:r1, None])

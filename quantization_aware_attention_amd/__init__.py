@@ -24,6 +24,7 @@ from .build import LIB_PATH
 QUANT_Q, QUANT_K, QUANT_V, QUANT_P = 1, 2, 4, 8
 QUANT_ALL = 15
 AXIS_D, AXIS_N = 0, 1
+P_NORMALISED, P_ROWMAX = 0, 1
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "misaligned",
           4: "workspace too small", 5: "HIP error"}
@@ -42,6 +43,7 @@ class Problem(ctypes.Structure):
         ("dout", Strides), ("dq", Strides), ("dk", Strides), ("dv", Strides),
         ("kv_block_idx", ctypes.c_void_p), ("topk", ctypes.c_int32),
         ("block_tokens", ctypes.c_int32),
+        ("p_mode", ctypes.c_uint32), ("row_max", ctypes.c_void_p),
     ]
 
 
@@ -153,7 +155,8 @@ def strides_of(t: torch.Tensor) -> Strides:
 
 
 def make_problem(q, k, sm_scale, quant_mask, *, v=None, o=None, do=None, dq=None, dk=None,
-                 dv=None, kv_block_idx=None, block_tokens=128) -> Problem:
+                 dv=None, kv_block_idx=None, block_tokens=128, p_mode=P_NORMALISED,
+                 row_max=None) -> Problem:
     B, H, Nq, D = q.shape
     Nk = k.shape[2]
     p = Problem()
@@ -168,6 +171,9 @@ def make_problem(q, k, sm_scale, quant_mask, *, v=None, o=None, do=None, dq=None
         p.kv_block_idx = kv_block_idx.data_ptr()
         p.topk = kv_block_idx.shape[-1]
     p.block_tokens = block_tokens
+    p.p_mode = int(p_mode)
+    if row_max is not None:
+        p.row_max = row_max.data_ptr()
     return p
 
 
@@ -199,8 +205,10 @@ def fakequant(x: torch.Tensor, axis: str = "d", return_scale_codes: bool = False
 
 
 def fwd(q, k, v, sm_scale=None, quant="qkvp", kv_block_idx=None, block_tokens=128,
-        out=None, lse=None, workspace=None, stream=None):
-    """O (bf16) and LSE (fp32, natural log) of Attn-QAT attention."""
+        out=None, lse=None, workspace=None, stream=None, p_mode=P_NORMALISED, row_max=None):
+    """O (bf16) and LSE (fp32, natural log) of Attn-QAT attention; with
+    p_mode=P_ROWMAX also the row maxima of S (fp32 [B,H,Nq]), which the
+    backward of that mode needs: returns (O, LSE, row_max)."""
     L = load()
     for n, t in (("q", q), ("k", k), ("v", v)):
         _check4(n, t)
@@ -211,22 +219,26 @@ def fwd(q, k, v, sm_scale=None, quant="qkvp", kv_block_idx=None, block_tokens=12
                                                 device=q.device)
     lse = lse if lse is not None else torch.empty((B, H, Nq), dtype=torch.float32,
                                                   device=q.device)
+    if p_mode == P_ROWMAX and row_max is None:
+        row_max = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     p = make_problem(q, k, sm_scale, quant, v=v, o=o, kv_block_idx=kv_block_idx,
-                     block_tokens=block_tokens)
+                     block_tokens=block_tokens, p_mode=p_mode, row_max=row_max)
     need = L.attnqat_fwd_workspace_bytes(ctypes.byref(p))
-    if need == 0:
+    if need == 0:  # invalid problem: the call reports why
         check(L.attnqat_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                             o.data_ptr(), lse.data_ptr(), None, 0, _stream(stream)))
     ws = workspace if workspace is not None and workspace.numel() >= need else \
         _workspace(need, q.device)
     check(L.attnqat_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                         lse.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)))
-    return o, lse
+    return (o, lse, row_max) if p_mode == P_ROWMAX else (o, lse)
 
 
 def bwd(q, k, v, o, lse, do, sm_scale=None, quant="qkvp", kv_block_idx=None, block_tokens=128,
-        dq=None, dk=None, dv=None, workspace=None, stream=None):
-    """dQ, dK, dV (bf16) of Attn-QAT attention with straight-through quantizers."""
+        dq=None, dk=None, dv=None, workspace=None, stream=None, p_mode=P_NORMALISED,
+        row_max=None):
+    """dQ, dK, dV (bf16) of Attn-QAT attention with straight-through quantizers
+    (p_mode=P_ROWMAX needs the forward's row_max)."""
     L = load()
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
         _check4(n, t)
@@ -237,9 +249,10 @@ def bwd(q, k, v, o, lse, do, sm_scale=None, quant="qkvp", kv_block_idx=None, blo
     dk = dk if dk is not None else torch.empty_like(k, memory_format=torch.contiguous_format)
     dv = dv if dv is not None else torch.empty_like(v, memory_format=torch.contiguous_format)
     p = make_problem(q, k, sm_scale, quant, v=v, o=o, do=do, dq=dq, dk=dk, dv=dv,
-                     kv_block_idx=kv_block_idx, block_tokens=block_tokens)
+                     kv_block_idx=kv_block_idx, block_tokens=block_tokens, p_mode=p_mode,
+                     row_max=row_max)
     need = L.attnqat_bwd_workspace_bytes(ctypes.byref(p))
-    if need == 0:
+    if need == 0:  # invalid problem: the call reports why
         check(L.attnqat_bwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                             o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
                             dk.data_ptr(), dv.data_ptr(), None, 0, _stream(stream)))
@@ -287,24 +300,28 @@ def profile_read() -> dict:
 
 
 class AttnQatFunction(torch.autograd.Function):
-    """Autograd wrapper: forward saves (O, LSE); backward is straight-through."""
+    """Autograd wrapper: forward saves (O, LSE[, row maxima]); backward is
+    straight-through."""
 
     @staticmethod
-    def forward(ctx, q, k, v, sm_scale, quant, kv_block_idx):
-        o, lse = fwd(q, k, v, sm_scale, quant, kv_block_idx)
-        ctx.save_for_backward(q, k, v, o, lse, kv_block_idx)
-        ctx.sm_scale, ctx.quant = sm_scale, quant
+    def forward(ctx, q, k, v, sm_scale, quant, kv_block_idx, p_mode=P_NORMALISED):
+        res = fwd(q, k, v, sm_scale, quant, kv_block_idx, p_mode=p_mode)
+        o, lse = res[0], res[1]
+        row_max = res[2] if p_mode == P_ROWMAX else None
+        ctx.save_for_backward(q, k, v, o, lse, kv_block_idx, row_max)
+        ctx.sm_scale, ctx.quant, ctx.p_mode = sm_scale, quant, p_mode
         return o
 
     @staticmethod
     def backward(ctx, do):
-        q, k, v, o, lse, idx = ctx.saved_tensors
+        q, k, v, o, lse, idx, row_max = ctx.saved_tensors
         do = do.contiguous()
-        dq, dk, dv = bwd(q, k, v, o, lse, do, ctx.sm_scale, ctx.quant, idx)
-        return dq, dk, dv, None, None, None
+        dq, dk, dv = bwd(q, k, v, o, lse, do, ctx.sm_scale, ctx.quant, idx, p_mode=ctx.p_mode,
+                         row_max=row_max)
+        return dq, dk, dv, None, None, None, None
 
 
-def attention(q, k, v, sm_scale=None, quant="qkvp", kv_block_idx=None):
+def attention(q, k, v, sm_scale=None, quant="qkvp", kv_block_idx=None, p_mode=P_NORMALISED):
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(q.shape[-1])
-    return AttnQatFunction.apply(q, k, v, sm_scale, quant, kv_block_idx)
+    return AttnQatFunction.apply(q, k, v, sm_scale, quant, kv_block_idx, p_mode)

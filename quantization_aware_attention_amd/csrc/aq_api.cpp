@@ -207,6 +207,8 @@ struct Plan {
     Strides q, k, v, o, dout, dq, dk, dv;
     bool sparse;
     int nbq, nbk;
+    bool rowmax_out;  // p_mode is ATTNQAT_P_ROWMAX: the forward writes the row maxima
+    bool rowmax;      // ... and P is quantized: passes 2 and dK/dV use them
 };
 
 int validate_problem(const attnqat_problem* p, Plan& pl) {
@@ -240,6 +242,15 @@ int validate_problem(const attnqat_problem* p, Plan& pl) {
     pl.dq = resolve(p->dq, p->H, p->Nq, p->D);
     pl.dk = resolve(p->dk, p->H, p->Nk, p->D);
     pl.dv = resolve(p->dv, p->H, p->Nk, p->D);
+    if (p->p_mode != ATTNQAT_P_NORMALISED && p->p_mode != ATTNQAT_P_ROWMAX)
+        return fail(ATTNQAT_E_INVALID, "unknown p_mode %u", p->p_mode);
+    pl.rowmax_out = p->p_mode == ATTNQAT_P_ROWMAX;
+    pl.rowmax = pl.rowmax_out && (p->quant_mask & ATTNQAT_QUANT_P);
+    if (pl.rowmax_out) {
+        if (!p->row_max) return fail(ATTNQAT_E_INVALID, "p_mode ATTNQAT_P_ROWMAX needs row_max");
+        if (((uintptr_t)p->row_max) % 4)
+            return fail(ATTNQAT_E_MISALIGNED, "row_max is not 4-byte aligned");
+    }
     pl.sparse = p->kv_block_idx != nullptr;
     pl.nbq = pl.nbk = 0;
     if (pl.sparse) {
@@ -260,7 +271,7 @@ int validate_problem(const attnqat_problem* p, Plan& pl) {
 
 // Workspace layout (bytes, each region 256-byte aligned).
 struct Layout {
-    size_t qw, kw, vw, kt, vt, dow, lse2, delta, qlist, qcount, total;
+    size_t qw, kw, vw, kt, vt, dow, lse2, delta, qlist, qcount, dowkv, lse2kv, deltakv, total;
 };
 
 Layout layout(const Plan& pl, bool bwd) {
@@ -284,6 +295,11 @@ Layout layout(const Plan& pl, bool bwd) {
         if (pl.sparse) {
             L.qlist = take((size_t)pl.BH * pl.nbk * pl.nbq * 4);
             L.qcount = take((size_t)pl.BH * pl.nbk * 4);
+        }
+        if (pl.rowmax) {  // dK/dV inputs of the row-max-relative variant
+            L.dowkv = take(qb);
+            L.lse2kv = take((size_t)pl.BH * pl.Nq_pad * 4);
+            L.deltakv = take((size_t)pl.BH * pl.Nq_pad * 4);
         }
     } else {
         L.vw = take(kb);
@@ -453,13 +469,17 @@ int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const vo
     const Range ro = extent(o, pl.o, pl.B, pl.H, pl.Nq, pl.D, 2);
     const Range rl = {(uintptr_t)lse, (uintptr_t)lse + (uintptr_t)(pl.BH * pl.Nq * 4)};
     const Range rw = {(uintptr_t)workspace, (uintptr_t)workspace + L.total};
+    const Range rm = pl.rowmax_out ? Range{(uintptr_t)p->row_max,
+                                           (uintptr_t)p->row_max + (uintptr_t)(pl.BH * pl.Nq * 4)}
+                                   : Range{0, 0};
     const Range ins[3] = {extent(q, pl.q, pl.B, pl.H, pl.Nq, pl.D, 2),
                           extent(k, pl.k, pl.B, pl.H, pl.Nk, pl.D, 2),
                           extent(v, pl.v, pl.B, pl.H, pl.Nk, pl.D, 2)};
     for (const Range& r : ins)
-        if (overlaps(r, ro) || overlaps(r, rl) || overlaps(r, rw))
+        if (overlaps(r, ro) || overlaps(r, rl) || overlaps(r, rw) || overlaps(r, rm))
             return fail(ATTNQAT_E_INVALID, "an output or the workspace overlaps an input");
-    if (overlaps(ro, rl) || overlaps(ro, rw) || overlaps(rl, rw))
+    if (overlaps(ro, rl) || overlaps(ro, rw) || overlaps(rl, rw) || overlaps(rm, ro) ||
+        overlaps(rm, rl) || overlaps(rm, rw))
         return fail(ATTNQAT_E_INVALID, "outputs overlap each other or the workspace");
     if ((rc = check_device())) return rc;
 
@@ -469,6 +489,8 @@ int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const vo
     aq::AttnArgs a = attn_args(p, pl, ws, L);
     a.Vt = (const uint16_t*)(ws + L.vt);
     a.lse_out = lse;
+    a.row_max_out = pl.rowmax_out ? p->row_max : nullptr;
+    a.row_max = pl.rowmax ? p->row_max : nullptr;
     a.lse = lse;
     a.o = (uint16_t*)o;
     a.osb = pl.o.b;
@@ -506,14 +528,17 @@ int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const vo
                            extent(dk, pl.dk, pl.B, pl.H, pl.Nk, pl.D, 2),
                            extent(dv, pl.dv, pl.B, pl.H, pl.Nk, pl.D, 2),
                            {(uintptr_t)workspace, (uintptr_t)workspace + L.total}};
-    const Range ins[6] = {extent(q, pl.q, pl.B, pl.H, pl.Nq, pl.D, 2),
-                          extent(k, pl.k, pl.B, pl.H, pl.Nk, pl.D, 2),
-                          extent(v, pl.v, pl.B, pl.H, pl.Nk, pl.D, 2),
-                          extent(o, pl.o, pl.B, pl.H, pl.Nq, pl.D, 2),
-                          extent(dout, pl.dout, pl.B, pl.H, pl.Nq, pl.D, 2),
-                          {(uintptr_t)lse, (uintptr_t)lse + (uintptr_t)(pl.BH * pl.Nq * 4)}};
+    const Range ins[7] = {
+        extent(q, pl.q, pl.B, pl.H, pl.Nq, pl.D, 2),
+        extent(k, pl.k, pl.B, pl.H, pl.Nk, pl.D, 2),
+        extent(v, pl.v, pl.B, pl.H, pl.Nk, pl.D, 2),
+        extent(o, pl.o, pl.B, pl.H, pl.Nq, pl.D, 2),
+        extent(dout, pl.dout, pl.B, pl.H, pl.Nq, pl.D, 2),
+        {(uintptr_t)lse, (uintptr_t)lse + (uintptr_t)(pl.BH * pl.Nq * 4)},
+        pl.rowmax ? Range{(uintptr_t)p->row_max, (uintptr_t)p->row_max + (uintptr_t)(pl.BH * pl.Nq * 4)}
+                  : Range{0, 0}};
     for (int i = 0; i < 4; ++i) {
-        for (int j = 0; j < 6; ++j)
+        for (int j = 0; j < 7; ++j)
             if (overlaps(outs[i], ins[j]))
                 return fail(ATTNQAT_E_INVALID, "an output or the workspace overlaps an input");
         for (int j = i + 1; j < 4; ++j)
@@ -538,6 +563,12 @@ int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const vo
     pa.delta = (float*)(ws + L.delta);
     pa.lse2 = (float*)(ws + L.lse2);
     pa.dOw = (uint16_t*)(ws + L.dow);
+    if (pl.rowmax) {
+        pa.row_max = p->row_max;
+        pa.dOw_kv = (uint16_t*)(ws + L.dowkv);
+        pa.lse2_kv = (float*)(ws + L.lse2kv);
+        pa.delta_kv = (float*)(ws + L.deltakv);
+    }
     pa.BH = pl.BH;
     pa.H = pl.H;
     pa.Nq = pl.Nq;
@@ -573,7 +604,16 @@ int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const vo
             return rc;
     }
     const DimArgs da{a, (int)pl.D};
-    if ((rc = launch(K_BWD_DKDV, st, thunk<DimArgs, do_bwd_dkdv>, &da, "backward dK/dV")))
+    // row-max-relative variant: dK/dV quantizes exp(S - m) and takes dO and Dl
+    // scaled by 1/l (the backward preprocess wrote them)
+    aq::AttnArgs akv = a;
+    if (pl.rowmax) {
+        akv.dOw = (const uint16_t*)(ws + L.dowkv);
+        akv.lse2 = (const float*)(ws + L.lse2kv);
+        akv.delta = (const float*)(ws + L.deltakv);
+    }
+    const DimArgs dkv{akv, (int)pl.D};
+    if ((rc = launch(K_BWD_DKDV, st, thunk<DimArgs, do_bwd_dkdv>, &dkv, "backward dK/dV")))
         return rc;
     if ((rc = launch(K_BWD_DQ, st, thunk<DimArgs, do_bwd_dq>, &da, "backward dQ"))) return rc;
     return ok();

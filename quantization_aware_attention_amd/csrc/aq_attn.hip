@@ -336,7 +336,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_lse_kernel(AttnArgs a) {
     const float lt = l * __builtin_amdgcn_exp2f((m - mt) * a.c) +
                      lp * __builtin_amdgcn_exp2f((mp - mt) * a.c);
     const int q = q0 + l32;
-    if (hh == 0 && q < a.Nq) a.lse_out[(size_t)bh * a.Nq + q] = (mt * a.c + log2f(lt)) * kLn2;
+    if (hh == 0 && q < a.Nq) {
+        a.lse_out[(size_t)bh * a.Nq + q] = (mt * a.c + log2f(lt)) * kLn2;
+        if (a.row_max_out) a.row_max_out[(size_t)bh * a.Nq + q] = mt * a.sm_scale;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -345,6 +348,23 @@ __global__ __launch_bounds__(NW * 64) void fwd_lse_kernel(AttnArgs a) {
 // block holds keys 16 hh .. 16 hh + 15 for its query: one whole P group.
 // With F16 (P and V both quantized) the P V product runs on fp16 operands,
 // which hold NVFP4 values exactly, and V^T is stored as fp16.
+// Exponent offset of the P quantizer and output factor for query q of head
+// bh: the normalised P uses lse2 = LSE log2(e) and factor 1; the
+// row-max-relative variant (a.row_max set, P quantized) quantizes
+// exp(S - m), i.e. uses m2 = m log2(e), and scales O by 1 / l = exp2(m2 - lse2).
+template <bool QP>
+__device__ __forceinline__ void p_offset(const AttnArgs& a, int64_t bh, int q, float& off,
+                                         float& post) {
+    const float lse2 = (q < a.Nq) ? a.lse[bh * a.Nq + q] * kLog2e : 0.0f;
+    off = lse2;
+    post = 1.0f;
+    if (QP && a.row_max && q < a.Nq) {
+        const float m2 = a.row_max[bh * a.Nq + q] * kLog2e;
+        off = m2;
+        post = __builtin_amdgcn_exp2f(m2 - lse2);
+    }
+}
+
 template <int D, bool QP, bool F16>
 struct FwdOut {
     static constexpr int BN = 64;
@@ -432,7 +452,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_out_kernel(AttnA
 #pragma unroll
     for (int c = 0; c < D / 16; ++c)
         qf[c] = *(const u32x4*)(Qb + (size_t)(q0 + l32) * D + c * 16 + hh * 8);
-    const float lse2 = (q < a.Nq) ? a.lse[(size_t)bh * a.Nq + q] * kLog2e : 0.0f;
+    float lse2, post;
+    p_offset<QP>(a, bh, q, lse2, post);
     f32x16 o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
@@ -457,7 +478,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_out_kernel(AttnA
         });
     if (q < a.Nq) {
         const int64_t b = bh / a.H, h = bh % a.H;
-        store_rows_T<D>(a.o + b * a.osb + h * a.osh + (int64_t)q * a.osn, o, 1.0f, hh);
+        store_rows_T<D>(a.o + b * a.osb + h * a.osh + (int64_t)q * a.osn, o, post, hh);
     }
 }
 
@@ -1045,7 +1066,8 @@ __global__ __launch_bounds__(1024) void fwd_out_pc_kernel(AttnArgs a) {
 #pragma unroll
         for (int c = 0; c < D / 16; ++c)
             qf[c] = *(const u32x4*)(Qb + (size_t)q * D + c * 16 + hh * 8);
-        const float lse2 = (q < a.Nq) ? a.lse[(size_t)bh * a.Nq + q] * kLog2e : 0.0f;
+        float lse2, post;
+        p_offset<QP>(a, bh, q, lse2, post);
         // let these loads land before any tile copy is issued (the copies
         // are invisible to the compiler's wait counts)
         wait_vm<0>();
@@ -1107,8 +1129,10 @@ __global__ __launch_bounds__(1024) void fwd_out_pc_kernel(AttnArgs a) {
             lds_mfma_chain<D / 8, 4>();
         }
         if (q < a.Nq) {
+            float off, post;
+            p_offset<QP>(a, bh, q, off, post);
             const int64_t b = bh / a.H, h = bh % a.H;
-            store_rows_T<D>(a.o + b * a.osb + h * a.osh + (int64_t)q * a.osn, o, 1.0f, hh);
+            store_rows_T<D>(a.o + b * a.osb + h * a.osh + (int64_t)q * a.osn, o, post, hh);
         }
     }
 }

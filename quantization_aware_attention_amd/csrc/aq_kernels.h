@@ -30,6 +30,14 @@ struct PreArgs {
     float* delta;      // [BH][Nq_pad]
     float* lse2;       // [BH][Nq_pad]
     uint16_t* dOw;     // [BH][Nq_pad][D]
+    // row-max-relative P quantization (NULL row_max: off): the dK/dV kernel
+    // gets dO and Dl scaled per row by 1/l = exp2(m2 - lse2) and m2 = m log2(e)
+    // in place of lse2, so that it quantizes exp(S - m) and its products
+    // carry the 1/l
+    const float* row_max;  // [BH][Nq]
+    float* delta_kv;       // [BH][Nq_pad]
+    float* lse2_kv;        // [BH][Nq_pad]
+    uint16_t* dOw_kv;      // [BH][Nq_pad][D]
     int64_t BH, H, Nq, Nq_pad;
     int D;
 };
@@ -47,6 +55,8 @@ struct AttnArgs {
     const float* lse2;    // backward: LSE * log2(e), [BH][Nq_pad]
     const float* delta;   // backward: [BH][Nq_pad]
     float* lse_out;       // forward pass 1 output [BH][Nq]
+    float* row_max_out;   // forward pass 1: row maxima of S [BH][Nq] (NULL: not written)
+    const float* row_max; // forward pass 2: quantize exp(S - m) and scale O by 1/l (NULL: off)
     uint16_t* o;          // strided outputs
     int64_t osb, osh, osn;
     uint16_t* dq;

@@ -183,9 +183,24 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(PreArgs a) {
     for (int off = lanes_per_row / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
     if (!active) return;
     *(u32x4*)(a.dOw + (size_t)row_global * a.D + sub * 8) = dv;
+    const float lse2 = (n < a.Nq) ? a.lse[bh * a.Nq + n] * kLog2e : 0.0f;
     if (sub == 0) {
         a.delta[row_global] = acc;
-        a.lse2[row_global] = (n < a.Nq) ? a.lse[bh * a.Nq + n] * kLog2e : 0.0f;
+        a.lse2[row_global] = lse2;
+    }
+    if (a.row_max) {
+        // dK/dV inputs of the row-max-relative variant: m2 = m log2(e) and
+        // dO, Dl scaled by 1/l = exp2(m2 - lse2) (padded rows: zero)
+        const float m2 = (n < a.Nq) ? a.row_max[bh * a.Nq + n] * kLog2e : 0.0f;
+        const float post = (n < a.Nq) ? __builtin_amdgcn_exp2f(m2 - lse2) : 0.0f;
+        u32x4 sv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sv[j] = pack_rne(bf_lo(dv[j]) * post, bf_hi(dv[j]) * post);
+        *(u32x4*)(a.dOw_kv + (size_t)row_global * a.D + sub * 8) = sv;
+        if (sub == 0) {
+            a.delta_kv[row_global] = acc * post;
+            a.lse2_kv[row_global] = m2;
+        }
     }
 }
 

@@ -54,7 +54,7 @@ def test_exports_every_declared_function(L):
     assert declared == set(qaa.EXPORTS), declared ^ set(qaa.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.attnqat_abi_version() == 1
+    assert L.attnqat_abi_version() == 2
 
 
 def test_status_strings(L):
@@ -174,3 +174,24 @@ def test_workspace_sizes_scale_with_problem(L):
 def test_mask_parsing():
     assert qaa.parse_mask("qkvp") == 15 and qaa.parse_mask("p") == 8 and qaa.parse_mask(5) == 5
     assert math.isclose(1 / math.sqrt(128), 0.08838834764831845)
+
+
+def test_row_max_mode_validation(L):
+    """p_mode: unknown values, a missing or misaligned row_max, and a row_max
+    that overlaps an output or input are rejected before any HIP call."""
+    assert _fwd(L, _prob(p_mode=2)) == E_INVALID
+    assert _fwd(L, _prob(p_mode=1)) == E_INVALID                       # row_max missing
+    assert _fwd(L, _prob(p_mode=1, row_max=30 * A + 2)) == E_MISALIGNED
+    assert _fwd(L, _prob(p_mode=1, row_max=5 * A)) == E_INVALID       # overlaps lse
+    assert _fwd(L, _prob(p_mode=1, row_max=A)) == E_INVALID           # overlaps q
+    assert _bwd(L, _prob(p_mode=1, row_max=7 * A)) == E_INVALID       # overlaps dq
+    assert _bwd(L, _prob(p_mode=1)) == E_INVALID
+    # the row-max backward needs room for its scaled dO copy and statistics
+    need0 = L.attnqat_bwd_workspace_bytes(ctypes.byref(_prob()))
+    need1 = L.attnqat_bwd_workspace_bytes(ctypes.byref(_prob(p_mode=1, row_max=30 * A)))
+    assert need1 > need0
+    # without P quantization the variant is the normalised one: no extra room
+    need2 = L.attnqat_bwd_workspace_bytes(ctypes.byref(_prob(p_mode=1, row_max=30 * A,
+                                                             quant_mask=7)))
+    assert need2 == need0
+

@@ -381,6 +381,25 @@ def test_block_sparse_equals_masked_dense(mask):
         np.testing.assert_allclose(O2, Or2, rtol=1e-12, atol=1e-13)
 
 
+def test_block_sparse_rowmax_equals_masked_dense():
+    """Row-max variant, sparse: the row maximum is taken over the selected
+    keys only, as in dense attention with the unselected keys masked out."""
+    N, bt, D, topk = 384, 128, 16, 2
+    q, k, v, do = (_bf16(60 + i, (1, 1, N, D)) for i in range(4))
+    idx = bsp.select_blocks(q, k, bt, topk)
+    O, L = bsp.forward(q, k, v, 0.3, idx, bt, att.MASK_ALL, p_mode=att.P_ROWMAX)
+    qq, kq, vq = att.quantize_operands(q, k, v, att.MASK_ALL)
+    for i in range(N // bt):
+        keys = np.concatenate([np.arange(j * bt, (j + 1) * bt) for j in idx[0, 0, i]])
+        S = 0.3 * qq[0, 0, i * bt:(i + 1) * bt] @ kq[0, 0, keys].T
+        m = S.max(axis=1, keepdims=True)
+        lse = m[:, 0] + np.log(np.exp(S - m).sum(axis=1))
+        Pq = nvfp4.fake_quant(np.exp(S - m), -1) / np.exp(lse[:, None] - m)
+        np.testing.assert_allclose(O[0, 0, i * bt:(i + 1) * bt], Pq @ vq[0, 0, keys], rtol=1e-12,
+                                   atol=1e-14)
+        np.testing.assert_allclose(L[0, 0, i * bt:(i + 1) * bt], lse, rtol=0, atol=1e-12)
+
+
 def test_block_helpers_match_full_sparse_oracle():
     bt, nb, topk = 32, 5, 2
     N = bt * nb - 7                       # ragged last block
