@@ -48,6 +48,13 @@ and the unquantized P = exp(S - LSE) in the softmax Jacobian. With the p bit
 clear both modes give Pq = P. Because exp(S - m) has maximum 1, the group
 scales do not flush to zero on long rows as those of the normalised P do.
 
+Additive straight-through output (the second alternative reading of the
+softmax-backward delta): the forward also forms the STE product of the
+unquantized P with Vq, O_ste = P Vq, and the backward takes its delta from
+it, D'_i = sum_c dO_ic O_ste_ic (``backward(..., O=O_ste)``). This is the
+gradient of the surrogate whose quantized P enters as P + (Pq0 - P0) with
+the difference frozen, i.e. Pq with a pure straight-through estimator.
+
 Everything is float64; S and P are materialised in row blocks.
 """
 from __future__ import annotations
@@ -92,27 +99,30 @@ def probabilities(S: np.ndarray, lse: np.ndarray, mask: int, p_mode: int = P_NOR
 
 
 def head_forward(qq, kq, vq, sm_scale: float, mask: int, rows=None, row_block: int = 512,
-                 p_mode: int = P_NORMALISED, with_max: bool = False):
+                 p_mode: int = P_NORMALISED, with_max: bool = False, with_ste: bool = False):
     """Forward for one head on already-quantized operands.
 
     ``rows`` (optional index array) restricts the query rows computed; the
-    result then has len(rows) rows. Returns (O [n, D], LSE [n]), and the row
-    maxima of S [n] as a third value with ``with_max``.
+    result then has len(rows) rows. Returns (O [n, D], LSE [n]), then the row
+    maxima of S [n] with ``with_max`` and O_ste = P Vq [n, D] with ``with_ste``.
     """
     qsel = qq if rows is None else qq[rows]
     n = qsel.shape[0]
     O = np.empty((n, vq.shape[1]))
+    Os = np.empty((n, vq.shape[1]))
     L = np.empty(n)
     M = np.empty(n)
     for r0 in range(0, n, row_block):
         r1 = min(n, r0 + row_block)
         S = sm_scale * (qsel[r0:r1] @ kq.T)
         lse = _lse(S)
-        _, Pq = probabilities(S, lse, mask, p_mode)
+        P, Pq = probabilities(S, lse, mask, p_mode)
         O[r0:r1] = Pq @ vq
+        if with_ste:
+            Os[r0:r1] = P @ vq
         L[r0:r1] = lse
         M[r0:r1] = np.max(S, axis=-1)
-    return (O, L, M) if with_max else (O, L)
+    return (O, L) + ((M,) if with_max else ()) + ((Os,) if with_ste else ())
 
 
 def _forward_rows_task(args):
@@ -143,21 +153,23 @@ def head_forward_all(qq, kq, vq, sm_scale: float, mask: int, workers: int = 0,
 
 
 def forward(q, k, v, sm_scale: float, mask: int = MASK_ALL, row_block: int = 512,
-            p_mode: int = P_NORMALISED, with_max: bool = False):
-    """O [B,H,Nq,D] and LSE [B,H,Nq] for real-valued inputs q, k, v (and the
-    row maxima of S [B,H,Nq] as a third value with ``with_max``)."""
+            p_mode: int = P_NORMALISED, with_max: bool = False, with_ste: bool = False):
+    """O [B,H,Nq,D] and LSE [B,H,Nq] for real-valued inputs q, k, v, then the
+    row maxima of S [B,H,Nq] with ``with_max`` and the straight-through output
+    O_ste = P Vq [B,H,Nq,D] with ``with_ste``."""
     q = np.asarray(q, np.float64)
     B, H, Nq, D = q.shape
     qq, kq, vq = quantize_operands(q, k, v, mask)
     O = np.empty((B, H, Nq, vq.shape[-1]))
+    Os = np.empty((B, H, Nq, vq.shape[-1]))
     L = np.empty((B, H, Nq))
     M = np.empty((B, H, Nq))
     for b in range(B):
         for h in range(H):
-            O[b, h], L[b, h], M[b, h] = head_forward(qq[b, h], kq[b, h], vq[b, h], sm_scale,
-                                                     mask, row_block=row_block, p_mode=p_mode,
-                                                     with_max=True)
-    return (O, L, M) if with_max else (O, L)
+            O[b, h], L[b, h], M[b, h], Os[b, h] = head_forward(
+                qq[b, h], kq[b, h], vq[b, h], sm_scale, mask, row_block=row_block,
+                p_mode=p_mode, with_max=True, with_ste=True)
+    return (O, L) + ((M,) if with_max else ()) + ((Os,) if with_ste else ())
 
 
 def head_backward(qq, kq, vq, do, O, lse, sm_scale: float, mask: int,

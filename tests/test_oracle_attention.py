@@ -248,6 +248,60 @@ def test_backward_quant_on_finite_differences(N, D, seed, p_mode):
         assert err < 1e-7, err
 
 
+def _surrogate_loss_ste(Q, K, V, W, rQ, rK, rV, R, scale):
+    S = scale * (Q + rQ) @ (K + rK).T
+    m = S.max(axis=1, keepdims=True)
+    P = np.exp(S - m)
+    P = P / P.sum(axis=1, keepdims=True)
+    return float(np.sum(W * ((P + R) @ (V + rV))))
+
+
+@pytest.mark.parametrize("N,D,seed", [(32, 16, 5), (40, 32, 6)])
+def test_backward_additive_ste_delta_finite_differences(N, D, seed):
+    """With the quantized P entering as P + (Pq0 - P0) (difference frozen, no
+    LSE factor), central differences give the backward whose delta is
+    D' = rowsum(dO * O_ste), O_ste = P Vq: the oracle's backward fed O_ste."""
+    Q = _bf16(500 + seed, (N, D), 1.5)
+    K = _bf16(600 + seed, (N, D), 1.5)
+    V = _bf16(700 + seed, (N, D))
+    W = _bf16(800 + seed, (N, D))
+    scale = 1 / math.sqrt(D)
+    Qq, Kq, Vq = nvfp4.fake_quant(Q, -1), nvfp4.fake_quant(K, -1), nvfp4.fake_quant(V, -2)
+    rQ, rK, rV = Qq - Q, Kq - K, Vq - V
+    S0 = scale * Qq @ Kq.T
+    P0 = np.exp(S0 - np.log(np.exp(S0).sum(axis=1))[:, None])
+    R = nvfp4.fake_quant(P0, -1) - P0
+    O, L, Os = att.forward(Q[None, None], K[None, None], V[None, None], scale, att.MASK_ALL,
+                           with_ste=True)
+    np.testing.assert_allclose(Os[0, 0], P0 @ Vq, rtol=1e-12, atol=1e-14)
+    dq, dk, dv = att.backward(Q[None, None], K[None, None], V[None, None], W[None, None],
+                              scale, att.MASK_ALL, O=Os, lse=L)
+    h = 1e-6
+    for X, G in ((Q, dq[0, 0]), (K, dk[0, 0]), (V, dv[0, 0])):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(*X.shape):
+            old = X[idx]
+            X[idx] = old + h
+            fp = _surrogate_loss_ste(Q, K, V, W, rQ, rK, rV, R, scale)
+            X[idx] = old - h
+            fm = _surrogate_loss_ste(Q, K, V, W, rQ, rK, rV, R, scale)
+            X[idx] = old
+            num[idx] = (fp - fm) / (2 * h)
+        err = np.linalg.norm(num - G) / np.linalg.norm(G)
+        assert err < 1e-7, err
+    # and it differs from the delta of the quantized output
+    dq2, _, _ = att.backward(Q[None, None], K[None, None], V[None, None], W[None, None],
+                             scale, att.MASK_ALL, O=O, lse=L)
+    assert np.linalg.norm(dq2 - dq) > 1e-3 * np.linalg.norm(dq)
+
+
+def test_ste_output_equals_output_without_p_quant():
+    q, k, v = _bf16(37, (1, 1, 20, 16)), _bf16(38, (1, 1, 30, 16)), _bf16(39, (1, 1, 30, 16))
+    for mask in (0, att.MASK_Q | att.MASK_K | att.MASK_V):
+        O, L, Os = att.forward(q, k, v, 0.3, mask=mask, with_ste=True)
+        np.testing.assert_array_equal(Os, O)
+
+
 def test_dk_sums_to_zero_without_p_quant():
     q = _bf16(20, (1, 1, 48, 32))
     k = _bf16(21, (1, 1, 48, 32))
