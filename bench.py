@@ -263,43 +263,54 @@ def main():
         fq[f"axis_{axis}"] = {"ms_per_launch": round(ms, 4), "algo_gbs": round(gbs, 1),
                               "frac_hbm": round(gbs / PEAK_HBM_GBS, 3)}
     out["fakequant_standalone"] = fq
-    # Row-max-relative P quantization variant on the same inputs (reported
-    # beside the metric, which is the normalised reading): same credited FLOPs.
+    # Variants of the P quantizer on the same inputs, reported beside the
+    # metric (which is the normalised reading with the plain STE) and credited
+    # the same FLOPs: the row-max-relative P and the additive straight-through
+    # output O_ste = P Vq, which the backward then takes as its o.
     if mask & qaa.QUANT_P:
         rm = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-        pr = qaa.make_problem(q, k, w.sm_scale, mask, v=v, o=o, do=do, dq=dq, dk=dk, dv=dv,
-                              kv_block_idx=kv_idx, p_mode=qaa.P_ROWMAX, row_max=rm)
-        ws_bv = torch.empty(L.attnqat_bwd_workspace_bytes(ctypes.byref(pr)), dtype=torch.uint8,
-                            device=dev)
+        os_ = torch.empty_like(o)
+        variants = {}
 
-        def step_rowmax(ev=None):
-            if ev:
-                ev[0].record()
-            qaa.fwd(q, k, v, w.sm_scale, mask, kv_idx, out=o, lse=lse, workspace=ws_f,
-                    p_mode=qaa.P_ROWMAX, row_max=rm)
-            if ev:
-                ev[1].record()
-            qaa.bwd(q, k, v, o, lse, do, w.sm_scale, mask, kv_idx, dq=dq, dk=dk, dv=dv,
-                    workspace=ws_bv, p_mode=qaa.P_ROWMAX, row_max=rm)
-            if ev:
-                ev[2].record()
+        def time_variant(name, fwd_kw, bwd_o, bwd_kw):
+            pr = qaa.make_problem(q, k, w.sm_scale, mask, v=v, o=o, do=do, dq=dq, dk=dk, dv=dv,
+                                  kv_block_idx=kv_idx, **bwd_kw)
+            ws_bv = torch.empty(L.attnqat_bwd_workspace_bytes(ctypes.byref(pr)),
+                                dtype=torch.uint8, device=dev)
 
-        for _ in range(2):
-            step_rowmax()
-        nv = max(1, min(args.steps, 5))
-        evv = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nv)]
-        torch.cuda.synchronize()
-        for i in range(nv):
-            step_rowmax(evv[i])
-        torch.cuda.synchronize()
-        vf = float(np.mean([a.elapsed_time(b) for a, b, _ in evv]))
-        vb = float(np.mean([b.elapsed_time(c) for _, b, c in evv]))
-        out["variants"] = {"p_rowmax": {
-            "steps": nv, "fwd_ms": round(vf, 4), "bwd_ms": round(vb, 4),
-            "ms_per_step": round(vf + vb, 4),
-            "tflops": round((f_fwd + f_bwd) / ((vf + vb) * 1e-3) / 1e12, 1),
-            "frac_peak": round((f_fwd + f_bwd) / ((vf + vb) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}}
-        del ws_bv
+            def step(ev=None):
+                if ev:
+                    ev[0].record()
+                qaa.fwd(q, k, v, w.sm_scale, mask, kv_idx, out=o, lse=lse, workspace=ws_f,
+                        **fwd_kw)
+                if ev:
+                    ev[1].record()
+                qaa.bwd(q, k, v, bwd_o, lse, do, w.sm_scale, mask, kv_idx, dq=dq, dk=dk, dv=dv,
+                        workspace=ws_bv, **bwd_kw)
+                if ev:
+                    ev[2].record()
+
+            for _ in range(2):
+                step()
+            nv = max(1, min(args.steps, 5))
+            evv = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nv)]
+            torch.cuda.synchronize()
+            for i in range(nv):
+                step(evv[i])
+            torch.cuda.synchronize()
+            vf = float(np.mean([a.elapsed_time(b) for a, b, _ in evv]))
+            vb = float(np.mean([b.elapsed_time(c) for _, b, c in evv]))
+            tf = (f_fwd + f_bwd) / ((vf + vb) * 1e-3) / 1e12
+            variants[name] = {"steps": nv, "fwd_ms": round(vf, 4), "bwd_ms": round(vb, 4),
+                              "ms_per_step": round(vf + vb, 4), "tflops": round(tf, 1),
+                              "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+            del ws_bv
+
+        rmk = dict(p_mode=qaa.P_ROWMAX, row_max=rm)
+        time_variant("p_rowmax", rmk, o, rmk)
+        time_variant("ste_delta", dict(o_ste=os_), os_, {})
+        out["variants"] = variants
+        del rm, os_
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)

@@ -113,6 +113,13 @@ typedef struct {
      * ATTNQAT_P_ROWMAX (required then, and must not overlap any other
      * argument); ignored otherwise. */
     float* row_max;
+    /* Optional second forward output (NULL: not formed), bf16 [B,H,Nq,D] with
+     * the strides of o: O_ste = P FQ_tokens(V) with the unquantized P (the
+     * P of p_mode), the straight-through counterpart of O. Passing it as the
+     * backward's `o` gives the additive straight-through delta
+     * Dl = rowsum(dout * O_ste) (the pages' SM120 route joins a quantized and
+     * an STE P@V). */
+    void* o_ste;
 } attnqat_problem;
 
 /* ABI version of the loaded library (ATTNQAT_ABI_VERSION it was built with). */

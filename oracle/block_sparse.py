@@ -92,15 +92,17 @@ def _keys_of(blocks, block_tokens: int, Nk: int) -> np.ndarray:
 
 
 def forward(q, k, v, sm_scale: float, idx: np.ndarray, block_tokens: int,
-            mask: int = MASK_ALL, p_mode: int = P_NORMALISED):
+            mask: int = MASK_ALL, p_mode: int = P_NORMALISED, with_ste: bool = False):
     """Block-sparse O [B,H,Nq,D] and LSE [B,H,Nq] for the selection ``idx``
     (``p_mode`` as in ``oracle.attention``: the row maximum is taken over the
-    selected keys)."""
+    selected keys), then O_ste = P Vq over the selected keys with
+    ``with_ste``."""
     q = np.asarray(q, np.float64)
     B, H, Nq, D = q.shape
     Nk = np.asarray(k).shape[2]
     qq, kq, vq = quantize_operands(q, k, v, mask)
     O = np.zeros((B, H, Nq, vq.shape[-1]))
+    Os = np.zeros((B, H, Nq, vq.shape[-1]))
     L = np.zeros((B, H, Nq))
     nbq = idx.shape[2]
     for b in range(B):
@@ -110,10 +112,11 @@ def forward(q, k, v, sm_scale: float, idx: np.ndarray, block_tokens: int,
                 keys = _keys_of(idx[b, h, i], block_tokens, Nk)
                 S = sm_scale * (qq[b, h, r0:r1] @ kq[b, h, keys].T)
                 lse = _lse(S)
-                _, Pq = probabilities(S, lse, mask, p_mode)
+                P, Pq = probabilities(S, lse, mask, p_mode)
                 O[b, h, r0:r1] = Pq @ vq[b, h, keys]
+                Os[b, h, r0:r1] = P @ vq[b, h, keys]
                 L[b, h, r0:r1] = lse
-    return O, L
+    return (O, L) + ((Os,) if with_ste else ())
 
 
 def backward(q, k, v, do, sm_scale: float, idx: np.ndarray, block_tokens: int,

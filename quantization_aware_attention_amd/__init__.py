@@ -43,7 +43,7 @@ class Problem(ctypes.Structure):
         ("dout", Strides), ("dq", Strides), ("dk", Strides), ("dv", Strides),
         ("kv_block_idx", ctypes.c_void_p), ("topk", ctypes.c_int32),
         ("block_tokens", ctypes.c_int32),
-        ("p_mode", ctypes.c_uint32), ("row_max", ctypes.c_void_p),
+        ("p_mode", ctypes.c_uint32), ("row_max", ctypes.c_void_p), ("o_ste", ctypes.c_void_p),
     ]
 
 
@@ -156,7 +156,7 @@ def strides_of(t: torch.Tensor) -> Strides:
 
 def make_problem(q, k, sm_scale, quant_mask, *, v=None, o=None, do=None, dq=None, dk=None,
                  dv=None, kv_block_idx=None, block_tokens=128, p_mode=P_NORMALISED,
-                 row_max=None) -> Problem:
+                 row_max=None, o_ste=None) -> Problem:
     B, H, Nq, D = q.shape
     Nk = k.shape[2]
     p = Problem()
@@ -174,6 +174,8 @@ def make_problem(q, k, sm_scale, quant_mask, *, v=None, o=None, do=None, dq=None
     p.p_mode = int(p_mode)
     if row_max is not None:
         p.row_max = row_max.data_ptr()
+    if o_ste is not None:
+        p.o_ste = o_ste.data_ptr()
     return p
 
 
@@ -205,10 +207,14 @@ def fakequant(x: torch.Tensor, axis: str = "d", return_scale_codes: bool = False
 
 
 def fwd(q, k, v, sm_scale=None, quant="qkvp", kv_block_idx=None, block_tokens=128,
-        out=None, lse=None, workspace=None, stream=None, p_mode=P_NORMALISED, row_max=None):
+        out=None, lse=None, workspace=None, stream=None, p_mode=P_NORMALISED, row_max=None,
+        o_ste=None):
     """O (bf16) and LSE (fp32, natural log) of Attn-QAT attention; with
     p_mode=P_ROWMAX also the row maxima of S (fp32 [B,H,Nq]), which the
-    backward of that mode needs: returns (O, LSE, row_max)."""
+    backward of that mode needs: returns (O, LSE, row_max). ``o_ste`` (a bf16
+    tensor shaped and strided like the output) also receives the
+    straight-through output P Vq; pass it as the backward's ``o`` for the
+    additive straight-through delta."""
     L = load()
     for n, t in (("q", q), ("k", k), ("v", v)):
         _check4(n, t)
@@ -221,8 +227,12 @@ def fwd(q, k, v, sm_scale=None, quant="qkvp", kv_block_idx=None, block_tokens=12
                                                   device=q.device)
     if p_mode == P_ROWMAX and row_max is None:
         row_max = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if o_ste is not None:
+        _check4("o_ste", o_ste)
+        if tuple(o_ste.shape) != tuple(o.shape) or o_ste.stride() != o.stride():
+            raise ValueError("o_ste must have the shape and strides of the output")
     p = make_problem(q, k, sm_scale, quant, v=v, o=o, kv_block_idx=kv_block_idx,
-                     block_tokens=block_tokens, p_mode=p_mode, row_max=row_max)
+                     block_tokens=block_tokens, p_mode=p_mode, row_max=row_max, o_ste=o_ste)
     need = L.attnqat_fwd_workspace_bytes(ctypes.byref(p))
     if need == 0:  # invalid problem: the call reports why
         check(L.attnqat_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),

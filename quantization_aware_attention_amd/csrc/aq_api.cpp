@@ -209,6 +209,7 @@ struct Plan {
     int nbq, nbk;
     bool rowmax_out;  // p_mode is ATTNQAT_P_ROWMAX: the forward writes the row maxima
     bool rowmax;      // ... and P is quantized: passes 2 and dK/dV use them
+    bool f16_pv;      // forward P V on fp16 operands (V^T stored as fp16)
 };
 
 int validate_problem(const attnqat_problem* p, Plan& pl) {
@@ -251,6 +252,10 @@ int validate_problem(const attnqat_problem* p, Plan& pl) {
         if (((uintptr_t)p->row_max) % 4)
             return fail(ATTNQAT_E_MISALIGNED, "row_max is not 4-byte aligned");
     }
+    // P and V both quantized: the P V product runs on fp16 operands, which hold
+    // NVFP4 values exactly, unless the unquantized P is multiplied too (o_ste)
+    pl.f16_pv = (p->quant_mask & ATTNQAT_QUANT_P) && (p->quant_mask & ATTNQAT_QUANT_V) &&
+                !p->o_ste;
     pl.sparse = p->kv_block_idx != nullptr;
     pl.nbq = pl.nbk = 0;
     if (pl.sparse) {
@@ -329,11 +334,6 @@ aq::FqArgs fq_args(const void* x, const Strides& xs, void* y, const Strides& ys,
     return a;
 }
 
-// The forward's P V product runs on fp16 operands when both P and V are
-// NVFP4 values (fp16 holds them exactly); V^T is then stored as fp16.
-bool pv_f16(uint32_t mask) {
-    return (mask & ATTNQAT_QUANT_P) && (mask & ATTNQAT_QUANT_V);
-}
 
 // Quantize (or copy) q, k, v into the padded workspace operands.
 int prepare_operands(const Plan& pl, uint32_t mask, const void* q, const void* k, const void* v,
@@ -355,7 +355,7 @@ int prepare_operands(const Plan& pl, uint32_t mask, const void* q, const void* k
     if (rc) return rc;
     if (!bwd)
         return run_transpose((const uint16_t*)(ws + L.vw), (uint16_t*)(ws + L.vt), pl.BH, pl.Nk_pad,
-                             pl.D, false, st, "transpose V", pv_f16(mask));
+                             pl.D, false, st, "transpose V", pl.f16_pv);
     return run_transpose((const uint16_t*)(ws + L.kw), (uint16_t*)(ws + L.kt), pl.BH, pl.Nk_pad,
                          pl.D, true, st, "transpose K");
 }
@@ -374,7 +374,7 @@ aq::AttnArgs attn_args(const attnqat_problem* p, const Plan& pl, char* ws, const
     a.sm_scale = p->sm_scale;
     a.c = p->sm_scale * aq::kLog2e;
     a.quant_p = (p->quant_mask & ATTNQAT_QUANT_P) ? 1 : 0;
-    a.pv_f16 = pv_f16(p->quant_mask) ? 1 : 0;
+    a.pv_f16 = pl.f16_pv ? 1 : 0;
     if (pl.sparse) {
         a.kv_idx = p->kv_block_idx;
         a.topk = p->topk;
@@ -472,14 +472,18 @@ int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const vo
     const Range rm = pl.rowmax_out ? Range{(uintptr_t)p->row_max,
                                            (uintptr_t)p->row_max + (uintptr_t)(pl.BH * pl.Nq * 4)}
                                    : Range{0, 0};
+    if (p->o_ste && (rc = check_tensor("o_ste", p->o_ste, pl.o, pl.H, pl.Nq, pl.D))) return rc;
+    const Range rs = p->o_ste ? extent(p->o_ste, pl.o, pl.B, pl.H, pl.Nq, pl.D, 2) : Range{0, 0};
     const Range ins[3] = {extent(q, pl.q, pl.B, pl.H, pl.Nq, pl.D, 2),
                           extent(k, pl.k, pl.B, pl.H, pl.Nk, pl.D, 2),
                           extent(v, pl.v, pl.B, pl.H, pl.Nk, pl.D, 2)};
     for (const Range& r : ins)
-        if (overlaps(r, ro) || overlaps(r, rl) || overlaps(r, rw) || overlaps(r, rm))
+        if (overlaps(r, ro) || overlaps(r, rl) || overlaps(r, rw) || overlaps(r, rm) ||
+            overlaps(r, rs))
             return fail(ATTNQAT_E_INVALID, "an output or the workspace overlaps an input");
     if (overlaps(ro, rl) || overlaps(ro, rw) || overlaps(rl, rw) || overlaps(rm, ro) ||
-        overlaps(rm, rl) || overlaps(rm, rw))
+        overlaps(rm, rl) || overlaps(rm, rw) || overlaps(rs, ro) || overlaps(rs, rl) ||
+        overlaps(rs, rw) || overlaps(rs, rm))
         return fail(ATTNQAT_E_INVALID, "outputs overlap each other or the workspace");
     if ((rc = check_device())) return rc;
 
@@ -490,6 +494,7 @@ int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const vo
     a.Vt = (const uint16_t*)(ws + L.vt);
     a.lse_out = lse;
     a.row_max_out = pl.rowmax_out ? p->row_max : nullptr;
+    a.o_ste = (uint16_t*)p->o_ste;
     a.row_max = pl.rowmax ? p->row_max : nullptr;
     a.lse = lse;
     a.o = (uint16_t*)o;

@@ -483,6 +483,123 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_out_kernel(AttnA
 }
 
 // ---------------------------------------------------------------------------
+// Forward pass 2 with the additive straight-through output: besides
+// O = Pq Vq it forms O_ste = P Vq with the unquantized P, whose row sums
+// against dO are the backward delta of the pure straight-through reading
+// (the caller passes O_ste as the backward's o). One wave per 32 queries as in
+// fwd_out_kernel; each V^T operand read feeds both products. P V runs on bf16
+// operands here (P is not an NVFP4 value).
+template <int D, bool QP>
+struct FwdOutSte {
+    static constexpr int BN = 64;
+    // Pq and P of one 32-key score block, each as two B operands
+    template <bool tail>
+    __device__ __forceinline__ static void probs(f32x16 acc, int k0, int Nk, float c, float off, int hh, u32x4* bq,
+                                 u32x4* bp) {
+        float x[16], r[16], sp = 1.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            x[j] = acc[j];
+            if (tail && k0 + 16 * hh + j >= Nk) x[j] = -INFINITY;
+        }
+        if (QP) {
+            quant_p_group16_bwd(x, c, off, bq, r, sp);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) r[j] = __builtin_amdgcn_exp2f(fmaf(x[j], c, -off));
+        }
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const float* e = r + 8 * g;
+            bp[g] = u32x4{pack_rne(e[0] * sp, e[1] * sp), pack_rne(e[2] * sp, e[3] * sp),
+                          pack_rne(e[4] * sp, e[5] * sp), pack_rne(e[6] * sp, e[7] * sp)};
+            if (!QP) bq[g] = bp[g];
+        }
+    }
+    __device__ __forceinline__ static void pv2(const uint16_t* sV, int kb, const u32x4* bq, const u32x4* bp,
+                               f32x16* o, f32x16* os, int l32, int hh) {
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const u32x4 vf = *(const u32x4*)(sV + toff<BN>(db * 32 + l32, 4 * kb + 2 * hh + g));
+                o[db] = mfma(vf, bq[g], o[db]);
+                if (QP) os[db] = mfma(vf, bp[g], os[db]);
+            }
+        }
+    }
+    // one 32-key block at a time: two output accumulators leave no room for
+    // the two-block software pipeline of FwdOut
+    template <bool tail>
+    __device__ __forceinline__ static void block(const uint16_t* sK, const uint16_t* sV, int kt,
+                                                 int Nk, const u32x4* qf, float c, float off,
+                                                 f32x16* o, f32x16* os, int l32, int hh) {
+#pragma unroll
+        for (int kb = 0; kb < BN / 32; ++kb) {
+            const f32x16 sc = scores_T<D>(sK, kb * 32, qf, l32, hh);
+            u32x4 bq[2], bp[2];
+            probs<tail>(sc, kt + kb * 32, Nk, c, off, hh, bq, bp);
+            pv2(sV, kb, bq, bp, o, os, l32, hh);
+        }
+    }
+};
+
+template <int D, bool QP, int NW, bool SPARSE>
+__global__ __launch_bounds__(NW * 64) void fwd_out_ste_kernel(AttnArgs a) {
+    using F = FwdOutSte<D, QP>;
+    constexpr int BN = F::BN;
+    static_assert(!SPARSE || NW == 4, "sparse workgroups cover one 128-query block");
+    struct Buf {
+        uint16_t k[BN * D];
+        uint16_t v[D * BN];
+    };
+    __shared__ __attribute__((aligned(1024))) Buf s0, s1;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int bh = blockIdx.y, qblk = blockIdx.x;
+    const int q0 = qblk * (NW * 32) + wave * 32;
+    const int q = q0 + l32;
+    const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
+    const uint16_t* Kb = a.Kw + (size_t)bh * a.Nk_pad * D;
+    const uint16_t* Vtb = a.Vt + (size_t)bh * D * a.Nk_pad;
+    u32x4 qf[D / 16];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+        qf[c] = *(const u32x4*)(Qb + (size_t)(q0 + l32) * D + c * 16 + hh * 8);
+    float off, post;
+    p_offset<QP>(a, bh, q, off, post);
+    f32x16 o[D / 32], os[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = os[db] = f32x16{};
+    __shared__ int lst[SPARSE ? kMaxBlockList : 1];
+    if (SPARSE) stage_list(lst, a.kv_idx + ((size_t)bh * a.nbq + qblk) * a.topk, a.topk);
+    const int n_iter = SPARSE ? a.topk * 2 : (a.Nk + BN - 1) / BN;
+    auto tile_at = [&](int it) { return tile_start<SPARSE, BN>(lst, it); };
+    AsyncTile<BN, D, NW * 64, true> tk;
+    AsyncTile<D, BN, NW * 64> tv;
+    tk.init(D, tid);
+    tv.init(a.Nk_pad, tid);
+    tile_pipeline(
+        n_iter, tile_at(n_iter - 1) + BN > a.Nk,
+        [&](auto b, int it) {
+            const int kt = tile_at(it);
+            tk.issue(sel(b, &s0, &s1)->k, Kb + (size_t)kt * D);
+            tv.issue(sel(b, &s0, &s1)->v, Vtb + kt);
+        },
+        [&](auto b, int it, auto tail) {
+            F::template block<decltype(tail)::value>(sel(b, &s0, &s1)->k, sel(b, &s0, &s1)->v,
+                                                     tile_at(it), a.Nk, qf, a.c, off, o, os, l32,
+                                                     hh);
+        });
+    if (q < a.Nq) {
+        const int64_t b = bh / a.H, h = bh % a.H, at = b * a.osb + h * a.osh + (int64_t)q * a.osn;
+        store_rows_T<D>(a.o + at, o, post, hh);
+        // without P quantization Pq = P and the two outputs are the same
+        store_rows_T<D>(a.o_ste + at, QP ? os : o, post, hh);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Backward dQ: NW waves x 32 queries, loop over 64-key tiles.
 // Backward dQ: NW waves x 32 QB queries, loop over 64-key tiles. A wave
 // keeps the Q and dO B operands of its QB 32-query blocks in registers; each
@@ -1171,8 +1288,21 @@ static void fwd_out_go(const AttnArgs& a, bool sp, hipStream_t st) {
     }
 }
 
+template <int D, bool QP>
+static void fwd_out_ste_go(const AttnArgs& a, bool sp, hipStream_t st) {
+    // four waves of 32 queries, one per SIMD: the two output accumulators and
+    // the quantizer need more than the 256 registers of two waves per SIMD
+    if (sp) fwd_out_ste_kernel<D, QP, 4, true><<<dim3(a.nbq, a.BH), 256, 0, st>>>(a);
+    else fwd_out_ste_kernel<D, QP, 4, false><<<dim3((a.Nq + 127) / 128, a.BH), 256, 0, st>>>(a);
+}
+
 template <int D>
 static void fwd_out_d(const AttnArgs& a, bool sp, hipStream_t st) {
+    if (a.o_ste) {  // V^T is bf16 then (pv_f16 off)
+        if (a.quant_p) fwd_out_ste_go<D, true>(a, sp, st);
+        else fwd_out_ste_go<D, false>(a, sp, st);
+        return;
+    }
     if (a.quant_p && a.pv_f16) fwd_out_go<D, true, true>(a, sp, st);
     else if (a.quant_p) fwd_out_go<D, true, false>(a, sp, st);
     else fwd_out_go<D, false, false>(a, sp, st);

@@ -58,6 +58,7 @@ struct AttnArgs {
     float* row_max_out;   // forward pass 1: row maxima of S [BH][Nq] (NULL: not written)
     const float* row_max; // forward pass 2: quantize exp(S - m) and scale O by 1/l (NULL: off)
     uint16_t* o;          // strided outputs
+    uint16_t* o_ste;      // forward: P Vq with the unquantized P (o's strides; NULL: not formed)
     int64_t osb, osh, osn;
     uint16_t* dq;
     int64_t dqsb, dqsh, dqsn;

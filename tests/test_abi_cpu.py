@@ -195,3 +195,11 @@ def test_row_max_mode_validation(L):
                                                              quant_mask=7)))
     assert need2 == need0
 
+
+def test_ste_output_validation(L):
+    """o_ste takes o's strides; it must be 16-byte aligned and overlap neither
+    an input nor another output."""
+    assert _fwd(L, _prob(o_ste=40 * A + 8)) == E_MISALIGNED
+    assert _fwd(L, _prob(o_ste=A)) == E_INVALID        # overlaps q
+    assert _fwd(L, _prob(o_ste=4 * A)) == E_INVALID    # overlaps o
+

@@ -488,3 +488,18 @@ def test_parallel_full_head_forward_matches():
     O2, L2 = att.head_forward_all(qq, kq, vq, 0.2, 15, workers=2, chunk=64)
     np.testing.assert_array_equal(O1, O2)
     np.testing.assert_array_equal(L1, L2)
+
+
+def test_block_sparse_ste_output():
+    """Sparse O_ste: with every key block selected it is the dense O_ste; with
+    P unquantized it is the sparse O."""
+    N, bt, D = 96, 32, 16
+    q, k, v = (_bf16(70 + i, (1, 1, N, D)) for i in range(3))
+    idx_all = np.arange(3, dtype=np.int32)[None, None, None].repeat(3, axis=2)
+    _, _, Os = bsp.forward(q, k, v, 0.3, idx_all, bt, att.MASK_ALL, with_ste=True)
+    _, _, Osd = att.forward(q, k, v, 0.3, att.MASK_ALL, with_ste=True)
+    np.testing.assert_allclose(Os, Osd, rtol=1e-12, atol=1e-14)
+    idx = bsp.select_blocks(q, k, bt, 1)
+    O, _, Os = bsp.forward(q, k, v, 0.3, idx, bt, att.MASK_Q | att.MASK_K | att.MASK_V,
+                           with_ste=True)
+    np.testing.assert_array_equal(Os, O)
