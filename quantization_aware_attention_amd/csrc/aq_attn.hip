@@ -600,7 +600,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_out_ste_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Backward dQ: NW waves x 32 queries, loop over 64-key tiles.
 // Backward dQ: NW waves x 32 QB queries, loop over 64-key tiles. A wave
 // keeps the Q and dO B operands of its QB 32-query blocks in registers; each
 // K, V or K^T operand read from LDS feeds QB products.
