@@ -263,6 +263,36 @@ def main():
         fq[f"axis_{axis}"] = {"ms_per_launch": round(ms, 4), "algo_gbs": round(gbs, 1),
                               "frac_hbm": round(gbs / PEAK_HBM_GBS, 3)}
     out["fakequant_standalone"] = fq
+    # VSA coarse branch and gated combination on the same tensors (128-token
+    # blocks): its kernels are passes over the token tensors, reported as
+    # algorithmic GB/s (bf16 bytes each pass must move) next to HBM peak.
+    gate = torch.randn_like(q)
+    vq, vk, vv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
+    vo = torch.empty_like(o)
+    for _ in range(2):
+        qaa.vsa_fwd(q, k, v, gate, o, w.sm_scale, out=vo)
+        qaa.vsa_bwd(q, k, v, gate, do, vq, vk, vv, w.sm_scale)
+    torch.cuda.synchronize()
+    qaa.profile_enable(True)
+    for _ in range(10):
+        qaa.vsa_fwd(q, k, v, gate, o, w.sm_scale, out=vo)
+        qaa.vsa_bwd(q, k, v, gate, do, vq, vk, vv, w.sm_scale)
+    torch.cuda.synchronize()
+    rec = qaa.profile_read()
+    qaa.profile_enable(False)
+    tok = 2.0 * B * H * D  # bytes per token row of one bf16 tensor
+    vbytes = {"vsa_pool": tok * 3 * N, "vsa_combine": tok * 3 * N, "vsa_gate_reduce": tok * 3 * N,
+              "vsa_grad_add": tok * 6 * N}
+    vs = {}
+    for name, (tot, cnt) in rec.items():
+        ms = tot / cnt
+        e = {"ms_per_launch": round(ms, 4), "launches_per_step": cnt / 10}
+        if name in vbytes:
+            e["algo_gbs"] = round(vbytes[name] / (ms * 1e-3) / 1e9, 1)
+            e["frac_hbm"] = round(e["algo_gbs"] / PEAK_HBM_GBS, 3)
+        vs[name] = e
+    out["vsa_coarse"] = {"kernels": vs, "ms_per_step": round(sum(v["ms_per_launch"] * v["launches_per_step"] for v in vs.values()), 4)}
+    del gate, vq, vk, vv, vo
     # Variants of the P quantizer on the same inputs, reported beside the
     # metric (which is the normalised reading with the plain STE) and credited
     # the same FLOPs: the row-max-relative P and the additive straight-through

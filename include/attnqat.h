@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define ATTNQAT_ABI_VERSION 2
+#define ATTNQAT_ABI_VERSION 3
 
 /* status codes */
 #define ATTNQAT_OK 0
@@ -205,6 +205,46 @@ size_t attnqat_block_select_workspace_bytes(const attnqat_problem* p);
 int attnqat_block_select(const attnqat_problem* p, const void* q, const void* k,
                          int32_t* kv_block_idx, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/* Workspace bytes attnqat_vsa_fwd and attnqat_vsa_bwd need (one size for both). */
+size_t attnqat_vsa_workspace_bytes(const attnqat_problem* p);
+
+/*
+ * VSA coarse branch and its gated combination with the fine branch
+ * (checkpoint metadata: attention kind vsa, backend VSA_QAT_TRAIN_C128,
+ * precision.coarse = BF16 with quantize_coarse = false, compression_gates
+ * trained; the fastvideo-kernel commit message scatters the gate with Q, K and
+ * V, so the gate is a per-token [B,H,Nq,D] tensor). With blocks of
+ * p->block_tokens (must be 128) tokens, a partial last block averaged over its
+ * own tokens, and Qbar, Kbar, Vbar the bf16-rounded block means of the raw q,
+ * k, v (as for attnqat_block_select):
+ *   O_c = softmax(sm_scale Qbar Kbar^T) Vbar   (fp32 from the bf16 means)
+ *   o   = o_fine + gate * O_c[block(t)]        (bf16, rounded once)
+ * o_fine is the fine branch's output (attnqat_fwd with kv_block_idx). gate,
+ * o_fine and o are bf16 [B,H,Nq,D] with the strides of p->o; q, k, v use their
+ * own. o must not overlap any input or the workspace. ceil(Nq/128) and
+ * ceil(Nk/128) must be at most 1024. p->quant_mask, p_mode and kv_block_idx
+ * are not used (the coarse branch is never quantized).
+ */
+int attnqat_vsa_fwd(const attnqat_problem* p, const void* q, const void* k, const void* v,
+                    const void* gate, const void* o_fine, void* o, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of the coarse branch and the combination, to be run after
+ * attnqat_bwd of the fine branch (called with o = o_fine, so that its softmax
+ * delta is rowsum(dout * o_fine)). Adds in place to dq, dk, dv (bf16, which
+ * hold the fine gradients) the coarse contributions: dO_c[i] = sum over the
+ * tokens of query block i of gate * dout, dS = P (dO_c Vbar^T - rowsum(dO_c
+ * O_c)), dQbar = sm_scale dS Kbar, dKbar = sm_scale dS^T Qbar, dVbar = P^T
+ * dO_c, and every token of a block receives its block mean's gradient divided
+ * by the block's token count. Writes dgate = dout * O_c[block(t)] (bf16, the
+ * strides of p->o) unless dgate is NULL. dq, dk, dv and dgate must not overlap
+ * each other, any input or the workspace.
+ */
+int attnqat_vsa_bwd(const attnqat_problem* p, const void* q, const void* k, const void* v,
+                    const void* gate, const void* dout, void* dq, void* dk, void* dv,
+                    void* dgate, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Kernel timing (diagnostics). While enabled on the calling thread, every

@@ -51,7 +51,8 @@ EXPORTS = [
     "attnqat_abi_version", "attnqat_status_string", "attnqat_last_error",
     "attnqat_fakequant_nvfp4", "attnqat_fwd_workspace_bytes", "attnqat_fwd",
     "attnqat_bwd_workspace_bytes", "attnqat_bwd", "attnqat_block_select_workspace_bytes",
-    "attnqat_block_select", "attnqat_profile_enable", "attnqat_profile_read",
+    "attnqat_block_select", "attnqat_vsa_workspace_bytes", "attnqat_vsa_fwd", "attnqat_vsa_bwd",
+    "attnqat_profile_enable", "attnqat_profile_read",
 ]
 
 _lib = None
@@ -105,6 +106,12 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.attnqat_block_select_workspace_bytes.argtypes = [pp]
     lib.attnqat_block_select.restype = ctypes.c_int
     lib.attnqat_block_select.argtypes = [pp, P, P, P, P, SZ, V]
+    lib.attnqat_vsa_workspace_bytes.restype = SZ
+    lib.attnqat_vsa_workspace_bytes.argtypes = [pp]
+    lib.attnqat_vsa_fwd.restype = ctypes.c_int
+    lib.attnqat_vsa_fwd.argtypes = [pp, P, P, P, P, P, P, P, SZ, V]
+    lib.attnqat_vsa_bwd.restype = ctypes.c_int
+    lib.attnqat_vsa_bwd.argtypes = [pp, P, P, P, P, P, P, P, P, P, P, SZ, V]
     lib.attnqat_profile_enable.restype = ctypes.c_int
     lib.attnqat_profile_enable.argtypes = [ctypes.c_int]
     lib.attnqat_profile_read.restype = ctypes.c_int
@@ -289,6 +296,59 @@ def block_select(q, k, topk: int, block_tokens: int = 128, stream=None) -> torch
     check(L.attnqat_block_select(ctypes.byref(p), q.data_ptr(), k.data_ptr(), idx.data_ptr(),
                                  ws.data_ptr(), ws.numel(), _stream(stream)))
     return idx
+
+
+def vsa_fwd(q, k, v, gate, o_fine, sm_scale=None, out=None, workspace=None, stream=None):
+    """VSA coarse branch and gated combination: o_fine + gate * O_c[block(t)]
+    (bf16 [B,H,Nq,D]; gate, o_fine and the output share one stride layout)."""
+    L = load()
+    for n, t in (("q", q), ("k", k), ("v", v), ("gate", gate), ("o_fine", o_fine)):
+        _check4(n, t)
+    B, H, Nq, D = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    o = out if out is not None else torch.empty_like(o_fine)
+    _check4("out", o)
+    for n, t in (("gate", gate), ("out", o)):
+        if tuple(t.shape) != tuple(o_fine.shape) or t.stride() != o_fine.stride():
+            raise ValueError(f"{n} must have the shape and strides of o_fine")
+    p = make_problem(q, k, sm_scale, 0, v=v, o=o_fine)
+    need = L.attnqat_vsa_workspace_bytes(ctypes.byref(p))
+    ws = workspace if workspace is not None and workspace.numel() >= need else \
+        _workspace(need, q.device)
+    check(L.attnqat_vsa_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                            gate.data_ptr(), o_fine.data_ptr(), o.data_ptr(), ws.data_ptr(),
+                            ws.numel(), _stream(stream)))
+    return o
+
+
+def vsa_bwd(q, k, v, gate, do, dq, dk, dv, sm_scale=None, dgate=None, want_dgate=True,
+            workspace=None, stream=None):
+    """Adds the coarse branch's gradients to dq, dk, dv in place (they hold
+    the fine branch's) and returns (dq, dk, dv, dgate); dgate is shaped and
+    strided like gate (None with want_dgate=False)."""
+    L = load()
+    for n, t in (("q", q), ("k", k), ("v", v), ("gate", gate), ("do", do), ("dq", dq),
+                 ("dk", dk), ("dv", dv)):
+        _check4(n, t)
+    B, H, Nq, D = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    if want_dgate and dgate is None:
+        dgate = torch.empty_like(gate)
+    if dgate is not None:
+        _check4("dgate", dgate)
+        if tuple(dgate.shape) != tuple(gate.shape) or dgate.stride() != gate.stride():
+            raise ValueError("dgate must have the shape and strides of gate")
+    p = make_problem(q, k, sm_scale, 0, v=v, o=gate, do=do, dq=dq, dk=dk, dv=dv)
+    need = L.attnqat_vsa_workspace_bytes(ctypes.byref(p))
+    ws = workspace if workspace is not None and workspace.numel() >= need else \
+        _workspace(need, q.device)
+    check(L.attnqat_vsa_bwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                            gate.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                            dv.data_ptr(), dgate.data_ptr() if dgate is not None else None,
+                            ws.data_ptr(), ws.numel(), _stream(stream)))
+    return dq, dk, dv, dgate
 
 
 def profile_enable(on: bool = True) -> None:

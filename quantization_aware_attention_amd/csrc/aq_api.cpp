@@ -67,11 +67,13 @@ int hip_check(hipError_t e, const char* what) {
 // optional per-thread kernel timing
 enum Kind {
     K_FQ_D, K_FQ_N, K_TRANSPOSE, K_FWD_LSE, K_FWD_OUT, K_BWD_PRE, K_BWD_DKDV, K_BWD_DQ,
-    K_BLOCK_POOL, K_BLOCK_TOPK, K_REVERSE_INDEX, K_NUM
+    K_BLOCK_POOL, K_BLOCK_TOPK, K_REVERSE_INDEX, K_VSA_POOL, K_VSA_COARSE, K_VSA_COMBINE,
+    K_VSA_GATE, K_VSA_COARSE_BWD, K_VSA_GRAD_ADD, K_NUM
 };
 const char* const kKindName[K_NUM] = {
     "fq_axis_d", "fq_axis_n", "transpose_perm", "fwd_lse", "fwd_out", "bwd_pre", "bwd_dkdv",
-    "bwd_dq", "block_pool", "block_topk", "reverse_index"};
+    "bwd_dq", "block_pool", "block_topk", "reverse_index", "vsa_pool", "vsa_coarse",
+    "vsa_combine", "vsa_gate_reduce", "vsa_coarse_bwd", "vsa_grad_add"};
 
 constexpr int kMaxTimed = 65536;
 
@@ -702,6 +704,226 @@ int attnqat_block_select(const attnqat_problem* p, const void* q, const void* k,
         return rc;
     if ((rc = launch(K_BLOCK_TOPK, st, thunk<aq::SelectArgs, aq::launch_block_topk>, &a,
                      "block top-k")))
+        return rc;
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+// VSA coarse branch
+namespace {
+
+struct VsaLayout {
+    size_t qbar, kbar, vbar, oc, lsec, doc, dcc, dqb, dkb, dvb, total;
+};
+
+VsaLayout vsa_layout(int64_t BH, int64_t nbq, int64_t nbk, int64_t D) {
+    VsaLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off += (bytes + 255) / 256 * 256;
+        return at;
+    };
+    L.qbar = take((size_t)(BH * nbq * D * 2));
+    L.kbar = take((size_t)(BH * nbk * D * 2));
+    L.vbar = take((size_t)(BH * nbk * D * 2));
+    L.oc = take((size_t)(BH * nbq * D * 4));
+    L.lsec = take((size_t)(BH * nbq * 4));
+    L.doc = take((size_t)(BH * nbq * D * 4));
+    L.dcc = take((size_t)(BH * nbq * 4));
+    L.dqb = take((size_t)(BH * nbq * D * 4));
+    L.dkb = take((size_t)(BH * nbk * D * 4));
+    L.dvb = take((size_t)(BH * nbk * D * 4));
+    L.total = off;
+    return L;
+}
+
+int vsa_plan(const attnqat_problem* p, Plan& pl, int64_t& nbq, int64_t& nbk, VsaLayout& L) {
+    int rc = validate_problem(p, pl);
+    if (rc) return rc;
+    if (p->block_tokens != 128)
+        return fail(ATTNQAT_E_UNSUPPORTED, "VSA blocks must be 128 tokens (got %d)", p->block_tokens);
+    nbq = (pl.Nq + 127) / 128;
+    nbk = (pl.Nk + 127) / 128;
+    if (nbq > aq::kVsaMaxBlocks || nbk > aq::kVsaMaxBlocks)
+        return fail(ATTNQAT_E_UNSUPPORTED, "VSA supports at most %d blocks per sequence",
+                    aq::kVsaMaxBlocks);
+    L = vsa_layout(pl.BH, nbq, nbk, pl.D);
+    return ATTNQAT_OK;
+}
+
+aq::VsaArgs vsa_args(const attnqat_problem* p, const Plan& pl, int64_t nbq, int64_t nbk,
+                     const VsaLayout& L, char* ws, const void* q, const void* k, const void* v,
+                     const void* gate) {
+    aq::VsaArgs a{};
+    a.q = (const uint16_t*)q;
+    a.qsb = pl.q.b;
+    a.qsh = pl.q.h;
+    a.qsn = pl.q.n;
+    a.k = (const uint16_t*)k;
+    a.ksb = pl.k.b;
+    a.ksh = pl.k.h;
+    a.ksn = pl.k.n;
+    a.v = (const uint16_t*)v;
+    a.vsb = pl.v.b;
+    a.vsh = pl.v.h;
+    a.vsn = pl.v.n;
+    a.gate = (const uint16_t*)gate;
+    a.osb = pl.o.b;
+    a.osh = pl.o.h;
+    a.osn = pl.o.n;
+    a.qbar = (uint16_t*)(ws + L.qbar);
+    a.kbar = (uint16_t*)(ws + L.kbar);
+    a.vbar = (uint16_t*)(ws + L.vbar);
+    a.oc = (float*)(ws + L.oc);
+    a.lsec = (float*)(ws + L.lsec);
+    a.doc = (float*)(ws + L.doc);
+    a.dcc = (float*)(ws + L.dcc);
+    a.dqb = (float*)(ws + L.dqb);
+    a.dkb = (float*)(ws + L.dkb);
+    a.dvb = (float*)(ws + L.dvb);
+    a.BH = pl.BH;
+    a.H = pl.H;
+    a.Nq = (int)pl.Nq;
+    a.Nk = (int)pl.Nk;
+    a.bt = 128;
+    a.nbq = (int)nbq;
+    a.nbk = (int)nbk;
+    a.D = (int)pl.D;
+    a.sm_scale = p->sm_scale;
+    return a;
+}
+
+int check_workspace(void* ws, size_t have, size_t need) {
+    if (!ws || have < need)
+        return fail(ATTNQAT_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", need,
+                    ws ? have : (size_t)0);
+    if (((uintptr_t)ws) % 256) return fail(ATTNQAT_E_MISALIGNED, "workspace is not 256-byte aligned");
+    return ATTNQAT_OK;
+}
+
+// The coarse forward: block means, then the coarse attention rows.
+int vsa_coarse(const aq::VsaArgs& a, hipStream_t st) {
+    int rc;
+    if ((rc = launch(K_VSA_POOL, st, thunk<aq::VsaArgs, aq::launch_vsa_pool>, &a, "VSA block means")))
+        return rc;
+    return launch(K_VSA_COARSE, st, thunk<aq::VsaArgs, aq::launch_vsa_coarse_fwd>, &a,
+                  "VSA coarse attention");
+}
+
+}  // namespace
+
+size_t attnqat_vsa_workspace_bytes(const attnqat_problem* p) {
+    Plan pl;
+    int64_t nbq, nbk;
+    VsaLayout L;
+    if (vsa_plan(p, pl, nbq, nbk, L)) return 0;
+    return L.total;
+}
+
+int attnqat_vsa_fwd(const attnqat_problem* p, const void* q, const void* k, const void* v,
+                    const void* gate, const void* o_fine, void* o, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    Plan pl;
+    int64_t nbq, nbk;
+    VsaLayout L;
+    int rc = vsa_plan(p, pl, nbq, nbk, L);
+    if (rc) return rc;
+    if ((rc = check_tensor("q", q, pl.q, pl.H, pl.Nq, pl.D))) return rc;
+    if ((rc = check_tensor("k", k, pl.k, pl.H, pl.Nk, pl.D))) return rc;
+    if ((rc = check_tensor("v", v, pl.v, pl.H, pl.Nk, pl.D))) return rc;
+    if ((rc = check_tensor("gate", gate, pl.o, pl.H, pl.Nq, pl.D))) return rc;
+    if ((rc = check_tensor("o_fine", o_fine, pl.o, pl.H, pl.Nq, pl.D))) return rc;
+    if ((rc = check_tensor("o", o, pl.o, pl.H, pl.Nq, pl.D))) return rc;
+    if ((rc = check_workspace(workspace, workspace_bytes, L.total))) return rc;
+    const Range ins[5] = {extent(q, pl.q, pl.B, pl.H, pl.Nq, pl.D, 2),
+                          extent(k, pl.k, pl.B, pl.H, pl.Nk, pl.D, 2),
+                          extent(v, pl.v, pl.B, pl.H, pl.Nk, pl.D, 2),
+                          extent(gate, pl.o, pl.B, pl.H, pl.Nq, pl.D, 2),
+                          extent(o_fine, pl.o, pl.B, pl.H, pl.Nq, pl.D, 2)};
+    const Range ro = extent(o, pl.o, pl.B, pl.H, pl.Nq, pl.D, 2);
+    const Range rw = {(uintptr_t)workspace, (uintptr_t)workspace + L.total};
+    if (overlaps(ro, rw)) return fail(ATTNQAT_E_INVALID, "o overlaps the workspace");
+    for (const Range& r : ins)
+        if (overlaps(r, ro) || overlaps(r, rw))
+            return fail(ATTNQAT_E_INVALID, "o or the workspace overlaps an input");
+    if ((rc = check_device())) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    aq::VsaArgs a = vsa_args(p, pl, nbq, nbk, L, (char*)workspace, q, k, v, gate);
+    a.o_fine = (const uint16_t*)o_fine;
+    a.o = (uint16_t*)o;
+    if ((rc = vsa_coarse(a, st))) return rc;
+    if ((rc = launch(K_VSA_COMBINE, st, thunk<aq::VsaArgs, aq::launch_vsa_combine>, &a,
+                     "VSA gated combination")))
+        return rc;
+    return ok();
+}
+
+int attnqat_vsa_bwd(const attnqat_problem* p, const void* q, const void* k, const void* v,
+                    const void* gate, const void* dout, void* dq, void* dk, void* dv,
+                    void* dgate, void* workspace, size_t workspace_bytes, void* stream) {
+    Plan pl;
+    int64_t nbq, nbk;
+    VsaLayout L;
+    int rc = vsa_plan(p, pl, nbq, nbk, L);
+    if (rc) return rc;
+    if ((rc = check_tensor("q", q, pl.q, pl.H, pl.Nq, pl.D))) return rc;
+    if ((rc = check_tensor("k", k, pl.k, pl.H, pl.Nk, pl.D))) return rc;
+    if ((rc = check_tensor("v", v, pl.v, pl.H, pl.Nk, pl.D))) return rc;
+    if ((rc = check_tensor("gate", gate, pl.o, pl.H, pl.Nq, pl.D))) return rc;
+    if ((rc = check_tensor("dout", dout, pl.dout, pl.H, pl.Nq, pl.D))) return rc;
+    if ((rc = check_tensor("dq", dq, pl.dq, pl.H, pl.Nq, pl.D))) return rc;
+    if ((rc = check_tensor("dk", dk, pl.dk, pl.H, pl.Nk, pl.D))) return rc;
+    if ((rc = check_tensor("dv", dv, pl.dv, pl.H, pl.Nk, pl.D))) return rc;
+    if (dgate && (rc = check_tensor("dgate", dgate, pl.o, pl.H, pl.Nq, pl.D))) return rc;
+    if ((rc = check_workspace(workspace, workspace_bytes, L.total))) return rc;
+    const Range ins[5] = {extent(q, pl.q, pl.B, pl.H, pl.Nq, pl.D, 2),
+                          extent(k, pl.k, pl.B, pl.H, pl.Nk, pl.D, 2),
+                          extent(v, pl.v, pl.B, pl.H, pl.Nk, pl.D, 2),
+                          extent(gate, pl.o, pl.B, pl.H, pl.Nq, pl.D, 2),
+                          extent(dout, pl.dout, pl.B, pl.H, pl.Nq, pl.D, 2)};
+    const Range outs[5] = {extent(dq, pl.dq, pl.B, pl.H, pl.Nq, pl.D, 2),
+                           extent(dk, pl.dk, pl.B, pl.H, pl.Nk, pl.D, 2),
+                           extent(dv, pl.dv, pl.B, pl.H, pl.Nk, pl.D, 2),
+                           dgate ? extent(dgate, pl.o, pl.B, pl.H, pl.Nq, pl.D, 2) : Range{0, 0},
+                           {(uintptr_t)workspace, (uintptr_t)workspace + L.total}};
+    for (int i = 0; i < 5; ++i) {
+        for (const Range& r : ins)
+            if (overlaps(outs[i], r))
+                return fail(ATTNQAT_E_INVALID, "an output or the workspace overlaps an input");
+        for (int j = i + 1; j < 5; ++j)
+            if (overlaps(outs[i], outs[j]))
+                return fail(ATTNQAT_E_INVALID, "outputs overlap each other or the workspace");
+    }
+    if ((rc = check_device())) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    aq::VsaArgs a = vsa_args(p, pl, nbq, nbk, L, (char*)workspace, q, k, v, gate);
+    a.dout = (const uint16_t*)dout;
+    a.dsb = pl.dout.b;
+    a.dsh = pl.dout.h;
+    a.dsn = pl.dout.n;
+    a.dq = (uint16_t*)dq;
+    a.dqsb = pl.dq.b;
+    a.dqsh = pl.dq.h;
+    a.dqsn = pl.dq.n;
+    a.dk = (uint16_t*)dk;
+    a.dksb = pl.dk.b;
+    a.dksh = pl.dk.h;
+    a.dksn = pl.dk.n;
+    a.dv = (uint16_t*)dv;
+    a.dvsb = pl.dv.b;
+    a.dvsh = pl.dv.h;
+    a.dvsn = pl.dv.n;
+    a.dgate = (uint16_t*)dgate;
+    if ((rc = vsa_coarse(a, st))) return rc;
+    if ((rc = launch(K_VSA_GATE, st, thunk<aq::VsaArgs, aq::launch_vsa_gate_reduce>, &a,
+                     "VSA gate reduction")))
+        return rc;
+    if ((rc = launch(K_VSA_COARSE_BWD, st, thunk<aq::VsaArgs, aq::launch_vsa_coarse_bwd>, &a,
+                     "VSA coarse backward")))
+        return rc;
+    if ((rc = launch(K_VSA_GRAD_ADD, st, thunk<aq::VsaArgs, aq::launch_vsa_grad_add>, &a,
+                     "VSA gradient broadcast")))
         return rc;
     return ok();
 }

@@ -1258,7 +1258,6 @@ __global__ __launch_bounds__(1024) void fwd_out_pc_kernel(AttnArgs a) {
 // brought into LDS serves 256 queries; sparse ones are one 128-query block
 // (4 waves).
 constexpr int kFwdDenseWaves = 8;
-constexpr int kFwdOutDenseWaves = 8;
 
 template <int D>
 static void fwd_lse_d(const AttnArgs& a, bool sp, hipStream_t st) {

@@ -61,6 +61,14 @@ __device__ __forceinline__ f32x16 mfma_f16(const u32x4& a, const u32x4& b, const
 }
 
 __device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// Nearest bf16 (ties to even) of a double, returned as bits.
+__device__ __forceinline__ uint16_t bf16_from_double(double x) {
+    uint64_t u = (uint64_t)__double_as_longlong(x);
+    u = (u + ((1ull << 44) - 1) + ((u >> 45) & 1ull)) & ~((1ull << 45) - 1);
+    const float f = (float)__longlong_as_double((long long)u);  // exact: 8 significant bits
+    return (uint16_t)(__float_as_uint(f) >> 16);
+}
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

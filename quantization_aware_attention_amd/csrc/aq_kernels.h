@@ -105,6 +105,47 @@ struct SelectArgs {
     int64_t BH, H;
     int Nq, Nk, bt, nbq, nbk, topk, D;
 };
+// VSA coarse branch and gated combination (aq_vsa.hip). Token tensors are
+// strided bf16 [B,H,N,D]; gate, o_fine, o and dgate share o's strides.
+// Workspace arrays are contiguous per (bh, block).
+constexpr int kVsaMaxBlocks = 1024;
+struct VsaArgs {
+    const uint16_t* q;
+    int64_t qsb, qsh, qsn;
+    const uint16_t* k;
+    int64_t ksb, ksh, ksn;
+    const uint16_t* v;
+    int64_t vsb, vsh, vsn;
+    const uint16_t* gate;
+    const uint16_t* o_fine;
+    uint16_t* o;
+    uint16_t* dgate;  // nullable
+    int64_t osb, osh, osn;
+    const uint16_t* dout;
+    int64_t dsb, dsh, dsn;
+    uint16_t* dq;
+    int64_t dqsb, dqsh, dqsn;
+    uint16_t* dk;
+    int64_t dksb, dksh, dksn;
+    uint16_t* dv;
+    int64_t dvsb, dvsh, dvsn;
+    uint16_t *qbar, *kbar, *vbar;  // [BH][nb][D] bf16 block means
+    float* oc;                     // [BH][nbq][D] coarse output
+    float* lsec;                   // [BH][nbq] coarse LSE
+    float* doc;                    // [BH][nbq][D] gradient of the coarse output
+    float* dcc;                    // [BH][nbq] rowsum(dO_c O_c)
+    float *dqb, *dkb, *dvb;        // [BH][nb][D] gradients of the block means
+    int64_t BH, H;
+    int Nq, Nk, bt, nbq, nbk, D;
+    float sm_scale;
+};
+hipError_t launch_vsa_pool(const VsaArgs& a, hipStream_t st);
+hipError_t launch_vsa_coarse_fwd(const VsaArgs& a, hipStream_t st);
+hipError_t launch_vsa_combine(const VsaArgs& a, hipStream_t st);
+hipError_t launch_vsa_gate_reduce(const VsaArgs& a, hipStream_t st);
+hipError_t launch_vsa_coarse_bwd(const VsaArgs& a, hipStream_t st);
+hipError_t launch_vsa_grad_add(const VsaArgs& a, hipStream_t st);
+
 hipError_t launch_block_pool(const SelectArgs& a, hipStream_t st);
 hipError_t launch_block_topk(const SelectArgs& a, hipStream_t st);
 hipError_t launch_reverse_index(const int32_t* idx, int32_t* q_list, int32_t* q_count, int64_t BH,

@@ -11,14 +11,6 @@
 
 namespace aq {
 
-// Nearest bf16 (ties to even) of a double, returned as bits.
-__device__ __forceinline__ uint16_t bf16_from_double(double x) {
-    uint64_t u = (uint64_t)__double_as_longlong(x);
-    u = (u + ((1ull << 44) - 1) + ((u >> 45) & 1ull)) & ~((1ull << 45) - 1);
-    const float f = (float)__longlong_as_double((long long)u);  // exact: 8 significant bits
-    return (uint16_t)(__float_as_uint(f) >> 16);
-}
-
 // One thread per (bh, block, column): mean over the block's tokens.
 __global__ __launch_bounds__(256) void block_pool_kernel(SelectArgs a) {
     const int64_t total_q = a.BH * a.nbq * a.D;

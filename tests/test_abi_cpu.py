@@ -54,7 +54,7 @@ def test_exports_every_declared_function(L):
     assert declared == set(qaa.EXPORTS), declared ^ set(qaa.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.attnqat_abi_version() == 2
+    assert L.attnqat_abi_version() == 3
 
 
 def test_status_strings(L):
@@ -203,3 +203,39 @@ def test_ste_output_validation(L):
     assert _fwd(L, _prob(o_ste=A)) == E_INVALID        # overlaps q
     assert _fwd(L, _prob(o_ste=4 * A)) == E_INVALID    # overlaps o
 
+
+
+def _vsa_fwd(L, p, q=A, k=2 * A, v=3 * A, gate=4 * A, of=5 * A, o=6 * A, ws=7 * A, wsb=1 << 40):
+    return L.attnqat_vsa_fwd(ctypes.byref(p), q, k, v, gate, of, o, ws, wsb, None)
+
+
+def _vsa_bwd(L, p, ws=20 * A, wsb=1 << 40, **ptrs):
+    d = dict(q=A, k=2 * A, v=3 * A, gate=4 * A, do=5 * A, dq=6 * A, dk=7 * A, dv=8 * A, dg=9 * A)
+    d.update(ptrs)
+    return L.attnqat_vsa_bwd(ctypes.byref(p), d["q"], d["k"], d["v"], d["gate"], d["do"], d["dq"],
+                             d["dk"], d["dv"], d["dg"], ws, wsb, None)
+
+
+def test_vsa_validation(L):
+    """The VSA coarse entry points: 128-token blocks only, workspace size and
+    alignment, o / gradient aliasing and pointer alignment are all rejected
+    before any HIP call."""
+    p = _prob()
+    need = L.attnqat_vsa_workspace_bytes(ctypes.byref(p))
+    assert need > 0
+    assert L.attnqat_vsa_workspace_bytes(ctypes.byref(_prob(block_tokens=64))) == 0
+    assert _vsa_fwd(L, _prob(block_tokens=64)) == E_UNSUPPORTED
+    assert _vsa_fwd(L, p, wsb=need - 1) == E_WORKSPACE
+    assert _vsa_fwd(L, p, ws=7 * A + 16) == E_MISALIGNED
+    assert _vsa_fwd(L, p, gate=4 * A + 8) == E_MISALIGNED
+    assert _vsa_fwd(L, p, o=A) == E_INVALID          # o overlaps q
+    assert _vsa_fwd(L, p, o=5 * A) == E_INVALID      # o overlaps o_fine
+    assert _vsa_fwd(L, p, ws=4 * A) == E_INVALID     # workspace overlaps the gate
+    assert _vsa_fwd(L, _prob(D=96)) == E_UNSUPPORTED
+    assert _vsa_bwd(L, _prob(block_tokens=256)) == E_UNSUPPORTED
+    assert _vsa_bwd(L, p, dq=7 * A) == E_INVALID      # dq overlaps dk
+    assert _vsa_bwd(L, p, dg=6 * A) == E_INVALID      # dgate overlaps dq
+    assert _vsa_bwd(L, p, dv=5 * A) == E_INVALID      # dv overlaps dout
+    assert _vsa_bwd(L, p, wsb=16) == E_WORKSPACE
+    assert _vsa_bwd(L, p, dk=7 * A + 4) == E_MISALIGNED
+    assert _vsa_bwd(L, p, q=0) == E_INVALID
