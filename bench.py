@@ -341,6 +341,33 @@ def main():
         time_variant("ste_delta", dict(o_ste=os_), os_, {})
         out["variants"] = variants
         del rm, os_
+    # Quantization off on the same inputs (plain attention; the forward is the
+    # single-pass kernel), credited the same FLOPs.
+    if mask:
+        pr0 = qaa.make_problem(q, k, w.sm_scale, 0, v=v, o=o, do=do, dq=dq, dk=dk, dv=dv,
+                               kv_block_idx=kv_idx)
+        ws0 = torch.empty(L.attnqat_bwd_workspace_bytes(ctypes.byref(pr0)), dtype=torch.uint8,
+                          device=dev)
+        ev0 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(5)]
+        for i in range(7):
+            e = ev0[i - 2] if i >= 2 else None
+            if e:
+                e[0].record()
+            qaa.fwd(q, k, v, w.sm_scale, 0, kv_idx, out=o, lse=lse, workspace=ws_f)
+            if e:
+                e[1].record()
+            qaa.bwd(q, k, v, o, lse, do, w.sm_scale, 0, kv_idx, dq=dq, dk=dk, dv=dv, workspace=ws0)
+            if e:
+                e[2].record()
+        torch.cuda.synchronize()
+        vf = float(np.mean([a_.elapsed_time(b_) for a_, b_, _ in ev0]))
+        vb = float(np.mean([b_.elapsed_time(c_) for _, b_, c_ in ev0]))
+        tf = (f_fwd + f_bwd) / ((vf + vb) * 1e-3) / 1e12
+        out.setdefault("variants", {})["quant_off"] = {
+            "steps": 5, "fwd_ms": round(vf, 4), "bwd_ms": round(vb, 4),
+            "ms_per_step": round(vf + vb, 4), "tflops": round(tf, 1),
+            "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del ws0
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)

@@ -66,12 +66,12 @@ int hip_check(hipError_t e, const char* what) {
 // ---------------------------------------------------------------------------
 // optional per-thread kernel timing
 enum Kind {
-    K_FQ_D, K_FQ_N, K_TRANSPOSE, K_FWD_LSE, K_FWD_OUT, K_BWD_PRE, K_BWD_DKDV, K_BWD_DQ,
+    K_FQ_D, K_FQ_N, K_TRANSPOSE, K_FWD_LSE, K_FWD_OUT, K_FWD_SINGLE, K_BWD_PRE, K_BWD_DKDV, K_BWD_DQ,
     K_BLOCK_POOL, K_BLOCK_TOPK, K_REVERSE_INDEX, K_VSA_POOL, K_VSA_COARSE, K_VSA_COMBINE,
     K_VSA_GATE, K_VSA_COARSE_BWD, K_VSA_GRAD_ADD, K_NUM
 };
 const char* const kKindName[K_NUM] = {
-    "fq_axis_d", "fq_axis_n", "transpose_perm", "fwd_lse", "fwd_out", "bwd_pre", "bwd_dkdv",
+    "fq_axis_d", "fq_axis_n", "transpose_perm", "fwd_lse", "fwd_out", "fwd_single", "bwd_pre", "bwd_dkdv",
     "bwd_dq", "block_pool", "block_topk", "reverse_index", "vsa_pool", "vsa_coarse",
     "vsa_combine", "vsa_gate_reduce", "vsa_coarse_bwd", "vsa_grad_add"};
 
@@ -133,6 +133,9 @@ struct DimArgs {
 };
 hipError_t do_fwd_lse(const DimArgs& d, hipStream_t st) { return aq::launch_fwd_lse(d.a, d.D, st); }
 hipError_t do_fwd_out(const DimArgs& d, hipStream_t st) { return aq::launch_fwd_out(d.a, d.D, st); }
+hipError_t do_fwd_single(const DimArgs& d, hipStream_t st) {
+    return aq::launch_fwd_single(d.a, d.D, st);
+}
 hipError_t do_bwd_dq(const DimArgs& d, hipStream_t st) { return aq::launch_bwd_dq(d.a, d.D, st); }
 hipError_t do_bwd_dkdv(const DimArgs& d, hipStream_t st) {
     return aq::launch_bwd_dkdv(d.a, d.D, st);
@@ -504,6 +507,12 @@ int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const vo
     a.osh = pl.o.h;
     a.osn = pl.o.n;
     const DimArgs da{a, (int)pl.D};
+    if (!(p->quant_mask & ATTNQAT_QUANT_P)) {
+        // no P quantizer: nothing needs the final LSE before P V
+        if ((rc = launch(K_FWD_SINGLE, st, thunk<DimArgs, do_fwd_single>, &da, "forward")))
+            return rc;
+        return ok();
+    }
     if ((rc = launch(K_FWD_LSE, st, thunk<DimArgs, do_fwd_lse>, &da, "forward pass 1"))) return rc;
     if ((rc = launch(K_FWD_OUT, st, thunk<DimArgs, do_fwd_out>, &da, "forward pass 2"))) return rc;
     return ok();

@@ -600,6 +600,117 @@ __global__ __launch_bounds__(NW * 64) void fwd_out_ste_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Single-pass forward for problems whose P is not quantized. Without a P
+// quantizer nothing needs the final LSE before P V, so O, LSE and the row
+// maxima come from one sweep over the keys with an online softmax. The running
+// maximum m (shared by the two lanes of a query row) moves only when a block's
+// maximum exceeds it by more than 2^kLazyLog2 in P. Then P = 2^((S - m) c)
+// stays below 2^kLazyLog2, the fp32 sums keep their full relative precision,
+// and the O accumulators are rescaled only on the rare blocks that move m.
+// Tiles and operand layouts are those of the straight-through forward: waves
+// of 32 queries, K in perm32 order, V^T in token order.
+constexpr float kLazyLog2 = 8.0f;
+template <int D, int NW, bool SPARSE>
+__global__ __launch_bounds__(NW * 64) void fwd_single_kernel(AttnArgs a) {
+    using F = FwdOutSte<D, false>;
+    constexpr int BN = F::BN;
+    static_assert(!SPARSE || NW == 4, "sparse workgroups cover one 128-query block");
+    struct Buf {
+        uint16_t k[BN * D];
+        uint16_t v[D * BN];
+    };
+    __shared__ __attribute__((aligned(1024))) Buf s0, s1;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int bh = blockIdx.y, qblk = blockIdx.x;
+    const int q0 = qblk * (NW * 32) + wave * 32;
+    const int q = q0 + l32;
+    const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
+    const uint16_t* Kb = a.Kw + (size_t)bh * a.Nk_pad * D;
+    const uint16_t* Vtb = a.Vt + (size_t)bh * D * a.Nk_pad;
+    u32x4 qf[D / 16];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+        qf[c] = *(const u32x4*)(Qb + (size_t)(q0 + l32) * D + c * 16 + hh * 8);
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+    float m = -INFINITY, mt = -INFINITY, l = 0.0f;
+    const float tau = kLazyLog2 / a.c;  // the lazy threshold in units of raw scores
+    __shared__ int lst[SPARSE ? kMaxBlockList : 1];
+    if (SPARSE) stage_list(lst, a.kv_idx + ((size_t)bh * a.nbq + qblk) * a.topk, a.topk);
+    const int n_iter = SPARSE ? a.topk * 2 : (a.Nk + BN - 1) / BN;
+    auto tile_at = [&](int it) { return tile_start<SPARSE, BN>(lst, it); };
+    AsyncTile<BN, D, NW * 64, true> tk;
+    AsyncTile<D, BN, NW * 64> tv;
+    tk.init(D, tid);
+    tv.init(a.Nk_pad, tid);
+    tile_pipeline(
+        n_iter, tile_at(n_iter - 1) + BN > a.Nk,
+        [&](auto b, int it) {
+            const int kt = tile_at(it);
+            tk.issue(sel(b, &s0, &s1)->k, Kb + (size_t)kt * D);
+            tv.issue(sel(b, &s0, &s1)->v, Vtb + kt);
+        },
+        [&](auto b, int it, auto tail) {
+            constexpr bool TL = decltype(tail)::value;
+            const uint16_t* K = sel(b, &s0, &s1)->k;
+            const uint16_t* V = sel(b, &s0, &s1)->v;
+            const int kt = tile_at(it);
+#pragma unroll
+            for (int kb = 0; kb < BN / 32; ++kb) {
+                const f32x16 sc = scores_T<D>(K, kb * 32, qf, l32, hh);
+                float x[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    x[j] = sc[j];
+                    if (TL && kt + kb * 32 + 16 * hh + j >= a.Nk) x[j] = -INFINITY;
+                }
+                float bm = x[0];
+#pragma unroll
+                for (int j = 1; j < 16; ++j) bm = fmaxf(bm, x[j]);
+                bm = fmaxf(bm, partner_lane(bm));
+                mt = fmaxf(mt, bm);
+                const bool up = bm > m + tau;
+                if (__any(up)) {
+                    const float mn = up ? bm : m;
+                    const float al = __builtin_amdgcn_exp2f((m - mn) * a.c);
+                    l *= al;
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) o[db][r] *= al;
+                    m = mn;
+                }
+                const float mc = m * a.c;
+                float r[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    r[j] = __builtin_amdgcn_exp2f(fmaf(x[j], a.c, -mc));
+                    l += r[j];
+                }
+                u32x4 bp[2];
+#pragma unroll
+                for (int g = 0; g < 2; ++g)
+                    bp[g] = u32x4{pack_rne(r[8 * g], r[8 * g + 1]), pack_rne(r[8 * g + 2], r[8 * g + 3]),
+                                  pack_rne(r[8 * g + 4], r[8 * g + 5]), pack_rne(r[8 * g + 6], r[8 * g + 7])};
+                F::pv2(V, kb, bp, bp, o, o, l32, hh);
+            }
+        });
+    const float lt = l + partner_lane(l);
+    if (q < a.Nq) {
+        const int64_t b = bh / a.H, h = bh % a.H, at = b * a.osb + h * a.osh + (int64_t)q * a.osn;
+        store_rows_T<D>(a.o + at, o, 1.0f / lt, hh);
+        // without P quantization the straight-through output is O itself
+        if (a.o_ste) store_rows_T<D>(a.o_ste + at, o, 1.0f / lt, hh);
+        if (hh == 0) {
+            a.lse_out[(size_t)bh * a.Nq + q] = (m * a.c + log2f(lt)) * kLn2;
+            if (a.row_max_out) a.row_max_out[(size_t)bh * a.Nq + q] = mt * a.sm_scale;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Backward dQ: NW waves x 32 QB queries, loop over 64-key tiles. A wave
 // keeps the Q and dO B operands of its QB 32-query blocks in registers; each
 // K, V or K^T operand read from LDS feeds QB products.
@@ -1294,22 +1405,40 @@ static void fwd_out_ste_go(const AttnArgs& a, bool sp, hipStream_t st) {
     else fwd_out_ste_kernel<D, QP, 4, false><<<dim3((a.Nq + 127) / 128, a.BH), 256, 0, st>>>(a);
 }
 
+// Pass 2 runs only when P is quantized (otherwise the single-pass forward
+// runs instead of both passes).
 template <int D>
 static void fwd_out_d(const AttnArgs& a, bool sp, hipStream_t st) {
     if (a.o_ste) {  // V^T is bf16 then (pv_f16 off)
-        if (a.quant_p) fwd_out_ste_go<D, true>(a, sp, st);
-        else fwd_out_ste_go<D, false>(a, sp, st);
+        fwd_out_ste_go<D, true>(a, sp, st);
         return;
     }
-    if (a.quant_p && a.pv_f16) fwd_out_go<D, true, true>(a, sp, st);
-    else if (a.quant_p) fwd_out_go<D, true, false>(a, sp, st);
-    else fwd_out_go<D, false, false>(a, sp, st);
+    if (a.pv_f16) fwd_out_go<D, true, true>(a, sp, st);
+    else fwd_out_go<D, true, false>(a, sp, st);
 }
 
 hipError_t launch_fwd_out(const AttnArgs& a, int D, hipStream_t st) {
     const bool sp = a.kv_idx != nullptr;
     if (D == 128) fwd_out_d<128>(a, sp, st);
     else fwd_out_d<64>(a, sp, st);
+    return hipGetLastError();
+}
+
+template <int D>
+static void fwd_single_d(const AttnArgs& a, bool sp, hipStream_t st) {
+    if (sp) {
+        fwd_single_kernel<D, 4, true><<<dim3(a.nbq, a.BH), 256, 0, st>>>(a);
+    } else {
+        constexpr int NW = kFwdDenseWaves;
+        fwd_single_kernel<D, NW, false><<<dim3((a.Nq + NW * 32 - 1) / (NW * 32), a.BH), NW * 64, 0,
+                                          st>>>(a);
+    }
+}
+
+hipError_t launch_fwd_single(const AttnArgs& a, int D, hipStream_t st) {
+    const bool sp = a.kv_idx != nullptr;
+    if (D == 128) fwd_single_d<128>(a, sp, st);
+    else fwd_single_d<64>(a, sp, st);
     return hipGetLastError();
 }
 

@@ -89,6 +89,8 @@ hipError_t launch_bwd_pre(const PreArgs& a, hipStream_t st);
 
 hipError_t launch_fwd_lse(const AttnArgs& a, int D, hipStream_t st);
 hipError_t launch_fwd_out(const AttnArgs& a, int D, hipStream_t st);
+// forward without P quantization: O, LSE (and row maxima) in one pass
+hipError_t launch_fwd_single(const AttnArgs& a, int D, hipStream_t st);
 hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t st);
 hipError_t launch_bwd_dkdv(const AttnArgs& a, int D, hipStream_t st);
 
