@@ -395,3 +395,45 @@ def attention(q, k, v, sm_scale=None, quant="qkvp", kv_block_idx=None, p_mode=P_
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(q.shape[-1])
     return AttnQatFunction.apply(q, k, v, sm_scale, quant, kv_block_idx, p_mode)
+
+
+def effective_topk(num_blocks: int, sparsity: float = 0.9) -> int:
+    """Key blocks kept per query block: max(1, min(ceil((1 - sparsity) n), n))."""
+    return max(1, min(int(math.ceil((1.0 - sparsity) * num_blocks)), num_blocks))
+
+
+class VsaAttentionFunction(torch.autograd.Function):
+    """VSA attention: block-sparse Attn-QAT fine branch over the selected key
+    blocks plus the gated coarse branch. Backward: the fine branch's
+    straight-through backward (with its own output as o), then the coarse
+    branch's gradients added in place, and the gate's gradient."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, gate, sm_scale, quant, kv_block_idx):
+        o_fine, lse = fwd(q, k, v, sm_scale, quant, kv_block_idx)
+        o = vsa_fwd(q, k, v, gate, o_fine, sm_scale)
+        ctx.save_for_backward(q, k, v, gate, o_fine, lse, kv_block_idx)
+        ctx.sm_scale, ctx.quant = sm_scale, quant
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, gate, o_fine, lse, idx = ctx.saved_tensors
+        do = do.contiguous()
+        dq, dk, dv = bwd(q, k, v, o_fine, lse, do, ctx.sm_scale, ctx.quant, idx)
+        dq, dk, dv, dgate = vsa_bwd(q, k, v, gate, do, dq, dk, dv, ctx.sm_scale,
+                                    want_dgate=ctx.needs_input_grad[3])
+        return dq, dk, dv, dgate, None, None, None
+
+
+def vsa_attention(q, k, v, gate, topk=None, sparsity=0.9, sm_scale=None, quant="qkvp",
+                  kv_block_idx=None):
+    """VSA attention with 128-token blocks. The key blocks come from the coarse
+    selection (top ``topk`` per query block, default effective_topk(blocks,
+    sparsity)) unless ``kv_block_idx`` is given."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(q.shape[-1])
+    if kv_block_idx is None:
+        nbk = -(-k.shape[2] // 128)
+        kv_block_idx = block_select(q, k, topk if topk is not None else effective_topk(nbk, sparsity))
+    return VsaAttentionFunction.apply(q, k, v, gate, sm_scale, quant, kv_block_idx)

@@ -142,3 +142,24 @@ def test_vsa_strided(gpu_lib):
     msg = _report("strided", errs)
     for e in errs.values():
         assert e <= TOL_PLAIN, msg
+
+
+def test_vsa_autograd_matches_entry_points(gpu_lib):
+    """The autograd wrapper runs exactly the entry-point sequence (bitwise)."""
+    bits = _bits(140, 1, 2, 700, 700, 128)
+    t = {k: to_dev(v) for k, v in bits.items()}
+    sc = 1.0 / np.sqrt(128)
+    idx = gpu_lib.block_select(t["q"], t["k"], 2)
+    leaves = {n: t[n].clone().requires_grad_(True) for n in ("q", "k", "v", "g")}
+    o = gpu_lib.vsa_attention(leaves["q"], leaves["k"], leaves["v"], leaves["g"], sm_scale=sc,
+                              kv_block_idx=idx)
+    o.backward(t["do"])
+    of, lse = gpu_lib.fwd(t["q"], t["k"], t["v"], sc, "qkvp", idx)
+    o2 = gpu_lib.vsa_fwd(t["q"], t["k"], t["v"], t["g"], of, sc)
+    dq, dk, dv = gpu_lib.bwd(t["q"], t["k"], t["v"], of, lse, t["do"], sc, "qkvp", idx)
+    _, _, _, dg = gpu_lib.vsa_bwd(t["q"], t["k"], t["v"], t["g"], t["do"], dq, dk, dv, sc)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    for n, ref in (("q", dq), ("k", dk), ("v", dv), ("g", dg)):
+        assert torch.equal(leaves[n].grad, ref), n
+    assert gpu_lib.effective_topk(6, 0.9) == 1 and gpu_lib.effective_topk(256, 0.9) == 26
