@@ -93,6 +93,8 @@ def parse():
                     help="synthetic workload id (see synthetic.WORKLOADS)")
     ap.add_argument("--quant", default="qkvp", help="quantized operands, e.g. qkvp or none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sparse", action="store_true",
+                    help="skip the block-sparse VSA step at its own configuration")
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="query rows of head 0 in the CPU-oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -341,6 +343,47 @@ def main():
         time_variant("ste_delta", dict(o_ste=os_), os_, {})
         out["variants"] = variants
         del rm, os_
+    # The block-sparse VSA step at its own configuration (12 heads x 32,768
+    # tokens, 256 blocks of 128 tokens, top-26 key blocks per query block):
+    # coarse selection, quantized fine branch and gated coarse branch, forward
+    # and backward; credited FLOPs are the dense ones scaled by the density.
+    if not args.no_sparse and args.workload != 5:
+        w5 = WORKLOADS[5]
+        b5 = make_inputs(5)
+        t5 = {k_: torch.from_numpy(v_.view(np.int16)).view(torch.bfloat16).to(dev) for k_, v_ in b5.items()}
+        del b5
+        g5 = torch.randn_like(t5["q"])
+        o5f, o5 = torch.empty_like(t5["q"]), torch.empty_like(t5["q"])
+        l5 = torch.empty(w5.shape[:3], dtype=torch.float32, device=dev)
+        d5 = [torch.empty_like(t5["q"]) for _ in range(3)]
+        ev5 = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(5)]
+        for i in range(7):
+            e = ev5[i - 2] if i >= 2 else None
+            if e:
+                e[0].record()
+            idx5 = qaa.block_select(t5["q"], t5["k"], w5.topk, w5.block_tokens)
+            if e:
+                e[1].record()
+            qaa.fwd(t5["q"], t5["k"], t5["v"], w5.sm_scale, mask, idx5, out=o5f, lse=l5)
+            qaa.vsa_fwd(t5["q"], t5["k"], t5["v"], g5, o5f, w5.sm_scale, out=o5)
+            if e:
+                e[2].record()
+            qaa.bwd(t5["q"], t5["k"], t5["v"], o5f, l5, t5["do"], w5.sm_scale, mask, idx5,
+                    dq=d5[0], dk=d5[1], dv=d5[2])
+            qaa.vsa_bwd(t5["q"], t5["k"], t5["v"], g5, t5["do"], d5[0], d5[1], d5[2], w5.sm_scale)
+            if e:
+                e[3].record()
+        torch.cuda.synchronize()
+        sel = float(np.mean([a_.elapsed_time(b_) for a_, b_, _, _ in ev5]))
+        f5 = float(np.mean([b_.elapsed_time(c_) for _, b_, c_, _ in ev5]))
+        bw5 = float(np.mean([c_.elapsed_time(d_) for _, _, c_, d_ in ev5]))
+        cf, cb = w5.credited_flops()
+        out["sparse_vsa"] = {
+            "workload": w5.name, "shape": list(w5.shape), "topk": w5.topk, "steps": 5,
+            "select_ms": round(sel, 4), "fwd_ms": round(f5, 4), "bwd_ms": round(bw5, 4),
+            "ms_per_step": round(sel + f5 + bw5, 4),
+            "credited_tflops": round((cf + cb) / ((sel + f5 + bw5) * 1e-3) / 1e12, 1)}
+        del t5, g5, o5f, o5, l5, d5
     # Quantization off on the same inputs (plain attention; the forward is the
     # single-pass kernel), credited the same FLOPs.
     if mask:
