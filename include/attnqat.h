@@ -60,7 +60,7 @@ extern "C" {
 /* status codes */
 #define ATTNQAT_OK 0
 #define ATTNQAT_E_INVALID 1     /* null pointer, bad size, bad mask, bad scale, aliasing */
-#define ATTNQAT_E_UNSUPPORTED 2 /* head dim not 64/128, device is not gfx950 */
+#define ATTNQAT_E_UNSUPPORTED 2 /* head dim not 64/128, B*H > 65535, device is not gfx950 */
 #define ATTNQAT_E_MISALIGNED 3  /* pointer not 16-byte aligned or stride not a multiple of 8 */
 #define ATTNQAT_E_WORKSPACE 4   /* workspace missing or too small */
 #define ATTNQAT_E_HIP 5         /* a HIP call or kernel launch failed */

@@ -232,6 +232,10 @@ int validate_problem(const attnqat_problem* p, Plan& pl) {
     // the kernels index tokens with 32-bit ints
     if (p->Nq > (1 << 30) || p->Nk > (1 << 30) || p->B * p->H > (1 << 30))
         return fail(ATTNQAT_E_INVALID, "sizes too large");
+    // (batch, head) pairs index the second grid dimension of every kernel
+    if (p->B * p->H > 65535)
+        return fail(ATTNQAT_E_UNSUPPORTED, "B * H = %lld exceeds 65535",
+                    (long long)(p->B * p->H));
     pl.B = p->B;
     pl.H = p->H;
     pl.BH = p->B * p->H;
@@ -663,6 +667,10 @@ int attnqat_block_select(const attnqat_problem* p, const void* q, const void* k,
         return fail(ATTNQAT_E_INVALID, "topk %d outside [1, %lld]", p->topk, (long long)nbk);
     if (p->Nq > (1 << 30) || p->Nk > (1 << 30) || p->B * p->H > (1 << 30))
         return fail(ATTNQAT_E_INVALID, "sizes too large");
+    // (batch, head) pairs index the second grid dimension of every kernel
+    if (p->B * p->H > 65535)
+        return fail(ATTNQAT_E_UNSUPPORTED, "B * H = %lld exceeds 65535",
+                    (long long)(p->B * p->H));
     const Strides sq = resolve(p->q, p->H, p->Nq, p->D), sk = resolve(p->k, p->H, p->Nk, p->D);
     int rc;
     if ((rc = check_tensor("q", q, sq, p->H, p->Nq, p->D))) return rc;

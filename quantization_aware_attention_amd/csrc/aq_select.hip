@@ -71,28 +71,43 @@ __global__ __launch_bounds__(256) void block_topk_kernel(SelectArgs a) {
 }
 
 // Reverse index: for each key block, the ascending list of query blocks that
-// selected it.
+// selected it. One workgroup per (bh, key block j): thread t checks query
+// blocks t, t + 256, ... (binary search of j in the ascending row), and a
+// ballot and prefix count place the selecting ones in ascending order.
 __global__ __launch_bounds__(256) void reverse_index_kernel(const int32_t* __restrict__ idx,
                                                             int32_t* __restrict__ q_list,
                                                             int32_t* __restrict__ q_count,
                                                             int64_t BH, int nbq, int nbk, int topk) {
-    const int64_t gi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    if (gi >= BH * nbk) return;
-    const int64_t bh = gi / nbk;
-    const int j = (int)(gi % nbk);
-    int cnt = 0;
+    __shared__ int wsum[4];
+    const int j = blockIdx.x;
+    const int64_t bh = blockIdx.y, gi = bh * nbk + j;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     int32_t* lst = q_list + gi * nbq;
-    for (int i = 0; i < nbq; ++i) {
-        const int32_t* r = idx + (bh * nbq + i) * topk;
-        int lo = 0, hi = topk;  // binary search in the ascending row
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (r[mid] < j) lo = mid + 1;
-            else hi = mid;
+    int total = 0;
+    for (int base = 0; base < nbq; base += 256) {
+        const int i = base + threadIdx.x;
+        bool f = false;
+        if (i < nbq) {
+            const int32_t* r = idx + (bh * nbq + i) * topk;
+            int lo = 0, hi = topk;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (r[mid] < j) lo = mid + 1;
+                else hi = mid;
+            }
+            f = lo < topk && r[lo] == j;
         }
-        if (lo < topk && r[lo] == j) lst[cnt++] = i;
+        const unsigned long long b = __ballot(f);
+        const int before = __popcll(b & ((1ull << lane) - 1ull));
+        if (lane == 0) wsum[w] = __popcll(b);
+        __syncthreads();
+        int off = total;
+        for (int ww = 0; ww < w; ++ww) off += wsum[ww];
+        if (f) lst[off + before] = i;
+        total += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        __syncthreads();
     }
-    q_count[gi] = cnt;
+    if (threadIdx.x == 0) q_count[gi] = total;
 }
 
 hipError_t launch_block_pool(const SelectArgs& a, hipStream_t st) {
@@ -110,9 +125,8 @@ hipError_t launch_block_topk(const SelectArgs& a, hipStream_t st) {
 
 hipError_t launch_reverse_index(const int32_t* idx, int32_t* q_list, int32_t* q_count, int64_t BH,
                                 int nbq, int nbk, int topk, hipStream_t st) {
-    const int64_t total = BH * nbk;
-    reverse_index_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(idx, q_list, q_count, BH,
-                                                                          nbq, nbk, topk);
+    reverse_index_kernel<<<dim3(nbk, (unsigned)BH), 256, 0, st>>>(idx, q_list, q_count, BH, nbq,
+                                                                 nbk, topk);
     return hipGetLastError();
 }
 

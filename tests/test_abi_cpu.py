@@ -239,3 +239,11 @@ def test_vsa_validation(L):
     assert _vsa_bwd(L, p, wsb=16) == E_WORKSPACE
     assert _vsa_bwd(L, p, dk=7 * A + 4) == E_MISALIGNED
     assert _vsa_bwd(L, p, q=0) == E_INVALID
+
+
+def test_batch_heads_limit(L):
+    """(batch, head) pairs index the second grid dimension: more than 65535
+    is rejected, as unsupported, before any HIP call."""
+    assert _fwd(L, _prob(B=2, H=40000)) == E_UNSUPPORTED
+    assert L.attnqat_fwd_workspace_bytes(ctypes.byref(_prob(B=2, H=40000))) == 0
+
