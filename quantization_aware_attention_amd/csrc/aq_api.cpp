@@ -658,6 +658,8 @@ int attnqat_block_select(const attnqat_problem* p, const void* q, const void* k,
     if (p->D != 64 && p->D != 128)
         return fail(ATTNQAT_E_UNSUPPORTED, "head dimension %lld (supported: 64, 128)",
                     (long long)p->D);
+    if (p->B * p->H > 65535)
+        return fail(ATTNQAT_E_UNSUPPORTED, "B * H = %lld exceeds 65535", (long long)(p->B * p->H));
     if (p->block_tokens < 1 || p->block_tokens > 4096)
         return fail(ATTNQAT_E_INVALID, "block_tokens %d outside [1, 4096]", p->block_tokens);
     const int64_t nbq = (p->Nq + p->block_tokens - 1) / p->block_tokens;

@@ -11,28 +11,42 @@
 
 namespace aq {
 
-// One thread per (bh, block, column): mean over the block's tokens.
+// Block means, one workgroup per (block, bh, tensor: 0 = q, 1 = k): thread
+// (r, c) sums columns 8 c .. 8 c + 7 of token rows r, r + R, ... in fp64 and
+// the R partial sums are added in fp64 (exact, so order-independent).
+template <int D>
 __global__ __launch_bounds__(256) void block_pool_kernel(SelectArgs a) {
-    const int64_t total_q = a.BH * a.nbq * a.D;
-    const int64_t total = total_q + a.BH * a.nbk * a.D;
-    for (int64_t gi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; gi < total;
-         gi += (int64_t)gridDim.x * blockDim.x) {
-        const bool isq = gi < total_q;
-        const int64_t li = isq ? gi : gi - total_q;
-        const int nb = isq ? a.nbq : a.nbk;
-        const int N = isq ? a.Nq : a.Nk;
-        const int d = (int)(li % a.D);
-        const int j = (int)((li / a.D) % nb);
-        const int64_t bh = li / ((int64_t)a.D * nb);
-        const int64_t b = bh / a.H, h = bh % a.H;
-        const uint16_t* base = isq ? a.q + b * a.qsb + h * a.qsh : a.k + b * a.ksb + h * a.ksh;
-        const int64_t sn = isq ? a.qsn : a.ksn;
-        const int t0 = j * a.bt, t1 = min(N, (j + 1) * a.bt);
+    constexpr int C = D / 8, R = 256 / C;
+    __shared__ double part[R][D];
+    const bool isq = blockIdx.z == 0;
+    const int nb = isq ? a.nbq : a.nbk;
+    const int j = blockIdx.x;
+    if (j >= nb) return;  // the grid covers the larger of nbq and nbk
+    const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+    const int N = isq ? a.Nq : a.Nk;
+    const uint16_t* base = isq ? a.q + b * a.qsb + h * a.qsh : a.k + b * a.ksb + h * a.ksh;
+    const int64_t sn = isq ? a.qsn : a.ksn;
+    const int c = threadIdx.x % C, r = threadIdx.x / C;
+    const int t0 = j * a.bt, t1 = min(N, (j + 1) * a.bt);
+    double acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+    for (int t = t0 + r; t < t1; t += R) {
+        const u32x4 w = *(const u32x4*)(base + (int64_t)t * sn + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += (double)bf2f(w[e] & 0xffffu);
+            acc[2 * e + 1] += (double)bf2f(w[e] >> 16);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part[r][8 * c + e] = acc[e];
+    __syncthreads();
+    if (threadIdx.x < D) {
         double sum = 0.0;
-        for (int t = t0; t < t1; ++t) sum += (double)bf2f(base[(int64_t)t * sn + d]);
-        const uint16_t m = bf16_from_double(sum / (double)(t1 - t0));
+        for (int rr = 0; rr < R; ++rr) sum += part[rr][threadIdx.x];
         uint16_t* out = isq ? a.qbar : a.kbar;
-        out[(bh * nb + j) * a.D + d] = m;
+        out[(bh * nb + j) * D + threadIdx.x] = bf16_from_double(sum / (double)(t1 - t0));
     }
 }
 
@@ -46,8 +60,16 @@ __global__ __launch_bounds__(256) void block_topk_kernel(SelectArgs a) {
     const uint16_t* qb = a.qbar + row * a.D;
     for (int j = threadIdx.x; j < a.nbk; j += blockDim.x) {
         const uint16_t* kb = a.kbar + (bh * a.nbk + j) * a.D;
-        double acc = 0.0;
-        for (int d = 0; d < a.D; ++d) acc += (double)bf2f(qb[d]) * (double)bf2f(kb[d]);
+        double acc = 0.0;  // the products are exact; the sum runs in column order
+        for (int c = 0; c < a.D / 8; ++c) {
+            const u32x4 x = *(const u32x4*)(qb + 8 * c);
+            const u32x4 y = *(const u32x4*)(kb + 8 * c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc += (double)bf2f(x[e] & 0xffffu) * (double)bf2f(y[e] & 0xffffu);
+                acc += (double)bf2f(x[e] >> 16) * (double)bf2f(y[e] >> 16);
+            }
+        }
         sc[j] = bf2f(bf16_from_double(acc));
     }
     __syncthreads();
@@ -111,10 +133,9 @@ __global__ __launch_bounds__(256) void reverse_index_kernel(const int32_t* __res
 }
 
 hipError_t launch_block_pool(const SelectArgs& a, hipStream_t st) {
-    const int64_t total = a.BH * (int64_t)(a.nbq + a.nbk) * a.D;
-    int64_t g = (total + 255) / 256;
-    if (g > 65535) g = 65535;
-    block_pool_kernel<<<(unsigned)g, 256, 0, st>>>(a);
+    const dim3 g(max(a.nbq, a.nbk), (unsigned)a.BH, 2);
+    if (a.D == 128) block_pool_kernel<128><<<g, 256, 0, st>>>(a);
+    else block_pool_kernel<64><<<g, 256, 0, st>>>(a);
     return hipGetLastError();
 }
 
