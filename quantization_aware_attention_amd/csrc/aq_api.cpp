@@ -302,7 +302,7 @@ Layout layout(const Plan& pl, bool bwd) {
     L.kw = take(kb);
     if (bwd) {
         L.vw = take(kb);
-        L.kt = take(kb);
+        if (!pl.sparse) L.kt = take(kb);
         L.dow = take(qb);
         L.lse2 = take((size_t)pl.BH * pl.Nq_pad * 4);
         L.delta = take((size_t)pl.BH * pl.Nq_pad * 4);
@@ -365,6 +365,9 @@ int prepare_operands(const Plan& pl, uint32_t mask, const void* q, const void* k
     if (!bwd)
         return run_transpose((const uint16_t*)(ws + L.vw), (uint16_t*)(ws + L.vt), pl.BH, pl.Nk_pad,
                              pl.D, false, st, "transpose V", pl.f16_pv);
+    // the permuted K^T serves the dense dQ kernel only (the block-sparse one
+    // reads K^T operands from its K tiles)
+    if (pl.sparse) return ATTNQAT_OK;
     return run_transpose((const uint16_t*)(ws + L.kw), (uint16_t*)(ws + L.kt), pl.BH, pl.Nk_pad,
                          pl.D, true, st, "transpose K");
 }
@@ -598,7 +601,7 @@ int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const vo
                      "backward preprocess")))
         return rc;
     aq::AttnArgs a = attn_args(p, pl, ws, L);
-    a.Kt = (const uint16_t*)(ws + L.kt);
+    a.Kt = pl.sparse ? nullptr : (const uint16_t*)(ws + L.kt);
     a.dOw = (const uint16_t*)(ws + L.dow);
     a.lse2 = (const float*)(ws + L.lse2);
     a.delta = (const float*)(ws + L.delta);

@@ -58,6 +58,23 @@ __device__ __forceinline__ int toff(int row, int c) {
     return row * W + ((c ^ swz<W>(row)) << 3);
 }
 
+// Natural-layout [64][D] query tile (row = query): logical 16-byte chunk c of
+// row r sits at chunk c ^ nswz(r). Both reads of the fused backward are then
+// free of bank conflicts: 16-byte reads of one chunk in 16 consecutive rows
+// (the B operands of S^T and dP^T) and transposing reads that cover 4
+// consecutive rows x 4 consecutive chunks per 32 lanes (the A operands of
+// dV^T and dK^T).
+template <int D>
+__device__ __forceinline__ int nswz(int row) {
+    static_assert(D == 64 || D == 128, "head dim");
+    if (D == 128) return 4 * (row & 3) + ((row >> 2) & 3);
+    return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
+}
+template <int D>
+__device__ __forceinline__ int noff(int row, int c) {
+    return row * D + ((c ^ nswz<D>(row)) << 3);
+}
+
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 // 16-byte (and 4-byte) LDS-DMA copies: lane i's global bytes land at LDS
@@ -865,6 +882,133 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Backward dQ, block-sparse: one 128-query block (4 waves of 32 queries) per
+// workgroup, over the 64-key tiles of its selected key blocks. K tiles are
+// kept in the natural layout (nswz) and the dQ product reads its K^T operands
+// from them with transposing reads, so no K^T tile is staged: 32 KB per tile
+// stage, two workgroups (two waves per SIMD) per CU.
+// K^T operand of dQ^T += K^T dS^T for d-block db and key group g of a 32-key
+// block: lane (hh, r) holds d = 32 db + r of keys 16 g + 4 hh + 0..3 and
+// 16 g + 8 + 4 hh + 0..3, the accumulator-row order of the dS operand; two
+// transposing reads of 4 consecutive key rows each (t = 0, 1).
+template <int D>
+__device__ __forceinline__ int ktr_lane(int db, int t, int lane) {
+    const int G = lane >> 4, i = lane & 15;
+    const int hh = G >> 1, j = i >> 2, q = i & 3;
+    const int d = 32 * db + 16 * (G & 1) + 4 * q;
+    return noff<D>(8 * t + 4 * hh + j, d >> 3) + (d & 7);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dq_sparse_kernel(AttnArgs a) {
+    using DQ = BwdDq<D, 1>;
+    constexpr int BN = 64, NT = 256, NW = 4;
+    struct Buf {
+        uint16_t k[BN * D];  // natural layout (nswz)
+        uint16_t v[BN * D];  // toff<D>
+    };
+    __shared__ __attribute__((aligned(1024))) Buf s0, s1;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int bh = blockIdx.y, qblk = blockIdx.x;
+    const int q = qblk * 128 + wave * 32 + l32;
+    const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
+    const uint16_t* dOb = a.dOw + (size_t)bh * a.Nq_pad * D;
+    const uint16_t* Kb = a.Kw + (size_t)bh * a.Nk_pad * D;
+    const uint16_t* Vb = a.Vw + (size_t)bh * a.Nk_pad * D;
+    u32x4 qf[1][D / 16], df[1][D / 16];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+        qf[0][c] = *(const u32x4*)(Qb + (size_t)q * D + c * 16 + hh * 8);
+        df[0][c] = *(const u32x4*)(dOb + (size_t)q * D + c * 16 + hh * 8);
+    }
+    const float lse2[1] = {a.lse2[(size_t)bh * a.Nq_pad + q]};
+    const float dl[1] = {a.delta[(size_t)bh * a.Nq_pad + q]};
+    f32x16 dqa[1][D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) dqa[0][db] = f32x16{};
+    // the block list is read from global memory (uniform loads): staging it
+    // in LDS would push the workgroup past the 64 KB that lets two share a CU
+    const int32_t* lst = a.kv_idx + ((size_t)bh * a.nbq + qblk) * a.topk;
+    const int n_iter = a.topk * 2;
+    auto tile_at = [&](int it) { return lst[it >> 1] * 128 + (it & 1) * BN; };
+    // K tile copies: 1 KB blocks b = j NW + wave hold RB rows of CR chunks;
+    // lane i fills slot 16 i with logical chunk (i % CR) ^ nswz(row)
+    constexpr int CR = D / 8, RB = 64 / CR, NKB = BN * D * 2 / 1024 / NW;
+    uint32_t koff[NKB];
+#pragma unroll
+    for (int j = 0; j < NKB; ++j) {
+        const int row = (j * NW + wave) * RB + lane / CR;
+        koff[j] = (uint32_t)(row * D + (((lane % CR) ^ nswz<D>(row)) << 3)) * 2u;
+    }
+    AsyncTile<BN, D, NT> tv;
+    tv.init(D, tid);
+    int lo[D / 32][2];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) lo[db][t] = ktr_lane<D>(db, t, lane);
+    // S^T and dP^T of 32-key block kb (K rows read from the natural tile)
+    auto sdp = [&](const uint16_t* sK, const uint16_t* sV, int kb, f32x16& s, f32x16& dp) {
+        s = dp = f32x16{};
+#pragma unroll
+        for (int cc = 0; cc < D / 16; ++cc) {
+            const int row = kb * 32 + l32;
+            const u32x4 ka = *(const u32x4*)(sK + noff<D>(row, 2 * cc + hh));
+            s = mfma(ka, qf[0][cc], s);
+            const u32x4 va = *(const u32x4*)(sV + toff<D>(row, 2 * cc + hh));
+            dp = mfma(va, df[0][cc], dp);
+        }
+    };
+    // dQ^T += K^T dS^T of block kb, K^T operands by transposing reads
+    auto dqp = [&](const uint16_t* sK, int kb, const u32x4* bfr) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const uint16_t* base = sK + (32 * kb + 16 * g) * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) {
+                const u32x2 r0 = lds_read_tr16(base + lo[db][0]);
+                const u32x2 r1 = lds_read_tr16(base + lo[db][1]);
+                dqa[0][db] = mfma(u32x4{r0[0], r0[1], r1[0], r1[1]}, bfr[g], dqa[0][db]);
+            }
+        }
+    };
+    tile_pipeline(
+        n_iter, tile_at(n_iter - 1) + BN > a.Nk,
+        [&](auto b, int it) {
+            const int kt = tile_at(it);
+            Buf* t = sel(b, &s0, &s1);
+#pragma unroll
+            for (int j = 0; j < NKB; ++j)
+                dma16(lds_addr(t->k + (j * NW + wave) * 512), Kb + (size_t)kt * D, koff[j]);
+            tv.issue(t->v, Vb + (size_t)kt * D);
+        },
+        [&](auto b, int it, auto tail) {
+            constexpr bool TL = decltype(tail)::value;
+            const Buf* t = sel(b, &s0, &s1);
+            const int kt = tile_at(it);
+            // S/dP 0 | S/dP 1 + dS 0 | dQ 0 + dS 1 | dQ 1
+            f32x16 s0_, dp0, s1_, dp1;
+            u32x4 b0[1][2], b1[1][2];
+            sdp(t->k, t->v, 0, s0_, dp0);
+            mfma_chain_m<D / 8, 1, 4, 0>();
+            sdp(t->k, t->v, 1, s1_, dp1);
+            DQ::template dsop<TL>(s0_, dp0, kt, a.Nk, a.c, lse2[0], dl[0], hh, b0[0]);
+            mfma_chain_m<D / 8, 1, 4, 5>();
+            dqp(t->k, 0, b0[0]);
+            DQ::template dsop<TL>(s1_, dp1, kt + 32, a.Nk, a.c, lse2[0], dl[0], hh, b1[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            dqp(t->k, 1, b1[0]);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    if (q < a.Nq) {
+        const int64_t b = bh / a.H, h = bh % a.H;
+        store_rows_T<D>(a.dq + b * a.dqsb + h * a.dqsh + (int64_t)q * a.dqsn, dqa[0], a.sm_scale, hh);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Backward helpers. Scores are computed with keys on the accumulator rows
 // (S^T = K Q^T, perm32 key order: lane half hh holds keys 16 hh + r), the
 // layout in which P's 16-key groups are quantized, so P, Pq and dS have
@@ -957,23 +1101,6 @@ struct KVTile {
     float st[2 * BM];    // LSE * log2(e) for the BM queries, then Dl
 };
 
-
-// Natural-layout [64][D] query tile (row = query): logical 16-byte chunk c of
-// row r sits at chunk c ^ nswz(r). Both reads of the fused backward are then
-// free of bank conflicts: 16-byte reads of one chunk in 16 consecutive rows
-// (the B operands of S^T and dP^T) and transposing reads that cover 4
-// consecutive rows x 4 consecutive chunks per 32 lanes (the A operands of
-// dV^T and dK^T).
-template <int D>
-__device__ __forceinline__ int nswz(int row) {
-    static_assert(D == 64 || D == 128, "head dim");
-    if (D == 128) return 4 * (row & 3) + ((row >> 2) & 3);
-    return 4 * ((row >> 1) & 1) + ((row >> 2) & 3);
-}
-template <int D>
-__device__ __forceinline__ int noff(int row, int c) {
-    return row * D + ((c ^ nswz<D>(row)) << 3);
-}
 
 // B operand of S^T = K Q^T (or dP^T = V dO^T) for d-chunk cc of 32-query
 // sub-block sb: lane (hh, c) holds d = 16 cc + 8 hh .. + 7 of query 32 sb + c.
@@ -1445,8 +1572,8 @@ hipError_t launch_fwd_single(const AttnArgs& a, int D, hipStream_t st) {
 hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t st) {
     if (a.kv_idx) {
         dim3 grid(a.nbq, a.BH);
-        if (D == 128) bwd_dq_kernel<128, 4, 1, true><<<grid, 256, 0, st>>>(a);
-        else bwd_dq_kernel<64, 4, 1, true><<<grid, 256, 0, st>>>(a);
+        if (D == 128) bwd_dq_sparse_kernel<128><<<grid, 256, 0, st>>>(a);
+        else bwd_dq_sparse_kernel<64><<<grid, 256, 0, st>>>(a);
     } else {
         dim3 grid((a.Nq + 255) / 256, a.BH);
         if (D == 128) bwd_dq_kernel<128, 8, 1, false><<<grid, 512, 0, st>>>(a);
