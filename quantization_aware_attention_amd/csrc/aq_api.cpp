@@ -149,9 +149,11 @@ struct RevArgs {
     int32_t *q_list, *q_count;
     int64_t BH;
     int nbq, nbk, topk;
+    int32_t* order;
 };
 hipError_t do_reverse(const RevArgs& r, hipStream_t st) {
-    return aq::launch_reverse_index(r.idx, r.q_list, r.q_count, r.BH, r.nbq, r.nbk, r.topk, st);
+    return aq::launch_reverse_index(r.idx, r.q_list, r.q_count, r.BH, r.nbq, r.nbk, r.topk, r.order,
+                                    st);
 }
 
 int run_fq(bool axis_d, bool quant, const aq::FqArgs& a, hipStream_t st, const char* what) {
@@ -285,7 +287,8 @@ int validate_problem(const attnqat_problem* p, Plan& pl) {
 
 // Workspace layout (bytes, each region 256-byte aligned).
 struct Layout {
-    size_t qw, kw, vw, kt, vt, dow, lse2, delta, qlist, qcount, dowkv, lse2kv, deltakv, total;
+    size_t qw, kw, vw, kt, vt, dow, lse2, delta, qlist, qcount, korder, dowkv, lse2kv, deltakv,
+        total;
 };
 
 Layout layout(const Plan& pl, bool bwd) {
@@ -309,6 +312,7 @@ Layout layout(const Plan& pl, bool bwd) {
         if (pl.sparse) {
             L.qlist = take((size_t)pl.BH * pl.nbk * pl.nbq * 4);
             L.qcount = take((size_t)pl.BH * pl.nbk * 4);
+            L.korder = take((size_t)pl.BH * pl.nbk * 4);
         }
         if (pl.rowmax) {  // dK/dV inputs of the row-max-relative variant
             L.dowkv = take(qb);
@@ -620,8 +624,9 @@ int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const vo
     if (pl.sparse) {
         a.q_list = (const int32_t*)(ws + L.qlist);
         a.q_count = (const int32_t*)(ws + L.qcount);
+        a.kv_order = (const int32_t*)(ws + L.korder);
         const RevArgs ra{p->kv_block_idx, (int32_t*)(ws + L.qlist), (int32_t*)(ws + L.qcount),
-                         pl.BH, pl.nbq, pl.nbk, p->topk};
+                         pl.BH, pl.nbq, pl.nbk, p->topk, (int32_t*)(ws + L.korder)};
         if ((rc = launch(K_REVERSE_INDEX, st, thunk<RevArgs, do_reverse>, &ra,
                          "reverse block index")))
             return rc;

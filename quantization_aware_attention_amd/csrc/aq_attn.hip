@@ -1150,7 +1150,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnArgs a) {
     const int pair = wave & 3;
     const bool producer = wave < 4;  // wave-uniform
     const int l32 = lane & 31, hh = lane >> 5;
-    const int bh = blockIdx.y, kblk = blockIdx.x;
+    // sparse: workgroups run the key blocks of every head heaviest first
+    // (blockIdx.y is the rank of the block's selection count in its head)
+    const int bh = SPARSE ? blockIdx.x : blockIdx.y;
+    const int kblk = SPARSE ? a.kv_order[(size_t)bh * a.nbk + blockIdx.y] : blockIdx.x;
     const int k0 = kblk * KW + pair * 32;
     const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
     const uint16_t* dOb = a.dOw + (size_t)bh * a.Nq_pad * D;
@@ -1584,7 +1587,7 @@ hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t st) {
 
 template <int D>
 static void dkdv_d(const AttnArgs& a, bool sp, hipStream_t st) {
-    const dim3 g(sp ? a.nbk : (a.Nk + 127) / 128, a.BH);
+    const dim3 g(sp ? a.BH : (a.Nk + 127) / 128, sp ? a.nbk : a.BH);
     if (sp) {
         if (a.quant_p) bwd_dkdv_kernel<D, true, true><<<g, 512, 0, st>>>(a);
         else bwd_dkdv_kernel<D, false, true><<<g, 512, 0, st>>>(a);

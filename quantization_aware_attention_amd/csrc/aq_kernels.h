@@ -70,6 +70,7 @@ struct AttnArgs {
     const int32_t* kv_idx;   // [BH][nbq][topk]
     const int32_t* q_list;   // [BH][nbk][nbq] reverse index (query blocks per key block)
     const int32_t* q_count;  // [BH][nbk]
+    const int32_t* kv_order; // [BH][nbk] key blocks of each head by descending count
     int topk;
     int nbq, nbk;
     int64_t H;
@@ -151,6 +152,6 @@ hipError_t launch_vsa_grad_add(const VsaArgs& a, hipStream_t st);
 hipError_t launch_block_pool(const SelectArgs& a, hipStream_t st);
 hipError_t launch_block_topk(const SelectArgs& a, hipStream_t st);
 hipError_t launch_reverse_index(const int32_t* idx, int32_t* q_list, int32_t* q_count, int64_t BH,
-                                int nbq, int nbk, int topk, hipStream_t st);
+                                int nbq, int nbk, int topk, int32_t* kv_order, hipStream_t st);
 
 }  // namespace aq

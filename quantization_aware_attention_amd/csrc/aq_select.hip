@@ -132,6 +132,23 @@ __global__ __launch_bounds__(256) void reverse_index_kernel(const int32_t* __res
     if (threadIdx.x == 0) q_count[gi] = total;
 }
 
+// Key blocks of each head ordered by descending selection count (ties to
+// the lower index): one workgroup per head, each thread ranks its blocks.
+__global__ __launch_bounds__(256) void block_order_kernel(const int32_t* __restrict__ q_count,
+                                                          int32_t* __restrict__ order, int nbk) {
+    const int64_t bh = blockIdx.x;
+    const int32_t* c = q_count + bh * nbk;
+    for (int j = threadIdx.x; j < nbk; j += 256) {
+        const int cj = c[j];
+        int rank = 0;
+        for (int jj = 0; jj < nbk; ++jj) {
+            const int cc = c[jj];
+            rank += (cc > cj || (cc == cj && jj < j)) ? 1 : 0;
+        }
+        order[bh * nbk + rank] = j;
+    }
+}
+
 hipError_t launch_block_pool(const SelectArgs& a, hipStream_t st) {
     const dim3 g(max(a.nbq, a.nbk), (unsigned)a.BH, 2);
     if (a.D == 128) block_pool_kernel<128><<<g, 256, 0, st>>>(a);
@@ -145,9 +162,10 @@ hipError_t launch_block_topk(const SelectArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_reverse_index(const int32_t* idx, int32_t* q_list, int32_t* q_count, int64_t BH,
-                                int nbq, int nbk, int topk, hipStream_t st) {
+                                int nbq, int nbk, int topk, int32_t* kv_order, hipStream_t st) {
     reverse_index_kernel<<<dim3(nbk, (unsigned)BH), 256, 0, st>>>(idx, q_list, q_count, BH, nbq,
                                                                  nbk, topk);
+    block_order_kernel<<<(unsigned)BH, 256, 0, st>>>(q_count, kv_order, nbk);
     return hipGetLastError();
 }
 

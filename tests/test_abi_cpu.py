@@ -126,12 +126,13 @@ def test_sparse_problem_checks(L):
     assert _fwd(L, p) == E_INVALID
     p.topk = 3
     dense = _prob(Nq=1024, Nk=1024)
-    # the sparse backward adds the reverse index (int32 [BH][nbk][nbq] lists
-    # and [BH][nbk] counts, 256-byte aligned) and stages no permuted K^T
+    # the sparse backward adds the reverse index (int32 [BH][nbk][nbq] lists,
+    # [BH][nbk] counts and the [BH][nbk] dispatch order, 256-byte aligned)
+    # and stages no permuted K^T
     # (bf16 [BH][Nk_pad][D])
     nb = 1024 // 128
     kt = 2 * 1024 * 64 * 2
-    rev = -(-2 * nb * nb * 4 // 256) * 256 + -(-2 * nb * 4 // 256) * 256
+    rev = -(-2 * nb * nb * 4 // 256) * 256 + 2 * (-(-2 * nb * 4 // 256) * 256)
     assert (L.attnqat_bwd_workspace_bytes(ctypes.byref(p)) ==
             L.attnqat_bwd_workspace_bytes(ctypes.byref(dense)) - kt + rev)
 
