@@ -291,11 +291,20 @@ __device__ __forceinline__ void mfma_chain_m() {
 }
 
 // ---------------------------------------------------------------------------
-// Forward pass 1: LSE per query row. 4 waves x 32 queries, 64-key tiles.
+// Forward pass 1: LSE per query row. 8 waves x 32 queries, 64-key tiles.
+// Each lane keeps a reference m and the sum l of exp2((S - m) c) over its
+// keys; LSE log2(e) = m c + log2 l for any m, so m only has to keep the terms
+// finite and l's magnitude in range. With LAZY the lane first sums a block
+// against its current m and takes a new maximum only when that sum exceeds
+// kLazySum (always on its first block, where m c is -1e30 c): no per-element
+// maximum in the common case. Without LAZY m is the exact running maximum,
+// which the row-max variant stores.
+constexpr float kLazySum = 4294967296.0f;  // 2^32: far below fp32 overflow for any row length
+
 template <int D>
 struct FwdLse {
     static constexpr int BN = 64;
-    template <bool tail>
+    template <bool tail, bool LAZY>
     __device__ static void block(const uint16_t* sK, int kt, int Nk, const u32x4* qf, float c,
                                  float& m, float& l, int l32, int hh) {
 #pragma unroll
@@ -305,6 +314,16 @@ struct FwdLse {
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (kt + kb * 32 + acc_row(r, hh) >= Nk) acc[r] = -INFINITY;
+            }
+            if (LAZY) {
+                const float mc0 = m * c;
+                float s0 = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s0 += __builtin_amdgcn_exp2f(fmaf(acc[r], c, -mc0));
+                if (s0 <= kLazySum) {
+                    l += s0;
+                    continue;
+                }
             }
             float mx = m;
 #pragma unroll
@@ -319,7 +338,7 @@ struct FwdLse {
     }
 };
 
-template <int D, int NW, bool SPARSE>
+template <int D, int NW, bool SPARSE, bool LAZY>
 __global__ __launch_bounds__(NW * 64) void fwd_lse_kernel(AttnArgs a) {
     constexpr int BN = FwdLse<D>::BN;
     static_assert(!SPARSE || NW == 4, "sparse workgroups cover one 128-query block");
@@ -345,8 +364,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_lse_kernel(AttnArgs a) {
         n_iter, tile_at(n_iter - 1) + BN > a.Nk,
         [&](auto b, int it) { tk.issue(sel(b, sK0, sK1), Kb + (size_t)tile_at(it) * D); },
         [&](auto b, int it, auto tail) {
-            FwdLse<D>::template block<decltype(tail)::value>(sel(b, sK0, sK1), tile_at(it), a.Nk, qf,
-                                                             a.c, m, l, l32, hh);
+            FwdLse<D>::template block<decltype(tail)::value, LAZY>(sel(b, sK0, sK1), tile_at(it),
+                                                                   a.Nk, qf, a.c, m, l, l32, hh);
         });
     const float mp = partner_lane(m), lp = partner_lane(l);
     const float mt = fmaxf(m, mp);
@@ -1500,21 +1519,24 @@ __global__ __launch_bounds__(1024) void fwd_out_pc_kernel(AttnArgs a) {
 // (4 waves).
 constexpr int kFwdDenseWaves = 8;
 
-template <int D>
+template <int D, bool LAZY>
 static void fwd_lse_d(const AttnArgs& a, bool sp, hipStream_t st) {
     if (sp) {
-        fwd_lse_kernel<D, 4, true><<<dim3(a.nbq, a.BH), 256, 0, st>>>(a);
+        fwd_lse_kernel<D, 4, true, LAZY><<<dim3(a.nbq, a.BH), 256, 0, st>>>(a);
     } else {
         constexpr int NW = kFwdDenseWaves;
-        fwd_lse_kernel<D, NW, false><<<dim3((a.Nq + NW * 32 - 1) / (NW * 32), a.BH), NW * 64, 0,
-                                       st>>>(a);
+        fwd_lse_kernel<D, NW, false, LAZY>
+            <<<dim3((a.Nq + NW * 32 - 1) / (NW * 32), a.BH), NW * 64, 0, st>>>(a);
     }
 }
 
+// The lazy reference maximum is not the row maximum: the row-max variant,
+// which stores it, runs the exact running maximum.
 hipError_t launch_fwd_lse(const AttnArgs& a, int D, hipStream_t st) {
     const bool sp = a.kv_idx != nullptr;
-    if (D == 128) fwd_lse_d<128>(a, sp, st);
-    else fwd_lse_d<64>(a, sp, st);
+    const bool lazy = a.row_max_out == nullptr;
+    if (D == 128) lazy ? fwd_lse_d<128, true>(a, sp, st) : fwd_lse_d<128, false>(a, sp, st);
+    else lazy ? fwd_lse_d<64, true>(a, sp, st) : fwd_lse_d<64, false>(a, sp, st);
     return hipGetLastError();
 }
 

@@ -13,8 +13,10 @@ import torch
 
 from oracle import attention as oatt
 from oracle.block_sparse import bf16_round
+from oracle.nvfp4 import fake_quant
 from synthetic import WORKLOADS, make_inputs
-from tests.helpers import TOL_LSE, dev_f64, rel_l2, to_dev, to_f64, tol_for
+from tests.helpers import (LSE_FLIP, TOL_LSE, dev_f64, rel_l2, rel_l2_best_rows, to_dev, to_f64,
+                           tol_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -106,10 +108,16 @@ def test_sparse_full_size(gpu_lib):
         qq, kq, vq = oatt.quantize_operands(f["q"], f["k"], f["v"], 15)
         for i in (0, nb // 3, nb - 1):
             r0, r1 = i * bt, (i + 1) * bt
-            _, Oi, Li, _, _ = bsp.query_block_forward(qq, kq, vq, idx_r[0, h, i], r0, r1, bt, sc, 15)
+            keys, Oi, Li, Pi, _ = bsp.query_block_forward(qq, kq, vq, idx_r[0, h, i], r0, r1, bt,
+                                                          sc, 15)
             dqi = bsp.query_block_backward(qq, kq, vq, f["do"], bf16_round(Oi), idx_r[0, h, i],
                                            r0, r1, bt, sc, 15)
-            errs = {"o": rel_l2(dev_f64(o[0, h, r0:r1]), Oi),
+            # these rows' largest probabilities are 0.003-0.014, so the P
+            # quantizer's scales are near the E4M3 subnormal floor: accept the
+            # decisions the oracle takes at LSE -/+ LSE_FLIP as well
+            cands = [Oi] + [fake_quant(Pi * np.exp(-s), axis=-1) @ vq[keys]
+                            for s in (-LSE_FLIP, LSE_FLIP)]
+            errs = {"o": rel_l2_best_rows(dev_f64(o[0, h, r0:r1]), cands),
                     "dq": rel_l2(dev_f64(dq[0, h, r0:r1]), dqi, exact_zero=False)}
             lse_err = float(np.abs(lse[0, h, r0:r1].cpu().numpy() - Li).max())
             _check(f"sparse h={h} qblock={i}", errs, lse_err, 1e-2)

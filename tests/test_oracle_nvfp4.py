@@ -215,3 +215,21 @@ def test_lengths(n):
     for g0 in range(0, n, 16):
         ref += _fq_group_exact(x[g0:g0 + 16])[0]
     np.testing.assert_array_equal(y, ref)
+
+
+def test_row_flip_tolerant_comparison():
+    """The comparison used where the P quantizer's decisions are ill-conditioned
+    (scales near the E4M3 subnormal floor): each row is scored against its
+    closest candidate, and a row that matches no candidate still counts."""
+    from tests.helpers import rel_l2, rel_l2_best_rows
+    a = np.random.default_rng(3).standard_normal((4, 8))
+    b = a.copy()
+    b[2] = 0.0
+    got = b.copy()                       # row 2 took the other decision
+    assert rel_l2(got, a) > 0.1
+    assert rel_l2_best_rows(got, [a, b]) == 0.0
+    got[1] += 1.0                        # a wrong row
+    assert rel_l2_best_rows(got, [a, b]) == pytest.approx(np.sqrt(8.0) / np.linalg.norm(a))
+    z = np.zeros((2, 3))
+    assert rel_l2_best_rows(z, [z]) == 0.0
+    assert rel_l2_best_rows(np.ones((2, 3)), [z]) == float("inf")
