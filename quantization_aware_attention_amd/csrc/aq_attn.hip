@@ -905,7 +905,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
 // workgroup, over the 64-key tiles of its selected key blocks. K tiles are
 // kept in the natural layout (nswz) and the dQ product reads its K^T operands
 // from them with transposing reads, so no K^T tile is staged: 32 KB per tile
-// stage, two workgroups (two waves per SIMD) per CU.
+// stage. The launch bound holds the kernel to 256 registers per lane (at
+// d = 128 a few values spill), so that two workgroups (two waves per SIMD)
+// share a CU.
 // K^T operand of dQ^T += K^T dS^T for d-block db and key group g of a 32-key
 // block: lane (hh, r) holds d = 32 db + r of keys 16 g + 4 hh + 0..3 and
 // 16 g + 8 + 4 hh + 0..3, the accumulator-row order of the dS operand; two
@@ -919,7 +921,7 @@ __device__ __forceinline__ int ktr_lane(int db, int t, int lane) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dq_sparse_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void bwd_dq_sparse_kernel(AttnArgs a) {
     using DQ = BwdDq<D, 1>;
     constexpr int BN = 64, NT = 256, NW = 4;
     struct Buf {
