@@ -647,7 +647,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_out_ste_kernel(AttnArgs a) {
 // of 32 queries, K in perm32 order, V^T in token order.
 constexpr float kLazyLog2 = 8.0f;
 template <int D, int NW, bool SPARSE>
-__global__ __launch_bounds__(NW * 64) void fwd_single_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_single_kernel(AttnArgs a) {
     using F = FwdOutSte<D, false>;
     constexpr int BN = F::BN;
     static_assert(!SPARSE || NW == 4, "sparse workgroups cover one 128-query block");
