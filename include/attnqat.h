@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define ATTNQAT_ABI_VERSION 3
+#define ATTNQAT_ABI_VERSION 4
 
 /* status codes */
 #define ATTNQAT_OK 0
@@ -245,6 +245,34 @@ int attnqat_vsa_fwd(const attnqat_problem* p, const void* q, const void* k, cons
 int attnqat_vsa_bwd(const attnqat_problem* p, const void* q, const void* k, const void* v,
                     const void* gate, const void* dout, void* dq, void* dk, void* dv,
                     void* dgate, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attnqat_mxfp4_fwd needs for problem p (0 if p is invalid). */
+size_t attnqat_mxfp4_fwd_workspace_bytes(const attnqat_problem* p);
+
+/*
+ * Real-FP4 inference attention forward on MXFP4 operands: this chip's
+ * counterpart of the pages' real-FP4 inference attention (the inference
+ * backend pull request's FP4 attention call with single-level P
+ * quantization; the Attn-QAT guide's inference route), computed with the
+ * scaled FP4 matrix instruction. Its block format is MX, not NVFP4: every 32
+ * consecutive values share one power-of-two (E8M0) scale
+ *   X = 2^(floor(log2 amax) - 2)   (a block of zeros: 2^-127)
+ *   MX(x) = X E2M1(x / X)          round to nearest even, saturating at 6,
+ * with blocks along d for Q and K, along the tokens for V and along the keys
+ * for P, each starting at index 0 (a partial last block padded with zeros).
+ * Writes
+ *   o    bf16 [B,H,Nq,D] (strides p->o):  O = MX(P~) MX(V) / l
+ *   lse  fp32 [B,H,Nq] contiguous:        LSE = m + ln l
+ * with S = sm_scale MX(Q) MX(K)^T, m_i = max_j S_ij, P~ = exp(S - m) and
+ * l_i = sum_j P~_ij (unquantized). Requirements: quant_mask ==
+ * ATTNQAT_QUANT_ALL, kv_block_idx == NULL and o_ste == NULL (else
+ * ATTNQAT_E_UNSUPPORTED); p_mode and row_max are not used. Other arguments,
+ * alignment, overlap and error rules are those of attnqat_fwd; `workspace`
+ * (device, 256-byte aligned, attnqat_mxfp4_fwd_workspace_bytes(p) bytes) is
+ * scratch owned by the caller and holds the quantized operands afterwards.
+ */
+int attnqat_mxfp4_fwd(const attnqat_problem* p, const void* q, const void* k, const void* v,
+                      void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Kernel timing (diagnostics). While enabled on the calling thread, every

@@ -52,6 +52,7 @@ EXPORTS = [
     "attnqat_fakequant_nvfp4", "attnqat_fwd_workspace_bytes", "attnqat_fwd",
     "attnqat_bwd_workspace_bytes", "attnqat_bwd", "attnqat_block_select_workspace_bytes",
     "attnqat_block_select", "attnqat_vsa_workspace_bytes", "attnqat_vsa_fwd", "attnqat_vsa_bwd",
+    "attnqat_mxfp4_fwd_workspace_bytes", "attnqat_mxfp4_fwd",
     "attnqat_profile_enable", "attnqat_profile_read",
 ]
 
@@ -112,6 +113,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.attnqat_vsa_fwd.argtypes = [pp, P, P, P, P, P, P, P, SZ, V]
     lib.attnqat_vsa_bwd.restype = ctypes.c_int
     lib.attnqat_vsa_bwd.argtypes = [pp, P, P, P, P, P, P, P, P, P, P, SZ, V]
+    lib.attnqat_mxfp4_fwd_workspace_bytes.restype = SZ
+    lib.attnqat_mxfp4_fwd_workspace_bytes.argtypes = [pp]
+    lib.attnqat_mxfp4_fwd.restype = ctypes.c_int
+    lib.attnqat_mxfp4_fwd.argtypes = [pp, P, P, P, P, P, P, SZ, V]
     lib.attnqat_profile_enable.restype = ctypes.c_int
     lib.attnqat_profile_enable.argtypes = [ctypes.c_int]
     lib.attnqat_profile_read.restype = ctypes.c_int
@@ -296,6 +301,34 @@ def block_select(q, k, topk: int, block_tokens: int = 128, stream=None) -> torch
     check(L.attnqat_block_select(ctypes.byref(p), q.data_ptr(), k.data_ptr(), idx.data_ptr(),
                                  ws.data_ptr(), ws.numel(), _stream(stream)))
     return idx
+
+
+def mxfp4_fwd(q, k, v, sm_scale=None, out=None, lse=None, workspace=None, stream=None):
+    """Real-FP4 inference forward on MXFP4 operands (attnqat_mxfp4_fwd):
+    returns (o bf16 [B,H,Nq,D], lse fp32 [B,H,Nq])."""
+    L = load()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check4(n, t)
+    B, H, Nq, D = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    o = out if out is not None else torch.empty_like(q)
+    _check4("out", o)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("lse must be a contiguous float32 [B,H,Nq] tensor")
+    p = make_problem(q, k, sm_scale, QUANT_ALL, v=v, o=o)
+    need = L.attnqat_mxfp4_fwd_workspace_bytes(ctypes.byref(p))
+    if need == 0:
+        check(L.attnqat_mxfp4_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                  o.data_ptr(), lse.data_ptr(), None, 0, _stream(stream)))
+    ws = workspace if workspace is not None and workspace.numel() >= need else \
+        _workspace(need, q.device)
+    check(L.attnqat_mxfp4_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              o.data_ptr(), lse.data_ptr(), ws.data_ptr(), ws.numel(),
+                              _stream(stream)))
+    return o, lse
 
 
 def vsa_fwd(q, k, v, gate, o_fine, sm_scale=None, out=None, workspace=None, stream=None):

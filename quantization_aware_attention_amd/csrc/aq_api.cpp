@@ -68,12 +68,12 @@ int hip_check(hipError_t e, const char* what) {
 enum Kind {
     K_FQ_D, K_FQ_N, K_TRANSPOSE, K_FWD_LSE, K_FWD_OUT, K_FWD_SINGLE, K_BWD_PRE, K_BWD_DKDV, K_BWD_DQ,
     K_BLOCK_POOL, K_BLOCK_TOPK, K_REVERSE_INDEX, K_VSA_POOL, K_VSA_COARSE, K_VSA_COMBINE,
-    K_VSA_GATE, K_VSA_COARSE_BWD, K_VSA_GRAD_ADD, K_NUM
+    K_VSA_GATE, K_VSA_COARSE_BWD, K_VSA_GRAD_ADD, K_MX_QUANT, K_MX_FWD, K_NUM
 };
 const char* const kKindName[K_NUM] = {
     "fq_axis_d", "fq_axis_n", "transpose_perm", "fwd_lse", "fwd_out", "fwd_single", "bwd_pre", "bwd_dkdv",
     "bwd_dq", "block_pool", "block_topk", "reverse_index", "vsa_pool", "vsa_coarse",
-    "vsa_combine", "vsa_gate_reduce", "vsa_coarse_bwd", "vsa_grad_add"};
+    "vsa_combine", "vsa_gate_reduce", "vsa_coarse_bwd", "vsa_grad_add", "mx_quant", "mx_fwd"};
 
 constexpr int kMaxTimed = 65536;
 
@@ -991,6 +991,121 @@ int attnqat_profile_read(const char** names, double* total_ms, int* launches, in
     }
     ok();
     return n;
+}
+
+// ---------------------------------------------------------------------------
+// Real-FP4 (MXFP4) inference forward
+
+}  // extern "C"
+
+namespace {
+struct MxLayout {
+    size_t qm, qs, km, ks, vtm, vts, total;
+};
+MxLayout mx_layout(const Plan& pl) {
+    MxLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t n) {
+        const size_t at = off;
+        off += (n + 255) / 256 * 256;
+        return at;
+    };
+    const size_t bh = (size_t)pl.BH, D = (size_t)pl.D;
+    L.qm = take(bh * pl.Nq_pad * D / 2);
+    L.qs = take(bh * pl.Nq_pad * D / 32);
+    L.km = take(bh * pl.Nk_pad * D / 2);
+    L.ks = take(bh * pl.Nk_pad * D / 32);
+    L.vtm = take(bh * D * pl.Nk_pad / 2);
+    L.vts = take(bh * D * pl.Nk_pad / 32);
+    L.total = off;
+    return L;
+}
+int mx_plan(const attnqat_problem* p, Plan& pl) {
+    if (!p) return fail(ATTNQAT_E_INVALID, "problem is NULL");
+    if (p->kv_block_idx)
+        return fail(ATTNQAT_E_UNSUPPORTED, "the MXFP4 forward is dense: kv_block_idx must be NULL");
+    if (p->o_ste)
+        return fail(ATTNQAT_E_UNSUPPORTED, "the MXFP4 forward has no straight-through output");
+    if (p->quant_mask != ATTNQAT_QUANT_ALL)
+        return fail(ATTNQAT_E_UNSUPPORTED,
+                    "the MXFP4 forward quantizes Q, K, V and P: quant_mask must be ATTNQAT_QUANT_ALL");
+    attnqat_problem c = *p;  // P is always row-max relative here; p_mode and row_max are unused
+    c.p_mode = ATTNQAT_P_NORMALISED;
+    c.row_max = nullptr;
+    return validate_problem(&c, pl);
+}
+}  // namespace
+
+extern "C" {
+
+size_t attnqat_mxfp4_fwd_workspace_bytes(const attnqat_problem* p) {
+    Plan pl;
+    if (mx_plan(p, pl)) return 0;
+    return mx_layout(pl).total;
+}
+
+int attnqat_mxfp4_fwd(const attnqat_problem* p, const void* q, const void* k, const void* v, void* o,
+                      float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    Plan pl;
+    int rc = mx_plan(p, pl);
+    if (rc) return rc;
+    if ((rc = check_tensor("q", q, pl.q, pl.H, pl.Nq, pl.D))) return rc;
+    if ((rc = check_tensor("k", k, pl.k, pl.H, pl.Nk, pl.D))) return rc;
+    if ((rc = check_tensor("v", v, pl.v, pl.H, pl.Nk, pl.D))) return rc;
+    if ((rc = check_tensor("o", o, pl.o, pl.H, pl.Nq, pl.D))) return rc;
+    if (!lse) return fail(ATTNQAT_E_INVALID, "lse is NULL");
+    if (((uintptr_t)lse) % 4) return fail(ATTNQAT_E_MISALIGNED, "lse is not 4-byte aligned");
+    const MxLayout L = mx_layout(pl);
+    if (!workspace || workspace_bytes < L.total)
+        return fail(ATTNQAT_E_WORKSPACE, "workspace needs %zu bytes (got %zu)", L.total,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (((uintptr_t)workspace) % 256)
+        return fail(ATTNQAT_E_MISALIGNED, "workspace is not 256-byte aligned");
+    const Range ro = extent(o, pl.o, pl.B, pl.H, pl.Nq, pl.D, 2);
+    const Range rl = {(uintptr_t)lse, (uintptr_t)lse + (uintptr_t)(pl.BH * pl.Nq * 4)};
+    const Range rw = {(uintptr_t)workspace, (uintptr_t)workspace + L.total};
+    const Range ins[3] = {extent(q, pl.q, pl.B, pl.H, pl.Nq, pl.D, 2),
+                          extent(k, pl.k, pl.B, pl.H, pl.Nk, pl.D, 2),
+                          extent(v, pl.v, pl.B, pl.H, pl.Nk, pl.D, 2)};
+    for (const Range& r : ins)
+        if (overlaps(r, ro) || overlaps(r, rl) || overlaps(r, rw))
+            return fail(ATTNQAT_E_INVALID, "an output or the workspace overlaps an input");
+    if (overlaps(ro, rl) || overlaps(ro, rw) || overlaps(rl, rw))
+        return fail(ATTNQAT_E_INVALID, "outputs overlap each other or the workspace");
+    if ((rc = check_device())) return rc;
+
+    char* ws = (char*)workspace;
+    aq::MxArgs a{};
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k;
+    a.v = (const uint16_t*)v;
+    a.qsb = pl.q.b, a.qsh = pl.q.h, a.qsn = pl.q.n;
+    a.ksb = pl.k.b, a.ksh = pl.k.h, a.ksn = pl.k.n;
+    a.vsb = pl.v.b, a.vsh = pl.v.h, a.vsn = pl.v.n;
+    a.qm = (uint8_t*)(ws + L.qm);
+    a.qs = (uint8_t*)(ws + L.qs);
+    a.km = (uint8_t*)(ws + L.km);
+    a.ks = (uint8_t*)(ws + L.ks);
+    a.vtm = (uint8_t*)(ws + L.vtm);
+    a.vts = (uint8_t*)(ws + L.vts);
+    a.o = (uint16_t*)o;
+    a.osb = pl.o.b, a.osh = pl.o.h, a.osn = pl.o.n;
+    a.lse = lse;
+    a.BH = pl.BH;
+    a.H = pl.H;
+    a.Nq = (int)pl.Nq;
+    a.Nk = (int)pl.Nk;
+    a.Nq_pad = (int)pl.Nq_pad;
+    a.Nk_pad = (int)pl.Nk_pad;
+    a.D = (int)pl.D;
+    a.c = p->sm_scale * aq::kLog2e;
+    hipStream_t st = (hipStream_t)stream;
+    if ((rc = launch(K_MX_QUANT, st, thunk<aq::MxArgs, aq::launch_mx_quant>, &a,
+                     "MXFP4 operand quantization")))
+        return rc;
+    if ((rc = launch(K_MX_FWD, st, thunk<aq::MxArgs, aq::launch_mx_fwd>, &a, "MXFP4 forward")))
+        return rc;
+    return ok();
 }
 
 }  // extern "C"

@@ -149,6 +149,25 @@ hipError_t launch_vsa_gate_reduce(const VsaArgs& a, hipStream_t st);
 hipError_t launch_vsa_coarse_bwd(const VsaArgs& a, hipStream_t st);
 hipError_t launch_vsa_grad_add(const VsaArgs& a, hipStream_t st);
 
+// Real-FP4 (MXFP4) inference forward. Workspace operands: Q and K rows as
+// packed E2M1 codes [BH][N_pad][D / 2] bytes with E8M0 scales [BH][N_pad][D / 32];
+// V^T codes [BH][D][Nk_pad / 2] with scales [BH][D][Nk_pad / 32].
+struct MxArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    int64_t qsb, qsh, qsn, ksb, ksh, ksn, vsb, vsh, vsn;
+    uint8_t *qm, *qs, *km, *ks, *vtm, *vts;
+    uint16_t* o;
+    int64_t osb, osh, osn;
+    float* lse;  // [BH][Nq]
+    int64_t BH, H;
+    int Nq, Nk, Nq_pad, Nk_pad, D;
+    float c;  // sm_scale * log2(e)
+};
+hipError_t launch_mx_quant(const MxArgs& a, hipStream_t st);
+hipError_t launch_mx_fwd(const MxArgs& a, hipStream_t st);
+
 hipError_t launch_block_pool(const SelectArgs& a, hipStream_t st);
 hipError_t launch_block_topk(const SelectArgs& a, hipStream_t st);
 hipError_t launch_reverse_index(const int32_t* idx, int32_t* q_list, int32_t* q_count, int64_t BH,

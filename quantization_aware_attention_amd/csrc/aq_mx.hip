@@ -1,0 +1,308 @@
+// Real-FP4 inference attention forward with MXFP4 operands, on the scaled
+// FP4 matrix instruction of gfx950 (v_mfma_scale_f32_32x32x64_f8f6f4).
+//
+// This is the chip's counterpart of the pages' real-FP4 inference attention
+// (the inference-backend pull request's FP4 attention call with single-level
+// P quantization; the Attn-QAT guide's inference route). The instruction
+// scales blocks of 32 FP4 (E2M1) values by one E8M0 power of two, so the
+// operands are MXFP4, not NVFP4:
+//   X = 2^(floor(log2 amax) - 2) per 32-value block (E8M0-clamped; a block of
+//   zeros gets 2^-127), elements E2M1(x / X) rounded to nearest even and
+//   saturated at 6.
+// Q and K are quantized along d, V along the tokens, and P~ = exp(S - m) (m
+// the row maximum) along the keys; O = MX(P~) MX(V) / l with l the
+// unquantized sum of P~, and LSE = m + ln l.
+//
+// Operand layout of the instruction (32x32x64, FP4 A and B): lane L supplies
+// row (A) or column (B) L % 32 and the 32 k-values 32 (L / 32) .. + 31 as 16
+// bytes, with one E8M0 scale byte for those 32 values. One lane's operand is
+// therefore exactly one MX block, in the nibble order the packer below uses
+// for every operand (element 2i in the low nibble of byte i).
+#include "aq_common.h"
+#include "aq_kernels.h"
+
+namespace aq {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// C += (A 2^(sa - 127)) (B 2^(sb - 127)) with FP4 A and B (only the low four
+// registers of each operand carry FP4 data).
+__device__ __forceinline__ f32x16 mfma_fp4(const u32x4& a, const u32x4& b, int sa, int sb,
+                                           const f32x16& c) {
+    const i32x8 av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+    const i32x8 bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 0, sa, 0, sb);
+}
+
+// One MX block of 32 values held by this thread: packed E2M1 codes (element
+// 2i in the low nibble of byte i) and the E8M0 scale byte.
+__device__ __forceinline__ int mx_block(const float* x, u32x4& codes) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    // floor(log2 amax) = frexp exponent - 1 (also for subnormal amax)
+    int se = -127;
+    if (amax > 0.0f) se = max(-127, min(127, __builtin_amdgcn_frexp_expf(amax) - 3));
+    // |x| / X < 8; the product is exact unless it is far below the E2M1 range
+    const float inv = __builtin_ldexpf(1.0f, -se);
+    float y[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) y[i] = __builtin_amdgcn_fmed3f(x[i] * inv, -6.0f, 6.0f);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float* z = y + 8 * w;
+        uint32_t cw = 0;
+        cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, z[0], z[1], 1.0f, 0);
+        cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, z[2], z[3], 1.0f, 1);
+        cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, z[4], z[5], 1.0f, 2);
+        cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, z[6], z[7], 1.0f, 3);
+        codes[w] = cw;
+    }
+    return se + 127;
+}
+
+// Q and K rows (blockIdx.z = 0, 1) in blocks of 32 along d: one thread per
+// (row, block). Rows at or beyond N (padding) are zero.
+template <int D>
+__global__ __launch_bounds__(256) void mx_quant_rows_kernel(MxArgs a) {
+    constexpr int NB = D / 32;
+    const bool isk = blockIdx.z == 1;
+    const int Npad = isk ? a.Nk_pad : a.Nq_pad, N = isk ? a.Nk : a.Nq;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int row = (int)(t / NB), blk = (int)(t % NB);
+    if (row >= Npad) return;
+    const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+    float x[32];
+    if (row < N) {
+        const uint16_t* src = isk ? a.k + b * a.ksb + h * a.ksh + (int64_t)row * a.ksn
+                                  : a.q + b * a.qsb + h * a.qsh + (int64_t)row * a.qsn;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 w = *(const u32x4*)(src + blk * 32 + 8 * i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x[8 * i + 2 * j] = bf_lo(w[j]);
+                x[8 * i + 2 * j + 1] = bf_hi(w[j]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) x[i] = 0.0f;
+    }
+    u32x4 codes;
+    const int sc = mx_block(x, codes);
+    const int64_t r = bh * Npad + row;
+    uint8_t* m = isk ? a.km : a.qm;
+    uint8_t* s = isk ? a.ks : a.qs;
+    *(u32x4*)(m + r * (D / 2) + blk * 16) = codes;
+    s[r * NB + blk] = (uint8_t)sc;
+}
+
+// V along the tokens: one thread per (column d, 32-token block), written as
+// V^T [BH][D][Nk_pad / 2] bytes with scales [BH][D][Nk_pad / 32]. Threads of a
+// wave take consecutive columns, so each token row is read coalesced.
+template <int D>
+__global__ __launch_bounds__(256) void mx_quant_vt_kernel(MxArgs a) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int nblk = a.Nk_pad / 32;
+    const int tb = (int)(t / D), d = (int)(t % D);
+    if (tb >= nblk) return;
+    const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+    const uint16_t* src = a.v + b * a.vsb + h * a.vsh + d;
+    float x[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        const int tok = tb * 32 + j;
+        x[j] = tok < a.Nk ? bf2f(src[(int64_t)tok * a.vsn]) : 0.0f;
+    }
+    u32x4 codes;
+    const int sc = mx_block(x, codes);
+    const int64_t r = bh * D + d;
+    *(u32x4*)(a.vtm + r * (a.Nk_pad / 2) + tb * 16) = codes;
+    a.vts[r * nblk + tb] = (uint8_t)sc;
+}
+
+// Forward: 4 waves x 32 queries per workgroup, 64-key tiles, two passes over
+// the keys (pass 1: row maximum m and l; pass 2: P~, its MX quantization and
+// O^T += V^T P~^T). Operands are read straight from the quantized workspace
+// (16 bytes per lane per operand, L2-resident across the workgroups of a
+// head); the next tile's operands are loaded while the current one is used.
+//
+// Score tiles are S^T = K Q^T (keys on rows). For 32-key block kb of a tile,
+// accumulator row rho = 8 (r / 4) + 4 hh + r % 4 of lane half hh is given key
+// 32 hh + 16 kb + r (K rows are read in that order), so lane half hh holds
+// keys 32 hh .. 32 hh + 31 of the tile for its query across the two blocks:
+// one whole 32-key MX block of P~, which is then this lane's B operand of
+// the P V product as it stands.
+__device__ __forceinline__ int mx_key_of_row(int kb, int row) {
+    return 32 * ((row >> 2) & 1) + 16 * kb + 4 * (row >> 3) + (row & 3);
+}
+
+template <int D>
+struct MxTile {
+    u32x4 k[2][D / 64];
+    int ks[2][D / 64];
+    u32x4 v[D / 32];
+    int vs[D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ void mx_load_k(const MxArgs& a, int64_t bh, int kt, int l32, int hh,
+                                          MxTile<D>& T) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const int64_t r = bh * a.Nk_pad + kt + mx_key_of_row(kb, l32);
+#pragma unroll
+        for (int c = 0; c < D / 64; ++c) {
+            T.k[kb][c] = *(const u32x4*)(a.km + r * (D / 2) + 32 * c + 16 * hh);
+            T.ks[kb][c] = a.ks[r * (D / 32) + 2 * c + hh];
+        }
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void mx_load_v(const MxArgs& a, int64_t bh, int kt, int l32, int hh,
+                                          MxTile<D>& T) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+        const int64_t r = bh * D + 32 * db + l32;
+        T.v[db] = *(const u32x4*)(a.vtm + r * (a.Nk_pad / 2) + (kt + 32 * hh) / 2);
+        T.vs[db] = a.vts[r * (a.Nk_pad / 32) + kt / 32 + hh];
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void mx_scores(const MxTile<D>& T, const u32x4* qa, const int* qs,
+                                          f32x16* s) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < D / 64; ++c) s[kb] = mfma_fp4(T.k[kb][c], qa[c], T.ks[kb][c], qs[c], s[kb]);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void mx_fwd_kernel(MxArgs a) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int64_t bh = blockIdx.y;
+    const int q = blockIdx.x * 128 + wave * 32 + l32;
+    u32x4 qa[D / 64];
+    int qs[D / 64];
+    {
+        const int64_t r = bh * a.Nq_pad + q;
+#pragma unroll
+        for (int c = 0; c < D / 64; ++c) {
+            qa[c] = *(const u32x4*)(a.qm + r * (D / 2) + 32 * c + 16 * hh);
+            qs[c] = a.qs[r * (D / 32) + 2 * c + hh];
+        }
+    }
+    const int n_tiles = (a.Nk + 63) / 64;
+    const float c = a.c;
+    // pass 1: exact running maximum m (log2 units, of x = S c) and l
+    float m = kNegBig, l = 0.0f;
+    MxTile<D> T0, T1;
+    mx_load_k<D>(a, bh, 0, l32, hh, T0);
+    for (int it = 0; it < n_tiles; ++it) {
+        MxTile<D>& T = (it & 1) ? T1 : T0;
+        MxTile<D>& Tn = (it & 1) ? T0 : T1;
+        const int kt = it * 64;
+        if (it + 1 < n_tiles) mx_load_k<D>(a, bh, kt + 64, l32, hh, Tn);
+        f32x16 s[2];
+        mx_scores<D>(T, qa, qs, s);
+        float x[32], mx = m;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            x[j] = s[j >> 4][j & 15] * c;
+            asm volatile("" : "+v"(x[j]));
+            if (kt + 32 * hh + j >= a.Nk) x[j] = -INFINITY;
+            mx = fmaxf(mx, x[j]);
+        }
+        float sum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) sum += __builtin_amdgcn_exp2f(x[j] - mx);
+        l = l * __builtin_amdgcn_exp2f(m - mx) + sum;
+        m = mx;
+    }
+    const float mp = partner_lane(m), lp = partner_lane(l);
+    const float mt = fmaxf(m, mp);
+    const float lt = l * __builtin_amdgcn_exp2f(m - mt) + lp * __builtin_amdgcn_exp2f(mp - mt);
+    // pass 2
+    f32x16 o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+    mx_load_k<D>(a, bh, 0, l32, hh, T0);
+    mx_load_v<D>(a, bh, 0, l32, hh, T0);
+    for (int it = 0; it < n_tiles; ++it) {
+        MxTile<D>& T = (it & 1) ? T1 : T0;
+        MxTile<D>& Tn = (it & 1) ? T0 : T1;
+        const int kt = it * 64;
+        if (it + 1 < n_tiles) {
+            mx_load_k<D>(a, bh, kt + 64, l32, hh, Tn);
+            mx_load_v<D>(a, bh, kt + 64, l32, hh, Tn);
+        }
+        f32x16 s[2];
+        mx_scores<D>(T, qa, qs, s);
+        // x - mt is exactly 0 at the row maximum, so that block's amax is 1:
+        // x is the same rounded product as in pass 1. The empty asm keeps the
+        // compiler from fusing the product and the subtraction into an FMA,
+        // whose result at the maximum would be the product's rounding error.
+        float p[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            float x = s[j >> 4][j & 15] * c;
+            asm volatile("" : "+v"(x));
+            p[j] = __builtin_amdgcn_exp2f(x - mt);
+            if (kt + 32 * hh + j >= a.Nk) p[j] = 0.0f;
+        }
+        u32x4 pc;
+        const int ps = mx_block(p, pc);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[db] = mfma_fp4(T.v[db], pc, T.vs[db], ps, o[db]);
+    }
+    if (q < a.Nq) {
+        const int64_t b = bh / a.H, h = bh % a.H;
+        uint16_t* dst = a.o + b * a.osb + h * a.osh + (int64_t)q * a.osn;
+        const float inv = 1.0f / lt;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                // rows 8 rr + 4 hh + 0..3 of d-block db
+                u32x2 w;
+                w[0] = pack_rne(o[db][4 * rr] * inv, o[db][4 * rr + 1] * inv);
+                w[1] = pack_rne(o[db][4 * rr + 2] * inv, o[db][4 * rr + 3] * inv);
+                *(u32x2*)(dst + 32 * db + 8 * rr + 4 * hh) = w;
+            }
+        }
+        if (hh == 0) a.lse[bh * a.Nq + q] = (mt + log2f(lt)) * kLn2;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_mx_quant(const MxArgs& a, hipStream_t st) {
+    const int64_t rows = (int64_t)(a.Nq_pad > a.Nk_pad ? a.Nq_pad : a.Nk_pad) * (a.D / 32);
+    const dim3 gr((unsigned)((rows + 255) / 256), (unsigned)a.BH, 2);
+    const int64_t cols = (int64_t)(a.Nk_pad / 32) * a.D;
+    const dim3 gv((unsigned)((cols + 255) / 256), (unsigned)a.BH);
+    if (a.D == 128) {
+        mx_quant_rows_kernel<128><<<gr, 256, 0, st>>>(a);
+        mx_quant_vt_kernel<128><<<gv, 256, 0, st>>>(a);
+    } else {
+        mx_quant_rows_kernel<64><<<gr, 256, 0, st>>>(a);
+        mx_quant_vt_kernel<64><<<gv, 256, 0, st>>>(a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_mx_fwd(const MxArgs& a, hipStream_t st) {
+    const dim3 g((unsigned)(a.Nq_pad / 128), (unsigned)a.BH);
+    if (a.D == 128) mx_fwd_kernel<128><<<g, 256, 0, st>>>(a);
+    else mx_fwd_kernel<64><<<g, 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace aq

@@ -54,7 +54,7 @@ def test_exports_every_declared_function(L):
     assert declared == set(qaa.EXPORTS), declared ^ set(qaa.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.attnqat_abi_version() == 3
+    assert L.attnqat_abi_version() == 4
 
 
 def test_status_strings(L):
@@ -254,3 +254,30 @@ def test_batch_heads_limit(L):
     assert _fwd(L, _prob(B=2, H=40000)) == E_UNSUPPORTED
     assert L.attnqat_fwd_workspace_bytes(ctypes.byref(_prob(B=2, H=40000))) == 0
 
+
+
+def _mx(L, p, q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, ws=6 * A, wsb=1 << 40):
+    return L.attnqat_mxfp4_fwd(ctypes.byref(p), q, k, v, o, lse, ws, wsb, None)
+
+
+def test_mxfp4_validation(L):
+    """The MXFP4 forward: dense, every quantizer, no straight-through output;
+    the exact workspace size (codes and scales of Q, K and V^T, token counts
+    padded to 256); workspace, alignment and aliasing errors before any HIP
+    call."""
+    p = _prob()
+    need = L.attnqat_mxfp4_fwd_workspace_bytes(ctypes.byref(p))
+    # B H = 2, D = 64, Nq_pad = Nk_pad = 256: 2 * 256 * 32 code bytes and
+    # 2 * 256 * 2 scale bytes for each of Q, K and V^T
+    assert need == 3 * (2 * 256 * 32) + 3 * (2 * 256 * 2)
+    assert L.attnqat_mxfp4_fwd_workspace_bytes(ctypes.byref(_prob(quant_mask=7))) == 0
+    assert _mx(L, _prob(quant_mask=7)) == E_UNSUPPORTED
+    assert _mx(L, _prob(kv_block_idx=9 * A, topk=1)) == E_UNSUPPORTED
+    assert _mx(L, _prob(o_ste=9 * A)) == E_UNSUPPORTED
+    assert _mx(L, _prob(D=96)) == E_UNSUPPORTED
+    assert _mx(L, p, wsb=need - 1) == E_WORKSPACE
+    assert _mx(L, p, ws=6 * A + 16) == E_MISALIGNED
+    assert _mx(L, p, lse=5 * A + 2) == E_MISALIGNED
+    assert _mx(L, p, o=A) == E_INVALID          # output overlaps q
+    assert _mx(L, p, ws=4 * A) == E_INVALID     # workspace overlaps o
+    assert _mx(L, p, q=0) == E_INVALID
