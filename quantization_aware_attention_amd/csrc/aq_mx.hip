@@ -201,43 +201,46 @@ __global__ __launch_bounds__(256, 2) void mx_fwd_kernel(MxArgs a) {
     }
     const int n_tiles = (a.Nk + 63) / 64;
     const float c = a.c;
-    // pass 1: exact running maximum m (log2 units, of x = S c) and l
-    float m = kNegBig, l = 0.0f;
-    MxTile<D> T0, T1;
-    mx_load_k<D>(a, bh, 0, l32, hh, T0);
-    for (int it = 0; it < n_tiles; ++it) {
-        MxTile<D>& T = (it & 1) ? T1 : T0;
-        MxTile<D>& Tn = (it & 1) ? T0 : T1;
+    // pass 1: the row maximum m of x = S c (log2 units). Pass 2 forms
+    // P~ / X = exp2(x - m - se) for every key anyway, so the sum l is taken
+    // there (l = sum over blocks of 2^se times the block's unclamped values)
+    // and pass 1 needs no exponentials.
+    float m = -INFINITY;
+    MxTile<D> T0, T1, T2, T3;
+    // Pass 1 has little work per tile, so its K operands come through a ring
+    // of four (the output accumulators are not live yet), loaded three tiles
+    // ahead; the loops are unrolled so that every buffer is a fixed register
+    // set.
+    auto pass1 = [&](MxTile<D>& T, MxTile<D>& Tn, int it) {
         const int kt = it * 64;
-        if (it + 1 < n_tiles) mx_load_k<D>(a, bh, kt + 64, l32, hh, Tn);
+        if (it + 3 < n_tiles) mx_load_k<D>(a, bh, kt + 192, l32, hh, Tn);
         f32x16 s[2];
         mx_scores<D>(T, qa, qs, s);
-        float x[32], mx = m;
+        // maximum over the raw scores (rounding x = S c is monotone, so the
+        // maximum of the rounded products is the rounded product of it)
+        float smax = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            x[j] = s[j >> 4][j & 15] * c;
-            asm volatile("" : "+v"(x[j]));
-            if (kt + 32 * hh + j >= a.Nk) x[j] = -INFINITY;
-            mx = fmaxf(mx, x[j]);
-        }
-        float sum = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) sum += __builtin_amdgcn_exp2f(x[j] - mx);
-        l = l * __builtin_amdgcn_exp2f(m - mx) + sum;
-        m = mx;
+        for (int j = 0; j < 32; ++j)
+            if (kt + 32 * hh + j < a.Nk) smax = fmaxf(smax, s[j >> 4][j & 15]);
+        m = fmaxf(m, smax * c);
+    };
+    mx_load_k<D>(a, bh, 0, l32, hh, T0);
+    if (n_tiles > 1) mx_load_k<D>(a, bh, 64, l32, hh, T1);
+    if (n_tiles > 2) mx_load_k<D>(a, bh, 128, l32, hh, T2);
+    for (int it = 0; it < n_tiles; it += 4) {
+        pass1(T0, T3, it);
+        if (it + 1 < n_tiles) pass1(T1, T0, it + 1);
+        if (it + 2 < n_tiles) pass1(T2, T1, it + 2);
+        if (it + 3 < n_tiles) pass1(T3, T2, it + 3);
     }
-    const float mp = partner_lane(m), lp = partner_lane(l);
-    const float mt = fmaxf(m, mp);
-    const float lt = l * __builtin_amdgcn_exp2f(m - mt) + lp * __builtin_amdgcn_exp2f(mp - mt);
+    const float mt = fmaxf(m, partner_lane(m));
+    float l = 0.0f;
     // pass 2
     f32x16 o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-    mx_load_k<D>(a, bh, 0, l32, hh, T0);
-    mx_load_v<D>(a, bh, 0, l32, hh, T0);
-    for (int it = 0; it < n_tiles; ++it) {
-        MxTile<D>& T = (it & 1) ? T1 : T0;
-        MxTile<D>& Tn = (it & 1) ? T0 : T1;
+    // pass 2: one tile with operands in T, the next loaded into Tn
+    auto pass2 = [&](MxTile<D>& T, MxTile<D>& Tn, int it) {
         const int kt = it * 64;
         if (it + 1 < n_tiles) {
             mx_load_k<D>(a, bh, kt + 64, l32, hh, Tn);
@@ -245,23 +248,53 @@ __global__ __launch_bounds__(256, 2) void mx_fwd_kernel(MxArgs a) {
         }
         f32x16 s[2];
         mx_scores<D>(T, qa, qs, s);
-        // x - mt is exactly 0 at the row maximum, so that block's amax is 1:
-        // x is the same rounded product as in pass 1. The empty asm keeps the
-        // compiler from fusing the product and the subtraction into an FMA,
-        // whose result at the maximum would be the product's rounding error.
-        float p[32];
+        // The block's scale exponent comes from its largest score: amax =
+        // exp2(xmax - mt), so se = floor(xmax - mt) - 2 (xmax = mt in the
+        // block holding the row maximum: se = -2, and that element maps to
+        // exactly 4). The scaled values P~ / X = exp2(S c - (mt + se)) then
+        // take one FMA and one exp each.
+        float smax = -INFINITY;
 #pragma unroll
         for (int j = 0; j < 32; ++j) {
-            float x = s[j >> 4][j & 15] * c;
-            asm volatile("" : "+v"(x));
-            p[j] = __builtin_amdgcn_exp2f(x - mt);
-            if (kt + 32 * hh + j >= a.Nk) p[j] = 0.0f;
+            if (kt + 32 * hh + j >= a.Nk) s[j >> 4][j & 15] = -INFINITY;
+            smax = fmaxf(smax, s[j >> 4][j & 15]);
         }
+        float xmax = smax * c;
+        asm volatile("" : "+v"(xmax));
+        const float lb = xmax - mt;  // log2 of the block's amax (-inf: empty block)
+        const int se = lb > -125.0f ? max(-127, (int)floorf(lb) - 2) : -127;
+        const float off = mt + (float)se;
+        float bsum = 0.0f;
         u32x4 pc;
-        const int ps = mx_block(p, pc);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            float y[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int jj = 8 * w + i;
+                y[i] = __builtin_amdgcn_exp2f(fmaf(s[jj >> 4][jj & 15], c, -off));
+                bsum += y[i];
+                y[i] = fminf(y[i], 6.0f);
+            }
+            uint32_t cw = 0;
+            cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, y[0], y[1], 1.0f, 0);
+            cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, y[2], y[3], 1.0f, 1);
+            cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, y[4], y[5], 1.0f, 2);
+            cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, y[6], y[7], 1.0f, 3);
+            pc[w] = cw;
+        }
+        const int ps = se + 127;
+        l += __builtin_ldexpf(bsum, se);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) o[db] = mfma_fp4(T.v[db], pc, T.vs[db], ps, o[db]);
+    };
+    mx_load_k<D>(a, bh, 0, l32, hh, T0);
+    mx_load_v<D>(a, bh, 0, l32, hh, T0);
+    for (int it = 0; it < n_tiles; it += 2) {
+        pass2(T0, T1, it);
+        if (it + 1 < n_tiles) pass2(T1, T0, it + 1);
     }
+    const float lt = l + partner_lane(l);
     if (q < a.Nq) {
         const int64_t b = bh / a.H, h = bh % a.H;
         uint16_t* dst = a.o + b * a.osb + h * a.osh + (int64_t)q * a.osn;
