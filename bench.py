@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense BF16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_FP4_TFLOPS = 10100.0  # dense FP4 MFMA peak of MI355X
 METRIC = "Attn-QAT fwd+bwd ms & TFLOP/s (% BF16 MFMA peak), H=6 N=31200 d=128"
 
 # Algorithmic FLOPs per (query, key) pair and head dimension unit, per kernel:
@@ -295,6 +296,28 @@ def main():
         vs[name] = e
     out["vsa_coarse"] = {"kernels": vs, "ms_per_step": round(sum(v["ms_per_launch"] * v["launches_per_step"] for v in vs.values()), 4)}
     del gate, vq, vk, vv, vo
+    # Real-FP4 inference forward (MXFP4 operands on the scaled FP4 matrix
+    # instruction) on the same inputs: 4 B H N^2 D credited FLOPs per forward,
+    # against the dense FP4 peak.
+    mo = torch.empty_like(q)
+    ml = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        qaa.mxfp4_fwd(q, k, v, w.sm_scale, out=mo, lse=ml)
+    torch.cuda.synchronize()
+    qaa.profile_enable(True)
+    for _ in range(5):
+        qaa.mxfp4_fwd(q, k, v, w.sm_scale, out=mo, lse=ml)
+    torch.cuda.synchronize()
+    rec = qaa.profile_read()
+    qaa.profile_enable(False)
+    mk = {name: round(tot / cnt, 4) for name, (tot, cnt) in rec.items()}
+    mfwd = sum(mk.values())
+    mflops = 4.0 * B * H * N * N * D
+    out["mxfp4_infer"] = {
+        "kernels_ms": mk, "fwd_ms": round(mfwd, 4),
+        "tflops": round(mflops / (mfwd * 1e-3) / 1e12, 1),
+        "frac_fp4_peak": round(mflops / (mfwd * 1e-3) / 1e12 / PEAK_FP4_TFLOPS, 4)}
+    del mo, ml
     # Variants of the P quantizer on the same inputs, reported beside the
     # metric (which is the normalised reading with the plain STE) and credited
     # the same FLOPs: the row-max-relative P and the additive straight-through

@@ -22,7 +22,6 @@
 #include "aq_kernels.h"
 
 namespace aq {
-namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -313,8 +312,6 @@ __global__ __launch_bounds__(256, 2) void mx_fwd_kernel(MxArgs a) {
         if (hh == 0) a.lse[bh * a.Nq + q] = (mt + log2f(lt)) * kLn2;
     }
 }
-
-}  // namespace
 
 hipError_t launch_mx_quant(const MxArgs& a, hipStream_t st) {
     const int64_t rows = (int64_t)(a.Nq_pad > a.Nk_pad ? a.Nq_pad : a.Nk_pad) * (a.D / 32);
