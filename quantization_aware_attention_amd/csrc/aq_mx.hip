@@ -124,9 +124,8 @@ __global__ __launch_bounds__(256) void mx_quant_vt_kernel(MxArgs a) {
 
 // Forward: 4 waves x 32 queries per workgroup, 64-key tiles, two passes over
 // the keys (pass 1: row maximum m and l; pass 2: P~, its MX quantization and
-// O^T += V^T P~^T). Operands are read straight from the quantized workspace
-// (16 bytes per lane per operand, L2-resident across the workgroups of a
-// head); the next tile's operands are loaded while the current one is used.
+// O^T += V^T P~^T). Each 64-key tile of quantized K (and V^T) is copied once
+// per workgroup into LDS, where the four waves read their operands.
 //
 // Score tiles are S^T = K Q^T (keys on rows). For 32-key block kb of a tile,
 // accumulator row rho = 8 (r / 4) + 4 hh + r % 4 of lane half hh is given key
@@ -138,52 +137,90 @@ __device__ __forceinline__ int mx_key_of_row(int kb, int row) {
     return 32 * ((row >> 2) & 1) + 16 * kb + 4 * (row >> 3) + (row & 3);
 }
 
+// One 64-key tile in LDS: K codes (row-major, D / 2 bytes per key) and
+// scales (D / 32 per key), V^T codes (32 bytes per d row: 64 tokens) and
+// scales (2 per d row).
 template <int D>
-struct MxTile {
-    u32x4 k[2][D / 64];
-    int ks[2][D / 64];
-    u32x4 v[D / 32];
-    int vs[D / 32];
+struct MxLds {
+    uint8_t k[64 * D / 2];
+    uint8_t ks[64 * D / 32];
+    uint8_t v[D * 32];
+    uint8_t vs[D * 2];
 };
 
+// This thread's share of a tile copy: one 16-byte chunk of K codes and of V^T
+// codes (each tile holds 2 D chunks of either: threads below 2 D), 4 bytes of
+// K scales (below D / 2) and 2 bytes of V^T scales (below D).
+struct MxStage {
+    u32x4 k, v;
+    uint32_t ks;
+    uint16_t vs;
+};
+
+template <int D, bool V>
+__device__ __forceinline__ void mx_fetch(const MxArgs& a, int64_t bh, int kt, int t, MxStage& g) {
+    if (t < 2 * D) {
+        const int row = t / (D / 32), col = t % (D / 32);
+        g.k = *(const u32x4*)(a.km + (bh * a.Nk_pad + kt + row) * (D / 2) + col * 16);
+        if (V) {
+            const int d = t >> 1, half = t & 1;
+            g.v = *(const u32x4*)(a.vtm + (bh * D + d) * (a.Nk_pad / 2) + kt / 2 + half * 16);
+        }
+    }
+    if (t < D / 2) g.ks = *(const uint32_t*)(a.ks + (bh * a.Nk_pad + kt) * (D / 32) + 4 * t);
+    if (V && t < D) g.vs = *(const uint16_t*)(a.vts + (bh * D + t) * (a.Nk_pad / 32) + kt / 32);
+}
+
+template <int D, bool V>
+__device__ __forceinline__ void mx_store(MxLds<D>& L, int t, const MxStage& g) {
+    if (t < 2 * D) {
+        *(u32x4*)(L.k + 16 * t) = g.k;
+        if (V) *(u32x4*)(L.v + 16 * t) = g.v;
+    }
+    if (t < D / 2) *(uint32_t*)(L.ks + 4 * t) = g.ks;
+    if (V && t < D) *(uint16_t*)(L.vs + 2 * t) = g.vs;
+}
+
+// S^T of the tile's two 32-key blocks, K operands read from LDS
 template <int D>
-__device__ __forceinline__ void mx_load_k(const MxArgs& a, int64_t bh, int kt, int l32, int hh,
-                                          MxTile<D>& T) {
+__device__ __forceinline__ void mx_scores(const MxLds<D>& L, const u32x4* qa, const int* qs,
+                                          int l32, int hh, f32x16* s) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-        const int64_t r = bh * a.Nk_pad + kt + mx_key_of_row(kb, l32);
+        const int row = mx_key_of_row(kb, l32);
+        s[kb] = f32x16{};
 #pragma unroll
         for (int c = 0; c < D / 64; ++c) {
-            T.k[kb][c] = *(const u32x4*)(a.km + r * (D / 2) + 32 * c + 16 * hh);
-            T.ks[kb][c] = a.ks[r * (D / 32) + 2 * c + hh];
+            const u32x4 ka = *(const u32x4*)(L.k + row * (D / 2) + 32 * c + 16 * hh);
+            s[kb] = mfma_fp4(ka, qa[c], L.ks[row * (D / 32) + 2 * c + hh], qs[c], s[kb]);
         }
     }
 }
 
-template <int D>
-__device__ __forceinline__ void mx_load_v(const MxArgs& a, int64_t bh, int kt, int l32, int hh,
-                                          MxTile<D>& T) {
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-        const int64_t r = bh * D + 32 * db + l32;
-        T.v[db] = *(const u32x4*)(a.vtm + r * (a.Nk_pad / 2) + (kt + 32 * hh) / 2);
-        T.vs[db] = a.vts[r * (a.Nk_pad / 32) + kt / 32 + hh];
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void mx_scores(const MxTile<D>& T, const u32x4* qa, const int* qs,
-                                          f32x16* s) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-#pragma unroll
-        for (int c = 0; c < D / 64; ++c) s[kb] = mfma_fp4(T.k[kb][c], qa[c], T.ks[kb][c], qs[c], s[kb]);
+// Runs body(L, it) over the key tiles with the tiles staged in LDS by the
+// whole workgroup: double-buffered, the next tile's global loads in flight
+// during the current tile's work, one barrier per tile (every wave runs the
+// same number of tiles).
+template <int D, bool V, class F>
+__device__ __forceinline__ void mx_tiles(const MxArgs& a, int64_t bh, int n_tiles, MxLds<D>* L,
+                                         F body) {
+    const int t = threadIdx.x;
+    MxStage g;
+    mx_fetch<D, V>(a, bh, 0, t, g);
+    mx_store<D, V>(L[0], t, g);
+    __syncthreads();
+    for (int it = 0; it < n_tiles; ++it) {
+        const bool more = it + 1 < n_tiles;
+        if (more) mx_fetch<D, V>(a, bh, (it + 1) * 64, t, g);
+        body(L[it & 1], it);
+        if (more) mx_store<D, V>(L[(it + 1) & 1], t, g);
+        __syncthreads();
     }
 }
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void mx_fwd_kernel(MxArgs a) {
+    __shared__ __attribute__((aligned(16))) MxLds<D> L[2];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
     const int64_t bh = blockIdx.y;
@@ -205,16 +242,10 @@ __global__ __launch_bounds__(256, 2) void mx_fwd_kernel(MxArgs a) {
     // there (l = sum over blocks of 2^se times the block's unclamped values)
     // and pass 1 needs no exponentials.
     float m = -INFINITY;
-    MxTile<D> T0, T1, T2, T3;
-    // Pass 1 has little work per tile, so its K operands come through a ring
-    // of four (the output accumulators are not live yet), loaded three tiles
-    // ahead; the loops are unrolled so that every buffer is a fixed register
-    // set.
-    auto pass1 = [&](MxTile<D>& T, MxTile<D>& Tn, int it) {
+    mx_tiles<D, false>(a, bh, n_tiles, L, [&](const MxLds<D>& T, int it) {
         const int kt = it * 64;
-        if (it + 3 < n_tiles) mx_load_k<D>(a, bh, kt + 192, l32, hh, Tn);
         f32x16 s[2];
-        mx_scores<D>(T, qa, qs, s);
+        mx_scores<D>(T, qa, qs, l32, hh, s);
         // maximum over the raw scores (rounding x = S c is monotone, so the
         // maximum of the rounded products is the rounded product of it)
         float smax = -INFINITY;
@@ -222,36 +253,23 @@ __global__ __launch_bounds__(256, 2) void mx_fwd_kernel(MxArgs a) {
         for (int j = 0; j < 32; ++j)
             if (kt + 32 * hh + j < a.Nk) smax = fmaxf(smax, s[j >> 4][j & 15]);
         m = fmaxf(m, smax * c);
-    };
-    mx_load_k<D>(a, bh, 0, l32, hh, T0);
-    if (n_tiles > 1) mx_load_k<D>(a, bh, 64, l32, hh, T1);
-    if (n_tiles > 2) mx_load_k<D>(a, bh, 128, l32, hh, T2);
-    for (int it = 0; it < n_tiles; it += 4) {
-        pass1(T0, T3, it);
-        if (it + 1 < n_tiles) pass1(T1, T0, it + 1);
-        if (it + 2 < n_tiles) pass1(T2, T1, it + 2);
-        if (it + 3 < n_tiles) pass1(T3, T2, it + 3);
-    }
+    });
     const float mt = fmaxf(m, partner_lane(m));
-    float l = 0.0f;
     // pass 2
+    float l = 0.0f;
     f32x16 o[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-    // pass 2: one tile with operands in T, the next loaded into Tn
-    auto pass2 = [&](MxTile<D>& T, MxTile<D>& Tn, int it) {
+    mx_tiles<D, true>(a, bh, n_tiles, L, [&](const MxLds<D>& T, int it) {
         const int kt = it * 64;
-        if (it + 1 < n_tiles) {
-            mx_load_k<D>(a, bh, kt + 64, l32, hh, Tn);
-            mx_load_v<D>(a, bh, kt + 64, l32, hh, Tn);
-        }
         f32x16 s[2];
-        mx_scores<D>(T, qa, qs, s);
+        mx_scores<D>(T, qa, qs, l32, hh, s);
         // The block's scale exponent comes from its largest score: amax =
         // exp2(xmax - mt), so se = floor(xmax - mt) - 2 (xmax = mt in the
         // block holding the row maximum: se = -2, and that element maps to
         // exactly 4). The scaled values P~ / X = exp2(S c - (mt + se)) then
-        // take one FMA and one exp each.
+        // take one FMA and one exp each. The empty asm keeps xmax the same
+        // rounded product as in pass 1 (no FMA with the subtraction).
         float smax = -INFINITY;
 #pragma unroll
         for (int j = 0; j < 32; ++j) {
@@ -285,14 +303,12 @@ __global__ __launch_bounds__(256, 2) void mx_fwd_kernel(MxArgs a) {
         const int ps = se + 127;
         l += __builtin_ldexpf(bsum, se);
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[db] = mfma_fp4(T.v[db], pc, T.vs[db], ps, o[db]);
-    };
-    mx_load_k<D>(a, bh, 0, l32, hh, T0);
-    mx_load_v<D>(a, bh, 0, l32, hh, T0);
-    for (int it = 0; it < n_tiles; it += 2) {
-        pass2(T0, T1, it);
-        if (it + 1 < n_tiles) pass2(T1, T0, it + 1);
-    }
+        for (int db = 0; db < D / 32; ++db) {
+            const int d = 32 * db + l32;
+            const u32x4 va = *(const u32x4*)(T.v + d * 32 + 16 * hh);
+            o[db] = mfma_fp4(va, pc, T.vs[d * 2 + hh], ps, o[db]);
+        }
+    });
     const float lt = l + partner_lane(l);
     if (q < a.Nq) {
         const int64_t b = bh / a.H, h = bh % a.H;
