@@ -218,13 +218,13 @@ __device__ __forceinline__ void mx_tiles(const MxArgs& a, int64_t bh, int n_tile
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void mx_fwd_kernel(MxArgs a) {
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void mx_fwd_kernel(MxArgs a) {
     __shared__ __attribute__((aligned(16))) MxLds<D> L[2];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
     const int64_t bh = blockIdx.y;
-    const int q = blockIdx.x * 128 + wave * 32 + l32;
+    const int q = blockIdx.x * (NW * 32) + wave * 32 + l32;
     u32x4 qa[D / 64];
     int qs[D / 64];
     {
@@ -344,10 +344,14 @@ hipError_t launch_mx_quant(const MxArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// 8 waves (256 queries) per workgroup, so that each tile copied into LDS
+// serves 256 queries; Nq_pad is a multiple of 256.
+constexpr int kMxWaves = 8;
 hipError_t launch_mx_fwd(const MxArgs& a, hipStream_t st) {
-    const dim3 g((unsigned)(a.Nq_pad / 128), (unsigned)a.BH);
-    if (a.D == 128) mx_fwd_kernel<128><<<g, 256, 0, st>>>(a);
-    else mx_fwd_kernel<64><<<g, 256, 0, st>>>(a);
+    constexpr int NW = kMxWaves;
+    const dim3 g((unsigned)(a.Nq_pad / (NW * 32)), (unsigned)a.BH);
+    if (a.D == 128) mx_fwd_kernel<128, NW><<<g, NW * 64, 0, st>>>(a);
+    else mx_fwd_kernel<64, NW><<<g, NW * 64, 0, st>>>(a);
     return hipGetLastError();
 }
 
