@@ -122,10 +122,10 @@ __global__ __launch_bounds__(256) void mx_quant_vt_kernel(MxArgs a) {
     a.vts[r * nblk + tb] = (uint8_t)sc;
 }
 
-// Forward: 4 waves x 32 queries per workgroup, 64-key tiles, two passes over
+// Forward: NW waves x 32 queries per workgroup, 64-key tiles, two passes over
 // the keys (pass 1: row maximum m and l; pass 2: P~, its MX quantization and
 // O^T += V^T P~^T). Each 64-key tile of quantized K (and V^T) is copied once
-// per workgroup into LDS, where the four waves read their operands.
+// per workgroup into LDS, where the workgroup's waves read their operands.
 //
 // Score tiles are S^T = K Q^T (keys on rows). For 32-key block kb of a tile,
 // accumulator row rho = 8 (r / 4) + 4 hh + r % 4 of lane half hh is given key
