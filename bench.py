@@ -96,6 +96,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sparse", action="store_true",
                     help="skip the block-sparse VSA step at its own configuration")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the timing of the other workloads (tiny, DiT, tail)")
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="query rows of head 0 in the CPU-oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -125,10 +127,114 @@ def cpu_baseline(bits, w, rows, mask):
     oatt.head_backward(qq, kq, vq, do, O, L, w.sm_scale, mask)
     dt = time.perf_counter() - t0
     flops = 4.0 * rows * w.N * w.D * 3.5
+    full_flops = sum(w.credited_flops())
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"fwd+bwd of {rows} query rows of head 0 against all {w.N} keys "
-                      f"(credited {flops / 1e9:.1f} GFLOP), fp64 numpy oracle"}
+                      f"(credited {flops / 1e9:.1f} GFLOP), fp64 numpy oracle",
+            "extrapolated_full_workload_s": round(dt * full_flops / flops, 1),
+            "extrapolation": "linear in query rows and heads (rows are independent)",
+            "host_cpus": os.cpu_count(), "cpu_model": _cpu_model(),
+            "blas_threads": int(threads)}
+
+
+def _cpu_model():
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:  # pragma: no cover
+        pass
+    return None
+
+
+def machine_probes(torch, dev):
+    """Dense BF16 MFMA rate and shader clock under that load (probe kernel),
+    and the bandwidth of a plain 1 GiB device copy after a cache flush."""
+    import ctypes
+    from quantization_aware_attention_amd.build import PROBE_PATH
+    out = {}
+    if os.path.exists(PROBE_PATH):
+        lib = ctypes.CDLL(PROBE_PATH)
+        fn = lib.aq_probe_mfma_peak
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                       ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                       ctypes.c_void_p]
+        blocks = 1024  # four workgroups of four waves per CU: four waves per SIMD
+        sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+        stamps = torch.zeros(4, dtype=torch.int64, device=dev)
+        tf, mhz = ctypes.c_double(), ctypes.c_double()
+        best = (0.0, 0.0)
+        for it in (2000, 50000, 50000, 50000):
+            rc = fn(blocks, it, sink.data_ptr(), stamps.data_ptr(), ctypes.byref(tf),
+                    ctypes.byref(mhz), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if rc == 0 and it > 2000 and tf.value > best[0]:
+                best = (tf.value, mhz.value)
+        out["mfma_bf16_tflops_measured"] = round(best[0], 1)
+        out["clock_mhz_under_mfma"] = round(best[1], 0)
+        del sink, stamps
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    times = []
+    for i in range(4):
+        flush.fill_(i)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = float(sorted(times[1:])[1])
+    out["hbm_copy_gbs"] = round(2.0 * (1 << 30) / (ms * 1e-3) / 1e9, 1)
+    out["hbm_copy_note"] = "1 GiB device-to-device copy (read + write bytes) after a 1 GiB flush"
+    del flush, src, dst
+    return out
+
+
+def time_configs(qaa, torch, np, dev, skip):
+    from synthetic import WORKLOADS, make_inputs
+    res = {}
+    for cid, masks in ((1, (15,)), (2, (15,)), (4, (15, 0))):
+        if cid == skip:
+            continue
+        w = WORKLOADS[cid]
+        bits = make_inputs(cid)
+        t = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).to(dev)
+             for k, v in bits.items()}
+        del bits
+        o, lse = torch.empty_like(t["q"]), torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
+        g = [torch.empty_like(t["q"]) for _ in range(3)]
+        f_fwd, f_bwd = w.credited_flops()
+        for mask in masks:
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(10)]
+            for i in range(13):
+                e = ev[i - 3] if i >= 3 else None
+                if e:
+                    e[0].record()
+                qaa.fwd(t["q"], t["k"], t["v"], w.sm_scale, mask, out=o, lse=lse)
+                if e:
+                    e[1].record()
+                qaa.bwd(t["q"], t["k"], t["v"], o, lse, t["do"], w.sm_scale, mask,
+                        dq=g[0], dk=g[1], dv=g[2])
+                if e:
+                    e[2].record()
+            torch.cuda.synchronize()
+            fm = float(np.median([a.elapsed_time(b) for a, b, _ in ev]))
+            bm = float(np.median([b.elapsed_time(c) for _, b, c in ev]))
+            tf_f, tf_b = f_fwd / (fm * 1e-3) / 1e12, f_bwd / (bm * 1e-3) / 1e12
+            tf = (f_fwd + f_bwd) / ((fm + bm) * 1e-3) / 1e12
+            res[f"{w.name}/{'qkvp' if mask == 15 else 'none'}"] = {
+                "shape": list(w.shape), "steps": 10, "stat": "median",
+                "fwd_ms": round(fm, 4), "bwd_ms": round(bm, 4), "ms_per_step": round(fm + bm, 4),
+                "fwd_tflops": round(tf_f, 1), "bwd_tflops": round(tf_b, 1),
+                "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del t, o, lse, g
+        torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -177,10 +283,12 @@ def main():
     def step(ev=None):
         if ev:
             ev[0].record()
-        qaa.fwd(q, k, v, w.sm_scale, mask, kv_idx, out=o, lse=lse, workspace=ws_f)
+        qaa.fwd(q, k, v, w.sm_scale, mask, kv_idx, out=o, lse=lse, workspace=ws_f,
+                validate_index=False)
         if ev:
             ev[1].record()
-        qaa.bwd(q, k, v, o, lse, do, w.sm_scale, mask, kv_idx, dq=dq, dk=dk, dv=dv, workspace=ws_b)
+        qaa.bwd(q, k, v, o, lse, do, w.sm_scale, mask, kv_idx, dq=dq, dk=dk, dv=dv, workspace=ws_b,
+                validate_index=False)
         if ev:
             ev[2].record()
 
@@ -249,6 +357,10 @@ def main():
     }
     # Standalone fake quantization of one input (HBM-bound): 4 bytes per
     # element (2 read, 2 written), along d (Q's layout) and along tokens (V's).
+    # Every launch below follows a 1 GiB fill of a scratch buffer (outside the
+    # timed events), which evicts the 256 MB last-level cache and the L2s, so
+    # the GB/s are HBM figures, not cache figures.
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     fq_out = torch.empty_like(q)
     fq = {}
     for axis, x in (("d", q), ("n", v)):
@@ -256,7 +368,8 @@ def main():
             qaa.fakequant(x, axis, out=fq_out)
         torch.cuda.synchronize()
         qaa.profile_enable(True)
-        for _ in range(20):
+        for i in range(20):
+            flush.fill_(i)
             qaa.fakequant(x, axis, out=fq_out)
         torch.cuda.synchronize()
         (tot, cnt), = qaa.profile_read().values()
@@ -264,8 +377,23 @@ def main():
         ms = tot / cnt
         gbs = 4.0 * x.numel() / (ms * 1e-3) / 1e9
         fq[f"axis_{axis}"] = {"ms_per_launch": round(ms, 4), "algo_gbs": round(gbs, 1),
-                              "frac_hbm": round(gbs / PEAK_HBM_GBS, 3)}
+                              "frac_hbm": round(gbs / PEAK_HBM_GBS, 3), "cache": "flushed"}
     out["fakequant_standalone"] = fq
+    # The backward preprocess (Dl = rowsum(dO * O)), timed inside whole
+    # backward calls that each follow a flush: its O and dO are not resident.
+    qaa.profile_enable(True)
+    for i in range(10):
+        flush.fill_(i)
+        qaa.bwd(q, k, v, o, lse, do, w.sm_scale, mask, kv_idx, dq=dq, dk=dk, dv=dv,
+                workspace=ws_b, validate_index=False)
+    torch.cuda.synchronize()
+    rec = qaa.profile_read()
+    qaa.profile_enable(False)
+    tot, cnt = rec["bwd_pre"]
+    ms = tot / cnt
+    gbs = ALGO_BYTES["bwd_pre"](B * H, N, D) / (ms * 1e-3) / 1e9
+    out["bwd_pre_flushed"] = {"ms_per_launch": round(ms, 4), "algo_gbs": round(gbs, 1),
+                              "frac_hbm": round(gbs / PEAK_HBM_GBS, 3)}
     # VSA coarse branch and gated combination on the same tensors (128-token
     # blocks): its kernels are passes over the token tensors, reported as
     # algorithmic GB/s (bf16 bytes each pass must move) next to HBM peak.
@@ -277,8 +405,10 @@ def main():
         qaa.vsa_bwd(q, k, v, gate, do, vq, vk, vv, w.sm_scale)
     torch.cuda.synchronize()
     qaa.profile_enable(True)
-    for _ in range(10):
+    for i in range(10):
+        flush.fill_(i)
         qaa.vsa_fwd(q, k, v, gate, o, w.sm_scale, out=vo)
+        flush.fill_(i + 1)
         qaa.vsa_bwd(q, k, v, gate, do, vq, vk, vv, w.sm_scale)
     torch.cuda.synchronize()
     rec = qaa.profile_read()
@@ -294,8 +424,10 @@ def main():
             e["algo_gbs"] = round(vbytes[name] / (ms * 1e-3) / 1e9, 1)
             e["frac_hbm"] = round(e["algo_gbs"] / PEAK_HBM_GBS, 3)
         vs[name] = e
-    out["vsa_coarse"] = {"kernels": vs, "ms_per_step": round(sum(v["ms_per_launch"] * v["launches_per_step"] for v in vs.values()), 4)}
-    del gate, vq, vk, vv, vo
+    out["vsa_coarse"] = {"kernels": vs, "cache": "flushed before each call",
+                         "ms_per_step": round(sum(v["ms_per_launch"] * v["launches_per_step"]
+                                                  for v in vs.values()), 4)}
+    del gate, vq, vk, vv, vo, flush
     # Real-FP4 inference forward (MXFP4 operands on the scaled FP4 matrix
     # instruction) on the same inputs: 4 B H N^2 D credited FLOPs per forward,
     # against the dense FP4 peak.
@@ -387,12 +519,13 @@ def main():
             idx5 = qaa.block_select(t5["q"], t5["k"], w5.topk, w5.block_tokens)
             if e:
                 e[1].record()
-            qaa.fwd(t5["q"], t5["k"], t5["v"], w5.sm_scale, mask, idx5, out=o5f, lse=l5)
+            qaa.fwd(t5["q"], t5["k"], t5["v"], w5.sm_scale, mask, idx5, out=o5f, lse=l5,
+                    validate_index=False)
             qaa.vsa_fwd(t5["q"], t5["k"], t5["v"], g5, o5f, w5.sm_scale, out=o5)
             if e:
                 e[2].record()
             qaa.bwd(t5["q"], t5["k"], t5["v"], o5f, l5, t5["do"], w5.sm_scale, mask, idx5,
-                    dq=d5[0], dk=d5[1], dv=d5[2])
+                    dq=d5[0], dk=d5[1], dv=d5[2], validate_index=False)
             qaa.vsa_bwd(t5["q"], t5["k"], t5["v"], g5, t5["do"], d5[0], d5[1], d5[2], w5.sm_scale)
             if e:
                 e[3].record()
@@ -434,6 +567,14 @@ def main():
             "ms_per_step": round(vf + vb, 4), "tflops": round(tf, 1),
             "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
         del ws0
+    # The other workloads, each on its own synthetic inputs (the DiT layer of
+    # 12 heads x 25,088 tokens, the 16,411-token tail case with every quantizer
+    # on and off, and the tiny case): forward and backward ms, credited
+    # TFLOP/s and the fraction of the BF16 peak.
+    if not args.no_configs:
+        del ws_f, ws_b
+        out["configs"] = time_configs(qaa, torch, np, dev, args.workload)
+    out["machine"] = machine_probes(torch, dev)
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)

@@ -55,15 +55,19 @@
 extern "C" {
 #endif
 
-#define ATTNQAT_ABI_VERSION 4
+#define ATTNQAT_ABI_VERSION 5
 
 /* status codes */
 #define ATTNQAT_OK 0
 #define ATTNQAT_E_INVALID 1     /* null pointer, bad size, bad mask, bad scale, aliasing */
-#define ATTNQAT_E_UNSUPPORTED 2 /* head dim not 64/128, B*H > 65535, device is not gfx950 */
+#define ATTNQAT_E_UNSUPPORTED 2 /* head dim not 64/128, B*H > 65535, Nq or Nk above
+                                 * ATTNQAT_MAX_TOKENS, device is not gfx950 */
 #define ATTNQAT_E_MISALIGNED 3  /* pointer not 16-byte aligned or stride not a multiple of 8 */
 #define ATTNQAT_E_WORKSPACE 4   /* workspace missing or too small */
 #define ATTNQAT_E_HIP 5         /* a HIP call or kernel launch failed */
+
+/* longest query or key sequence the attention entry points accept */
+#define ATTNQAT_MAX_TOKENS 4194304
 
 /* quantization mask bits: which operands are NVFP4 fake-quantized */
 #define ATTNQAT_QUANT_Q 1u
@@ -92,10 +96,14 @@ typedef struct {
     uint32_t quant_mask; /* OR of ATTNQAT_QUANT_* bits (0 = plain attention) */
     attnqat_strides q, k, v, o, dout, dq, dk, dv;
     /* Block-sparse fine attention (VSA-style), NULL for dense attention.
-     * Device array int32 [B, H, ceil(Nq/block_tokens), topk] of key-block
-     * indices, ascending and distinct within each row, each in
+     * Device array int32 [B, H, ceil(Nq/block_tokens), topk] (contiguous) of
+     * key-block indices, strictly ascending within each row, each in
      * [0, ceil(Nk/block_tokens)). Query block i attends only to the keys of
-     * the listed key blocks; LSE and P are taken over those keys only. */
+     * the listed key blocks; LSE and P are taken over those keys only.
+     * attnqat_fwd and attnqat_bwd check these rules on the device before any
+     * sparse kernel reads the index: if an entry breaks them, the attention
+     * kernels do no work, every output of the call is filled with NaN, and
+     * attnqat_block_idx_status reports the failure. */
     const int32_t* kv_block_idx;
     int32_t topk;         /* entries per row of kv_block_idx (ignored when dense) */
     int32_t block_tokens; /* tokens per block; must be 128 when kv_block_idx != NULL;
@@ -155,7 +163,14 @@ int attnqat_fakequant_nvfp4(const void* x, attnqat_strides xs, void* y, attnqat_
 size_t attnqat_fwd_workspace_bytes(const attnqat_problem* p);
 
 /*
- * Forward pass. Writes
+ * Forward pass of quantization-aware attention. Definition: the VSA
+ * checkpoint metadata, attention.precision ("NVFP4 fake-quant with BF16
+ * matmul", quant_p and quant_v set, no global scale factors), for which
+ * operands are quantized and in which number format the products run; the
+ * Attn-QAT training guide (FWD_EXACT_M row of its environment table) and the
+ * fastvideo-kernel commit message (SM100 route paragraph) for the softmax
+ * statistics the forward saves and the backward reuses, which make the
+ * quantized P that of the normalised probabilities. Writes
  *   o    bf16 [B,H,Nq,D] (strides p->o):  O = FQ_keys(P) FQ_tokens(V)
  *   lse  fp32 [B,H,Nq] contiguous:        LSE = ln sum_j exp(S_ij)
  * with S = sm_scale FQ_d(Q) FQ_d(K)^T and P = exp(S - LSE) (normalised); each
@@ -175,7 +190,11 @@ int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const vo
 size_t attnqat_bwd_workspace_bytes(const attnqat_problem* p);
 
 /*
- * Backward pass with straight-through quantizers. Given the forward inputs,
+ * Backward pass with straight-through quantizers. Definition: the Attn-QAT
+ * training guide and the fastvideo-kernel commit message (SM100 route
+ * paragraph: the backward recomputes P from the saved statistics, with
+ * bitwise reproducible gradients) and the VSA checkpoint metadata's
+ * attention.precision (the same quantizers as the forward). Given the forward inputs,
  * the forward output `o` and statistics `lse` (as written by attnqat_fwd) and
  * the output gradient `dout`, writes bf16 dq, dk, dv:
  *   Dl = rowsum(dout * o)
@@ -188,6 +207,25 @@ size_t attnqat_bwd_workspace_bytes(const attnqat_problem* p);
 int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const void* v,
                 const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Result of the device-side check of p->kv_block_idx made by the last
+ * block-sparse attnqat_fwd or attnqat_bwd that used `workspace` (the same
+ * pointer, with that call's work enqueued on `stream` or completed). Enqueues
+ * a 4-byte copy on `stream`, waits for it, and sets *invalid to 1 if the index
+ * broke its rules (the call's outputs are then NaN), else 0. Undefined after a
+ * dense call, which does not run the check.
+ */
+int attnqat_block_idx_status(const void* workspace, int* invalid, void* stream);
+
+/*
+ * Key blocks kept per query block by the pages' selection rule (VSA
+ * checkpoint metadata, attention.selection: effective_topk =
+ * max(1, min(ceil((1 - sparsity) num_blocks), num_blocks)), evaluated in
+ * double precision). Returns the count, or -ATTNQAT_E_INVALID if num_blocks
+ * < 1 or sparsity is outside [0, 1]. Host-only; enqueues nothing.
+ */
+int attnqat_effective_topk(int64_t num_blocks, double sparsity);
 
 /* Workspace bytes attnqat_block_select needs. */
 size_t attnqat_block_select_workspace_bytes(const attnqat_problem* p);

@@ -126,30 +126,33 @@ def head_forward(qq, kq, vq, sm_scale: float, mask: int, rows=None, row_block: i
 
 
 def _forward_rows_task(args):
-    qq, kq, vq, sm_scale, mask, r0, r1, p_mode = args
+    qq, kq, vq, sm_scale, mask, r0, r1, kw = args
     try:
         from threadpoolctl import threadpool_limits
         with threadpool_limits(1):
-            return head_forward(qq[r0:r1], kq, vq, sm_scale, mask, p_mode=p_mode)
+            return head_forward(qq[r0:r1], kq, vq, sm_scale, mask, **kw)
     except ImportError:  # pragma: no cover
-        return head_forward(qq[r0:r1], kq, vq, sm_scale, mask, p_mode=p_mode)
+        return head_forward(qq[r0:r1], kq, vq, sm_scale, mask, **kw)
 
 
 def head_forward_all(qq, kq, vq, sm_scale: float, mask: int, workers: int = 0,
-                     chunk: int = 1024, p_mode: int = P_NORMALISED):
+                     chunk: int = 1024, p_mode: int = P_NORMALISED, with_max: bool = False,
+                     with_ste: bool = False):
     """``head_forward`` over every query row, split into row chunks across
     ``workers`` processes (0 or 1: in this process). Rows are independent in
-    the forward, so the result is identical to a single call."""
+    the forward, so the result is identical to a single call, extra outputs
+    (``with_max``, ``with_ste``) included."""
     n = qq.shape[0]
     spans = [(r0, min(n, r0 + chunk)) for r0 in range(0, n, chunk)]
+    kw = dict(p_mode=p_mode, with_max=with_max, with_ste=with_ste)
     if workers <= 1:
-        parts = [head_forward(qq[a:b], kq, vq, sm_scale, mask, p_mode=p_mode) for a, b in spans]
+        parts = [head_forward(qq[a:b], kq, vq, sm_scale, mask, **kw) for a, b in spans]
     else:
         import multiprocessing as mp
         with mp.get_context("fork").Pool(workers) as pool:
             parts = pool.map(_forward_rows_task,
-                             [(qq, kq, vq, sm_scale, mask, a, b, p_mode) for a, b in spans])
-    return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+                             [(qq, kq, vq, sm_scale, mask, a, b, kw) for a, b in spans])
+    return tuple(np.concatenate([p[i] for p in parts]) for i in range(len(parts[0])))
 
 
 def forward(q, k, v, sm_scale: float, mask: int = MASK_ALL, row_block: int = 512,

@@ -53,8 +53,10 @@ EXPORTS = [
     "attnqat_bwd_workspace_bytes", "attnqat_bwd", "attnqat_block_select_workspace_bytes",
     "attnqat_block_select", "attnqat_vsa_workspace_bytes", "attnqat_vsa_fwd", "attnqat_vsa_bwd",
     "attnqat_mxfp4_fwd_workspace_bytes", "attnqat_mxfp4_fwd",
-    "attnqat_profile_enable", "attnqat_profile_read",
+    "attnqat_profile_enable", "attnqat_profile_read", "attnqat_block_idx_status",
+    "attnqat_effective_topk",
 ]
+MAX_TOKENS = 4194304
 
 _lib = None
 
@@ -117,6 +119,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.attnqat_mxfp4_fwd_workspace_bytes.argtypes = [pp]
     lib.attnqat_mxfp4_fwd.restype = ctypes.c_int
     lib.attnqat_mxfp4_fwd.argtypes = [pp, P, P, P, P, P, P, SZ, V]
+    lib.attnqat_block_idx_status.restype = ctypes.c_int
+    lib.attnqat_block_idx_status.argtypes = [P, ctypes.POINTER(ctypes.c_int), V]
+    lib.attnqat_effective_topk.restype = ctypes.c_int
+    lib.attnqat_effective_topk.argtypes = [I64, ctypes.c_double]
     lib.attnqat_profile_enable.restype = ctypes.c_int
     lib.attnqat_profile_enable.argtypes = [ctypes.c_int]
     lib.attnqat_profile_read.restype = ctypes.c_int
@@ -166,6 +172,37 @@ def strides_of(t: torch.Tensor) -> Strides:
     return Strides(t.stride(0), t.stride(1), t.stride(2))
 
 
+def _check_block_idx(idx, B, H, Nq, block_tokens, device):
+    """Layout checks of a block index (the ranges and the ascending order of
+    its entries are checked on the device by the library)."""
+    if not isinstance(idx, torch.Tensor) or idx.dtype != torch.int32:
+        raise AttnQatError("kv_block_idx must be an int32 tensor (torch.topk returns int64)")
+    if not idx.is_cuda or idx.device != device:
+        raise AttnQatError("kv_block_idx must be on the device of q")
+    nbq = -(-Nq // block_tokens)
+    if idx.dim() != 4 or tuple(idx.shape[:3]) != (B, H, nbq) or idx.shape[3] < 1:
+        raise AttnQatError(f"kv_block_idx must be [B, H, ceil(Nq/{block_tokens}), topk] = "
+                           f"[{B}, {H}, {nbq}, topk], got {tuple(idx.shape)}")
+    if not idx.is_contiguous():
+        raise AttnQatError("kv_block_idx must be contiguous")
+
+
+def block_idx_status(workspace, stream=None) -> bool:
+    """True if the device-side check of the block index failed in the last
+    block-sparse fwd/bwd that used ``workspace`` (its outputs are then NaN).
+    Waits for that call."""
+    flag = ctypes.c_int(0)
+    check(load().attnqat_block_idx_status(workspace.data_ptr(), ctypes.byref(flag),
+                                          _stream(stream)))
+    return bool(flag.value)
+
+
+def _raise_if_bad_index(workspace, stream):
+    if block_idx_status(workspace, stream):
+        raise AttnQatError("kv_block_idx has an entry outside [0, ceil(Nk/128)) or a row that "
+                           "is not strictly ascending; the outputs were filled with NaN")
+
+
 def make_problem(q, k, sm_scale, quant_mask, *, v=None, o=None, do=None, dq=None, dk=None,
                  dv=None, kv_block_idx=None, block_tokens=128, p_mode=P_NORMALISED,
                  row_max=None, o_ste=None) -> Problem:
@@ -180,6 +217,7 @@ def make_problem(q, k, sm_scale, quant_mask, *, v=None, o=None, do=None, dq=None
         if t is not None:
             setattr(p, name, strides_of(t))
     if kv_block_idx is not None:
+        _check_block_idx(kv_block_idx, B, H, Nq, block_tokens, q.device)
         p.kv_block_idx = kv_block_idx.data_ptr()
         p.topk = kv_block_idx.shape[-1]
     p.block_tokens = block_tokens
@@ -220,13 +258,15 @@ def fakequant(x: torch.Tensor, axis: str = "d", return_scale_codes: bool = False
 
 def fwd(q, k, v, sm_scale=None, quant="qkvp", kv_block_idx=None, block_tokens=128,
         out=None, lse=None, workspace=None, stream=None, p_mode=P_NORMALISED, row_max=None,
-        o_ste=None):
+        o_ste=None, validate_index=True):
     """O (bf16) and LSE (fp32, natural log) of Attn-QAT attention; with
     p_mode=P_ROWMAX also the row maxima of S (fp32 [B,H,Nq]), which the
     backward of that mode needs: returns (O, LSE, row_max). ``o_ste`` (a bf16
     tensor shaped and strided like the output) also receives the
     straight-through output P Vq; pass it as the backward's ``o`` for the
-    additive straight-through delta."""
+    additive straight-through delta. With a block index and
+    ``validate_index``, the result of the library's device-side index check
+    is read back (a wait on the stream) and a failed check raises."""
     L = load()
     for n, t in (("q", q), ("k", k), ("v", v)):
         _check4(n, t)
@@ -253,14 +293,17 @@ def fwd(q, k, v, sm_scale=None, quant="qkvp", kv_block_idx=None, block_tokens=12
         _workspace(need, q.device)
     check(L.attnqat_fwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                         lse.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)))
+    if kv_block_idx is not None and validate_index:
+        _raise_if_bad_index(ws, stream)
     return (o, lse, row_max) if p_mode == P_ROWMAX else (o, lse)
 
 
 def bwd(q, k, v, o, lse, do, sm_scale=None, quant="qkvp", kv_block_idx=None, block_tokens=128,
         dq=None, dk=None, dv=None, workspace=None, stream=None, p_mode=P_NORMALISED,
-        row_max=None):
+        row_max=None, validate_index=True):
     """dQ, dK, dV (bf16) of Attn-QAT attention with straight-through quantizers
-    (p_mode=P_ROWMAX needs the forward's row_max)."""
+    (p_mode=P_ROWMAX needs the forward's row_max). ``validate_index`` as for
+    ``fwd``."""
     L = load()
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
         _check4(n, t)
@@ -283,6 +326,8 @@ def bwd(q, k, v, o, lse, do, sm_scale=None, quant="qkvp", kv_block_idx=None, blo
     check(L.attnqat_bwd(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                         lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                         dv.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)))
+    if kv_block_idx is not None and validate_index:
+        _raise_if_bad_index(ws, stream)
     return dq, dk, dv
 
 
@@ -420,7 +465,7 @@ class AttnQatFunction(torch.autograd.Function):
         q, k, v, o, lse, idx, row_max = ctx.saved_tensors
         do = do.contiguous()
         dq, dk, dv = bwd(q, k, v, o, lse, do, ctx.sm_scale, ctx.quant, idx, p_mode=ctx.p_mode,
-                         row_max=row_max)
+                         row_max=row_max, validate_index=False)  # the forward checked it
         return dq, dk, dv, None, None, None, None
 
 
@@ -431,8 +476,11 @@ def attention(q, k, v, sm_scale=None, quant="qkvp", kv_block_idx=None, p_mode=P_
 
 
 def effective_topk(num_blocks: int, sparsity: float = 0.9) -> int:
-    """Key blocks kept per query block: max(1, min(ceil((1 - sparsity) n), n))."""
-    return max(1, min(int(math.ceil((1.0 - sparsity) * num_blocks)), num_blocks))
+    """Key blocks kept per query block (the library's attnqat_effective_topk)."""
+    k = load().attnqat_effective_topk(int(num_blocks), float(sparsity))
+    if k < 0:
+        check(-k)
+    return k
 
 
 class VsaAttentionFunction(torch.autograd.Function):
@@ -443,7 +491,7 @@ class VsaAttentionFunction(torch.autograd.Function):
 
     @staticmethod
     def forward(ctx, q, k, v, gate, sm_scale, quant, kv_block_idx):
-        o_fine, lse = fwd(q, k, v, sm_scale, quant, kv_block_idx)
+        o_fine, lse = fwd(q, k, v, sm_scale, quant, kv_block_idx)  # checks the index
         o = vsa_fwd(q, k, v, gate, o_fine, sm_scale)
         ctx.save_for_backward(q, k, v, gate, o_fine, lse, kv_block_idx)
         ctx.sm_scale, ctx.quant = sm_scale, quant
@@ -453,7 +501,8 @@ class VsaAttentionFunction(torch.autograd.Function):
     def backward(ctx, do):
         q, k, v, gate, o_fine, lse, idx = ctx.saved_tensors
         do = do.contiguous()
-        dq, dk, dv = bwd(q, k, v, o_fine, lse, do, ctx.sm_scale, ctx.quant, idx)
+        dq, dk, dv = bwd(q, k, v, o_fine, lse, do, ctx.sm_scale, ctx.quant, idx,
+                         validate_index=False)  # the forward checked this index
         dq, dk, dv, dgate = vsa_bwd(q, k, v, gate, do, dq, dk, dv, ctx.sm_scale,
                                     want_dgate=ctx.needs_input_grad[3])
         return dq, dk, dv, dgate, None, None, None

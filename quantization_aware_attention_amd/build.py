@@ -29,10 +29,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; the Attn-QAT library needs ROCm's hipcc to build")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into LIB_PATH and return the path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
+# Machine probes for the benchmark (matrix-core rate and clock), kept out of
+# the attention library.
+PROBE_SOURCES = ["aq_probe.hip"]
+PROBE_PATH = os.path.join(PKG_DIR, "libaq_probe.so")
+
+
+def _compile(sources, out, verbose):
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = out + ".tmp"
     cmd = [hipcc()] + HIP_FLAGS + srcs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -43,7 +48,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
     if verbose and msgs:
         print(msgs)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library (LIB_PATH) and the benchmark's probe library
+    (PROBE_PATH); return LIB_PATH."""
+    _compile(SOURCES, LIB_PATH, verbose)
+    _compile(PROBE_SOURCES, PROBE_PATH, verbose)
     return LIB_PATH
 
 

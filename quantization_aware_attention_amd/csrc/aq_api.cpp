@@ -68,12 +68,14 @@ int hip_check(hipError_t e, const char* what) {
 enum Kind {
     K_FQ_D, K_FQ_N, K_TRANSPOSE, K_FWD_LSE, K_FWD_OUT, K_FWD_SINGLE, K_BWD_PRE, K_BWD_DKDV, K_BWD_DQ,
     K_BLOCK_POOL, K_BLOCK_TOPK, K_REVERSE_INDEX, K_VSA_POOL, K_VSA_COARSE, K_VSA_COMBINE,
-    K_VSA_GATE, K_VSA_COARSE_BWD, K_VSA_GRAD_ADD, K_MX_QUANT, K_MX_FWD, K_NUM
+    K_VSA_GATE, K_VSA_COARSE_BWD, K_VSA_GRAD_ADD, K_MX_QUANT, K_MX_FWD, K_CHECK_INDEX, K_POISON,
+    K_NUM
 };
 const char* const kKindName[K_NUM] = {
     "fq_axis_d", "fq_axis_n", "transpose_perm", "fwd_lse", "fwd_out", "fwd_single", "bwd_pre", "bwd_dkdv",
     "bwd_dq", "block_pool", "block_topk", "reverse_index", "vsa_pool", "vsa_coarse",
-    "vsa_combine", "vsa_gate_reduce", "vsa_coarse_bwd", "vsa_grad_add", "mx_quant", "mx_fwd"};
+    "vsa_combine", "vsa_gate_reduce", "vsa_coarse_bwd", "vsa_grad_add", "mx_quant", "mx_fwd",
+    "check_index", "poison_outputs"};
 
 constexpr int kMaxTimed = 65536;
 
@@ -150,10 +152,11 @@ struct RevArgs {
     int64_t BH;
     int nbq, nbk, topk;
     int32_t* order;
+    const int32_t* idx_err;
 };
 hipError_t do_reverse(const RevArgs& r, hipStream_t st) {
     return aq::launch_reverse_index(r.idx, r.q_list, r.q_count, r.BH, r.nbq, r.nbk, r.topk, r.order,
-                                    st);
+                                    r.idx_err, st);
 }
 
 int run_fq(bool axis_d, bool quant, const aq::FqArgs& a, hipStream_t st, const char* what) {
@@ -209,6 +212,10 @@ int check_tensor(const char* name, const void* p, const Strides& s, int64_t H, i
     return ATTNQAT_OK;
 }
 
+// Longest sequence (query or key tokens) the attention entry points accept.
+constexpr int64_t kMaxTokens = ATTNQAT_MAX_TOKENS;
+static_assert(kMaxTokens * 128 * 2 < (int64_t(1) << 31), "32-bit tile offsets");
+
 struct Plan {
     int64_t B, H, BH, Nq, Nk, D, Nq_pad, Nk_pad;
     Strides q, k, v, o, dout, dq, dk, dv;
@@ -231,9 +238,11 @@ int validate_problem(const attnqat_problem* p, Plan& pl) {
         return fail(ATTNQAT_E_INVALID, "sm_scale must be finite and > 0");
     if (p->quant_mask & ~ATTNQAT_QUANT_ALL)
         return fail(ATTNQAT_E_INVALID, "unknown quant_mask bits 0x%x", p->quant_mask);
-    // the kernels index tokens with 32-bit ints
-    if (p->Nq > (1 << 30) || p->Nk > (1 << 30) || p->B * p->H > (1 << 30))
-        return fail(ATTNQAT_E_INVALID, "sizes too large");
+    // the tile copies form 32-bit byte offsets of up to 128 rows of a
+    // transposed [D][N] operand: 128 x N x 2 bytes must stay below 2^31
+    if (p->Nq > kMaxTokens || p->Nk > kMaxTokens)
+        return fail(ATTNQAT_E_UNSUPPORTED, "sequence length above %lld tokens (Nq=%lld Nk=%lld)",
+                    (long long)kMaxTokens, (long long)p->Nq, (long long)p->Nk);
     // (batch, head) pairs index the second grid dimension of every kernel
     if (p->B * p->H > 65535)
         return fail(ATTNQAT_E_UNSUPPORTED, "B * H = %lld exceeds 65535",
@@ -287,8 +296,8 @@ int validate_problem(const attnqat_problem* p, Plan& pl) {
 
 // Workspace layout (bytes, each region 256-byte aligned).
 struct Layout {
-    size_t qw, kw, vw, kt, vt, dow, lse2, delta, qlist, qcount, korder, dowkv, lse2kv, deltakv,
-        total;
+    size_t flag, qw, kw, vw, kt, vt, dow, lse2, delta, qlist, qcount, korder, dowkv, lse2kv,
+        deltakv, total;
 };
 
 Layout layout(const Plan& pl, bool bwd) {
@@ -301,6 +310,7 @@ Layout layout(const Plan& pl, bool bwd) {
     };
     const size_t qb = (size_t)pl.BH * pl.Nq_pad * pl.D * 2;
     const size_t kb = (size_t)pl.BH * pl.Nk_pad * pl.D * 2;
+    L.flag = take(4);  // block-index check flag: offset 0 of every layout
     L.qw = take(qb);
     L.kw = take(kb);
     if (bwd) {
@@ -393,11 +403,48 @@ aq::AttnArgs attn_args(const attnqat_problem* p, const Plan& pl, char* ws, const
     a.pv_f16 = pl.f16_pv ? 1 : 0;
     if (pl.sparse) {
         a.kv_idx = p->kv_block_idx;
+        a.idx_err = (const int32_t*)(ws + L.flag);
         a.topk = p->topk;
         a.nbq = pl.nbq;
         a.nbk = pl.nbk;
     }
     return a;
+}
+
+// Block-sparse calls: check the caller's index on the device first; the
+// sparse kernels skip their work when it fails.
+struct CheckArgs {
+    const int32_t* idx;
+    int64_t rows;
+    int topk, nbk;
+    int32_t* flag;
+};
+hipError_t do_check(const CheckArgs& c, hipStream_t st) {
+    return aq::launch_check_index(c.idx, c.rows, c.topk, c.nbk, c.flag, st);
+}
+int check_index(const attnqat_problem* p, const Plan& pl, char* ws, const Layout& L,
+                hipStream_t st) {
+    const CheckArgs c{p->kv_block_idx, pl.BH * pl.nbq, p->topk, pl.nbk, (int32_t*)(ws + L.flag)};
+    return launch(K_CHECK_INDEX, st, thunk<CheckArgs, do_check>, &c, "block index check");
+}
+
+// ... and after the call, overwrite its outputs with NaN if the check failed.
+void poison_add(aq::PoisonArgs& a, void* t, const Strides& s, int64_t N) {
+    a.t[a.nt] = (uint16_t*)t;
+    a.sb[a.nt] = s.b;
+    a.sh[a.nt] = s.h;
+    a.sn[a.nt] = s.n;
+    a.N[a.nt] = N;
+    ++a.nt;
+}
+void poison_add_f32(aq::PoisonArgs& a, float* f, int64_t n) {
+    a.f[a.nf] = f;
+    a.fn[a.nf] = n;
+    ++a.nf;
+}
+int poison(const aq::PoisonArgs& a, hipStream_t st) {
+    return launch(K_POISON, st, thunk<aq::PoisonArgs, aq::launch_poison_outputs>, &a,
+                  "NaN fill after a failed index check");
 }
 
 }  // namespace
@@ -505,6 +552,7 @@ int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const vo
 
     hipStream_t st = (hipStream_t)stream;
     char* ws = (char*)workspace;
+    if (pl.sparse && (rc = check_index(p, pl, ws, L, st))) return rc;
     if ((rc = prepare_operands(pl, p->quant_mask, q, k, v, ws, L, false, st))) return rc;
     aq::AttnArgs a = attn_args(p, pl, ws, L);
     a.Vt = (const uint16_t*)(ws + L.vt);
@@ -522,10 +570,24 @@ int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const vo
         // no P quantizer: nothing needs the final LSE before P V
         if ((rc = launch(K_FWD_SINGLE, st, thunk<DimArgs, do_fwd_single>, &da, "forward")))
             return rc;
-        return ok();
+    } else {
+        if ((rc = launch(K_FWD_LSE, st, thunk<DimArgs, do_fwd_lse>, &da, "forward pass 1")))
+            return rc;
+        if ((rc = launch(K_FWD_OUT, st, thunk<DimArgs, do_fwd_out>, &da, "forward pass 2")))
+            return rc;
     }
-    if ((rc = launch(K_FWD_LSE, st, thunk<DimArgs, do_fwd_lse>, &da, "forward pass 1"))) return rc;
-    if ((rc = launch(K_FWD_OUT, st, thunk<DimArgs, do_fwd_out>, &da, "forward pass 2"))) return rc;
+    if (pl.sparse) {
+        aq::PoisonArgs pa{};
+        pa.flag = a.idx_err;
+        pa.BH = pl.BH;
+        pa.H = pl.H;
+        pa.D = (int)pl.D;
+        poison_add(pa, o, pl.o, pl.Nq);
+        if (p->o_ste) poison_add(pa, p->o_ste, pl.o, pl.Nq);
+        poison_add_f32(pa, lse, pl.BH * pl.Nq);
+        if (pl.rowmax_out) poison_add_f32(pa, p->row_max, pl.BH * pl.Nq);
+        if ((rc = poison(pa, st))) return rc;
+    }
     return ok();
 }
 
@@ -576,6 +638,7 @@ int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const vo
 
     hipStream_t st = (hipStream_t)stream;
     char* ws = (char*)workspace;
+    if (pl.sparse && (rc = check_index(p, pl, ws, L, st))) return rc;
     if ((rc = prepare_operands(pl, p->quant_mask, q, k, v, ws, L, true, st))) return rc;
     aq::PreArgs pa{};
     pa.o = (const uint16_t*)o;
@@ -626,7 +689,8 @@ int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const vo
         a.q_count = (const int32_t*)(ws + L.qcount);
         a.kv_order = (const int32_t*)(ws + L.korder);
         const RevArgs ra{p->kv_block_idx, (int32_t*)(ws + L.qlist), (int32_t*)(ws + L.qcount),
-                         pl.BH, pl.nbq, pl.nbk, p->topk, (int32_t*)(ws + L.korder)};
+                         pl.BH, pl.nbq, pl.nbk, p->topk, (int32_t*)(ws + L.korder),
+                         a.idx_err};
         if ((rc = launch(K_REVERSE_INDEX, st, thunk<RevArgs, do_reverse>, &ra,
                          "reverse block index")))
             return rc;
@@ -644,7 +708,45 @@ int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const vo
     if ((rc = launch(K_BWD_DKDV, st, thunk<DimArgs, do_bwd_dkdv>, &dkv, "backward dK/dV")))
         return rc;
     if ((rc = launch(K_BWD_DQ, st, thunk<DimArgs, do_bwd_dq>, &da, "backward dQ"))) return rc;
+    if (pl.sparse) {
+        aq::PoisonArgs pz{};
+        pz.flag = a.idx_err;
+        pz.BH = pl.BH;
+        pz.H = pl.H;
+        pz.D = (int)pl.D;
+        poison_add(pz, dq, pl.dq, pl.Nq);
+        poison_add(pz, dk, pl.dk, pl.Nk);
+        poison_add(pz, dv, pl.dv, pl.Nk);
+        if ((rc = poison(pz, st))) return rc;
+    }
     return ok();
+}
+
+int attnqat_block_idx_status(const void* workspace, int* invalid, void* stream) {
+    if (!workspace || !invalid) return fail(ATTNQAT_E_INVALID, "workspace or invalid is NULL");
+    if (((uintptr_t)workspace) % 256)
+        return fail(ATTNQAT_E_MISALIGNED, "workspace is not 256-byte aligned");
+    int rc = check_device();
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    int32_t flag = 0;
+    if ((rc = hip_check(hipMemcpyAsync(&flag, workspace, 4, hipMemcpyDeviceToHost, st),
+                        "hipMemcpyAsync")))
+        return rc;
+    if ((rc = hip_check(hipStreamSynchronize(st), "hipStreamSynchronize"))) return rc;
+    *invalid = flag != 0;
+    return ok();
+}
+
+int attnqat_effective_topk(int64_t num_blocks, double sparsity) {
+    if (num_blocks < 1 || num_blocks > (int64_t)1 << 30 || !(sparsity >= 0.0 && sparsity <= 1.0))
+        return -fail(ATTNQAT_E_INVALID, "num_blocks must be >= 1 and sparsity in [0, 1]");
+    const double kept = std::ceil((1.0 - sparsity) * (double)num_blocks);
+    int64_t k = (int64_t)kept;
+    if (k > num_blocks) k = num_blocks;
+    if (k < 1) k = 1;
+    ok();
+    return (int)k;
 }
 
 size_t attnqat_block_select_workspace_bytes(const attnqat_problem* p) {

@@ -174,17 +174,30 @@ __device__ __forceinline__ T* sel(B, T* b0, T* b1) {
     return B::value ? b1 : b0;
 }
 
+// Number of trailing tiles of a visiting order that can hold keys >= Nk and
+// must run masked: the last tile when it is partial (dense), or both tiles of
+// the last listed 128-token block when that block ends past Nk (sparse: the
+// list is ascending, so the sequence's partial last block, if selected, comes
+// last, and either of its two tiles may be partial or wholly past Nk).
+template <bool SPARSE, int T>
+__device__ __forceinline__ int masked_tiles(const int32_t* lst, int n_iter, int Nk) {
+    constexpr int PER = 128 / T;
+    if (n_iter <= 0) return 0;
+    if (SPARSE) return (lst[(n_iter - 1) / PER] * 128 + 128 > Nk) ? PER : 0;
+    return ((n_iter - 1) * T + T > Nk) ? 1 : 0;
+}
+
 // Double-buffered tile loop. issue(buf, it) starts the asynchronous copy of
 // tile it into buffer buf; body(buf, it, tail) consumes it; buf is a
 // compile-time 0 or 1 (the loop is unrolled by two). Full tiles run the
-// unmasked body; a partial last tile (last_partial) runs the masked body once,
+// unmasked body; the last n_masked tiles (at most two) run the masked body,
 // after the loop, so that only the unmasked body is live inside the loop.
 template <class Issue, class Body>
-__device__ __forceinline__ void tile_pipeline(int n_iter, bool last_partial, Issue issue,
+__device__ __forceinline__ void tile_pipeline(int n_iter, int n_masked, Issue issue,
                                               Body body) {
     using B0 = std::integral_constant<int, 0>;
     using B1 = std::integral_constant<int, 1>;
-    const int n_main = n_iter - (last_partial ? 1 : 0);
+    const int n_main = n_iter - n_masked;
     issue(B0{}, 0);
     int it = 0;
     for (; it + 1 < n_main; it += 2) {
@@ -204,11 +217,17 @@ __device__ __forceinline__ void tile_pipeline(int n_iter, bool last_partial, Iss
         body(B0{}, it, std::false_type{});
         ++it;
     }
-    if (last_partial) {
+    // masked tiles: tile `it` is in flight here, the next one is not
+    for (; it < n_iter; ++it) {
         wait_async();
         __syncthreads();
-        if (it & 1) body(B1{}, it, std::true_type{});
-        else body(B0{}, it, std::true_type{});
+        if (it & 1) {
+            if (it + 1 < n_iter) issue(B0{}, it + 1);
+            body(B1{}, it, std::true_type{});
+        } else {
+            if (it + 1 < n_iter) issue(B1{}, it + 1);
+            body(B0{}, it, std::true_type{});
+        }
     }
 }
 
@@ -340,6 +359,7 @@ struct FwdLse {
 
 template <int D, int NW, bool SPARSE, bool LAZY>
 __global__ __launch_bounds__(NW * 64) void fwd_lse_kernel(AttnArgs a) {
+    if (SPARSE && *a.idx_err) return;  // the block index failed its check
     constexpr int BN = FwdLse<D>::BN;
     static_assert(!SPARSE || NW == 4, "sparse workgroups cover one 128-query block");
     __shared__ __attribute__((aligned(1024))) uint16_t sK0[BN * D], sK1[BN * D];
@@ -361,7 +381,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_lse_kernel(AttnArgs a) {
     AsyncTile<BN, D, NW * 64> tk;
     tk.init(D, tid);
     tile_pipeline(
-        n_iter, tile_at(n_iter - 1) + BN > a.Nk,
+        n_iter, masked_tiles<SPARSE, BN>(lst, n_iter, a.Nk),
         [&](auto b, int it) { tk.issue(sel(b, sK0, sK1), Kb + (size_t)tile_at(it) * D); },
         [&](auto b, int it, auto tail) {
             FwdLse<D>::template block<decltype(tail)::value, LAZY>(sel(b, sK0, sK1), tile_at(it),
@@ -468,6 +488,7 @@ struct FwdOut {
 
 template <int D, bool QP, bool F16, int NW, bool SPARSE>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_out_kernel(AttnArgs a) {
+    if (SPARSE && *a.idx_err) return;  // the block index failed its check
     using F = FwdOut<D, QP, F16>;
     constexpr int BN = F::BN;
     static_assert(!SPARSE || NW == 4, "sparse workgroups cover one 128-query block");
@@ -502,7 +523,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_out_kernel(AttnA
     tk.init(D, tid);
     tv.init(a.Nk_pad, tid);
     tile_pipeline(
-        n_iter, tile_at(n_iter - 1) + BN > a.Nk,
+        n_iter, masked_tiles<SPARSE, BN>(lst, n_iter, a.Nk),
         [&](auto b, int it) {
             const int kt = tile_at(it);
             tk.issue(sel(b, &s0, &s1)->k, Kb + (size_t)kt * D);
@@ -582,6 +603,7 @@ struct FwdOutSte {
 
 template <int D, bool QP, int NW, bool SPARSE>
 __global__ __launch_bounds__(NW * 64) void fwd_out_ste_kernel(AttnArgs a) {
+    if (SPARSE && *a.idx_err) return;  // the block index failed its check
     using F = FwdOutSte<D, QP>;
     constexpr int BN = F::BN;
     static_assert(!SPARSE || NW == 4, "sparse workgroups cover one 128-query block");
@@ -616,7 +638,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_out_ste_kernel(AttnArgs a) {
     tk.init(D, tid);
     tv.init(a.Nk_pad, tid);
     tile_pipeline(
-        n_iter, tile_at(n_iter - 1) + BN > a.Nk,
+        n_iter, masked_tiles<SPARSE, BN>(lst, n_iter, a.Nk),
         [&](auto b, int it) {
             const int kt = tile_at(it);
             tk.issue(sel(b, &s0, &s1)->k, Kb + (size_t)kt * D);
@@ -648,6 +670,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_out_ste_kernel(AttnArgs a) {
 constexpr float kLazyLog2 = 8.0f;
 template <int D, int NW, bool SPARSE>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_single_kernel(AttnArgs a) {
+    if (SPARSE && *a.idx_err) return;  // the block index failed its check
     using F = FwdOutSte<D, false>;
     constexpr int BN = F::BN;
     static_assert(!SPARSE || NW == 4, "sparse workgroups cover one 128-query block");
@@ -682,7 +705,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_single_kernel(At
     tk.init(D, tid);
     tv.init(a.Nk_pad, tid);
     tile_pipeline(
-        n_iter, tile_at(n_iter - 1) + BN > a.Nk,
+        n_iter, masked_tiles<SPARSE, BN>(lst, n_iter, a.Nk),
         [&](auto b, int it) {
             const int kt = tile_at(it);
             tk.issue(sel(b, &s0, &s1)->k, Kb + (size_t)kt * D);
@@ -830,6 +853,7 @@ struct BwdDq {
 
 template <int D, int NW, int QB, bool SPARSE>
 __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
+    if (SPARSE && *a.idx_err) return;  // the block index failed its check
     using DQ = BwdDq<D, QB>;
     constexpr int BN = DQ::BN, NT = NW * 64;
     struct Buf {
@@ -876,7 +900,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
     tk.init(D, tid);
     tt.init(a.Nk_pad, tid);
     tile_pipeline(
-        n_iter, tile_at(n_iter - 1) + BN > a.Nk,
+        n_iter, masked_tiles<SPARSE, BN>(lst, n_iter, a.Nk),
         [&](auto b, int it) {
             const int kt = tile_at(it);
             Buf* t = sel(b, &s0, &s1);
@@ -922,6 +946,7 @@ __device__ __forceinline__ int ktr_lane(int db, int t, int lane) {
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_dq_sparse_kernel(AttnArgs a) {
+    if (*a.idx_err) return;  // the block index failed its check
     using DQ = BwdDq<D, 1>;
     constexpr int BN = 64, NT = 256, NW = 4;
     struct Buf {
@@ -996,7 +1021,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_sparse_kernel(AttnArgs a) {
         }
     };
     tile_pipeline(
-        n_iter, tile_at(n_iter - 1) + BN > a.Nk,
+        n_iter, masked_tiles<true, BN>(lst, n_iter, a.Nk),
         [&](auto b, int it) {
             const int kt = tile_at(it);
             Buf* t = sel(b, &s0, &s1);
@@ -1155,6 +1180,7 @@ __device__ __forceinline__ u32x4 aop_tr(const uint16_t* t, int sb, int g, const 
 
 template <int D, bool QP, bool SPARSE>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnArgs a) {
+    if (SPARSE && *a.idx_err) return;  // the block index failed its check
     using Tile = KVTile<D>;
     constexpr int BM = Tile::BM, KW = 128;
     // loads per wave per tile: Qq and dO rows (BM * D * 2 bytes each, in 1 KB

@@ -71,6 +71,7 @@ struct AttnArgs {
     const int32_t* q_list;   // [BH][nbk][nbq] reverse index (query blocks per key block)
     const int32_t* q_count;  // [BH][nbk]
     const int32_t* kv_order; // [BH][nbk] key blocks of each head by descending count
+    const int32_t* idx_err;  // block-index check flag: the sparse kernels skip their work if set
     int topk;
     int nbq, nbk;
     int64_t H;
@@ -171,6 +172,24 @@ hipError_t launch_mx_fwd(const MxArgs& a, hipStream_t st);
 hipError_t launch_block_pool(const SelectArgs& a, hipStream_t st);
 hipError_t launch_block_topk(const SelectArgs& a, hipStream_t st);
 hipError_t launch_reverse_index(const int32_t* idx, int32_t* q_list, int32_t* q_count, int64_t BH,
-                                int nbq, int nbk, int topk, int32_t* kv_order, hipStream_t st);
+                                int nbq, int nbk, int topk, int32_t* kv_order,
+                                const int32_t* idx_err, hipStream_t st);
+
+// Block-index check (flag = 1 when an entry is out of range or a row is not
+// strictly ascending) and the NaN fill of a call's outputs when it is set.
+struct PoisonArgs {
+    const int32_t* flag;
+    uint16_t* t[4];  // strided bf16 [B,H,N[i],D] token tensors
+    int64_t sb[4], sh[4], sn[4], N[4];
+    int nt;
+    float* f[2];  // contiguous fp32 arrays of fn[i] elements
+    int64_t fn[2];
+    int nf;
+    int64_t BH, H;
+    int D;
+};
+hipError_t launch_check_index(const int32_t* idx, int64_t rows, int topk, int nbk, int32_t* flag,
+                              hipStream_t st);
+hipError_t launch_poison_outputs(const PoisonArgs& a, hipStream_t st);
 
 }  // namespace aq

@@ -99,8 +99,10 @@ __global__ __launch_bounds__(256) void block_topk_kernel(SelectArgs a) {
 __global__ __launch_bounds__(256) void reverse_index_kernel(const int32_t* __restrict__ idx,
                                                             int32_t* __restrict__ q_list,
                                                             int32_t* __restrict__ q_count,
-                                                            int64_t BH, int nbq, int nbk, int topk) {
+                                                            int64_t BH, int nbq, int nbk, int topk,
+                                                            const int32_t* __restrict__ idx_err) {
     __shared__ int wsum[4];
+    if (*idx_err) return;
     const int j = blockIdx.x;
     const int64_t bh = blockIdx.y, gi = bh * nbk + j;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -135,7 +137,9 @@ __global__ __launch_bounds__(256) void reverse_index_kernel(const int32_t* __res
 // Key blocks of each head ordered by descending selection count (ties to
 // the lower index): one workgroup per head, each thread ranks its blocks.
 __global__ __launch_bounds__(256) void block_order_kernel(const int32_t* __restrict__ q_count,
-                                                          int32_t* __restrict__ order, int nbk) {
+                                                          int32_t* __restrict__ order, int nbk,
+                                                          const int32_t* __restrict__ idx_err) {
+    if (*idx_err) return;
     const int64_t bh = blockIdx.x;
     const int32_t* c = q_count + bh * nbk;
     for (int j = threadIdx.x; j < nbk; j += 256) {
@@ -147,6 +151,56 @@ __global__ __launch_bounds__(256) void block_order_kernel(const int32_t* __restr
         }
         order[bh * nbk + rank] = j;
     }
+}
+
+// Check of a caller's block index (int32 [rows][topk]): every entry in
+// [0, nbk) and every row strictly ascending. One workgroup, so that the
+// verdict is written by one thread after a barrier that ORs every thread's
+// finding: flag = 1 if the index breaks a rule, else 0. The sparse attention
+// kernels read the flag and skip their work when it is set (their loads
+// would otherwise follow the bad entries out of the operand buffers).
+__global__ __launch_bounds__(1024) void check_index_kernel(const int32_t* __restrict__ idx,
+                                                           int64_t rows, int topk, int nbk,
+                                                           int32_t* __restrict__ flag) {
+    int bad = 0;
+    const int64_t n = rows * topk;
+    for (int64_t e = threadIdx.x; e < n; e += 1024) {
+        const int v = idx[e];
+        bad |= (v < 0 || v >= nbk) ? 1 : 0;
+        if ((int)(e % topk) != topk - 1) bad |= (v < idx[e + 1]) ? 0 : 1;
+    }
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) *flag = bad ? 1 : 0;
+}
+
+// When the index check failed, every output of the call is overwritten with
+// NaN (bf16 0x7FC0 in the strided token tensors, fp32 NaN in the statistics),
+// so that a caller who does not read the flag cannot take stale memory for a
+// result. A set flag is rare; the common path reads it and returns.
+__global__ __launch_bounds__(256) void poison_outputs_kernel(PoisonArgs a) {
+    if (*a.flag == 0) return;
+    const int64_t tid = (int64_t)blockIdx.x * 256 + threadIdx.x, nth = (int64_t)gridDim.x * 256;
+    for (int i = 0; i < a.nt; ++i) {
+        const int64_t rows = a.BH * a.N[i];
+        for (int64_t r = tid; r < rows; r += nth) {
+            const int64_t bh = r / a.N[i], n = r % a.N[i], b = bh / a.H, h = bh % a.H;
+            uint16_t* row = a.t[i] + b * a.sb[i] + h * a.sh[i] + n * a.sn[i];
+            for (int d = 0; d < a.D; ++d) row[d] = 0x7FC0;
+        }
+    }
+    for (int i = 0; i < a.nf; ++i)
+        for (int64_t j = tid; j < a.fn[i]; j += nth) a.f[i][j] = __builtin_nanf("");
+}
+
+hipError_t launch_check_index(const int32_t* idx, int64_t rows, int topk, int nbk, int32_t* flag,
+                              hipStream_t st) {
+    check_index_kernel<<<1, 1024, 0, st>>>(idx, rows, topk, nbk, flag);
+    return hipGetLastError();
+}
+
+hipError_t launch_poison_outputs(const PoisonArgs& a, hipStream_t st) {
+    poison_outputs_kernel<<<256, 256, 0, st>>>(a);
+    return hipGetLastError();
 }
 
 hipError_t launch_block_pool(const SelectArgs& a, hipStream_t st) {
@@ -162,10 +216,11 @@ hipError_t launch_block_topk(const SelectArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_reverse_index(const int32_t* idx, int32_t* q_list, int32_t* q_count, int64_t BH,
-                                int nbq, int nbk, int topk, int32_t* kv_order, hipStream_t st) {
+                                int nbq, int nbk, int topk, int32_t* kv_order,
+                                const int32_t* idx_err, hipStream_t st) {
     reverse_index_kernel<<<dim3(nbk, (unsigned)BH), 256, 0, st>>>(idx, q_list, q_count, BH, nbq,
-                                                                 nbk, topk);
-    block_order_kernel<<<(unsigned)BH, 256, 0, st>>>(q_count, kv_order, nbk);
+                                                                 nbk, topk, idx_err);
+    block_order_kernel<<<(unsigned)BH, 256, 0, st>>>(q_count, kv_order, nbk, idx_err);
     return hipGetLastError();
 }
 

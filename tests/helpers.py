@@ -68,5 +68,12 @@ def rel_l2_best_rows(got: np.ndarray, cands) -> float:
     return float(np.sqrt(err2.sum()) / n)
 
 
+def best_candidate(got: np.ndarray, cands) -> np.ndarray:
+    """Per row of ``got``, the index of the closest of ``cands`` (the first
+    one on ties), as ``rel_l2_best_rows`` chooses it."""
+    err2 = np.stack([np.sum((got - c) ** 2, axis=-1) for c in cands])
+    return np.argmin(err2, axis=0)
+
+
 def tol_for(mask: int) -> float:
     return TOL_QUANT if mask else TOL_PLAIN

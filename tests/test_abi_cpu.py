@@ -54,7 +54,7 @@ def test_exports_every_declared_function(L):
     assert declared == set(qaa.EXPORTS), declared ^ set(qaa.EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.attnqat_abi_version() == 4
+    assert L.attnqat_abi_version() == 5
 
 
 def test_status_strings(L):
@@ -281,3 +281,57 @@ def test_mxfp4_validation(L):
     assert _mx(L, p, o=A) == E_INVALID          # output overlaps q
     assert _mx(L, p, ws=4 * A) == E_INVALID     # workspace overlaps o
     assert _mx(L, p, q=0) == E_INVALID
+
+
+def test_sequence_length_cap(L):
+    """Sequences beyond ATTNQAT_MAX_TOKENS are rejected as unsupported before
+    any HIP call (the tile copies form 32-bit byte offsets of up to 128 rows of
+    a transposed operand); the cap itself is accepted."""
+    cap = qaa.MAX_TOKENS
+    text = open(HEADER).read()
+    assert f"#define ATTNQAT_MAX_TOKENS {cap}" in text
+    assert 128 * cap * 2 < 2 ** 31
+    for kw in (dict(Nq=cap + 1), dict(Nk=cap + 1), dict(Nq=1 << 30, Nk=1 << 30)):
+        p = _prob(**kw)
+        assert _fwd(L, p) == E_UNSUPPORTED
+        assert b"sequence length" in L.attnqat_last_error()
+        assert _bwd(L, p) == E_UNSUPPORTED
+        assert _mx(L, p) == E_UNSUPPORTED
+        assert L.attnqat_fwd_workspace_bytes(ctypes.byref(p)) == 0
+        assert L.attnqat_bwd_workspace_bytes(ctypes.byref(p)) == 0
+    ok = _prob(Nq=cap, Nk=cap)
+    assert L.attnqat_fwd_workspace_bytes(ctypes.byref(ok)) > 0
+    assert L.attnqat_bwd_workspace_bytes(ctypes.byref(ok)) > 0
+
+
+def test_effective_topk_matches_the_oracle_formula(L):
+    """The library's selection count is the pages' formula, as the oracle
+    states it, over a grid of block counts and sparsities."""
+    from oracle import block_sparse as bsp
+    for n in (1, 2, 5, 6, 10, 100, 244, 256, 1000, 1024):
+        for sp in (0.0, 0.1, 0.5, 0.75, 0.9, 0.95, 0.99, 1.0):
+            assert L.attnqat_effective_topk(n, sp) == bsp.effective_topk(n, sp), (n, sp)
+    assert L.attnqat_effective_topk(256, 0.9) == 26
+    assert L.attnqat_effective_topk(0, 0.9) == -E_INVALID
+    assert L.attnqat_effective_topk(10, 1.5) == -E_INVALID
+    assert L.attnqat_effective_topk(10, float("nan")) == -E_INVALID
+    assert qaa.effective_topk(256, 0.9) == 26
+
+
+def test_block_idx_status_argument_checks(L):
+    flag = ctypes.c_int(0)
+    assert L.attnqat_block_idx_status(None, ctypes.byref(flag), None) == E_INVALID
+    assert L.attnqat_block_idx_status(A, None, None) == E_INVALID
+    assert L.attnqat_block_idx_status(A + 16, ctypes.byref(flag), None) == E_MISALIGNED
+
+
+def test_workspace_starts_with_the_index_flag(L):
+    """Both layouts keep the block-index check flag at offset 0 (one 256-byte
+    region), which attnqat_block_idx_status reads: the sparse forward's
+    workspace is the dense one's."""
+    dense = _prob(Nq=1024, Nk=1024)
+    sparse = _prob(Nq=1024, Nk=1024, kv_block_idx=30 * A, topk=3)
+    assert (L.attnqat_fwd_workspace_bytes(ctypes.byref(sparse)) ==
+            L.attnqat_fwd_workspace_bytes(ctypes.byref(dense)))
+    # operands: Qq, Kq, Vq, Vq^T of 2 heads x 1024 tokens x 64 bf16, plus the flag
+    assert L.attnqat_fwd_workspace_bytes(ctypes.byref(dense)) == 256 + 4 * 2 * 1024 * 64 * 2

@@ -71,3 +71,92 @@ def test_sparse_all_blocks_equals_dense(gpu_lib):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     for a, b in zip(d1, d2):
         assert torch.equal(a, b)
+
+
+def _index_with_last_block(seed, B, H, nbq, nbk, topk):
+    """Ascending rows of `topk` key blocks, each holding the sequence's last
+    (partial) block, so that every query block visits the masked tail."""
+    rs = np.random.RandomState(seed)
+    idx = np.empty((B, H, nbq, topk), np.int32)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nbq):
+                rest = rs.choice(nbk - 1, topk - 1, replace=False)
+                idx[b, h, i] = np.sort(np.concatenate([rest, [nbk - 1]]))
+    return idx
+
+
+@pytest.mark.parametrize("N,D,topk,mask", [(1050, 128, 3, 15), (1025, 64, 2, 15),
+                                           (1100, 128, 4, 15), (1050, 64, 3, 0),
+                                           (129, 128, 1, 15)])
+def test_sparse_partial_last_block(gpu_lib, N, D, topk, mask):
+    """The last key block holds N % 128 keys (26, 1, 76, 26, 1): both of its
+    64-key tiles run masked whether the first or only the second is partial,
+    so keys past N add nothing to LSE, P or the gradients."""
+    bits = _inputs(300 + N + D, (1, 2, N, D), 1.5)
+    f = {k: to_f64(v) for k, v in bits.items()}
+    nb = -(-N // 128)
+    idx = _index_with_last_block(N + topk, 1, 2, nb, nb, topk)
+    sc = 1.0 / np.sqrt(D)
+    O, L = bsp.forward(f["q"], f["k"], f["v"], sc, idx, 128, mask)
+    dq, dk, dv = bsp.backward(f["q"], f["k"], f["v"], f["do"], sc, idx, 128, mask,
+                              bf16_round(O), L)
+    t = {k: to_dev(v) for k, v in bits.items()}
+    it = torch.from_numpy(idx).to("cuda")
+    o, lse = gpu_lib.fwd(t["q"], t["k"], t["v"], sc, mask, it)
+    gdq, gdk, gdv = gpu_lib.bwd(t["q"], t["k"], t["v"], o, lse, t["do"], sc, mask, it)
+    torch.cuda.synchronize()
+    errs = {"o": rel_l2(dev_f64(o), O), "dq": rel_l2(dev_f64(gdq), dq, exact_zero=False),
+            "dk": rel_l2(dev_f64(gdk), dk, exact_zero=False), "dv": rel_l2(dev_f64(gdv), dv)}
+    lse_err = float(np.abs(lse.cpu().numpy() - L).max())
+    msg = f"sparse tail N={N} D={D} topk={topk} mask={mask} {errs} lse {lse_err:.2e}"
+    print(msg, flush=True)
+    assert lse_err <= TOL_LSE, msg
+    for e in errs.values():
+        assert e <= tol_for(mask), msg
+
+
+@pytest.mark.parametrize("fault", ["out_of_range", "negative", "descending", "duplicate"])
+def test_bad_block_index_is_caught_on_the_device(gpu_lib, fault):
+    """An index entry outside [0, nbk) or a row that is not strictly ascending
+    is found by the library's device-side check: no sparse kernel follows it,
+    the outputs are NaN, and the binding raises."""
+    N, D, topk = 512, 64, 2
+    bits = _inputs(11, (1, 2, N, D))
+    t = {k: to_dev(v) for k, v in bits.items()}
+    idx = np.tile(np.array([0, 2], np.int32), (1, 2, 4, 1))
+    bad = {"out_of_range": (1, 3, 1, 4), "negative": (0, 1, 0, -1),
+           "descending": (0, 0, 0, 3), "duplicate": (1, 1, 0, 2)}[fault]
+    idx[0, bad[0], bad[1], bad[2]] = bad[3]
+    it = torch.from_numpy(idx).to("cuda")
+    with pytest.raises(gpu_lib.AttnQatError, match="kv_block_idx"):
+        gpu_lib.fwd(t["q"], t["k"], t["v"], 0.125, 15, it)
+    o, lse = gpu_lib.fwd(t["q"], t["k"], t["v"], 0.125, 15, it, validate_index=False)
+    good = torch.from_numpy(np.tile(np.array([0, 2], np.int32), (1, 2, 4, 1))).to("cuda")
+    og, lg = gpu_lib.fwd(t["q"], t["k"], t["v"], 0.125, 15, good)
+    with pytest.raises(gpu_lib.AttnQatError, match="kv_block_idx"):
+        gpu_lib.bwd(t["q"], t["k"], t["v"], og, lg, t["do"], 0.125, 15, it)
+    grads = gpu_lib.bwd(t["q"], t["k"], t["v"], og, lg, t["do"], 0.125, 15, it,
+                        validate_index=False)
+    torch.cuda.synchronize()
+    assert torch.isnan(o.float()).all() and torch.isnan(lse).all()
+    for g in grads:
+        assert torch.isnan(g.float()).all()
+    # a valid index afterwards runs normally on the same workspace size
+    assert torch.isfinite(og.float()).all() and torch.isfinite(lg).all()
+
+
+def test_block_index_layout_checks(gpu_lib):
+    """int64 indices (what torch.topk returns), a wrong shape, or a
+    non-contiguous view are rejected by the binding before any call."""
+    bits = _inputs(12, (1, 1, 256, 64))
+    t = {k: to_dev(v) for k, v in bits.items()}
+    good = torch.zeros((1, 1, 2, 1), dtype=torch.int32, device="cuda")
+    strided = torch.zeros((1, 1, 2, 2), dtype=torch.int32, device="cuda")[..., :1]
+    assert not strided.is_contiguous()
+    for bad in (good.long(), good[:, :, :1], strided, good.cpu()):
+        with pytest.raises(gpu_lib.AttnQatError, match="kv_block_idx"):
+            gpu_lib.fwd(t["q"], t["k"], t["v"], 0.125, 15, bad)
+    o, lse = gpu_lib.fwd(t["q"], t["k"], t["v"], 0.125, 15, good)
+    torch.cuda.synchronize()
+    assert torch.isfinite(lse).all()

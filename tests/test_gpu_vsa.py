@@ -163,3 +163,39 @@ def test_vsa_autograd_matches_entry_points(gpu_lib):
     for n, ref in (("q", dq), ("k", dk), ("v", dv), ("g", dg)):
         assert torch.equal(leaves[n].grad, ref), n
     assert gpu_lib.effective_topk(6, 0.9) == 1 and gpu_lib.effective_topk(256, 0.9) == 26
+
+
+def test_vsa_pipeline_partial_last_block(gpu_lib):
+    """1,050 tokens (a last block of 26) with that block selected by every
+    query block: the fine branch's masked tail and the coarse branch's
+    partial-block means together, forward and backward."""
+    N, D, topk, mask = 1050, 128, 3, 15
+    bits = _bits(333, 1, 2, N, N, D)
+    t = {k: to_dev(v) for k, v in bits.items()}
+    f = {k: to_f64(v) for k, v in bits.items()}
+    sc = 1.0 / np.sqrt(D)
+    nb = -(-N // 128)
+    rs = np.random.RandomState(5)
+    idx = np.empty((1, 2, nb, topk), np.int32)
+    for h in range(2):
+        for i in range(nb):
+            idx[0, h, i] = np.sort(np.concatenate([rs.choice(nb - 1, topk - 1, replace=False),
+                                                   [nb - 1]]))
+    it = torch.from_numpy(idx).to("cuda")
+    of, lse = gpu_lib.fwd(t["q"], t["k"], t["v"], sc, mask, it)
+    o = gpu_lib.vsa_fwd(t["q"], t["k"], t["v"], t["g"], of, sc)
+    dq, dk, dv = gpu_lib.bwd(t["q"], t["k"], t["v"], of, lse, t["do"], sc, mask, it)
+    _, _, _, dg = gpu_lib.vsa_bwd(t["q"], t["k"], t["v"], t["g"], t["do"], dq, dk, dv, sc)
+    torch.cuda.synchronize()
+    O, Of, L = vsa.forward(f["q"], f["k"], f["v"], f["g"], sc, idx, 128, mask)
+    rq, rk, rv, rg = vsa.backward(f["q"], f["k"], f["v"], f["g"], f["do"], sc, idx, 128, mask,
+                                  bf16_round(Of), L)
+    errs = {"o": rel_l2(dev_f64(o), O, exact_zero=False),
+            "dq": rel_l2(dev_f64(dq), rq, exact_zero=False),
+            "dk": rel_l2(dev_f64(dk), rk, exact_zero=False),
+            "dv": rel_l2(dev_f64(dv), rv, exact_zero=False),
+            "dg": rel_l2(dev_f64(dg), rg, exact_zero=False)}
+    msg = _report(f"pipeline N={N} partial last block", errs)
+    assert float(np.abs(lse.cpu().numpy() - L).max()) <= 1e-3, msg
+    for e in errs.values():
+        assert e <= TOL_QUANT, msg
