@@ -186,6 +186,22 @@ size_t attnqat_fwd_workspace_bytes(const attnqat_problem* p);
 int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const void* v, void* o,
                 float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * attnqat_fwd without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation. Same arguments, results and errors as attnqat_fwd
+ * (the caller still passes every input and output); the scratch is a fixed
+ * 64 MiB device buffer inside the library, one per GPU, held until the
+ * process ends. The call itself allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine). Problems whose attnqat_fwd_workspace_bytes
+ * exceed 67108864 are rejected with ATTNQAT_E_UNSUPPORTED. Every call on a
+ * GPU shares that GPU's buffer, which keeps the last call's contents (the
+ * forward writes every scratch byte it reads, so nothing needs clearing):
+ * calls that overlap on one GPU, from several streams or threads, race.
+ */
+int attnqat_fwd_noalloc(const attnqat_problem* p, const void* q, const void* k, const void* v,
+                        void* o, float* lse, void* stream);
+
 /* Workspace bytes attnqat_bwd needs for problem p. */
 size_t attnqat_bwd_workspace_bytes(const attnqat_problem* p);
 

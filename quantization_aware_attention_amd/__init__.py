@@ -54,8 +54,9 @@ EXPORTS = [
     "attnqat_block_select", "attnqat_vsa_workspace_bytes", "attnqat_vsa_fwd", "attnqat_vsa_bwd",
     "attnqat_mxfp4_fwd_workspace_bytes", "attnqat_mxfp4_fwd",
     "attnqat_profile_enable", "attnqat_profile_read", "attnqat_block_idx_status",
-    "attnqat_effective_topk",
+    "attnqat_effective_topk", "attnqat_fwd_noalloc",
 ]
+NOALLOC_SCRATCH_BYTES = 64 << 20
 MAX_TOKENS = 4194304
 
 _lib = None
@@ -101,6 +102,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.attnqat_fwd_workspace_bytes.argtypes = [pp]
     lib.attnqat_fwd.restype = ctypes.c_int
     lib.attnqat_fwd.argtypes = [pp, P, P, P, P, P, P, SZ, V]
+    lib.attnqat_fwd_noalloc.restype = ctypes.c_int
+    lib.attnqat_fwd_noalloc.argtypes = [pp, P, P, P, P, P, V]
     lib.attnqat_bwd_workspace_bytes.restype = SZ
     lib.attnqat_bwd_workspace_bytes.argtypes = [pp]
     lib.attnqat_bwd.restype = ctypes.c_int
@@ -296,6 +299,24 @@ def fwd(q, k, v, sm_scale=None, quant="qkvp", kv_block_idx=None, block_tokens=12
     if kv_block_idx is not None and validate_index:
         _raise_if_bad_index(ws, stream)
     return (o, lse, row_max) if p_mode == P_ROWMAX else (o, lse)
+
+
+def fwd_noalloc(q, k, v, o, lse, sm_scale=None, quant="qkvp", kv_block_idx=None,
+                block_tokens=128, stream=None, p_mode=P_NORMALISED, row_max=None, o_ste=None):
+    """attnqat_fwd_noalloc: the forward into the caller's o (bf16) and lse
+    (fp32 [B,H,Nq]) with the library's fixed device scratch instead of a
+    workspace (for code that must not allocate, e.g. under graph capture);
+    o, lse (and row_max, o_ste) must be preallocated."""
+    L = load()
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check4(n, t)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(q.shape[-1])
+    p = make_problem(q, k, sm_scale, quant, v=v, o=o, kv_block_idx=kv_block_idx,
+                     block_tokens=block_tokens, p_mode=p_mode, row_max=row_max, o_ste=o_ste)
+    check(L.attnqat_fwd_noalloc(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                o.data_ptr(), lse.data_ptr(), _stream(stream)))
+    return o, lse
 
 
 def bwd(q, k, v, o, lse, do, sm_scale=None, quant="qkvp", kv_block_idx=None, block_tokens=128,

@@ -11,7 +11,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libattnqat.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["aq_prep.hip", "aq_attn.hip", "aq_select.hip", "aq_vsa.hip", "aq_mx.hip", "aq_api.cpp"]
+SOURCES = ["aq_prep.hip", "aq_attn.hip", "aq_select.hip", "aq_vsa.hip", "aq_mx.hip",
+           "aq_noalloc.hip", "aq_api.cpp"]
 
 # Packed fp32 VALU instructions are disabled on purpose: ordinary float code is
 # compiled to scalar-lane VALU operations only.

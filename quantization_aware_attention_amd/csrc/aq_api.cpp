@@ -591,6 +591,26 @@ int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const vo
     return ok();
 }
 
+int attnqat_fwd_noalloc(const attnqat_problem* p, const void* q, const void* k, const void* v,
+                        void* o, float* lse, void* stream) {
+    Plan pl;
+    int rc = validate_problem(p, pl);
+    if (rc) return rc;
+    const size_t need = layout(pl, false).total;
+    if (need > aq::kNoAllocScratchBytes)
+        return fail(ATTNQAT_E_UNSUPPORTED,
+                    "attnqat_fwd_noalloc: this problem needs %zu bytes of scratch; the fixed "
+                    "device buffer holds %zu (use attnqat_fwd with a workspace)",
+                    need, aq::kNoAllocScratchBytes);
+    if ((rc = check_device())) return rc;
+    int dev = 0;
+    if ((rc = hip_check(hipGetDevice(&dev), "hipGetDevice"))) return rc;
+    void* ws = nullptr;
+    if ((rc = hip_check(aq::noalloc_scratch(dev, &ws), "hipGetSymbolAddress of the scratch")))
+        return rc;
+    return attnqat_fwd(p, q, k, v, o, lse, ws, aq::kNoAllocScratchBytes, stream);
+}
+
 int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const void* v,
                 const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
                 void* workspace, size_t workspace_bytes, void* stream) {

@@ -8,6 +8,11 @@ namespace aq {
 // Tile sizes shared by the host planner and the kernels.
 constexpr int kTileN = 256;  // token padding granularity of every workspace operand
 
+// Size of the fixed device scratch behind attnqat_fwd_noalloc (aq_noalloc.hip)
+// and the lookup of its address on the current device.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(int dev, void** out);
+
 struct FqArgs {
     const uint16_t* x;
     int64_t xsb, xsh, xsn;

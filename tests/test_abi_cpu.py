@@ -335,3 +335,18 @@ def test_workspace_starts_with_the_index_flag(L):
             L.attnqat_fwd_workspace_bytes(ctypes.byref(dense)))
     # operands: Qq, Kq, Vq, Vq^T of 2 heads x 1024 tokens x 64 bf16, plus the flag
     assert L.attnqat_fwd_workspace_bytes(ctypes.byref(dense)) == 256 + 4 * 2 * 1024 * 64 * 2
+
+
+def test_noalloc_host_checks(L):
+    """attnqat_fwd_noalloc validates like attnqat_fwd and rejects, before any
+    HIP call, a problem whose workspace would not fit its fixed scratch."""
+    assert _fwd_noalloc(L, _prob(D=96)) == E_UNSUPPORTED
+    assert _fwd_noalloc(L, _prob(B=0)) == E_INVALID
+    big = _prob(H=64, Nq=4096, Nk=4096, D=128)
+    assert L.attnqat_fwd_workspace_bytes(ctypes.byref(big)) > qaa.NOALLOC_SCRATCH_BYTES
+    assert _fwd_noalloc(L, big) == E_UNSUPPORTED
+    assert b"scratch" in L.attnqat_last_error()
+
+
+def _fwd_noalloc(L, p, q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A):
+    return L.attnqat_fwd_noalloc(ctypes.byref(p), q, k, v, o, lse, None)
