@@ -96,6 +96,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sparse", action="store_true",
                     help="skip the block-sparse VSA step at its own configuration")
+    ap.add_argument("--main-only", action="store_true",
+                    help="time the metric's step only (no standalone kernels, variants, other "
+                         "workloads, probes or CPU oracle)")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the timing of the other workloads (tiny, DiT, tail)")
     ap.add_argument("--cpu-rows", type=int, default=8192,
@@ -357,6 +360,10 @@ def main():
     }
     # Standalone fake quantization of one input (HBM-bound): 4 bytes per
     # element (2 read, 2 written), along d (Q's layout) and along tokens (V's).
+    if args.main_only:
+        out["cpu_baseline"] = None
+        print(json.dumps(out), flush=True)
+        return
     # Every launch below follows a 1 GiB fill of a scratch buffer (outside the
     # timed events), which evicts the 256 MB last-level cache and the L2s, so
     # the GB/s are HBM figures, not cache figures.

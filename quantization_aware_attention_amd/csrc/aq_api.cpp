@@ -310,7 +310,7 @@ Layout layout(const Plan& pl, bool bwd) {
     };
     const size_t qb = (size_t)pl.BH * pl.Nq_pad * pl.D * 2;
     const size_t kb = (size_t)pl.BH * pl.Nk_pad * pl.D * 2;
-    L.flag = take(4);  // block-index check flag: offset 0 of every layout
+    L.flag = take(256);  // block-index check: flag word at offset 0, then 63 partial words
     L.qw = take(qb);
     L.kw = take(kb);
     if (bwd) {

@@ -154,23 +154,38 @@ __global__ __launch_bounds__(256) void block_order_kernel(const int32_t* __restr
 }
 
 // Check of a caller's block index (int32 [rows][topk]): every entry in
-// [0, nbk) and every row strictly ascending. One workgroup, so that the
-// verdict is written by one thread after a barrier that ORs every thread's
-// finding: flag = 1 if the index breaks a rule, else 0. The sparse attention
-// kernels read the flag and skip their work when it is set (their loads
-// would otherwise follow the bad entries out of the operand buffers).
-__global__ __launch_bounds__(1024) void check_index_kernel(const int32_t* __restrict__ idx,
-                                                           int64_t rows, int topk, int nbk,
-                                                           int32_t* __restrict__ flag) {
+// [0, nbk) and every row strictly ascending. Each workgroup checks a
+// grid-stride share of the rows (one thread per row) and writes whether any of
+// them broke a rule to part[blockIdx.x] (after a barrier that ORs its threads'
+// findings); a one-workgroup pass then ORs the parts into flag (1 if the index
+// is bad, else 0). No word is updated by more than one thread, so no clearing
+// and no atomics are needed. The sparse attention kernels read the flag and
+// skip their work when it is set (their loads would otherwise follow the bad
+// entries out of the operand buffers).
+__global__ __launch_bounds__(256) void check_index_kernel(const int32_t* __restrict__ idx,
+                                                          int64_t rows, int topk, int nbk,
+                                                          int32_t* __restrict__ part) {
     int bad = 0;
-    const int64_t n = rows * topk;
-    for (int64_t e = threadIdx.x; e < n; e += 1024) {
-        const int v = idx[e];
-        bad |= (v < 0 || v >= nbk) ? 1 : 0;
-        if ((int)(e % topk) != topk - 1) bad |= (v < idx[e + 1]) ? 0 : 1;
+    for (int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x; r < rows;
+         r += (int64_t)gridDim.x * 256) {
+        const int32_t* row = idx + r * topk;
+        int prev = -1;
+        for (int e = 0; e < topk; ++e) {
+            const int v = row[e];
+            bad |= (v <= prev || v >= nbk) ? 1 : 0;
+            prev = v;
+        }
     }
     bad = __syncthreads_or(bad);
-    if (threadIdx.x == 0) *flag = bad ? 1 : 0;
+    if (threadIdx.x == 0) part[blockIdx.x] = bad ? 1 : 0;
+}
+
+__global__ __launch_bounds__(64) void check_index_reduce_kernel(const int32_t* __restrict__ part,
+                                                                int nparts,
+                                                                int32_t* __restrict__ flag) {
+    const int bad = (int)threadIdx.x < nparts ? part[threadIdx.x] : 0;
+    const bool any = __any(bad != 0);
+    if (threadIdx.x == 0) *flag = any ? 1 : 0;
 }
 
 // When the index check failed, every output of the call is overwritten with
@@ -194,7 +209,12 @@ __global__ __launch_bounds__(256) void poison_outputs_kernel(PoisonArgs a) {
 
 hipError_t launch_check_index(const int32_t* idx, int64_t rows, int topk, int nbk, int32_t* flag,
                               hipStream_t st) {
-    check_index_kernel<<<1, 1024, 0, st>>>(idx, rows, topk, nbk, flag);
+    // the parts follow the flag word: at most 63 workgroups (the flag region
+    // holds 64 words)
+    int64_t g = (rows + 255) / 256;
+    if (g > 63) g = 63;
+    check_index_kernel<<<(unsigned)g, 256, 0, st>>>(idx, rows, topk, nbk, flag + 1);
+    check_index_reduce_kernel<<<1, 64, 0, st>>>(flag + 1, (int)g, flag);
     return hipGetLastError();
 }
 
