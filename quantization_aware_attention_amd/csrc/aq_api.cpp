@@ -58,6 +58,22 @@ int check_device() {
     return ATTNQAT_OK;
 }
 
+// Compute units of the current device (cached per device; 256 on gfx950).
+int g_dev_cus[kMaxDevices];
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    if (g_dev_cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n < 1)
+            n = 256;
+        g_dev_cus[dev] = n;
+    }
+    return g_dev_cus[dev];
+}
+
 int hip_check(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(ATTNQAT_E_HIP, "%s: %s", what, hipGetErrorString(e));
     return ATTNQAT_OK;
@@ -297,7 +313,7 @@ int validate_problem(const attnqat_problem* p, Plan& pl) {
 // Workspace layout (bytes, each region 256-byte aligned).
 struct Layout {
     size_t flag, qw, kw, vw, kt, vt, dow, lse2, delta, qlist, qcount, korder, dowkv, lse2kv,
-        deltakv, total;
+        deltakv, dkdvpart, total;
 };
 
 Layout layout(const Plan& pl, bool bwd) {
@@ -323,6 +339,11 @@ Layout layout(const Plan& pl, bool bwd) {
             L.qlist = take((size_t)pl.BH * pl.nbk * pl.nbq * 4);
             L.qcount = take((size_t)pl.BH * pl.nbk * 4);
             L.korder = take((size_t)pl.BH * pl.nbk * 4);
+        }
+        if (!pl.sparse) {  // partial sums of the key blocks dK/dV splits
+            const int64_t nkb = pl.BH * ((pl.Nk + 127) / 128);
+            const int64_t ns = nkb < aq::kMaxDkdvSplit ? nkb : aq::kMaxDkdvSplit;
+            L.dkdvpart = take((size_t)ns * aq::kMaxDkdvParts * 2 * 128 * pl.D * 4);
         }
         if (pl.rowmax) {  // dK/dV inputs of the row-max-relative variant
             L.dowkv = take(qb);
@@ -714,6 +735,26 @@ int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const vo
         if ((rc = launch(K_REVERSE_INDEX, st, thunk<RevArgs, do_reverse>, &ra,
                          "reverse block index")))
             return rc;
+    }
+    if (!pl.sparse) {
+        // dense dK/dV: one workgroup per key block runs in rounds of one
+        // workgroup per compute unit; the F blocks of the last, partial round
+        // are split into P parts along the queries (P <= 4, the one that
+        // minimises the last round's length ceil(F P / CUs) / P)
+        a.nbk = (int)((pl.Nk + 127) / 128);
+        const int64_t nkb = pl.BH * a.nbk;
+        int cus = device_cus();
+        if (cus > aq::kMaxDkdvSplit + 1) cus = aq::kMaxDkdvSplit + 1;
+        const int64_t F = nkb % cus;
+        const int64_t nt = (pl.Nq + 63) / 64;  // query tiles: a part has at least one
+        int P = 1;
+        for (int c = 2; c <= aq::kMaxDkdvParts && c <= nt; ++c)
+            if ((double)((F * c + cus - 1) / cus) / c < (double)((F * P + cus - 1) / cus) / P)
+                P = c;
+        if (F == 0) P = 1;
+        a.dkdv_parts = P;
+        a.dkdv_full = (int)(P > 1 ? nkb - F : nkb);
+        a.dkdv_part = (float*)(ws + L.dkdvpart);
     }
     const DimArgs da{a, (int)pl.D};
     // row-max-relative variant: dK/dV quantizes exp(S - m) and takes dO and Dl

@@ -151,11 +151,13 @@ __device__ __forceinline__ void wait_async() { __builtin_amdgcn_s_waitcnt(0x0F70
 // runs a contiguous range of the head-major work list keeps the workgroups in
 // flight on one XCD within one or two heads, so the K/V (or Q/dO) tiles they
 // all stream are fetched into that XCD's L2 once rather than by every XCD.
-__device__ __forceinline__ void xcd_work(int& tile, int& bh) {
-    const int nx = gridDim.x, n = gridDim.x * gridDim.y;
-    const int L = blockIdx.x + blockIdx.y * nx;
+__device__ __forceinline__ int xcd_index(int L, int n) {
     const int x = L & 7, slot = L >> 3, per = n >> 3, rem = n & 7;
-    const int w = x * per + (x < rem ? x : rem) + slot;
+    return x * per + (x < rem ? x : rem) + slot;
+}
+__device__ __forceinline__ void xcd_work(int& tile, int& bh) {
+    const int nx = gridDim.x;
+    const int w = xcd_index(blockIdx.x + blockIdx.y * nx, gridDim.x * gridDim.y);
     tile = w % nx;
     bh = w / nx;
 }
@@ -263,6 +265,17 @@ __device__ __forceinline__ void store_rows_T(uint16_t* out_row, const f32x16* ac
             *(u32x2*)(out_row + db * 32 + rr * 8 + hh * 4) = w;
         }
     }
+}
+
+// As store_rows_T, as fp32 without scaling: row points at this lane's token.
+template <int D>
+__device__ __forceinline__ void store_rows_f32(float* row, const f32x16* acc, int hh) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+            *(f32x4_t*)(row + db * 32 + rr * 8 + hh * 4) =
+                f32x4_t{acc[db][4 * rr], acc[db][4 * rr + 1], acc[db][4 * rr + 2], acc[db][4 * rr + 3]};
 }
 
 // S^T block (32 keys x 32 queries): keys are rows kr0.. of a swizzled [*, D]
@@ -1236,21 +1249,41 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnArgs a) {
     const int pair = wave & 3;
     const bool producer = wave < 4;  // wave-uniform
     const int l32 = lane & 31, hh = lane >> 5;
-    // sparse: workgroups run the key blocks of every head heaviest first
-    // (blockIdx.y is the rank of the block's selection count in its head)
-    int kblk = blockIdx.x, bh = blockIdx.y;
+    // Dense launches: the first a.dkdv_full workgroups take one whole key
+    // block each (kb = bh * nbk + kblk, head-major; each XCD a contiguous
+    // range); the remaining key blocks are split into a.dkdv_parts parts along
+    // the queries, one workgroup per part, written as fp32 partial sums that
+    // bwd_dkdv_fixup_kernel adds. The split makes the last round of
+    // workgroups as full as possible (the host picks the part count). Sparse
+    // launches: one key block per workgroup, the blocks of every head
+    // heaviest first (blockIdx.y is the rank of the block's selection count).
+    int kblk, bh, t0 = 0, n, side = -1;
     if (SPARSE) {
         bh = blockIdx.x;
         kblk = a.kv_order[(size_t)bh * a.nbk + blockIdx.y];
+        n = query_tiles<SPARSE>(a, bh, kblk, lst);
     } else {
-        xcd_work(kblk, bh);
+        const int nt = (a.Nq + BM - 1) / BM, L = blockIdx.x, nf = a.dkdv_full;
+        int kb;
+        if (L < nf) {
+            kb = xcd_index(L, nf);
+            n = nt;
+        } else {
+            const int w = xcd_index(L - nf, gridDim.x - nf), P = a.dkdv_parts;
+            side = w;  // partial slot
+            kb = nf + w / P;
+            const int part = w % P;
+            t0 = nt * part / P;
+            n = nt * (part + 1) / P - t0;
+        }
+        bh = kb / a.nbk;
+        kblk = kb % a.nbk;
     }
     const int k0 = kblk * KW + pair * 32;
     const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
     const uint16_t* dOb = a.dOw + (size_t)bh * a.Nq_pad * D;
     // statistics slice of this wave: waves 0..3 LSE2, 4..7 Dl, 16 queries each
     const float* Sb = (wave < 4 ? a.lse2 : a.delta) + (size_t)bh * a.Nq_pad + pair * 16;
-    const int n = query_tiles<SPARSE>(a, bh, kblk, lst);
     const bool tailk = kblk * KW + KW > a.Nk;
     // Per-lane source offsets of this wave's DMA blocks in a [BM][D] tile:
     // block b = j * 8 + wave covers tile rows RB b .. RB b + RB - 1 (RB rows of
@@ -1265,7 +1298,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnArgs a) {
     }
     auto issue = [&](int t) {
         Tile* T = ring + t % 3;
-        const int qt = tile_start<SPARSE, BM>(lst, t);
+        const int qt = tile_start<SPARSE, BM>(lst, t0 + t);
 #pragma unroll
         for (int j = 0; j < NJ / 2; ++j) {
             const uint32_t blk = (uint32_t)((j * 8 + wave) * 512);  // elements
@@ -1454,12 +1487,50 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnArgs a) {
             if (u < 2 * n) prefetch(u);
         }, std::false_type{});
         const int key = k0 + l32;
-        if (key < a.Nk) {
+        if (side >= 0) {
+            // fp32 partial sums [dK, dV][128 keys][D] of part slot `side`
+            float* ps = a.dkdv_part + (size_t)side * 2 * KW * D;
+            store_rows_f32<D>(ps + (size_t)(pair * 32 + l32) * D, dka, hh);
+            store_rows_f32<D>(ps + (size_t)(KW + pair * 32 + l32) * D, dva, hh);
+        } else if (key < a.Nk) {
             const int64_t b = bh / a.H, h = bh % a.H;
             store_rows_T<D>(a.dv + b * a.dvsb + h * a.dvsh + (int64_t)key * a.dvsn, dva, 1.0f, hh);
             store_rows_T<D>(a.dk + b * a.dksb + h * a.dksh + (int64_t)key * a.dksn, dka, a.sm_scale,
                             hh);
         }
+    }
+}
+
+// Sums the fp32 parts of every split key block of a dense dK/dV launch (in a
+// fixed order, part 0 first) and writes the block's dK (times sm_scale) and
+// dV as bf16. One workgroup per split block.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_fixup_kernel(AttnArgs a) {
+    constexpr int KW = 128;
+    const int P = a.dkdv_parts, kb = a.dkdv_full + blockIdx.x;
+    const int bh = kb / a.nbk, kblk = kb % a.nbk;
+    const int64_t b = bh / a.H, h = bh % a.H;
+    const float* p0 = a.dkdv_part + (size_t)blockIdx.x * P * 2 * KW * D;
+    // 8 consecutive d values per thread and pass
+    for (int e = threadIdx.x * 8; e < 2 * KW * D; e += 256 * 8) {
+        const int which = e / (KW * D), key = (e / D) % KW, d = e % D;
+        const int tok = kblk * KW + key;
+        if (tok >= a.Nk) continue;
+        f32x4_t x0 = *(const f32x4_t*)(p0 + e), x1 = *(const f32x4_t*)(p0 + e + 4);
+        for (int part = 1; part < P; ++part) {
+            const float* q = p0 + (size_t)part * 2 * KW * D + e;
+            x0 += *(const f32x4_t*)q;
+            x1 += *(const f32x4_t*)(q + 4);
+        }
+        const float f = which == 0 ? a.sm_scale : 1.0f;
+        u32x4 w;
+        w[0] = pack_rne(x0[0] * f, x0[1] * f);
+        w[1] = pack_rne(x0[2] * f, x0[3] * f);
+        w[2] = pack_rne(x1[0] * f, x1[1] * f);
+        w[3] = pack_rne(x1[2] * f, x1[3] * f);
+        uint16_t* dst = which == 0 ? a.dk + b * a.dksb + h * a.dksh + (int64_t)tok * a.dksn
+                                   : a.dv + b * a.dvsb + h * a.dvsh + (int64_t)tok * a.dvsn;
+        *(u32x4*)(dst + d) = w;
     }
 }
 
@@ -1693,15 +1764,20 @@ hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Dense: one workgroup per whole key block and one per part of a split one;
+// the split blocks are finished by the fixup.
 template <int D>
 static void dkdv_d(const AttnArgs& a, bool sp, hipStream_t st) {
-    const dim3 g(sp ? a.BH : (a.Nk + 127) / 128, sp ? a.nbk : a.BH);
     if (sp) {
+        const dim3 g(a.BH, a.nbk);
         if (a.quant_p) bwd_dkdv_kernel<D, true, true><<<g, 512, 0, st>>>(a);
         else bwd_dkdv_kernel<D, false, true><<<g, 512, 0, st>>>(a);
     } else {
+        const int split = a.BH * a.nbk - a.dkdv_full;
+        const int g = a.dkdv_full + split * a.dkdv_parts;
         if (a.quant_p) bwd_dkdv_kernel<D, true, false><<<g, 512, 0, st>>>(a);
         else bwd_dkdv_kernel<D, false, false><<<g, 512, 0, st>>>(a);
+        if (a.dkdv_parts > 1) bwd_dkdv_fixup_kernel<D><<<split, 256, 0, st>>>(a);
     }
 }
 

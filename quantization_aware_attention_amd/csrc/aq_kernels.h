@@ -8,6 +8,11 @@ namespace aq {
 // Tile sizes shared by the host planner and the kernels.
 constexpr int kTileN = 256;  // token padding granularity of every workspace operand
 
+// Dense dK/dV: most parts a key block is split into, and most split blocks
+// (fewer than one round of workgroups on a chip of 256 compute units).
+constexpr int kMaxDkdvParts = 4;
+constexpr int kMaxDkdvSplit = 255;
+
 // Size of the fixed device scratch behind attnqat_fwd_noalloc (aq_noalloc.hip)
 // and the lookup of its address on the current device.
 constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
@@ -77,6 +82,11 @@ struct AttnArgs {
     const int32_t* q_count;  // [BH][nbk]
     const int32_t* kv_order; // [BH][nbk] key blocks of each head by descending count
     const int32_t* idx_err;  // block-index check flag: the sparse kernels skip their work if set
+    // dense dK/dV: key blocks [0, dkdv_full) run whole, the others are split
+    // into dkdv_parts parts along the queries whose fp32 partial sums
+    // [split block][part][dK, dV][128 keys][D] the fixup adds
+    float* dkdv_part;
+    int dkdv_full, dkdv_parts;
     int topk;
     int nbq, nbk;
     int64_t H;

@@ -130,11 +130,15 @@ def test_sparse_problem_checks(L):
     # [BH][nbk] counts and the [BH][nbk] dispatch order, 256-byte aligned)
     # and stages no permuted K^T
     # (bf16 [BH][Nk_pad][D])
+    # and the dense one the fp32 partial sums of the key blocks its dK/dV
+    # launch may split (at most 4 parts of [dK, dV][128 keys][D] per block,
+    # for at most 255 blocks)
     nb = 1024 // 128
     kt = 2 * 1024 * 64 * 2
     rev = -(-2 * nb * nb * 4 // 256) * 256 + 2 * (-(-2 * nb * 4 // 256) * 256)
+    part = min(2 * nb, 255) * 4 * 2 * 128 * 64 * 4
     assert (L.attnqat_bwd_workspace_bytes(ctypes.byref(p)) ==
-            L.attnqat_bwd_workspace_bytes(ctypes.byref(dense)) - kt + rev)
+            L.attnqat_bwd_workspace_bytes(ctypes.byref(dense)) - kt - part + rev)
 
 
 def test_block_select_checks(L):
