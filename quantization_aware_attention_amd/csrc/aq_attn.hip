@@ -1671,6 +1671,159 @@ __global__ __launch_bounds__(1024) void fwd_out_pc_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Dense forward pass 2 with the additive straight-through output, with
+// producer/consumer wave pairs (a workgroup runs four pairs, 128 queries,
+// eight waves, two per SIMD):
+//   producer:  S^T = K Q^T, P = exp(S - LSE) and Pq = FQ(P), both packed as
+//              bf16 B operands of the P V products and written to an LDS
+//              exchange slot (16 products per 64-key step);
+//   consumer:  O^T += V^T Pq^T and O_ste^T += V^T P^T, each V^T operand read
+//              once for both (32 products per step).
+// As in fwd_out_pc_kernel the producers run one key tile ahead of the
+// consumers (K tiles one tile ahead of V^T tiles, both double-buffered, the
+// exchange by step parity, one barrier per step). V^T is bf16 here (P is not
+// an NVFP4 value). A three-role form (one consumer per output, twelve waves)
+// measured the same within 1%.
+template <int D>
+__global__ __launch_bounds__(512) void fwd_out_ste_pc_kernel(AttnArgs a) {
+    using F = FwdOutSte<D, true>;
+    constexpr int BN = F::BN, NT = 4, NWV = 8;
+    constexpr int KBLK = BN * D * 2 / 1024, VBLK = D * BN * 2 / 1024;  // 1 KB DMA blocks per tile
+    __shared__ __attribute__((aligned(1024))) uint16_t sK[2][BN * D];
+    __shared__ __attribute__((aligned(1024))) uint16_t sV[2][D * BN];
+    // exchange: [parity][pair][Pq, P][32-key block][chunk g][lane][4 dwords]
+    __shared__ __attribute__((aligned(1024))) uint32_t sX[2][NT][2][2][2][64 * 4];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pair = wave & 3, role = wave >> 2;  // 0 producer, 1 consumer
+    const int l32 = lane & 31, hh = lane >> 5;
+    int qblk, bh;
+    xcd_work(qblk, bh);
+    const int q = qblk * (NT * 32) + pair * 32 + l32;
+    const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
+    const uint16_t* Kb = a.Kw + (size_t)bh * a.Nk_pad * D;
+    const uint16_t* Vtb = a.Vt + (size_t)bh * D * a.Nk_pad;
+    const int nt = (a.Nk + BN - 1) / BN;
+    const bool last_partial = nt * BN > a.Nk;
+    // this wave's DMA blocks: blocks wave, wave + 8, ... of each tile (where
+    // they exist); K rows in perm32 order, lane i fills slot 16 i
+    constexpr int NJ = (KBLK + NWV - 1) / NWV;
+    static_assert(KBLK == VBLK, "tiles of equal size");
+    uint32_t koff[NJ], voff[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int blk = wave + j * NWV;
+        constexpr int CH = D / 8;  // 16-byte chunks per K row
+        const int kr = blk * (64 / CH) + lane / CH, kc = lane % CH;
+        const int src = (kr & ~31) | perm32(kr & 31);
+        koff[j] = (uint32_t)(src * D + ((kc ^ swz<D>(kr)) << 3)) * 2u;
+        const int vr = blk * 8 + (lane >> 3), vc = lane & 7;
+        voff[j] = (uint32_t)(vr * a.Nk_pad + ((vc ^ swz<BN>(vr)) << 3)) * 2u;
+    }
+    auto issue_k = [&](int t) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            if (wave + j * NWV < KBLK)
+                dma16(lds_addr(sK[t & 1] + (wave + j * NWV) * 512), Kb + (size_t)t * BN * D, koff[j]);
+    };
+    auto issue_v = [&](int t) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+            if (wave + j * NWV < VBLK)
+                dma16(lds_addr(sV[t & 1] + (wave + j * NWV) * 512), Vtb + t * BN, voff[j]);
+    };
+    if (role == 0) {
+        u32x4 qf[D / 16];
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c)
+            qf[c] = *(const u32x4*)(Qb + (size_t)q * D + c * 16 + hh * 8);
+        float off, post;
+        p_offset<true>(a, bh, q, off, post);
+        // let these loads land before any tile copy is issued (the copies
+        // are invisible to the compiler's wait counts)
+        wait_vm<0>();
+        issue_k(0);
+        wait_vm<0>();
+        __syncthreads();
+        for (int t = 0; t <= nt; ++t) {
+            if (t > 0) {
+                wait_vm<0>();
+                __syncthreads();
+            }
+            if (t + 1 < nt) issue_k(t + 1);
+            if (t < nt) issue_v(t);
+            if (t >= nt) continue;
+            const uint16_t* K = sK[t & 1];
+            uint32_t* X = &sX[t & 1][pair][0][0][0][0];
+            auto run = [&](auto tail) {
+                constexpr bool TL = decltype(tail)::value;
+                const f32x16 s0 = scores_T<D>(K, 0, qf, l32, hh);
+                lds_mfma_chain<D / 16, 4>();
+                const f32x16 s1 = scores_T<D>(K, 32, qf, l32, hh);
+                u32x4 q0[2], p0[2], q1[2], p1[2];
+                F::template probs<TL>(s0, t * BN, a.Nk, a.c, off, hh, q0, p0);
+                mfma_chain_front<D / 16, 1, 4, 64, 0>();
+                F::template probs<TL>(s1, t * BN + 32, a.Nk, a.c, off, hh, q1, p1);
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    *(u32x4*)(X + ((0 * 4 + 0 * 2 + g) * 64 + lane) * 4) = q0[g];
+                    *(u32x4*)(X + ((0 * 4 + 1 * 2 + g) * 64 + lane) * 4) = q1[g];
+                    *(u32x4*)(X + ((1 * 4 + 0 * 2 + g) * 64 + lane) * 4) = p0[g];
+                    *(u32x4*)(X + ((1 * 4 + 1 * 2 + g) * 64 + lane) * 4) = p1[g];
+                }
+            };
+            if (last_partial && t == nt - 1) run(std::true_type{});
+            else run(std::false_type{});
+        }
+    } else {
+        f32x16 o[D / 32], os[D / 32];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[db] = os[db] = f32x16{};
+        issue_k(0);
+        wait_vm<0>();
+        __syncthreads();
+        for (int t = 0; t <= nt; ++t) {
+            if (t > 0) {
+                wait_vm<0>();
+                __syncthreads();
+            }
+            if (t + 1 < nt) issue_k(t + 1);
+            if (t < nt) issue_v(t);
+            if (t == 0) continue;
+            const uint16_t* V = sV[(t - 1) & 1];
+            const uint32_t* X = &sX[(t - 1) & 1][pair][0][0][0][0];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                u32x4 bq[2], bp[2];
+#pragma unroll
+                for (int g = 0; g < 2; ++g) {
+                    bq[g] = *(const u32x4*)(X + ((0 * 4 + kb * 2 + g) * 64 + lane) * 4);
+                    bp[g] = *(const u32x4*)(X + ((1 * 4 + kb * 2 + g) * 64 + lane) * 4);
+                }
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+                    for (int g = 0; g < 2; ++g) {
+                        const u32x4 vf =
+                            *(const u32x4*)(V + toff<BN>(db * 32 + l32, 4 * kb + 2 * hh + g));
+                        o[db] = mfma(vf, bq[g], o[db]);
+                        os[db] = mfma(vf, bp[g], os[db]);
+                    }
+                }
+            }
+            mfma_chain_m<D / 4, 2, 4, 0>();
+        }
+        if (q < a.Nq) {
+            float off, post;
+            p_offset<true>(a, bh, q, off, post);
+            const int64_t b = bh / a.H, h = bh % a.H;
+            store_rows_T<D>(a.o + b * a.osb + h * a.osh + (int64_t)q * a.osn, o, post, hh);
+            store_rows_T<D>(a.o_ste + b * a.osb + h * a.osh + (int64_t)q * a.osn, os, post, hh);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Dense forward workgroups are 8 waves (256 queries), so that each K/V tile
 // brought into LDS serves 256 queries; sparse ones are one 128-query block
 // (4 waves).
@@ -1708,10 +1861,12 @@ static void fwd_out_go(const AttnArgs& a, bool sp, hipStream_t st) {
 
 template <int D, bool QP>
 static void fwd_out_ste_go(const AttnArgs& a, bool sp, hipStream_t st) {
-    // four waves of 32 queries, one per SIMD: the two output accumulators and
-    // the quantizer need more than the 256 registers of two waves per SIMD
+    // sparse: four waves of 32 queries, one per SIMD, each forming S, P, Pq
+    // and both products (the two output accumulators and the quantizer need
+    // more than the 256 registers of two waves per SIMD); dense: producer /
+    // consumer pairs, 128 queries per workgroup
     if (sp) fwd_out_ste_kernel<D, QP, 4, true><<<dim3(a.nbq, a.BH), 256, 0, st>>>(a);
-    else fwd_out_ste_kernel<D, QP, 4, false><<<dim3((a.Nq + 127) / 128, a.BH), 256, 0, st>>>(a);
+    else fwd_out_ste_pc_kernel<D><<<dim3((a.Nq + 127) / 128, a.BH), 512, 0, st>>>(a);
 }
 
 // Pass 2 runs only when P is quantized (otherwise the single-pass forward
