@@ -167,7 +167,7 @@ hipError_t launch_vsa_grad_add(const VsaArgs& a, hipStream_t st);
 
 // Real-FP4 (MXFP4) inference forward. Workspace operands: Q and K rows as
 // packed E2M1 codes [BH][N_pad][D / 2] bytes with E8M0 scales [BH][N_pad][D / 32];
-// V^T codes [BH][D][Nk_pad / 2] with scales [BH][D][Nk_pad / 32].
+// V^T codes [BH][D][Nk_pad / 2] with scales [BH][Nk_pad / 64][D][2] (tile by tile).
 struct MxArgs {
     const uint16_t* q;
     const uint16_t* k;
