@@ -59,18 +59,45 @@ def test_sparse_attention(gpu_lib, N, D, topk, mask):
         assert e <= tol_for(mask), msg
 
 
-def test_sparse_all_blocks_equals_dense(gpu_lib):
-    bits = _inputs(7, (1, 2, 512, 64), 1.5)
+def _all_blocks_vs_dense(gpu_lib, seed, shape):
+    N = shape[2]
+    nb = (N + 127) // 128
+    bits = _inputs(seed, shape, 1.5)
     t = {k: to_dev(v) for k, v in bits.items()}
-    idx = torch.arange(4, dtype=torch.int32, device="cuda").repeat(1, 2, 4, 1).contiguous()
+    idx = torch.arange(nb, dtype=torch.int32, device="cuda").repeat(1, shape[1], nb, 1).contiguous()
     o1, l1 = gpu_lib.fwd(t["q"], t["k"], t["v"], 0.125, 15, idx)
     o2, l2 = gpu_lib.fwd(t["q"], t["k"], t["v"], 0.125, 15)
     d1 = gpu_lib.bwd(t["q"], t["k"], t["v"], o1, l1, t["do"], 0.125, 15, idx)
     d2 = gpu_lib.bwd(t["q"], t["k"], t["v"], o2, l2, t["do"], 0.125, 15)
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
-    for a, b in zip(d1, d2):
-        assert torch.equal(a, b)
+    return (o1, l1) + tuple(d1), (o2, l2) + tuple(d2)
+
+
+def test_sparse_all_blocks_equals_dense(gpu_lib):
+    """Selecting every key block reproduces the dense path. The forward, LSE
+    and dQ accumulate in the same order and match bit for bit. A dense dK/dV
+    launch whose key blocks do not fill whole rounds of compute units splits
+    the last round's blocks into query parts summed in fp32 afterwards (a
+    different summation order), so here dK and dV may differ by bf16
+    rounding flips only."""
+    sp, de = _all_blocks_vs_dense(gpu_lib, 7, (1, 2, 512, 64))
+    for name, a, b in zip(("o", "lse", "dq"), sp[:3], de[:3]):
+        assert torch.equal(a, b), name
+    for name, a, b in zip(("dk", "dv"), sp[3:], de[3:]):
+        a, b = a.float(), b.float()
+        tol = 2.0 ** -7 * a.abs().maximum(b.abs()) + 1e-3 * float(b.abs().max())
+        assert bool(((a - b).abs() <= tol).all()), name
+
+
+def test_sparse_all_blocks_equals_dense_unsplit(gpu_lib):
+    """With as many key blocks as compute units the dense dK/dV launch runs
+    whole blocks only, and every output matches the sparse path bit for
+    bit."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert cus % 2 == 0 and cus <= 512
+    sp, de = _all_blocks_vs_dense(gpu_lib, 8, (1, 2, 128 * cus // 2, 64))
+    for name, a, b in zip(("o", "lse", "dq", "dk", "dv"), sp, de):
+        assert torch.equal(a, b), name
 
 
 def _index_with_last_block(seed, B, H, nbq, nbk, topk):
