@@ -240,6 +240,18 @@ def time_configs(qaa, torch, np, dev, skip):
     return res
 
 
+def copy_calibration(torch, dev):
+    """One plain 1 GiB device-to-device copy, a kernel of known traffic (1 GiB
+    read, 1 GiB written) against which HBM byte counters are scaled."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    return 1 << 30
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -361,6 +373,8 @@ def main():
     # Standalone fake quantization of one input (HBM-bound): 4 bytes per
     # element (2 read, 2 written), along d (Q's layout) and along tokens (V's).
     if args.main_only:
+        if args.copy_calibration:
+            out["copy_calibration_bytes"] = copy_calibration(torch, dev)
         out["cpu_baseline"] = None
         print(json.dumps(out), flush=True)
         return
@@ -583,13 +597,7 @@ def main():
         out["configs"] = time_configs(qaa, torch, np, dev, args.workload)
     out["machine"] = machine_probes(torch, dev)
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        out["copy_calibration_bytes"] = 1 << 30
-        del src, dst
+        out["copy_calibration_bytes"] = copy_calibration(torch, dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(bits, w, args.cpu_rows, mask)
