@@ -393,7 +393,7 @@ struct FwdLse {
             }
             float mx = m;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+            for (int r = 0; r < 16; ++r) mx = vmax(mx, acc[r]);
             const float mc = mx * c;
             float sum = 0.0f;
 #pragma unroll
@@ -778,7 +778,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_single_kernel(At
                 }
                 float bm = x[0];
 #pragma unroll
-                for (int j = 1; j < 16; ++j) bm = fmaxf(bm, x[j]);
+                for (int j = 1; j < 16; ++j) bm = vmax(bm, x[j]);
                 bm = fmaxf(bm, partner_lane(bm));
                 mt = fmaxf(mt, bm);
                 const bool up = bm > m + tau;

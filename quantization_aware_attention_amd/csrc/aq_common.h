@@ -83,6 +83,13 @@ __device__ __forceinline__ uint32_t pack_rne(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// Larger of two scores. IEEE maximum (NaN-propagating) instead of fmaxf:
+// fmaxf must quiet signalling NaNs, so on values the compiler cannot prove
+// canonical (matrix-unit results) it inserts a self-max before every use,
+// while maximum lowers to one v_maximum3_f32 per two new values. The two
+// agree on everything the kernels feed them (finite values and -inf).
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Value of x held by lane l ^ 32.
 __device__ __forceinline__ float partner_lane(float x) {
     auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -148,7 +155,7 @@ template <bool F16>
 __device__ __forceinline__ void quant_p_group16(const float* x, float c, float lse2, u32x4* out) {
     float mx = x[0];
 #pragma unroll
-    for (int j = 1; j < 16; ++j) mx = __builtin_fmaxf(mx, x[j]);
+    for (int j = 1; j < 16; ++j) mx = vmax(mx, x[j]);
     const float pmax = __builtin_amdgcn_exp2f(__builtin_fmaf(mx, c, -lse2));
     const float a6 = pmax * (1.0f / 6.0f);
     const i16x2 z = {0, 0};
@@ -202,7 +209,7 @@ __device__ __forceinline__ void quant_p_group16_bwd(const float* x, float c, flo
                                                     float* r, float& sp_out) {
     float mx = x[0];
 #pragma unroll
-    for (int j = 1; j < 16; ++j) mx = __builtin_fmaxf(mx, x[j]);
+    for (int j = 1; j < 16; ++j) mx = vmax(mx, x[j]);
     const float pmax = __builtin_amdgcn_exp2f(__builtin_fmaf(mx, c, -lse2));
     const float a6 = pmax * (1.0f / 6.0f);
     const i16x2 z = {0, 0};

@@ -140,7 +140,22 @@ __device__ __forceinline__ int mx_key_of_row(int kb, int row) {
 
 // One 64-key tile in LDS: K codes (row-major, D / 2 bytes per key) and
 // scales (D / 32 per key), V^T codes (32 bytes per d row: 64 tokens) and
-// scales (2 per d row).
+// scales (2 per d row). The 16-byte chunks of each K row and V^T row are
+// stored XOR-swizzled (mx_kswz, mx_vswz) so that the operand reads below
+// touch 16 different 16-byte bank groups per 16 lanes: a key row's chunk cc
+// sits at position cc ^ mx_kswz(row), a V^T row's half h at h ^ mx_vswz(d).
+// A 16-lane group of a K operand read covers key rows {r..r+3, r+4..r+7,
+// r+32..r+35, r+36..r+39} (mx_key_of_row), whose unswizzled chunks share
+// bank groups whenever the rows agree mod 4 (d = 128, 64-byte rows) or mod 8
+// (d = 64, 32-byte rows); bits 2 and 5 of the row separate them.
+template <int D>
+__device__ __forceinline__ int mx_kswz(int row) {
+    return D == 128 ? (((row >> 2) & 1) | (((row >> 5) & 1) << 1)) : ((row >> 5) & 1);
+}
+// V^T operand reads: 16 lanes read rows d..d+15 (32-byte rows), and rows d
+// and d + 8 share bank groups unless bit 3 of d moves one half.
+__device__ __forceinline__ int mx_vswz(int d) { return (d >> 3) & 1; }
+
 template <int D>
 struct MxLds {
     uint8_t k[64 * D / 2];
@@ -179,23 +194,28 @@ __device__ __forceinline__ void mx_dma4(const void* lds, const void* g, uint32_t
 // 1 KB blocks of K codes (contiguous rows), D / 32 blocks of V^T codes (32
 // bytes of each d row, 16 per lane), and the K and V^T scales (D * 2 bytes
 // each, contiguous: V^T scales are stored tile by tile). Block j goes to wave
-// j % NW.
+// j % NW. Lane i of a block fills LDS slot i, so it fetches the global chunk
+// that the swizzle puts there.
 template <int D, int NW, bool V>
 __device__ __forceinline__ void mx_issue(const MxArgs& a, int64_t bh, int kt, MxLds<D>& L, int wave,
                                          int lane) {
     constexpr int NB = D / 32;  // 1 KB blocks of K codes, and of V^T codes
+    constexpr int CPR = D / 32;  // 16-byte chunks per K row
 #pragma unroll
     for (int j = 0; j < NB; ++j)
-        if (j % NW == wave)
+        if (j % NW == wave) {
+            const int row = j * (64 / CPR) + lane / CPR;
+            const int cc = (lane % CPR) ^ mx_kswz<D>(row);
             mx_dma16(L.k + j * 1024, a.km + (bh * a.Nk_pad + kt) * (D / 2) + j * 1024,
-                     16u * (uint32_t)lane);
+                     (uint32_t)(16 * ((lane / CPR) * CPR + cc)));
+        }
     if (NB % NW == wave && lane < D / 2)
         mx_dma4(L.ks, a.ks + (bh * a.Nk_pad + kt) * (D / 32), 4u * (uint32_t)lane);
     if (V) {
 #pragma unroll
         for (int j = 0; j < NB; ++j)
             if ((NB + 1 + j) % NW == wave) {
-                const int idx = j * 64 + lane, d = idx >> 1, half = idx & 1;
+                const int idx = j * 64 + lane, d = idx >> 1, half = (idx & 1) ^ mx_vswz(d);
                 mx_dma16(L.v + j * 1024, a.vtm + (bh * D) * (a.Nk_pad / 2) + kt / 2,
                          (uint32_t)(d * (a.Nk_pad / 2) + half * 16));
             }
@@ -214,7 +234,7 @@ __device__ __forceinline__ void mx_scores(const MxLds<D>& L, const u32x4* qa, co
         s[kb] = f32x16{};
 #pragma unroll
         for (int c = 0; c < D / 64; ++c) {
-            const u32x4 ka = *(const u32x4*)(L.k + row * (D / 2) + 32 * c + 16 * hh);
+            const u32x4 ka = *(const u32x4*)(L.k + row * (D / 2) + 16 * ((2 * c + hh) ^ mx_kswz<D>(row)));
             s[kb] = mfma_fp4(ka, qa[c], L.ks[row * (D / 32) + 2 * c + hh], qs[c], s[kb]);
         }
     }
@@ -274,11 +294,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 1) void mx_fwd_kernel(MxArgs
         if (it < n_full) {
 #pragma unroll
             for (int j = 0; j < 32; j += 2)
-                smax = __builtin_fmaxf(smax, __builtin_fmaxf(s[j >> 4][j & 15], s[j >> 4][(j & 15) + 1]));
+                smax = vmax(smax, vmax(s[j >> 4][j & 15], s[j >> 4][(j & 15) + 1]));
         } else {
 #pragma unroll
             for (int j = 0; j < 32; ++j)
-                if (kt + 32 * hh + j < a.Nk) smax = fmaxf(smax, s[j >> 4][j & 15]);
+                if (kt + 32 * hh + j < a.Nk) smax = vmax(smax, s[j >> 4][j & 15]);
         }
         m = fmaxf(m, smax * c);
     });
@@ -306,7 +326,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 1) void mx_fwd_kernel(MxArgs
         }
 #pragma unroll
         for (int j = 0; j < 32; j += 2)
-            smax = __builtin_fmaxf(smax, __builtin_fmaxf(s[j >> 4][j & 15], s[j >> 4][(j & 15) + 1]));
+            smax = vmax(smax, vmax(s[j >> 4][j & 15], s[j >> 4][(j & 15) + 1]));
         float xmax = smax * c;
         asm volatile("" : "+v"(xmax));
         const float lb = xmax - mt;  // log2 of the block's amax (-inf: empty block)
@@ -335,7 +355,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 1) void mx_fwd_kernel(MxArgs
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
             const int d = 32 * db + l32;
-            const u32x4 va = *(const u32x4*)(T.v + d * 32 + 16 * hh);
+            const u32x4 va = *(const u32x4*)(T.v + d * 32 + 16 * (hh ^ mx_vswz(d)));
             o[db] = mfma_fp4(va, pc, T.vs[d * 2 + hh], ps, o[db]);
         }
     });
