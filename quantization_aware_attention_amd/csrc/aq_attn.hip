@@ -1116,10 +1116,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_sparse_kernel(AttnArgs a) {
 // Transpose of a 32 x 32 score tile packed as bf16 pairs (w[g] holds keys
 // 16 hh + 8 g .. + 7 of query l32) through LDS: transpose_write stores it
 // with row = query (64 bytes per row, two 16-byte writes per lane; 16-byte
-// chunk c of row q sits at c ^ ((q / 4) % 4), so that the row writes and the
-// transposing column reads avoid bank conflicts); transpose_read returns two
-// B operands with keys on lanes and queries 16 g + 8 hh + j on the k-slots.
-__device__ __forceinline__ int xoff(int q, int c) { return q * 32 + ((c ^ ((q >> 2) & 3)) << 3); }
+// chunk c of row q sits at c ^ (((q >> 1) ^ (q >> 3)) & 3)); transpose_read
+// returns two B operands with keys on lanes and queries 16 g + 8 hh + j on the
+// k-slots. The swizzle keeps both sides free of bank conflicts: 16-byte
+// writes go through the banks eight lanes (128 bytes) at a time, and the rows
+// of eight consecutive queries, 64 bytes apart, then fall on eight different
+// 16-byte bank groups; the transposing reads (32 lanes, 256 bytes at a time)
+// touch 32 different 8-byte bank pairs. (Measured with the access patterns in
+// isolation: the earlier swizzle c ^ ((q >> 2) & 3) left the writes 2-way
+// conflicted.)
+__device__ __forceinline__ int xoff(int q, int c) { return q * 32 + ((c ^ (((q >> 1) ^ (q >> 3)) & 3)) << 3); }
 __device__ __forceinline__ void transpose_write(const u32x4* w, uint16_t* T, int lane) {
     const int l32 = lane & 31, hh = lane >> 5;
 #pragma unroll
