@@ -99,24 +99,35 @@ __global__ __launch_bounds__(256) void mx_quant_rows_kernel(MxArgs a) {
 }
 
 // V along the tokens: one thread per (column d, 32-token block), written as
-// V^T [BH][D][Nk_pad / 2] bytes with scales [BH][Nk_pad / 64][D][2]. Threads of a
-// wave take consecutive columns, so each token row is read coalesced.
+// V^T [BH][D][Nk_pad / 2] bytes with scales [BH][Nk_pad / 64][D][2]. A
+// workgroup of 256 threads covers 256 / D token blocks: it first copies their
+// rows into LDS with 16-byte loads (rows padded by 4 bytes, so that the
+// column reads of consecutive threads fall in different banks), then each
+// thread reads its column's 32 values from there.
 template <int D>
 __global__ __launch_bounds__(256) void mx_quant_vt_kernel(MxArgs a) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int nblk = a.Nk_pad / 32;
-    const int tb = (int)(t / D), d = (int)(t % D);
-    if (tb >= nblk) return;
+    constexpr int TB = 256 / D, ROWS = TB * 32, RS = D + 2;  // row stride in elements
+    __shared__ __attribute__((aligned(16))) uint16_t tile[ROWS * RS];
     const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
-    const uint16_t* src = a.v + b * a.vsb + h * a.vsh + d;
+    const int tok0 = blockIdx.x * ROWS;
+    const uint16_t* src = a.v + b * a.vsb + h * a.vsh;
+    constexpr int CPR = D / 8;  // 16-byte chunks per row
+    for (int e = threadIdx.x; e < ROWS * CPR; e += 256) {
+        const int r = e / CPR, c = e % CPR, tok = tok0 + r;
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (tok < a.Nk) w = *(const u32x4*)(src + (int64_t)tok * a.vsn + c * 8);
+        uint32_t* dst = (uint32_t*)(tile + r * RS + c * 8);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dst[k] = w[k];
+    }
+    __syncthreads();
+    const int tbl = threadIdx.x / D, d = threadIdx.x % D;
     float x[32];
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-        const int tok = tb * 32 + j;
-        x[j] = tok < a.Nk ? bf2f(src[(int64_t)tok * a.vsn]) : 0.0f;
-    }
+    for (int j = 0; j < 32; ++j) x[j] = bf2f(tile[(tbl * 32 + j) * RS + d]);
     u32x4 codes;
     const int sc = mx_block(x, codes);
+    const int tb = blockIdx.x * TB + tbl;
     const int64_t r = bh * D + d;
     *(u32x4*)(a.vtm + r * (a.Nk_pad / 2) + tb * 16) = codes;
     // scales tile by tile: [BH][Nk_pad / 64][D][2], so a tile's are contiguous
@@ -382,8 +393,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 1) void mx_fwd_kernel(MxArgs
 hipError_t launch_mx_quant(const MxArgs& a, hipStream_t st) {
     const int64_t rows = (int64_t)(a.Nq_pad > a.Nk_pad ? a.Nq_pad : a.Nk_pad) * (a.D / 32);
     const dim3 gr((unsigned)((rows + 255) / 256), (unsigned)a.BH, 2);
-    const int64_t cols = (int64_t)(a.Nk_pad / 32) * a.D;
-    const dim3 gv((unsigned)((cols + 255) / 256), (unsigned)a.BH);
+    // 256 / D token blocks of 32 per workgroup; Nk_pad is a multiple of 256
+    const dim3 gv((unsigned)(a.Nk_pad / 32 / (256 / a.D)), (unsigned)a.BH);
     if (a.D == 128) {
         mx_quant_rows_kernel<128><<<gr, 256, 0, st>>>(a);
         mx_quant_vt_kernel<128><<<gv, 256, 0, st>>>(a);
