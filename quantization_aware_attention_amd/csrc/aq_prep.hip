@@ -53,32 +53,39 @@ __global__ __launch_bounds__(256) void fq_axis_d_kernel(FqArgs a) {
     }
 }
 
-// One thread per (16-token group, 8 columns). Tokens >= N read as zero;
-// rows in [N, Nout) are written as zeros.
-template <bool QUANT>
+// One thread per (16-token group, CW columns). Tokens >= N read as zero;
+// rows in [N, Nout) are written as zeros. Two columns per thread (one 4-byte
+// word per row): a wave reads and writes whole 256-byte rows, with four times
+// as many threads as 8 columns (16-byte words) would give (measured on 6 x
+// 31,200 x 128 tokens: 0.045 -> 0.044 ms resident, 0.051 -> 0.046 ms after
+// a cache flush).
+template <bool QUANT, int CW>
 __global__ __launch_bounds__(256) void fq_axis_n_kernel(FqArgs a) {
-    const int C8 = a.D / 8;
+    static_assert(CW == 2 || CW == 8, "columns per thread");
+    constexpr int W = CW / 2;  // 32-bit words (bf16 pairs) per row
+    typedef uint32_t word_t __attribute__((ext_vector_type(W)));
+    const int CG = a.D / CW;
     const int64_t NGo = (a.Nout + 15) / 16;
-    const int64_t total = (int64_t)a.BH * NGo * C8;
+    const int64_t total = (int64_t)a.BH * NGo * CG;
     for (int64_t gi = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; gi < total;
          gi += (int64_t)gridDim.x * blockDim.x) {
-        const int dc = (int)(gi % C8);
-        const int64_t tg = (gi / C8) % NGo;
-        const int64_t bh = gi / ((int64_t)C8 * NGo);
+        const int dc = (int)(gi % CG);
+        const int64_t tg = (gi / CG) % NGo;
+        const int64_t bh = gi / ((int64_t)CG * NGo);
         const int64_t b = bh / a.H, h = bh % a.H;
-        const uint16_t* xb = a.x + b * a.xsb + h * a.xsh + dc * 8;
-        uint16_t* yb = a.y + b * a.ysb + h * a.ysh + dc * 8;
-        u32x4 v[16];
+        const uint16_t* xb = a.x + b * a.xsb + h * a.xsh + dc * CW;
+        uint16_t* yb = a.y + b * a.ysb + h * a.ysh + dc * CW;
+        word_t v[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
             const int64_t row = tg * 16 + t;
-            if (row < a.N) v[t] = *(const u32x4*)(xb + row * a.xsn);
-            else v[t] = u32x4{0u, 0u, 0u, 0u};
+            if (row < a.N) v[t] = *(const word_t*)(xb + row * a.xsn);
+            else v[t] = word_t{};
         }
         if (QUANT) {
-            float s[8];
+            float s[CW];
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
+            for (int c = 0; c < CW; ++c) {
                 float amax = 0.0f;
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
@@ -90,22 +97,22 @@ __global__ __launch_bounds__(256) void fq_axis_n_kernel(FqArgs a) {
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
 #pragma unroll
-                for (int c2 = 0; c2 < 4; ++c2) {
+                for (int c2 = 0; c2 < W; ++c2) {
                     const uint32_t wd = v[t][c2];
                     v[t][c2] = pack_exact(fq_elem_exact(bf_lo(wd), s[2 * c2]),
                                           fq_elem_exact(bf_hi(wd), s[2 * c2 + 1]));
                 }
             }
             if (a.codes && tg * 16 < a.N) {
-                uint8_t* cp = a.codes + (bh * ((a.N + 15) / 16) + tg) * a.D + dc * 8;
+                uint8_t* cp = a.codes + (bh * ((a.N + 15) / 16) + tg) * a.D + dc * CW;
 #pragma unroll
-                for (int c = 0; c < 8; ++c) cp[c] = e4m3_code(s[c]);
+                for (int c = 0; c < CW; ++c) cp[c] = e4m3_code(s[c]);
             }
         }
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
             const int64_t row = tg * 16 + t;
-            if (row < a.Nout) *(u32x4*)(yb + row * a.ysn) = v[t];
+            if (row < a.Nout) *(word_t*)(yb + row * a.ysn) = v[t];
         }
     }
 }
@@ -222,9 +229,10 @@ hipError_t launch_fq_axis_d(const FqArgs& a, bool quant, hipStream_t st) {
 }
 
 hipError_t launch_fq_axis_n(const FqArgs& a, bool quant, hipStream_t st) {
-    const int64_t work = (int64_t)a.BH * ((a.Nout + 15) / 16) * (a.D / 8);
-    if (quant) fq_axis_n_kernel<true><<<grid_for(work), 256, 0, st>>>(a);
-    else fq_axis_n_kernel<false><<<grid_for(work), 256, 0, st>>>(a);
+    constexpr int CW = 2;
+    const int64_t work = (int64_t)a.BH * ((a.Nout + 15) / 16) * (a.D / CW);
+    if (quant) fq_axis_n_kernel<true, CW><<<grid_for(work), 256, 0, st>>>(a);
+    else fq_axis_n_kernel<false, CW><<<grid_for(work), 256, 0, st>>>(a);
     return hipGetLastError();
 }
 
