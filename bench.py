@@ -378,6 +378,8 @@ def main():
         out["cpu_baseline"] = None
         print(json.dumps(out), flush=True)
         return
+    # Machine probes first: the MFMA-only rate and clock, and the copy rate.
+    out["machine"] = machine_probes(torch, dev)
     # Every launch below follows a 1 GiB fill of a scratch buffer (outside the
     # timed events), which evicts the 256 MB last-level cache and the L2s, so
     # the GB/s are HBM figures, not cache figures.
@@ -466,10 +468,20 @@ def main():
     mk = {name: round(tot / cnt, 4) for name, (tot, cnt) in rec.items()}
     mfwd = sum(mk.values())
     mflops = 4.0 * B * H * N * N * D
+    # The kernel is bound by vector work, not by the FP4 matrix rate: per
+    # score, pass 1 takes half a maximum instruction and pass 2 an FMA, an
+    # exponential (two issue slots), an add, half a maximum and half an FP4
+    # conversion (~2.5 slots), ~6.25 issue slots of a 64-lane instruction
+    # in all, each 4 cycles on one of the 1,024 SIMDs, at the clock the MFMA
+    # probe measures (or 2.4 GHz). That floor is reported beside the time.
+    clk = (out.get("machine") or {}).get("clock_mhz_under_mfma") or 2400.0
+    valu_ms = B * H * N * N * 6.25 / 64 * 4 / 1024 / (clk * 1e6) * 1e3
     out["mxfp4_infer"] = {
         "kernels_ms": mk, "fwd_ms": round(mfwd, 4),
         "tflops": round(mflops / (mfwd * 1e-3) / 1e12, 1),
-        "frac_fp4_peak": round(mflops / (mfwd * 1e-3) / 1e12 / PEAK_FP4_TFLOPS, 4)}
+        "frac_fp4_peak": round(mflops / (mfwd * 1e-3) / 1e12 / PEAK_FP4_TFLOPS, 4),
+        "valu_floor_ms": round(valu_ms, 3),
+        "frac_valu_floor": round(valu_ms / mk.get("mx_fwd", mfwd), 3)}
     del mo, ml
     # Variants of the P quantizer on the same inputs, reported beside the
     # metric (which is the normalised reading with the plain STE) and credited
@@ -595,7 +607,6 @@ def main():
     if not args.no_configs:
         del ws_f, ws_b
         out["configs"] = time_configs(qaa, torch, np, dev, args.workload)
-    out["machine"] = machine_probes(torch, dev)
     if args.copy_calibration:
         out["copy_calibration_bytes"] = copy_calibration(torch, dev)
     if not args.no_cpu_baseline:

@@ -162,6 +162,13 @@ hipError_t do_fq_d_q(const aq::FqArgs& a, hipStream_t st) { return aq::launch_fq
 hipError_t do_fq_d_c(const aq::FqArgs& a, hipStream_t st) { return aq::launch_fq_axis_d(a, false, st); }
 hipError_t do_fq_n_q(const aq::FqArgs& a, hipStream_t st) { return aq::launch_fq_axis_n(a, true, st); }
 hipError_t do_fq_n_c(const aq::FqArgs& a, hipStream_t st) { return aq::launch_fq_axis_n(a, false, st); }
+struct FqtArgs {
+    aq::FqArgs a;
+    bool quant, to_f16;
+};
+hipError_t do_fq_nt(const FqtArgs& t, hipStream_t st) {
+    return aq::launch_fq_n_transpose(t.a, t.quant, t.to_f16, st);
+}
 struct RevArgs {
     const int32_t* idx;
     int32_t *q_list, *q_count;
@@ -351,8 +358,7 @@ Layout layout(const Plan& pl, bool bwd) {
             L.deltakv = take((size_t)pl.BH * pl.Nq_pad * 4);
         }
     } else {
-        L.vw = take(kb);
-        L.vt = take(kb);
+        L.vt = take(kb);  // Vq^T only: the forward kernels read V transposed
     }
     L.total = off;
     return L;
@@ -393,13 +399,17 @@ int prepare_operands(const Plan& pl, uint32_t mask, const void* q, const void* k
                 fq_args(k, pl.k, ws + L.kw, wk, nullptr, pl.BH, pl.H, pl.Nk, pl.Nk_pad, pl.D), st,
                 "fake-quant K");
     if (rc) return rc;
+    if (!bwd) {
+        // the forward reads V only as V^T: quantize and transpose in one pass
+        const Strides wt{pl.H * pl.D * pl.Nk_pad, pl.D * pl.Nk_pad, 0};
+        const FqtArgs t{fq_args(v, pl.v, ws + L.vt, wt, nullptr, pl.BH, pl.H, pl.Nk, pl.Nk_pad, pl.D),
+                        (mask & ATTNQAT_QUANT_V) != 0, pl.f16_pv};
+        return launch(K_FQ_N, st, thunk<FqtArgs, do_fq_nt>, &t, "fake-quant and transpose V");
+    }
     rc = run_fq(false, mask & ATTNQAT_QUANT_V,
                 fq_args(v, pl.v, ws + L.vw, wk, nullptr, pl.BH, pl.H, pl.Nk, pl.Nk_pad, pl.D), st,
                 "fake-quant V");
     if (rc) return rc;
-    if (!bwd)
-        return run_transpose((const uint16_t*)(ws + L.vw), (uint16_t*)(ws + L.vt), pl.BH, pl.Nk_pad,
-                             pl.D, false, st, "transpose V", pl.f16_pv);
     // the permuted K^T serves the dense dQ kernel only (the block-sparse one
     // reads K^T operands from its K tiles)
     if (pl.sparse) return ATTNQAT_OK;
@@ -411,7 +421,7 @@ aq::AttnArgs attn_args(const attnqat_problem* p, const Plan& pl, char* ws, const
     aq::AttnArgs a{};
     a.Qw = (const uint16_t*)(ws + L.qw);
     a.Kw = (const uint16_t*)(ws + L.kw);
-    a.Vw = (const uint16_t*)(ws + L.vw);
+    a.Vw = L.vw ? (const uint16_t*)(ws + L.vw) : nullptr;  // offset 0 is the flag word
     a.H = pl.H;
     a.Nq = (int)pl.Nq;
     a.Nk = (int)pl.Nk;

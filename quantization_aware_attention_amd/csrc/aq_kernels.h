@@ -100,6 +100,9 @@ struct AttnArgs {
 
 hipError_t launch_fq_axis_d(const FqArgs& a, bool quant, hipStream_t st);
 hipError_t launch_fq_axis_n(const FqArgs& a, bool quant, hipStream_t st);
+// FQ along the tokens (quant) written transposed to y = [BH][D][Nout]
+// (contiguous; fp16 with to_f16). Nout and D multiples of 64.
+hipError_t launch_fq_n_transpose(const FqArgs& a, bool quant, bool to_f16, hipStream_t st);
 hipError_t launch_transpose_perm(const uint16_t* src, uint16_t* dst, int64_t BH, int Npad, int D,
                                  bool perm, bool to_f16, hipStream_t st);
 hipError_t launch_bwd_pre(const PreArgs& a, hipStream_t st);

@@ -117,6 +117,62 @@ __global__ __launch_bounds__(256) void fq_axis_n_kernel(FqArgs a) {
     }
 }
 
+// Fake quantization of V along the tokens fused with its transpose, for the
+// forward (which reads V only as V^T): y[bh][d][p] = FQ_tokens(x)[bh][p][d]
+// for p < Nout (tokens >= N are zero), the same 16-token groups and exact
+// arithmetic as fq_axis_n_kernel, so the values are bit-identical; with F16
+// they are stored as fp16 (exact for NVFP4 values). One 64-token x 64-column
+// tile per workgroup, staged in LDS (rows padded by 4 bytes); in the middle
+// each thread quantizes one 16-token group of one column in place.
+template <bool QUANT, bool F16>
+__global__ __launch_bounds__(256) void fq_n_transpose_kernel(FqArgs a) {
+    __shared__ uint16_t tile[64][64 + 2];
+    const int64_t bh = blockIdx.z, b = bh / a.H, h = bh % a.H;
+    const int n0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
+    const uint16_t* s = a.x + b * a.xsb + h * a.xsh;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < 64 * 8; i += 256) {
+        const int r = i / 8, cc = i % 8;
+        const int64_t row = n0 + r;
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if (row < a.N) w = *(const u32x4*)(s + row * a.xsn + d0 + cc * 8);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            tile[r][cc * 8 + 2 * j] = (uint16_t)(w[j] & 0xFFFFu);
+            tile[r][cc * 8 + 2 * j + 1] = (uint16_t)(w[j] >> 16);
+        }
+    }
+    __syncthreads();
+    if (QUANT) {
+        const int c = tid & 63, g = tid >> 6;  // column, 16-token group
+        float x[16], amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            x[i] = bf2f(tile[16 * g + i][c]);
+            amax = fmaxf(amax, fabsf(x[i]));
+        }
+        const float sc = e4m3_round(amax / 6.0f);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            tile[16 * g + i][c] = (uint16_t)(__float_as_uint(fq_elem_exact(x[i], sc)) >> 16);
+        __syncthreads();
+    }
+    uint16_t* o = a.y + bh * a.D * a.Nout;
+    for (int i = tid; i < 64 * 8; i += 256) {
+        const int dr = i / 8, pc = i % 8;  // output row d0 + dr, positions pc*8 .. pc*8+7
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            w[j] = (uint32_t)tile[pc * 8 + 2 * j][dr] | ((uint32_t)tile[pc * 8 + 2 * j + 1][dr] << 16);
+            if (F16) {
+                const f32x2 f = {bf_lo(w[j]), bf_hi(w[j])};
+                w[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+            }
+        }
+        *(u32x4*)(o + (int64_t)(d0 + dr) * a.Nout + n0 + pc * 8) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+}
+
 // Transposed copy: dst[bh][d][p] = src[bh][tok(p)][d] for a contiguous padded
 // [BH][Npad][D] source, with tok(p) = 16 (p / 16) + perm16(p % 16) when PERM
 // (operands read by MFMA k-slots in accumulator-row order) and tok(p) = p
@@ -233,6 +289,15 @@ hipError_t launch_fq_axis_n(const FqArgs& a, bool quant, hipStream_t st) {
     const int64_t work = (int64_t)a.BH * ((a.Nout + 15) / 16) * (a.D / CW);
     if (quant) fq_axis_n_kernel<true, CW><<<grid_for(work), 256, 0, st>>>(a);
     else fq_axis_n_kernel<false, CW><<<grid_for(work), 256, 0, st>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fq_n_transpose(const FqArgs& a, bool quant, bool to_f16, hipStream_t st) {
+    dim3 grid((unsigned)(a.Nout / 64), (unsigned)(a.D / 64), (unsigned)a.BH);
+    if (quant && to_f16) fq_n_transpose_kernel<true, true><<<grid, 256, 0, st>>>(a);
+    else if (quant) fq_n_transpose_kernel<true, false><<<grid, 256, 0, st>>>(a);
+    else if (to_f16) fq_n_transpose_kernel<false, true><<<grid, 256, 0, st>>>(a);
+    else fq_n_transpose_kernel<false, false><<<grid, 256, 0, st>>>(a);
     return hipGetLastError();
 }
 

@@ -337,8 +337,9 @@ def test_workspace_starts_with_the_index_flag(L):
     sparse = _prob(Nq=1024, Nk=1024, kv_block_idx=30 * A, topk=3)
     assert (L.attnqat_fwd_workspace_bytes(ctypes.byref(sparse)) ==
             L.attnqat_fwd_workspace_bytes(ctypes.byref(dense)))
-    # operands: Qq, Kq, Vq, Vq^T of 2 heads x 1024 tokens x 64 bf16, plus the flag
-    assert L.attnqat_fwd_workspace_bytes(ctypes.byref(dense)) == 256 + 4 * 2 * 1024 * 64 * 2
+    # operands: Qq, Kq and Vq^T (the forward reads V only transposed) of
+    # 2 heads x 1024 tokens x 64 bf16, plus the flag
+    assert L.attnqat_fwd_workspace_bytes(ctypes.byref(dense)) == 256 + 3 * 2 * 1024 * 64 * 2
 
 
 def test_noalloc_host_checks(L):

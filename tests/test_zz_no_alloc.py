@@ -80,7 +80,7 @@ def test_noalloc_rejects_problems_beyond_its_scratch(gpu_lib):
     o = torch.empty_like(t["q"])
     lse = torch.empty((1, 1, 8), dtype=torch.float32, device="cuda")
     p = _problem(gpu_lib, t, 0.1, 15, o)
-    p.H, p.Nq, p.Nk = 64, 4096, 4096      # 4 x 64 x 4096 x 128 x 2 B = 256 MiB of operands
+    p.H, p.Nq, p.Nk = 64, 4096, 4096      # 3 x 64 x 4096 x 128 x 2 B = 192 MiB of operands
     assert L.attnqat_fwd_workspace_bytes(ctypes.byref(p)) > gpu_lib.NOALLOC_SCRATCH_BYTES
     rc = L.attnqat_fwd_noalloc(ctypes.byref(p), t["q"].data_ptr(), t["k"].data_ptr(),
                                t["v"].data_ptr(), o.data_ptr(), lse.data_ptr(), None)
