@@ -384,7 +384,7 @@ struct FwdLse {
             }
             if (LAZY) {
                 const float mc0 = m * c;
-                float s0 = 0.0f;
+                float s0 = -0.0f;  // -0 + y = y: the first add folds away
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s0 += __builtin_amdgcn_exp2f(fmaf(acc[r], c, -mc0));
                 if (s0 <= kLazySum) {
@@ -396,7 +396,7 @@ struct FwdLse {
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = vmax(mx, acc[r]);
             const float mc = mx * c;
-            float sum = 0.0f;
+            float sum = -0.0f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) sum += __builtin_amdgcn_exp2f(fmaf(acc[r], c, -mc));
             l = l * __builtin_amdgcn_exp2f((m - mx) * c) + sum;

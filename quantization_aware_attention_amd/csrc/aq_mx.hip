@@ -305,7 +305,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 1) void mx_fwd_kernel(MxArgs
         if (it < n_full) {
 #pragma unroll
             for (int j = 0; j < 32; j += 2)
-                smax = vmax(smax, vmax(s[j >> 4][j & 15], s[j >> 4][(j & 15) + 1]));
+                smax = vmax(vmax(smax, s[j >> 4][j & 15]), s[j >> 4][(j & 15) + 1]);  // one maximum3 per pair
         } else {
 #pragma unroll
             for (int j = 0; j < 32; ++j)
@@ -337,13 +337,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 1) void mx_fwd_kernel(MxArgs
         }
 #pragma unroll
         for (int j = 0; j < 32; j += 2)
-            smax = vmax(smax, vmax(s[j >> 4][j & 15], s[j >> 4][(j & 15) + 1]));
+            smax = vmax(vmax(smax, s[j >> 4][j & 15]), s[j >> 4][(j & 15) + 1]);  // one maximum3 per pair
         float xmax = smax * c;
         asm volatile("" : "+v"(xmax));
         const float lb = xmax - mt;  // log2 of the block's amax (-inf: empty block)
         const int se = lb > -125.0f ? max(-127, (int)floorf(lb) - 2) : -127;
         const float off = mt + (float)se;
-        float bsum = 0.0f;
+        float bsum = -0.0f;  // -0 + y = y for every y: the first add folds away
         u32x4 pc;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
