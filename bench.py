@@ -468,14 +468,15 @@ def main():
     mk = {name: round(tot / cnt, 4) for name, (tot, cnt) in rec.items()}
     mfwd = sum(mk.values())
     mflops = 4.0 * B * H * N * N * D
-    # The kernel is bound by vector work, not by the FP4 matrix rate: per
-    # score, pass 1 takes half a maximum instruction and pass 2 an FMA, an
-    # exponential (two issue slots), an add, half a maximum and half an FP4
-    # conversion (~2.5 slots), ~6.25 issue slots of a 64-lane instruction
-    # in all, each 4 cycles on one of the 1,024 SIMDs, at the clock the MFMA
+    # The kernel is bound by vector work, not by the FP4 matrix rate. Its
+    # compiled loops issue, per 32 scores of a lane, ~26 instructions in pass
+    # 1 (maxima) and in pass 2 104 full-rate ones (FMA, add for l, maxima,
+    # addresses), 32 exponentials (two issue slots each) and 16 FP4
+    # conversions (~2.5 slots): ~7.3 slots of a 64-lane instruction per
+    # score, each 4 cycles on one of the 1,024 SIMDs, at the clock the MFMA
     # probe measures (or 2.4 GHz). That floor is reported beside the time.
     clk = (out.get("machine") or {}).get("clock_mhz_under_mfma") or 2400.0
-    valu_ms = B * H * N * N * 6.25 / 64 * 4 / 1024 / (clk * 1e6) * 1e3
+    valu_ms = B * H * N * N * 7.3 / 64 * 4 / 1024 / (clk * 1e6) * 1e3
     out["mxfp4_infer"] = {
         "kernels_ms": mk, "fwd_ms": round(mfwd, 4),
         "tflops": round(mflops / (mfwd * 1e-3) / 1e12, 1),
