@@ -74,6 +74,18 @@ int device_cus() {
     return g_dev_cus[dev];
 }
 
+// Parts to split each of the F workgroups of a launch's last, partial round
+// into (rounds of one workgroup per compute unit): the P <= kMaxDkdvParts,
+// at most `units` (a part has at least one tile), that minimises the last
+// round's length ceil(F P / CUs) / P; 1 when the last round is full.
+int split_parts(int64_t F, int cus, int64_t units) {
+    int P = 1;
+    if (F == 0) return 1;
+    for (int c = 2; c <= aq::kMaxDkdvParts && c <= units; ++c)
+        if ((double)((F * c + cus - 1) / cus) / c < (double)((F * P + cus - 1) / cus) / P) P = c;
+    return P;
+}
+
 int hip_check(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(ATTNQAT_E_HIP, "%s: %s", what, hipGetErrorString(e));
     return ATTNQAT_OK;
@@ -347,10 +359,14 @@ Layout layout(const Plan& pl, bool bwd) {
             L.qcount = take((size_t)pl.BH * pl.nbk * 4);
             L.korder = take((size_t)pl.BH * pl.nbk * 4);
         }
-        if (!pl.sparse) {  // partial sums of the key blocks dK/dV splits
+        if (!pl.sparse) {
+            // partial sums of the key blocks dK/dV splits ([part][2 x 128 rows]
+            // per block), then of the query blocks dQ splits ([part][256 rows])
             const int64_t nkb = pl.BH * ((pl.Nk + 127) / 128);
-            const int64_t ns = nkb < aq::kMaxDkdvSplit ? nkb : aq::kMaxDkdvSplit;
-            L.dkdvpart = take((size_t)ns * aq::kMaxDkdvParts * 2 * 128 * pl.D * 4);
+            const int64_t nqw = pl.BH * ((pl.Nq + 255) / 256);
+            const int64_t nb = nkb > nqw ? nkb : nqw;
+            const int64_t ns = nb < aq::kMaxDkdvSplit ? nb : aq::kMaxDkdvSplit;
+            L.dkdvpart = take((size_t)ns * aq::kMaxDkdvParts * 256 * pl.D * 4);
         }
         if (pl.rowmax) {  // dK/dV inputs of the row-max-relative variant
             L.dowkv = take(qb);
@@ -757,14 +773,18 @@ int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const vo
         if (cus > aq::kMaxDkdvSplit + 1) cus = aq::kMaxDkdvSplit + 1;
         const int64_t F = nkb % cus;
         const int64_t nt = (pl.Nq + 63) / 64;  // query tiles: a part has at least one
-        int P = 1;
-        for (int c = 2; c <= aq::kMaxDkdvParts && c <= nt; ++c)
-            if ((double)((F * c + cus - 1) / cus) / c < (double)((F * P + cus - 1) / cus) / P)
-                P = c;
-        if (F == 0) P = 1;
+        const int P = split_parts(F, cus, nt);
         a.dkdv_parts = P;
         a.dkdv_full = (int)(P > 1 ? nkb - F : nkb);
         a.dkdv_part = (float*)(ws + L.dkdvpart);
+        // dense dQ: one workgroup per 256-query block, likewise, split along
+        // the 64-key tiles into the same partial region
+        const int64_t nqw = pl.BH * ((pl.Nq + 255) / 256);
+        const int64_t Fq = nqw % cus;
+        const int Pq = split_parts(Fq, cus, (pl.Nk + 63) / 64);
+        a.dq_parts = Pq;
+        a.dq_full = (int)(Pq > 1 ? nqw - Fq : nqw);
+        a.dq_part = (float*)(ws + L.dkdvpart);
     }
     const DimArgs da{a, (int)pl.D};
     // row-max-relative variant: dK/dV quantizes exp(S - m) and takes dO and Dl

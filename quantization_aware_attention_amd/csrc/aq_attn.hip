@@ -916,9 +916,30 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) Buf s0, s1;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
-    int qblk = blockIdx.x, bh = blockIdx.y;
-    if (!SPARSE) xcd_work(qblk, bh);
-    const int q0 = qblk * (NW * 32 * QB) + wave * 32 * QB;
+    constexpr int QW = NW * 32 * QB;  // queries per workgroup
+    // Dense launches: a one-dimensional grid. The first a.dq_full workgroups
+    // take one whole query block each (head-major, each XCD a contiguous
+    // range); the blocks of the last, partial round are split into
+    // a.dq_parts parts along the keys, one workgroup per part, whose fp32
+    // partial sums bwd_dq_fixup_kernel adds (the host picks the part count).
+    int qblk = blockIdx.x, bh = blockIdx.y, t0 = 0, side = -1;
+    int n_iter = SPARSE ? a.topk * 2 : (a.Nk + BN - 1) / BN;
+    if (!SPARSE) {
+        const int nqb = (a.Nq + QW - 1) / QW, L = blockIdx.x, nf = a.dq_full;
+        int w;
+        if (L < nf) {
+            w = xcd_index(L, nf);
+        } else {
+            const int s = xcd_index(L - nf, gridDim.x - nf), P = a.dq_parts, part = s % P;
+            side = s;
+            w = nf + s / P;
+            t0 = n_iter * part / P;
+            n_iter = n_iter * (part + 1) / P - t0;
+        }
+        qblk = w % nqb;
+        bh = w / nqb;
+    }
+    const int q0 = qblk * QW + wave * 32 * QB;
     const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
     const uint16_t* dOb = a.dOw + (size_t)bh * a.Nq_pad * D;
     const uint16_t* Kb = a.Kw + (size_t)bh * a.Nk_pad * D;
@@ -946,14 +967,16 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
     static_assert(!SPARSE || (NW == 4 && QB == 1), "sparse dQ workgroups cover one query block");
     __shared__ int lst[SPARSE ? kMaxBlockList : 1];
     if (SPARSE) stage_list(lst, a.kv_idx + ((size_t)bh * a.nbq + qblk) * a.topk, a.topk);
-    const int n_iter = SPARSE ? a.topk * 2 : (a.Nk + BN - 1) / BN;
-    auto tile_at = [&](int it) { return tile_start<SPARSE, BN>(lst, it); };
+    auto tile_at = [&](int it) { return tile_start<SPARSE, BN>(lst, t0 + it); };
+    // dense: only a range that ends with the last key tile holds keys >= Nk
+    const int n_masked = SPARSE ? masked_tiles<SPARSE, BN>(lst, n_iter, a.Nk)
+                                : (n_iter > 0 && (t0 + n_iter) * BN > a.Nk ? 1 : 0);
     AsyncTile<BN, D, NT> tk;
     AsyncTile<D, BN, NT> tt;
     tk.init(D, tid);
     tt.init(a.Nk_pad, tid);
     tile_pipeline(
-        n_iter, masked_tiles<SPARSE, BN>(lst, n_iter, a.Nk),
+        n_iter, n_masked,
         [&](auto b, int it) {
             const int kt = tile_at(it);
             Buf* t = sel(b, &s0, &s1);
@@ -969,11 +992,44 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int q = q0 + qb * 32 + l32;
-        if (q < a.Nq) {
+        if (side >= 0) {
+            store_rows_f32<D>(a.dq_part + ((size_t)side * QW + (q - qblk * QW)) * D, dqa[qb], hh);
+        } else if (q < a.Nq) {
             const int64_t b = bh / a.H, h = bh % a.H;
             store_rows_T<D>(a.dq + b * a.dqsb + h * a.dqsh + (int64_t)q * a.dqsn, dqa[qb], a.sm_scale,
                             hh);
         }
+    }
+}
+
+// Sums the fp32 parts of every split query block of a dense dQ launch (in a
+// fixed order, part 0 first) and writes the block's dQ (times sm_scale) as
+// bf16. One workgroup per split block.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dq_fixup_kernel(AttnArgs a) {
+    constexpr int QW = 256;
+    const int P = a.dq_parts, w = a.dq_full + blockIdx.x;
+    const int nqb = (a.Nq + QW - 1) / QW;
+    const int bh = w / nqb, qblk = w % nqb;
+    const int64_t b = bh / a.H, h = bh % a.H;
+    const float* p0 = a.dq_part + (size_t)blockIdx.x * P * QW * D;
+    // 8 consecutive d values per thread and pass
+    for (int e = threadIdx.x * 8; e < QW * D; e += 256 * 8) {
+        const int q = qblk * QW + e / D, d = e % D;
+        if (q >= a.Nq) continue;
+        f32x4_t x0 = *(const f32x4_t*)(p0 + e), x1 = *(const f32x4_t*)(p0 + e + 4);
+        for (int part = 1; part < P; ++part) {
+            const float* r = p0 + (size_t)part * QW * D + e;
+            x0 += *(const f32x4_t*)r;
+            x1 += *(const f32x4_t*)(r + 4);
+        }
+        const float f = a.sm_scale;
+        u32x4 v;
+        v[0] = pack_rne(x0[0] * f, x0[1] * f);
+        v[1] = pack_rne(x0[2] * f, x0[3] * f);
+        v[2] = pack_rne(x1[0] * f, x1[1] * f);
+        v[3] = pack_rne(x1[2] * f, x1[3] * f);
+        *(u32x4*)(a.dq + b * a.dqsb + h * a.dqsh + (int64_t)q * a.dqsn + d) = v;
     }
 }
 
@@ -1919,9 +1975,16 @@ hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t st) {
         if (D == 128) bwd_dq_sparse_kernel<128><<<grid, 256, 0, st>>>(a);
         else bwd_dq_sparse_kernel<64><<<grid, 256, 0, st>>>(a);
     } else {
-        dim3 grid((a.Nq + 255) / 256, a.BH);
+        // one workgroup per whole query block and one per part of a split
+        // one; the split blocks are finished by the fixup
+        const int split = a.BH * ((a.Nq + 255) / 256) - a.dq_full;
+        const int grid = a.dq_full + split * a.dq_parts;
         if (D == 128) bwd_dq_kernel<128, 8, 1, false><<<grid, 512, 0, st>>>(a);
         else bwd_dq_kernel<64, 8, 1, false><<<grid, 512, 0, st>>>(a);
+        if (a.dq_parts > 1) {
+            if (D == 128) bwd_dq_fixup_kernel<128><<<split, 256, 0, st>>>(a);
+            else bwd_dq_fixup_kernel<64><<<split, 256, 0, st>>>(a);
+        }
     }
     return hipGetLastError();
 }

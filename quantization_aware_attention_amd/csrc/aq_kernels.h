@@ -87,6 +87,12 @@ struct AttnArgs {
     // [split block][part][dK, dV][128 keys][D] the fixup adds
     float* dkdv_part;
     int dkdv_full, dkdv_parts;
+    // dense dQ: query blocks (256 queries, head-major) [0, dq_full) run
+    // whole, the others are split into dq_parts parts along the keys whose
+    // fp32 partial sums [split block][part][256 queries][D] the fixup adds
+    // (the dK/dV partial region, free once its fixup has run)
+    float* dq_part;
+    int dq_full, dq_parts;
     int topk;
     int nbq, nbk;
     int64_t H;
