@@ -259,6 +259,7 @@ struct Plan {
     bool rowmax_out;  // p_mode is ATTNQAT_P_ROWMAX: the forward writes the row maxima
     bool rowmax;      // ... and P is quantized: passes 2 and dK/dV use them
     bool f16_pv;      // forward P V on fp16 operands (V^T stored as fp16)
+    size_t fo_region; // forward: bytes of the pass-2 partial sums (0: no split)
 };
 
 int validate_problem(const attnqat_problem* p, Plan& pl) {
@@ -326,13 +327,40 @@ int validate_problem(const attnqat_problem* p, Plan& pl) {
         if (((uintptr_t)p->kv_block_idx) % 4)
             return fail(ATTNQAT_E_MISALIGNED, "kv_block_idx is not 4-byte aligned");
     }
+    // dense forward pass 2 with producer/consumer pairs (P quantized, no
+    // O_ste) runs one workgroup per 256-query block in rounds of one per
+    // compute unit; the last round's blocks may be split along the keys
+    pl.fo_region = 0;
+    if (!pl.sparse && (p->quant_mask & ATTNQAT_QUANT_P) && !p->o_ste) {
+        const int64_t nqw = pl.BH * ((pl.Nq + 255) / 256), F = nqw % aq::kPlanCus;
+        const int P = split_parts(F, aq::kPlanCus, (pl.Nk + 63) / 64);
+        if (P > 1) pl.fo_region = (size_t)F * P * 256 * pl.D * 4;
+    }
     return ATTNQAT_OK;
+}
+
+// Forward pass-2 split of the current device: whole blocks and parts per
+// split block, or no split when it does not fit the planned region.
+void fwd_split(const Plan& pl, aq::AttnArgs& a, char* fo_part) {
+    const int64_t nqw = pl.BH * ((pl.Nq + 255) / 256);
+    a.fo_full = (int)nqw;
+    a.fo_parts = 1;
+    a.fo_part = nullptr;
+    if (pl.fo_region == 0) return;
+    int cus = device_cus();
+    if (cus > aq::kMaxDkdvSplit + 1) cus = aq::kMaxDkdvSplit + 1;
+    const int64_t F = nqw % cus;
+    const int P = split_parts(F, cus, (pl.Nk + 63) / 64);
+    if (P < 2 || (size_t)F * P * 256 * pl.D * 4 > pl.fo_region) return;
+    a.fo_full = (int)(nqw - F);
+    a.fo_parts = P;
+    a.fo_part = (float*)fo_part;
 }
 
 // Workspace layout (bytes, each region 256-byte aligned).
 struct Layout {
     size_t flag, qw, kw, vw, kt, vt, dow, lse2, delta, qlist, qcount, korder, dowkv, lse2kv,
-        deltakv, dkdvpart, total;
+        deltakv, dkdvpart, fopart, total;
 };
 
 Layout layout(const Plan& pl, bool bwd) {
@@ -375,6 +403,7 @@ Layout layout(const Plan& pl, bool bwd) {
         }
     } else {
         L.vt = take(kb);  // Vq^T only: the forward kernels read V transposed
+        if (pl.fo_region) L.fopart = take(pl.fo_region);
     }
     L.total = off;
     return L;
@@ -612,6 +641,7 @@ int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const vo
     a.osb = pl.o.b;
     a.osh = pl.o.h;
     a.osn = pl.o.n;
+    if (!pl.sparse) fwd_split(pl, a, ws + L.fopart);
     const DimArgs da{a, (int)pl.D};
     if (!(p->quant_mask & ATTNQAT_QUANT_P)) {
         // no P quantizer: nothing needs the final LSE before P V

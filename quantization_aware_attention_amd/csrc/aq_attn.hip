@@ -1627,14 +1627,32 @@ __global__ __launch_bounds__(1024) void fwd_out_pc_kernel(AttnArgs a) {
     const int pair = wave & 7;
     const bool producer = wave < 8;
     const int l32 = lane & 31, hh = lane >> 5;
-    int qblk, bh;
-    xcd_work(qblk, bh);
+    // A one-dimensional grid: the first a.fo_full workgroups take one whole
+    // query block each (head-major, each XCD a contiguous range); the blocks
+    // of the last, partial round are split into a.fo_parts parts along the
+    // key tiles [t0, t1), whose fp32 partial sums fwd_out_fixup_kernel adds.
+    const int nt = (a.Nk + BN - 1) / BN;
+    int qblk, bh, t0 = 0, t1 = nt, side = -1;
+    {
+        const int nqb = (a.Nq + 255) / 256, L = blockIdx.x, nf = a.fo_full;
+        int w;
+        if (L < nf) {
+            w = xcd_index(L, nf);
+        } else {
+            const int s = xcd_index(L - nf, gridDim.x - nf), P = a.fo_parts, part = s % P;
+            side = s;
+            w = nf + s / P;
+            t0 = nt * part / P;
+            t1 = nt * (part + 1) / P;
+        }
+        qblk = w % nqb;
+        bh = w / nqb;
+    }
     const int q0 = qblk * 256 + pair * 32;
     const int q = q0 + l32;
     const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
     const uint16_t* Kb = a.Kw + (size_t)bh * a.Nk_pad * D;
     const uint16_t* Vtb = a.Vt + (size_t)bh * D * a.Nk_pad;
-    const int nt = (a.Nk + BN - 1) / BN;
     const bool last_partial = nt * BN > a.Nk;
     // this wave's DMA blocks: block `wave` of the K tile (rows 4 b .. 4 b + 3
     // for D = 128, each 16 chunks; perm32 source rows) and of the V^T tile
@@ -1664,17 +1682,17 @@ __global__ __launch_bounds__(1024) void fwd_out_pc_kernel(AttnArgs a) {
         // let these loads land before any tile copy is issued (the copies
         // are invisible to the compiler's wait counts)
         wait_vm<0>();
-        issue_k(0);
+        issue_k(t0);
         wait_vm<0>();
         __syncthreads();
-        for (int t = 0; t <= nt; ++t) {
-            if (t > 0) {
+        for (int t = t0; t <= t1; ++t) {
+            if (t > t0) {
                 wait_vm<0>();
                 __syncthreads();
             }
-            if (t + 1 < nt) issue_k(t + 1);
-            if (t < nt) issue_v(t);
-            if (t >= nt) continue;
+            if (t + 1 < t1) issue_k(t + 1);
+            if (t < t1) issue_v(t);
+            if (t >= t1) continue;
             const uint16_t* K = sK[t & 1];
             uint32_t* X = &sX[t & 1][pair][0][0][0];
             auto run = [&](auto tail) {
@@ -1702,17 +1720,17 @@ __global__ __launch_bounds__(1024) void fwd_out_pc_kernel(AttnArgs a) {
         f32x16 o[D / 32];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-        issue_k(0);
+        issue_k(t0);
         wait_vm<0>();
         __syncthreads();
-        for (int t = 0; t <= nt; ++t) {
-            if (t > 0) {
+        for (int t = t0; t <= t1; ++t) {
+            if (t > t0) {
                 wait_vm<0>();
                 __syncthreads();
             }
-            if (t + 1 < nt) issue_k(t + 1);
-            if (t < nt) issue_v(t);
-            if (t == 0) continue;
+            if (t + 1 < t1) issue_k(t + 1);
+            if (t < t1) issue_v(t);
+            if (t == t0) continue;
             const uint16_t* V = sV[(t - 1) & 1];
             const uint32_t* X = &sX[(t - 1) & 1][pair][0][0][0];
 #pragma unroll
@@ -1724,7 +1742,9 @@ __global__ __launch_bounds__(1024) void fwd_out_pc_kernel(AttnArgs a) {
             }
             lds_mfma_chain<D / 8, 4>();
         }
-        if (q < a.Nq) {
+        if (side >= 0) {
+            store_rows_f32<D>(a.fo_part + ((size_t)side * 256 + pair * 32 + l32) * D, o, hh);
+        } else if (q < a.Nq) {
             float off, post;
             p_offset<QP>(a, bh, q, off, post);
             const int64_t b = bh / a.H, h = bh % a.H;
@@ -1732,6 +1752,39 @@ __global__ __launch_bounds__(1024) void fwd_out_pc_kernel(AttnArgs a) {
         }
     }
 }
+
+// Sums the fp32 parts of every split query block of a dense forward pass 2
+// (in a fixed order, part 0 first) and writes the block's O (times the
+// row's output factor) as bf16. One workgroup per split block.
+template <int D, bool QP>
+__global__ __launch_bounds__(256) void fwd_out_fixup_kernel(AttnArgs a) {
+    constexpr int QW = 256;
+    const int P = a.fo_parts, w = a.fo_full + blockIdx.x;
+    const int nqb = (a.Nq + QW - 1) / QW;
+    const int bh = w / nqb, qblk = w % nqb;
+    const int64_t b = bh / a.H, h = bh % a.H;
+    const float* p0 = a.fo_part + (size_t)blockIdx.x * P * QW * D;
+    // 8 consecutive d values per thread and pass
+    for (int e = threadIdx.x * 8; e < QW * D; e += 256 * 8) {
+        const int q = qblk * QW + e / D, d = e % D;
+        if (q >= a.Nq) continue;
+        f32x4_t x0 = *(const f32x4_t*)(p0 + e), x1 = *(const f32x4_t*)(p0 + e + 4);
+        for (int part = 1; part < P; ++part) {
+            const float* r = p0 + (size_t)part * QW * D + e;
+            x0 += *(const f32x4_t*)r;
+            x1 += *(const f32x4_t*)(r + 4);
+        }
+        float off, f;
+        p_offset<QP>(a, bh, q, off, f);
+        u32x4 v;
+        v[0] = pack_rne(x0[0] * f, x0[1] * f);
+        v[1] = pack_rne(x0[2] * f, x0[3] * f);
+        v[2] = pack_rne(x1[0] * f, x1[1] * f);
+        v[3] = pack_rne(x1[2] * f, x1[3] * f);
+        *(u32x4*)(a.o + b * a.osb + h * a.osh + (int64_t)q * a.osn + d) = v;
+    }
+}
+
 
 // ---------------------------------------------------------------------------
 // Dense forward pass 2 with the additive straight-through output, with
@@ -1918,7 +1971,11 @@ static void fwd_out_go(const AttnArgs& a, bool sp, hipStream_t st) {
     if (sp) {
         fwd_out_kernel<D, QP, F16, 4, true><<<dim3(a.nbq, a.BH), 256, 0, st>>>(a);
     } else {
-        fwd_out_pc_kernel<D, QP, F16><<<dim3((a.Nq + 255) / 256, a.BH), 1024, 0, st>>>(a);
+        // one workgroup per whole query block and one per part of a split
+        // one; the split blocks are finished by the fixup
+        const int split = a.BH * ((a.Nq + 255) / 256) - a.fo_full;
+        fwd_out_pc_kernel<D, QP, F16><<<a.fo_full + split * a.fo_parts, 1024, 0, st>>>(a);
+        if (a.fo_parts > 1) fwd_out_fixup_kernel<D, QP><<<split, 256, 0, st>>>(a);
     }
 }
 

@@ -12,6 +12,10 @@ constexpr int kTileN = 256;  // token padding granularity of every workspace ope
 // (fewer than one round of workgroups on a chip of 256 compute units).
 constexpr int kMaxDkdvParts = 4;
 constexpr int kMaxDkdvSplit = 255;
+// Compute units the forward's workspace planner assumes when it sizes the
+// pass-2 partial region (MI355X); a device with another count splits only
+// when its own split fits that region.
+constexpr int kPlanCus = 256;
 
 // Size of the fixed device scratch behind attnqat_fwd_noalloc (aq_noalloc.hip)
 // and the lookup of its address on the current device.
@@ -93,6 +97,12 @@ struct AttnArgs {
     // (the dK/dV partial region, free once its fixup has run)
     float* dq_part;
     int dq_full, dq_parts;
+    // dense forward pass 2 (P quantized, no O_ste): query blocks (256
+    // queries, head-major) [0, fo_full) run whole, the others are split into
+    // fo_parts parts along the keys whose fp32 partial sums
+    // [split block][part][256 queries][D] the fixup adds
+    float* fo_part;
+    int fo_full, fo_parts;
     int topk;
     int nbq, nbk;
     int64_t H;

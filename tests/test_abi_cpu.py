@@ -332,14 +332,34 @@ def test_block_idx_status_argument_checks(L):
 def test_workspace_starts_with_the_index_flag(L):
     """Both layouts keep the block-index check flag at offset 0 (one 256-byte
     region), which attnqat_block_idx_status reads: the sparse forward's
-    workspace is the dense one's."""
+    workspace is the dense one's operands."""
     dense = _prob(Nq=1024, Nk=1024)
     sparse = _prob(Nq=1024, Nk=1024, kv_block_idx=30 * A, topk=3)
-    assert (L.attnqat_fwd_workspace_bytes(ctypes.byref(sparse)) ==
-            L.attnqat_fwd_workspace_bytes(ctypes.byref(dense)))
     # operands: Qq, Kq and Vq^T (the forward reads V only transposed) of
     # 2 heads x 1024 tokens x 64 bf16, plus the flag
-    assert L.attnqat_fwd_workspace_bytes(ctypes.byref(dense)) == 256 + 3 * 2 * 1024 * 64 * 2
+    ops = 256 + 3 * 2 * 1024 * 64 * 2
+    assert L.attnqat_fwd_workspace_bytes(ctypes.byref(sparse)) == ops
+    # the dense pass 2 runs 8 workgroups of 256 queries, a partial round on a
+    # chip of 256 compute units, so each is split into 4 parts along its 16
+    # key tiles: fp32 partial sums of 8 x 4 x 256 x 64
+    assert L.attnqat_fwd_workspace_bytes(ctypes.byref(dense)) == ops + 8 * 4 * 256 * 64 * 4
+
+
+def test_forward_split_region(L):
+    """The pass-2 partial region exists only where the dense producer/consumer
+    pass 2 runs (P quantized, no O_ste) and its last round is partial."""
+    def fwd_ws(**kw):
+        return L.attnqat_fwd_workspace_bytes(ctypes.byref(_prob(**kw)))
+    ops = 256 + 3 * 2 * 1024 * 64 * 2
+    assert fwd_ws(Nq=1024, Nk=1024, quant_mask=7) == ops        # no P quantizer: one pass
+    assert fwd_ws(Nq=1024, Nk=1024, o_ste=30 * A) == ops        # pass 2 with O_ste
+    # 256 heads x 256 queries: one whole round of 256 workgroups
+    full = 256 + 3 * 256 * 256 * 64 * 2
+    assert fwd_ws(H=256, Nq=256, Nk=256) == full
+    # 264 heads: 8 workgroups in the second round, 4 key tiles each -> 4 parts
+    assert fwd_ws(H=264, Nq=256, Nk=256) == 256 + 3 * 264 * 256 * 64 * 2 + 8 * 4 * 256 * 64 * 4
+    # a single key tile cannot be split (Kq and Vq^T padded to 256 tokens)
+    assert fwd_ws(Nq=1024, Nk=64) == 256 + 2 * 1024 * 64 * 2 + 2 * (2 * 256 * 64 * 2)
 
 
 def test_noalloc_host_checks(L):
