@@ -86,6 +86,27 @@ int split_parts(int64_t F, int cus, int64_t units) {
     return P;
 }
 
+// Last-round split of a launch over nblk blocks of nt key tiles, one
+// workgroup per block per compute unit (dense dQ and forward pass 2): full
+// workgroups, and the tiles per further workgroup (chunk, 0: no split) and
+// their count (chunks) that spread the F = nblk % cus blocks of the last
+// round over up to `cus` workgroups of at least kMinChunkTiles tiles each.
+// A last round more than 4/5 full is left whole: the chip runs a partly
+// idle round at a higher clock, and at 86% (220 of 256 blocks, 6 heads x
+// 31,200 tokens) spreading it measured 1-3% slower with the fixup, against
+// 3-8% faster at 59% and 9% full.
+struct StreamSplit {
+    int64_t full, chunk, chunks;
+};
+StreamSplit stream_split(int64_t nblk, int64_t nt, int cus) {
+    const int64_t F = nblk % cus, total = F * nt;
+    int64_t g = total / aq::kMinChunkTiles;
+    if (g > cus) g = cus;
+    if (F == 0 || g <= F || 5 * F > 4 * (int64_t)cus) return {nblk, 0, 0};  // nothing to gain
+    const int64_t chunk = (total + g - 1) / g;
+    return {nblk - F, chunk, (total + chunk - 1) / chunk};
+}
+
 int hip_check(hipError_t e, const char* what) {
     if (e != hipSuccess) return fail(ATTNQAT_E_HIP, "%s: %s", what, hipGetErrorString(e));
     return ATTNQAT_OK;
@@ -259,6 +280,7 @@ struct Plan {
     bool rowmax_out;  // p_mode is ATTNQAT_P_ROWMAX: the forward writes the row maxima
     bool rowmax;      // ... and P is quantized: passes 2 and dK/dV use them
     bool f16_pv;      // forward P V on fp16 operands (V^T stored as fp16)
+    size_t q_region;  // dense: bytes of the dQ partial sums (0: no split)
     size_t fo_region; // forward: bytes of the pass-2 partial sums (0: no split)
 };
 
@@ -330,37 +352,37 @@ int validate_problem(const attnqat_problem* p, Plan& pl) {
     // dense forward pass 2 with producer/consumer pairs (P quantized, no
     // O_ste) runs one workgroup per 256-query block in rounds of one per
     // compute unit; the last round's blocks may be split along the keys
-    pl.fo_region = 0;
-    if (!pl.sparse && (p->quant_mask & ATTNQAT_QUANT_P) && !p->o_ste) {
-        const int64_t nqw = pl.BH * ((pl.Nq + 255) / 256), F = nqw % aq::kPlanCus;
-        const int P = split_parts(F, aq::kPlanCus, (pl.Nk + 63) / 64);
-        if (P > 1) pl.fo_region = (size_t)F * P * 256 * pl.D * 4;
-    }
+    // dense dQ and forward pass 2 (P quantized, no O_ste) run one workgroup
+    // per 256-query block in rounds of one per compute unit; the planned
+    // split of the last round sizes their partial regions (two slots of 256
+    // x D fp32 per last-round workgroup)
+    const int64_t nqw = pl.BH * ((pl.Nq + 255) / 256), nkt = (pl.Nk + 63) / 64;
+    const StreamSplit sq = stream_split(nqw, nkt, aq::kPlanCus);
+    pl.q_region = pl.sparse ? 0 : (size_t)(2 * sq.chunks) * 256 * pl.D * 4;
+    pl.fo_region = (!pl.sparse && (p->quant_mask & ATTNQAT_QUANT_P) && !p->o_ste) ? pl.q_region : 0;
     return ATTNQAT_OK;
 }
 
-// Forward pass-2 split of the current device: whole blocks and parts per
-// split block, or no split when it does not fit the planned region.
-void fwd_split(const Plan& pl, aq::AttnArgs& a, char* fo_part) {
+// Last-round split of dense dQ or forward pass 2 on the current device, or
+// none when it does not fit the planned region of `region` bytes.
+void query_split(const Plan& pl, size_t region, int& full, int& chunk, int& chunks) {
     const int64_t nqw = pl.BH * ((pl.Nq + 255) / 256);
-    a.fo_full = (int)nqw;
-    a.fo_parts = 1;
-    a.fo_part = nullptr;
-    if (pl.fo_region == 0) return;
+    full = (int)nqw;
+    chunk = chunks = 0;
+    if (region == 0) return;
     int cus = device_cus();
     if (cus > aq::kMaxDkdvSplit + 1) cus = aq::kMaxDkdvSplit + 1;
-    const int64_t F = nqw % cus;
-    const int P = split_parts(F, cus, (pl.Nk + 63) / 64);
-    if (P < 2 || (size_t)F * P * 256 * pl.D * 4 > pl.fo_region) return;
-    a.fo_full = (int)(nqw - F);
-    a.fo_parts = P;
-    a.fo_part = (float*)fo_part;
+    const StreamSplit s = stream_split(nqw, (pl.Nk + 63) / 64, cus);
+    if (!s.chunk || (size_t)(2 * s.chunks) * 256 * pl.D * 4 > region) return;
+    full = (int)s.full;
+    chunk = (int)s.chunk;
+    chunks = (int)s.chunks;
 }
 
 // Workspace layout (bytes, each region 256-byte aligned).
 struct Layout {
     size_t flag, qw, kw, vw, kt, vt, dow, lse2, delta, qlist, qcount, korder, dowkv, lse2kv,
-        deltakv, dkdvpart, fopart, total;
+        deltakv, dkdvpart, dkdvpart_bytes, fopart, total;
 };
 
 Layout layout(const Plan& pl, bool bwd) {
@@ -391,10 +413,10 @@ Layout layout(const Plan& pl, bool bwd) {
             // partial sums of the key blocks dK/dV splits ([part][2 x 128 rows]
             // per block), then of the query blocks dQ splits ([part][256 rows])
             const int64_t nkb = pl.BH * ((pl.Nk + 127) / 128);
-            const int64_t nqw = pl.BH * ((pl.Nq + 255) / 256);
-            const int64_t nb = nkb > nqw ? nkb : nqw;
-            const int64_t ns = nb < aq::kMaxDkdvSplit ? nb : aq::kMaxDkdvSplit;
-            L.dkdvpart = take((size_t)ns * aq::kMaxDkdvParts * 256 * pl.D * 4);
+            const int64_t ns = nkb < aq::kMaxDkdvSplit ? nkb : aq::kMaxDkdvSplit;
+            const size_t kv = (size_t)ns * aq::kMaxDkdvParts * 256 * pl.D * 4;
+            L.dkdvpart_bytes = kv > pl.q_region ? kv : pl.q_region;
+            L.dkdvpart = take(L.dkdvpart_bytes);
         }
         if (pl.rowmax) {  // dK/dV inputs of the row-max-relative variant
             L.dowkv = take(qb);
@@ -641,7 +663,10 @@ int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const vo
     a.osb = pl.o.b;
     a.osh = pl.o.h;
     a.osn = pl.o.n;
-    if (!pl.sparse) fwd_split(pl, a, ws + L.fopart);
+    if (!pl.sparse) {
+        query_split(pl, pl.fo_region, a.fo_full, a.fo_chunk, a.fo_chunks);
+        a.fo_part = (float*)(ws + L.fopart);
+    }
     const DimArgs da{a, (int)pl.D};
     if (!(p->quant_mask & ATTNQAT_QUANT_P)) {
         // no P quantizer: nothing needs the final LSE before P V
@@ -807,13 +832,9 @@ int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const vo
         a.dkdv_parts = P;
         a.dkdv_full = (int)(P > 1 ? nkb - F : nkb);
         a.dkdv_part = (float*)(ws + L.dkdvpart);
-        // dense dQ: one workgroup per 256-query block, likewise, split along
-        // the 64-key tiles into the same partial region
-        const int64_t nqw = pl.BH * ((pl.Nq + 255) / 256);
-        const int64_t Fq = nqw % cus;
-        const int Pq = split_parts(Fq, cus, (pl.Nk + 63) / 64);
-        a.dq_parts = Pq;
-        a.dq_full = (int)(Pq > 1 ? nqw - Fq : nqw);
+        // dense dQ: one workgroup per 256-query block, its last round shared
+        // out along the key tiles, partial sums in the same region
+        query_split(pl, L.dkdvpart_bytes, a.dq_full, a.dq_chunk, a.dq_chunks);
         a.dq_part = (float*)(ws + L.dkdvpart);
     }
     const DimArgs da{a, (int)pl.D};

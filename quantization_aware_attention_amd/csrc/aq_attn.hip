@@ -162,6 +162,51 @@ __device__ __forceinline__ void xcd_work(int& tile, int& bh) {
     bh = w / nx;
 }
 
+// Work of one workgroup of a dense launch over nblk blocks of nt tiles each
+// that runs in rounds of one workgroup per compute unit. The first nf
+// workgroups take one whole block each (head-major, each XCD a contiguous
+// range). The F = nblk - nf blocks of the last, partial round are dealt out
+// as one run of F nt tiles, `chunk` consecutive tiles per further workgroup
+// (stream-K), so that the round's work spreads over every compute unit. A
+// chunk (chunk <= nt) covers the end of one block and the start of the next
+// at most: up to two segments, whose fp32 partial sums go to slots 2 c and
+// 2 c + 1 of chunk c, for a fixup to add.
+struct Seg {
+    int blk, t0, t1, slot;  // block, tile range [t0, t1), partial slot (-1: whole block)
+};
+__device__ __forceinline__ int work_segments(int nf, int nblk, int nt, int chunk, Seg* s) {
+    const int L = blockIdx.x;
+    if (L < nf) {
+        s[0] = Seg{xcd_index(L, nf), 0, nt, -1};
+        return 1;
+    }
+    const int c = xcd_index(L - nf, gridDim.x - nf);
+    const int total = (nblk - nf) * nt, start = c * chunk, end = min(start + chunk, total);
+    const int j = start / nt, e0 = min(end, (j + 1) * nt);
+    s[0] = Seg{nf + j, start - j * nt, e0 - j * nt, 2 * c};
+    if (end <= e0) return 1;
+    s[1] = Seg{nf + j + 1, 0, end - (j + 1) * nt, 2 * c + 1};
+    return 2;
+}
+
+// Adds the partial sums of last-round block j (0-based within the round) in
+// chunk order: rows of 256 x D fp32 per slot; x (8 values at element e) is
+// the sum. Chunk c's segment in block j is its second when the chunk starts
+// in block j - 1.
+template <int D>
+__device__ __forceinline__ void sum_slots(const float* part, int j, int nt, int chunk, int e,
+                                          f32x4_t& x0, f32x4_t& x1) {
+    const int c0 = j * nt / chunk, c1 = ((j + 1) * nt - 1) / chunk;
+    x0 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    x1 = x0;
+    for (int c = c0; c <= c1; ++c) {
+        const int slot = 2 * c + (c * chunk / nt < j ? 1 : 0);
+        const float* r = part + (size_t)slot * 256 * D + e;
+        x0 += *(const f32x4_t*)r;
+        x1 += *(const f32x4_t*)(r + 4);
+    }
+}
+
 // Largest block list a sparse workgroup stages in LDS (key blocks per query
 // block, or query blocks per key block).
 constexpr int kMaxBlockList = 1024;
@@ -917,112 +962,105 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
     constexpr int QW = NW * 32 * QB;  // queries per workgroup
-    // Dense launches: a one-dimensional grid. The first a.dq_full workgroups
-    // take one whole query block each (head-major, each XCD a contiguous
-    // range); the blocks of the last, partial round are split into
-    // a.dq_parts parts along the keys, one workgroup per part, whose fp32
-    // partial sums bwd_dq_fixup_kernel adds (the host picks the part count).
-    int qblk = blockIdx.x, bh = blockIdx.y, t0 = 0, side = -1;
-    int n_iter = SPARSE ? a.topk * 2 : (a.Nk + BN - 1) / BN;
-    if (!SPARSE) {
-        const int nqb = (a.Nq + QW - 1) / QW, L = blockIdx.x, nf = a.dq_full;
-        int w;
-        if (L < nf) {
-            w = xcd_index(L, nf);
-        } else {
-            const int s = xcd_index(L - nf, gridDim.x - nf), P = a.dq_parts, part = s % P;
-            side = s;
-            w = nf + s / P;
-            t0 = n_iter * part / P;
-            n_iter = n_iter * (part + 1) / P - t0;
-        }
-        qblk = w % nqb;
-        bh = w / nqb;
-    }
-    const int q0 = qblk * QW + wave * 32 * QB;
-    const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
-    const uint16_t* dOb = a.dOw + (size_t)bh * a.Nq_pad * D;
-    const uint16_t* Kb = a.Kw + (size_t)bh * a.Nk_pad * D;
-    const uint16_t* Vb = a.Vw + (size_t)bh * a.Nk_pad * D;
-    const uint16_t* Ktb = a.Kt + (size_t)bh * D * a.Nk_pad;
-    u32x4 qf[QB][D / 16], df[QB][D / 16];
-    float lse2[QB], dl[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int q = q0 + qb * 32 + l32;
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-            qf[qb][c] = *(const u32x4*)(Qb + (size_t)q * D + c * 16 + hh * 8);
-            df[qb][c] = *(const u32x4*)(dOb + (size_t)q * D + c * 16 + hh * 8);
-        }
-        lse2[qb] = a.lse2[(size_t)bh * a.Nq_pad + q];
-        dl[qb] = a.delta[(size_t)bh * a.Nq_pad + q];
-    }
-    f32x16 dqa[QB][D / 32];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) dqa[qb][db] = f32x16{};
     // sparse launches use NW = 4, QB = 1 so that a workgroup is one 128-query block
     static_assert(!SPARSE || (NW == 4 && QB == 1), "sparse dQ workgroups cover one query block");
     __shared__ int lst[SPARSE ? kMaxBlockList : 1];
-    if (SPARSE) stage_list(lst, a.kv_idx + ((size_t)bh * a.nbq + qblk) * a.topk, a.topk);
-    auto tile_at = [&](int it) { return tile_start<SPARSE, BN>(lst, t0 + it); };
-    // dense: only a range that ends with the last key tile holds keys >= Nk
-    const int n_masked = SPARSE ? masked_tiles<SPARSE, BN>(lst, n_iter, a.Nk)
-                                : (n_iter > 0 && (t0 + n_iter) * BN > a.Nk ? 1 : 0);
     AsyncTile<BN, D, NT> tk;
     AsyncTile<D, BN, NT> tt;
     tk.init(D, tid);
     tt.init(a.Nk_pad, tid);
-    tile_pipeline(
-        n_iter, n_masked,
-        [&](auto b, int it) {
-            const int kt = tile_at(it);
-            Buf* t = sel(b, &s0, &s1);
-            tk.issue(t->k, Kb + (size_t)kt * D);
-            tk.issue(t->v, Vb + (size_t)kt * D);
-            tt.issue(t->kt, Ktb + kt);
-        },
-        [&](auto b, int it, auto tail) {
-            Buf* t = sel(b, &s0, &s1);
-            DQ::template block<decltype(tail)::value>(t->k, t->v, t->kt, tile_at(it), a.Nk, qf, df,
-                                                      a.c, lse2, dl, dqa, l32, hh);
-        });
+    // one query block qblk of head bh over key tiles [t0, t1); slot >= 0:
+    // fp32 partial sums to that slot instead of dQ
+    auto segment = [&](int qblk, int bh, int t0, int t1, int slot) {
+        const int q0 = qblk * QW + wave * 32 * QB;
+        const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
+        const uint16_t* dOb = a.dOw + (size_t)bh * a.Nq_pad * D;
+        const uint16_t* Kb = a.Kw + (size_t)bh * a.Nk_pad * D;
+        const uint16_t* Vb = a.Vw + (size_t)bh * a.Nk_pad * D;
+        const uint16_t* Ktb = a.Kt + (size_t)bh * D * a.Nk_pad;
+        u32x4 qf[QB][D / 16], df[QB][D / 16];
+        float lse2[QB], dl[QB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int q = q0 + qb * 32 + l32;
-        if (side >= 0) {
-            store_rows_f32<D>(a.dq_part + ((size_t)side * QW + (q - qblk * QW)) * D, dqa[qb], hh);
-        } else if (q < a.Nq) {
-            const int64_t b = bh / a.H, h = bh % a.H;
-            store_rows_T<D>(a.dq + b * a.dqsb + h * a.dqsh + (int64_t)q * a.dqsn, dqa[qb], a.sm_scale,
-                            hh);
+        for (int qb = 0; qb < QB; ++qb) {
+            const int q = q0 + qb * 32 + l32;
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) {
+                qf[qb][c] = *(const u32x4*)(Qb + (size_t)q * D + c * 16 + hh * 8);
+                df[qb][c] = *(const u32x4*)(dOb + (size_t)q * D + c * 16 + hh * 8);
+            }
+            lse2[qb] = a.lse2[(size_t)bh * a.Nq_pad + q];
+            dl[qb] = a.delta[(size_t)bh * a.Nq_pad + q];
         }
+        f32x16 dqa[QB][D / 32];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) dqa[qb][db] = f32x16{};
+        if (SPARSE) stage_list(lst, a.kv_idx + ((size_t)bh * a.nbq + qblk) * a.topk, a.topk);
+        const int n_iter = t1 - t0;
+        auto tile_at = [&](int it) { return tile_start<SPARSE, BN>(lst, t0 + it); };
+        // dense: only a range that ends with the last key tile holds keys >= Nk
+        const int n_masked = SPARSE ? masked_tiles<SPARSE, BN>(lst, n_iter, a.Nk)
+                                    : (n_iter > 0 && t1 * BN > a.Nk ? 1 : 0);
+        tile_pipeline(
+            n_iter, n_masked,
+            [&](auto b, int it) {
+                const int kt = tile_at(it);
+                Buf* t = sel(b, &s0, &s1);
+                tk.issue(t->k, Kb + (size_t)kt * D);
+                tk.issue(t->v, Vb + (size_t)kt * D);
+                tt.issue(t->kt, Ktb + kt);
+            },
+            [&](auto b, int it, auto tail) {
+                Buf* t = sel(b, &s0, &s1);
+                DQ::template block<decltype(tail)::value>(t->k, t->v, t->kt, tile_at(it), a.Nk, qf,
+                                                          df, a.c, lse2, dl, dqa, l32, hh);
+            });
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int q = q0 + qb * 32 + l32;
+            if (slot >= 0) {
+                store_rows_f32<D>(a.dq_part + ((size_t)slot * QW + (q - qblk * QW)) * D, dqa[qb], hh);
+            } else if (q < a.Nq) {
+                const int64_t b = bh / a.H, h = bh % a.H;
+                store_rows_T<D>(a.dq + b * a.dqsb + h * a.dqsh + (int64_t)q * a.dqsn, dqa[qb],
+                                a.sm_scale, hh);
+            }
+        }
+    };
+    if (SPARSE) {
+        segment(blockIdx.x, blockIdx.y, 0, a.topk * 2, -1);
+        return;
+    }
+    // dense: whole query blocks, or up to two segments of the last round
+    // (work_segments); the fixup adds the partial sums
+    static_assert(SPARSE || QW == 256, "dense dQ partial slots hold 256 queries");
+    const int nqb = (a.Nq + QW - 1) / QW, nt = (a.Nk + BN - 1) / BN;
+    Seg sg[2];
+    const int ns = work_segments(a.dq_full, a.BH * nqb, nt, a.dq_chunk, sg);
+    segment(sg[0].blk % nqb, sg[0].blk / nqb, sg[0].t0, sg[0].t1, sg[0].slot);
+    if (ns > 1) {
+        __syncthreads();  // every wave is done with the tile buffers
+        segment(sg[1].blk % nqb, sg[1].blk / nqb, sg[1].t0, sg[1].t1, sg[1].slot);
     }
 }
 
-// Sums the fp32 parts of every split query block of a dense dQ launch (in a
-// fixed order, part 0 first) and writes the block's dQ (times sm_scale) as
-// bf16. One workgroup per split block.
+// Sums the partial sums of every last-round query block of a dense dQ
+// launch that splits its last round (in chunk order) and writes the block's
+// dQ (times sm_scale) as bf16. One workgroup per block.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dq_fixup_kernel(AttnArgs a) {
     constexpr int QW = 256;
-    const int P = a.dq_parts, w = a.dq_full + blockIdx.x;
-    const int nqb = (a.Nq + QW - 1) / QW;
+    const int j = blockIdx.x, w = a.dq_full + j;
+    const int nqb = (a.Nq + QW - 1) / QW, nt = (a.Nk + 63) / 64;
     const int bh = w / nqb, qblk = w % nqb;
     const int64_t b = bh / a.H, h = bh % a.H;
-    const float* p0 = a.dq_part + (size_t)blockIdx.x * P * QW * D;
     // 8 consecutive d values per thread and pass
     for (int e = threadIdx.x * 8; e < QW * D; e += 256 * 8) {
         const int q = qblk * QW + e / D, d = e % D;
         if (q >= a.Nq) continue;
-        f32x4_t x0 = *(const f32x4_t*)(p0 + e), x1 = *(const f32x4_t*)(p0 + e + 4);
-        for (int part = 1; part < P; ++part) {
-            const float* r = p0 + (size_t)part * QW * D + e;
-            x0 += *(const f32x4_t*)r;
-            x1 += *(const f32x4_t*)(r + 4);
-        }
+        f32x4_t x0, x1;
+        sum_slots<D>(a.dq_part, j, nt, a.dq_chunk, e, x0, x1);
         const float f = a.sm_scale;
         u32x4 v;
         v[0] = pack_rne(x0[0] * f, x0[1] * f);
@@ -1627,33 +1665,13 @@ __global__ __launch_bounds__(1024) void fwd_out_pc_kernel(AttnArgs a) {
     const int pair = wave & 7;
     const bool producer = wave < 8;
     const int l32 = lane & 31, hh = lane >> 5;
-    // A one-dimensional grid: the first a.fo_full workgroups take one whole
-    // query block each (head-major, each XCD a contiguous range); the blocks
-    // of the last, partial round are split into a.fo_parts parts along the
-    // key tiles [t0, t1), whose fp32 partial sums fwd_out_fixup_kernel adds.
-    const int nt = (a.Nk + BN - 1) / BN;
-    int qblk, bh, t0 = 0, t1 = nt, side = -1;
-    {
-        const int nqb = (a.Nq + 255) / 256, L = blockIdx.x, nf = a.fo_full;
-        int w;
-        if (L < nf) {
-            w = xcd_index(L, nf);
-        } else {
-            const int s = xcd_index(L - nf, gridDim.x - nf), P = a.fo_parts, part = s % P;
-            side = s;
-            w = nf + s / P;
-            t0 = nt * part / P;
-            t1 = nt * (part + 1) / P;
-        }
-        qblk = w % nqb;
-        bh = w / nqb;
-    }
-    const int q0 = qblk * 256 + pair * 32;
-    const int q = q0 + l32;
-    const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
-    const uint16_t* Kb = a.Kw + (size_t)bh * a.Nk_pad * D;
-    const uint16_t* Vtb = a.Vt + (size_t)bh * D * a.Nk_pad;
+    // A one-dimensional grid: whole query blocks, or up to two segments of
+    // the last round's key tiles (work_segments), whose fp32 partial sums
+    // fwd_out_fixup_kernel adds.
+    const int nt = (a.Nk + BN - 1) / BN, nqb = (a.Nq + 255) / 256;
     const bool last_partial = nt * BN > a.Nk;
+    Seg sg[2];
+    const int ns = work_segments(a.fo_full, a.BH * nqb, nt, a.fo_chunk, sg);
     // this wave's DMA blocks: block `wave` of the K tile (rows 4 b .. 4 b + 3
     // for D = 128, each 16 chunks; perm32 source rows) and of the V^T tile
     // (rows 8 b .. 8 b + 7, 8 chunks each); lane i fills slot 16 i
@@ -1666,114 +1684,124 @@ __global__ __launch_bounds__(1024) void fwd_out_pc_kernel(AttnArgs a) {
         const int vr = wave * 8 + (lane >> 3), vc = lane & 7;
         voff = (uint32_t)(vr * a.Nk_pad + ((vc ^ swz<BN>(vr)) << 3)) * 2u;
     }
-    auto issue_k = [&](int t) {
-        if (wave < KBLK) dma16(lds_addr(sK[t & 1] + wave * 512), Kb + (size_t)t * BN * D, koff);
-    };
-    auto issue_v = [&](int t) {
-        if (wave < VBLK) dma16(lds_addr(sV[t & 1] + wave * 512), Vtb + t * BN, voff);
-    };
-    if (producer) {
-        u32x4 qf[D / 16];
+    auto segment = [&](const Seg& sgi) {
+        const int qblk = sgi.blk % nqb, bh = sgi.blk / nqb;
+        const int t0 = sgi.t0, t1 = sgi.t1, slot = sgi.slot;
+        const int q0 = qblk * 256 + pair * 32;
+        const int q = q0 + l32;
+        const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
+        const uint16_t* Kb = a.Kw + (size_t)bh * a.Nk_pad * D;
+        const uint16_t* Vtb = a.Vt + (size_t)bh * D * a.Nk_pad;
+        auto issue_k = [&](int t) {
+            if (wave < KBLK) dma16(lds_addr(sK[t & 1] + wave * 512), Kb + (size_t)t * BN * D, koff);
+        };
+        auto issue_v = [&](int t) {
+            if (wave < VBLK) dma16(lds_addr(sV[t & 1] + wave * 512), Vtb + t * BN, voff);
+        };
+        if (producer) {
+            u32x4 qf[D / 16];
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c)
-            qf[c] = *(const u32x4*)(Qb + (size_t)q * D + c * 16 + hh * 8);
-        float lse2, post;
-        p_offset<QP>(a, bh, q, lse2, post);
-        // let these loads land before any tile copy is issued (the copies
-        // are invisible to the compiler's wait counts)
-        wait_vm<0>();
-        issue_k(t0);
-        wait_vm<0>();
-        __syncthreads();
-        for (int t = t0; t <= t1; ++t) {
-            if (t > t0) {
-                wait_vm<0>();
-                __syncthreads();
-            }
-            if (t + 1 < t1) issue_k(t + 1);
-            if (t < t1) issue_v(t);
-            if (t >= t1) continue;
-            const uint16_t* K = sK[t & 1];
-            uint32_t* X = &sX[t & 1][pair][0][0][0];
-            auto run = [&](auto tail) {
-                constexpr bool TL = decltype(tail)::value;
-                const f32x16 s0 = scores_T<D>(K, 0, qf, l32, hh);
-                lds_mfma_chain<D / 16, 4>();
-                const f32x16 s1 = scores_T<D>(K, 32, qf, l32, hh);
-                u32x4 b0[2], b1[2];
-                F::template probs<TL>(s0, t * BN, a.Nk, a.c, lse2, hh, b0);
-                // the vector work of block 0 ahead of block 1's products
-                // (2.46 -> 2.40 ms at 6 heads x 31,200 tokens against one
-                // product per 8 vector instructions)
-                mfma_chain_front<D / 16, 1, 4, 64, 0>();
-                F::template probs<TL>(s1, t * BN + 32, a.Nk, a.c, lse2, hh, b1);
-#pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    *(u32x4*)(X + ((0 * 2 + g) * 64 + lane) * 4) = b0[g];
-                    *(u32x4*)(X + ((1 * 2 + g) * 64 + lane) * 4) = b1[g];
+            for (int c = 0; c < D / 16; ++c)
+                qf[c] = *(const u32x4*)(Qb + (size_t)q * D + c * 16 + hh * 8);
+            float lse2, post;
+            p_offset<QP>(a, bh, q, lse2, post);
+            // let these loads land before any tile copy is issued (the copies
+            // are invisible to the compiler's wait counts)
+            wait_vm<0>();
+            issue_k(t0);
+            wait_vm<0>();
+            __syncthreads();
+            for (int t = t0; t <= t1; ++t) {
+                if (t > t0) {
+                    wait_vm<0>();
+                    __syncthreads();
                 }
-            };
-            if (last_partial && t == nt - 1) run(std::true_type{});
-            else run(std::false_type{});
-        }
-    } else {
-        f32x16 o[D / 32];
+                if (t + 1 < t1) issue_k(t + 1);
+                if (t < t1) issue_v(t);
+                if (t >= t1) continue;
+                const uint16_t* K = sK[t & 1];
+                uint32_t* X = &sX[t & 1][pair][0][0][0];
+                auto run = [&](auto tail) {
+                    constexpr bool TL = decltype(tail)::value;
+                    const f32x16 s0 = scores_T<D>(K, 0, qf, l32, hh);
+                    lds_mfma_chain<D / 16, 4>();
+                    const f32x16 s1 = scores_T<D>(K, 32, qf, l32, hh);
+                    u32x4 b0[2], b1[2];
+                    F::template probs<TL>(s0, t * BN, a.Nk, a.c, lse2, hh, b0);
+                    // the vector work of block 0 ahead of block 1's products
+                    // (2.46 -> 2.40 ms at 6 heads x 31,200 tokens against one
+                    // product per 8 vector instructions)
+                    mfma_chain_front<D / 16, 1, 4, 64, 0>();
+                    F::template probs<TL>(s1, t * BN + 32, a.Nk, a.c, lse2, hh, b1);
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-        issue_k(t0);
-        wait_vm<0>();
-        __syncthreads();
-        for (int t = t0; t <= t1; ++t) {
-            if (t > t0) {
-                wait_vm<0>();
-                __syncthreads();
+                    for (int g = 0; g < 2; ++g) {
+                        *(u32x4*)(X + ((0 * 2 + g) * 64 + lane) * 4) = b0[g];
+                        *(u32x4*)(X + ((1 * 2 + g) * 64 + lane) * 4) = b1[g];
+                    }
+                };
+                if (last_partial && t == nt - 1) run(std::true_type{});
+                else run(std::false_type{});
             }
-            if (t + 1 < t1) issue_k(t + 1);
-            if (t < t1) issue_v(t);
-            if (t == t0) continue;
-            const uint16_t* V = sV[(t - 1) & 1];
-            const uint32_t* X = &sX[(t - 1) & 1][pair][0][0][0];
+        } else {
+            f32x16 o[D / 32];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                u32x4 bfr[2];
+            for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+            issue_k(t0);
+            wait_vm<0>();
+            __syncthreads();
+            for (int t = t0; t <= t1; ++t) {
+                if (t > t0) {
+                    wait_vm<0>();
+                    __syncthreads();
+                }
+                if (t + 1 < t1) issue_k(t + 1);
+                if (t < t1) issue_v(t);
+                if (t == t0) continue;
+                const uint16_t* V = sV[(t - 1) & 1];
+                const uint32_t* X = &sX[(t - 1) & 1][pair][0][0][0];
 #pragma unroll
-                for (int g = 0; g < 2; ++g) bfr[g] = *(const u32x4*)(X + ((kb * 2 + g) * 64 + lane) * 4);
-                F::pv(V, kb, bfr, o, l32, hh);
+                for (int kb = 0; kb < 2; ++kb) {
+                    u32x4 bfr[2];
+#pragma unroll
+                    for (int g = 0; g < 2; ++g)
+                        bfr[g] = *(const u32x4*)(X + ((kb * 2 + g) * 64 + lane) * 4);
+                    F::pv(V, kb, bfr, o, l32, hh);
+                }
+                lds_mfma_chain<D / 8, 4>();
             }
-            lds_mfma_chain<D / 8, 4>();
+            if (slot >= 0) {
+                store_rows_f32<D>(a.fo_part + ((size_t)slot * 256 + pair * 32 + l32) * D, o, hh);
+            } else if (q < a.Nq) {
+                float off, post;
+                p_offset<QP>(a, bh, q, off, post);
+                const int64_t b = bh / a.H, h = bh % a.H;
+                store_rows_T<D>(a.o + b * a.osb + h * a.osh + (int64_t)q * a.osn, o, post, hh);
+            }
         }
-        if (side >= 0) {
-            store_rows_f32<D>(a.fo_part + ((size_t)side * 256 + pair * 32 + l32) * D, o, hh);
-        } else if (q < a.Nq) {
-            float off, post;
-            p_offset<QP>(a, bh, q, off, post);
-            const int64_t b = bh / a.H, h = bh % a.H;
-            store_rows_T<D>(a.o + b * a.osb + h * a.osh + (int64_t)q * a.osn, o, post, hh);
-        }
+    };
+    segment(sg[0]);
+    if (ns > 1) {
+        __syncthreads();  // every wave is done with the tile buffers
+        segment(sg[1]);
     }
 }
 
-// Sums the fp32 parts of every split query block of a dense forward pass 2
-// (in a fixed order, part 0 first) and writes the block's O (times the
-// row's output factor) as bf16. One workgroup per split block.
+// Sums the partial sums of every last-round query block of a dense forward
+// pass 2 that splits its last round (in chunk order) and writes the block's
+// O (times the row's output factor) as bf16. One workgroup per block.
 template <int D, bool QP>
 __global__ __launch_bounds__(256) void fwd_out_fixup_kernel(AttnArgs a) {
     constexpr int QW = 256;
-    const int P = a.fo_parts, w = a.fo_full + blockIdx.x;
-    const int nqb = (a.Nq + QW - 1) / QW;
+    const int j = blockIdx.x, w = a.fo_full + j;
+    const int nqb = (a.Nq + QW - 1) / QW, nt = (a.Nk + 63) / 64;
     const int bh = w / nqb, qblk = w % nqb;
     const int64_t b = bh / a.H, h = bh % a.H;
-    const float* p0 = a.fo_part + (size_t)blockIdx.x * P * QW * D;
     // 8 consecutive d values per thread and pass
     for (int e = threadIdx.x * 8; e < QW * D; e += 256 * 8) {
         const int q = qblk * QW + e / D, d = e % D;
         if (q >= a.Nq) continue;
-        f32x4_t x0 = *(const f32x4_t*)(p0 + e), x1 = *(const f32x4_t*)(p0 + e + 4);
-        for (int part = 1; part < P; ++part) {
-            const float* r = p0 + (size_t)part * QW * D + e;
-            x0 += *(const f32x4_t*)r;
-            x1 += *(const f32x4_t*)(r + 4);
-        }
+        f32x4_t x0, x1;
+        sum_slots<D>(a.fo_part, j, nt, a.fo_chunk, e, x0, x1);
         float off, f;
         p_offset<QP>(a, bh, q, off, f);
         u32x4 v;
@@ -1784,7 +1812,6 @@ __global__ __launch_bounds__(256) void fwd_out_fixup_kernel(AttnArgs a) {
         *(u32x4*)(a.o + b * a.osb + h * a.osh + (int64_t)q * a.osn + d) = v;
     }
 }
-
 
 // ---------------------------------------------------------------------------
 // Dense forward pass 2 with the additive straight-through output, with
@@ -1971,11 +1998,11 @@ static void fwd_out_go(const AttnArgs& a, bool sp, hipStream_t st) {
     if (sp) {
         fwd_out_kernel<D, QP, F16, 4, true><<<dim3(a.nbq, a.BH), 256, 0, st>>>(a);
     } else {
-        // one workgroup per whole query block and one per part of a split
-        // one; the split blocks are finished by the fixup
+        // one workgroup per whole query block, then a.fo_chunks workgroups
+        // sharing the last round's blocks; the fixup finishes those blocks
         const int split = a.BH * ((a.Nq + 255) / 256) - a.fo_full;
-        fwd_out_pc_kernel<D, QP, F16><<<a.fo_full + split * a.fo_parts, 1024, 0, st>>>(a);
-        if (a.fo_parts > 1) fwd_out_fixup_kernel<D, QP><<<split, 256, 0, st>>>(a);
+        fwd_out_pc_kernel<D, QP, F16><<<a.fo_full + (a.fo_chunk ? a.fo_chunks : 0), 1024, 0, st>>>(a);
+        if (a.fo_chunk) fwd_out_fixup_kernel<D, QP><<<split, 256, 0, st>>>(a);
     }
 }
 
@@ -2032,13 +2059,13 @@ hipError_t launch_bwd_dq(const AttnArgs& a, int D, hipStream_t st) {
         if (D == 128) bwd_dq_sparse_kernel<128><<<grid, 256, 0, st>>>(a);
         else bwd_dq_sparse_kernel<64><<<grid, 256, 0, st>>>(a);
     } else {
-        // one workgroup per whole query block and one per part of a split
-        // one; the split blocks are finished by the fixup
+        // one workgroup per whole query block, then a.dq_chunks workgroups
+        // sharing the last round's blocks; the fixup finishes those blocks
         const int split = a.BH * ((a.Nq + 255) / 256) - a.dq_full;
-        const int grid = a.dq_full + split * a.dq_parts;
+        const int grid = a.dq_full + (a.dq_chunk ? a.dq_chunks : 0);
         if (D == 128) bwd_dq_kernel<128, 8, 1, false><<<grid, 512, 0, st>>>(a);
         else bwd_dq_kernel<64, 8, 1, false><<<grid, 512, 0, st>>>(a);
-        if (a.dq_parts > 1) {
+        if (a.dq_chunk) {
             if (D == 128) bwd_dq_fixup_kernel<128><<<split, 256, 0, st>>>(a);
             else bwd_dq_fixup_kernel<64><<<split, 256, 0, st>>>(a);
         }

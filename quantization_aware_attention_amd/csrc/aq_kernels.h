@@ -12,10 +12,13 @@ constexpr int kTileN = 256;  // token padding granularity of every workspace ope
 // (fewer than one round of workgroups on a chip of 256 compute units).
 constexpr int kMaxDkdvParts = 4;
 constexpr int kMaxDkdvSplit = 255;
-// Compute units the forward's workspace planner assumes when it sizes the
-// pass-2 partial region (MI355X); a device with another count splits only
-// when its own split fits that region.
+// Compute units the workspace planner assumes when it sizes the dQ and
+// forward pass-2 partial regions (MI355X); a device with another count
+// splits only when its own split fits the region.
 constexpr int kPlanCus = 256;
+// Fewest key tiles a last-round workgroup of a split dQ or pass-2 launch
+// takes.
+constexpr int kMinChunkTiles = 8;
 
 // Size of the fixed device scratch behind attnqat_fwd_noalloc (aq_noalloc.hip)
 // and the lookup of its address on the current device.
@@ -91,18 +94,17 @@ struct AttnArgs {
     // [split block][part][dK, dV][128 keys][D] the fixup adds
     float* dkdv_part;
     int dkdv_full, dkdv_parts;
-    // dense dQ: query blocks (256 queries, head-major) [0, dq_full) run
-    // whole, the others are split into dq_parts parts along the keys whose
-    // fp32 partial sums [split block][part][256 queries][D] the fixup adds
-    // (the dK/dV partial region, free once its fixup has run)
+    // dense dQ and dense forward pass 2 (P quantized, no O_ste): query blocks
+    // (256 queries, head-major) [0, *_full) run whole, one workgroup each;
+    // with *_chunk > 0 the remaining blocks' key tiles are shared out to
+    // *_chunks further workgroups, *_chunk consecutive tiles each, whose
+    // fp32 partial sums ([slot][256 queries][D], two slots per workgroup) a
+    // fixup adds. dQ uses the dK/dV partial region (free once its fixup has
+    // run).
     float* dq_part;
-    int dq_full, dq_parts;
-    // dense forward pass 2 (P quantized, no O_ste): query blocks (256
-    // queries, head-major) [0, fo_full) run whole, the others are split into
-    // fo_parts parts along the keys whose fp32 partial sums
-    // [split block][part][256 queries][D] the fixup adds
+    int dq_full, dq_chunk, dq_chunks;
     float* fo_part;
-    int fo_full, fo_parts;
+    int fo_full, fo_chunk, fo_chunks;
     int topk;
     int nbq, nbk;
     int64_t H;

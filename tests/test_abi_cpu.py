@@ -340,9 +340,9 @@ def test_workspace_starts_with_the_index_flag(L):
     ops = 256 + 3 * 2 * 1024 * 64 * 2
     assert L.attnqat_fwd_workspace_bytes(ctypes.byref(sparse)) == ops
     # the dense pass 2 runs 8 workgroups of 256 queries, a partial round on a
-    # chip of 256 compute units, so each is split into 4 parts along its 16
-    # key tiles: fp32 partial sums of 8 x 4 x 256 x 64
-    assert L.attnqat_fwd_workspace_bytes(ctypes.byref(dense)) == ops + 8 * 4 * 256 * 64 * 4
+    # chip of 256 compute units, so their 8 x 16 key tiles are shared out to
+    # 16 workgroups of 8 tiles, each with two partial slots of 256 x 64 fp32
+    assert L.attnqat_fwd_workspace_bytes(ctypes.byref(dense)) == ops + 2 * 16 * 256 * 64 * 4
 
 
 def test_forward_split_region(L):
@@ -356,8 +356,13 @@ def test_forward_split_region(L):
     # 256 heads x 256 queries: one whole round of 256 workgroups
     full = 256 + 3 * 256 * 256 * 64 * 2
     assert fwd_ws(H=256, Nq=256, Nk=256) == full
-    # 264 heads: 8 workgroups in the second round, 4 key tiles each -> 4 parts
-    assert fwd_ws(H=264, Nq=256, Nk=256) == 256 + 3 * 264 * 256 * 64 * 2 + 8 * 4 * 256 * 64 * 4
+    # 264 heads of 256 tokens: 8 workgroups in the second round with 4 key
+    # tiles each, too few to share out in chunks of at least 8 tiles
+    assert fwd_ws(H=264, Nq=256, Nk=256) == 256 + 3 * 264 * 256 * 64 * 2
+    # 264 heads of 1024 tokens: 32 last-round workgroups x 16 key tiles shared
+    # out to 64 workgroups of 8 tiles
+    assert (fwd_ws(H=264, Nq=1024, Nk=1024) ==
+            256 + 3 * 264 * 1024 * 64 * 2 + 2 * 64 * 256 * 64 * 4)
     # a single key tile cannot be split (Kq and Vq^T padded to 256 tokens)
     assert fwd_ws(Nq=1024, Nk=64) == 256 + 2 * 1024 * 64 * 2 + 2 * (2 * 256 * 64 * 2)
 
