@@ -282,6 +282,7 @@ struct Plan {
     bool f16_pv;      // forward P V on fp16 operands (V^T stored as fp16)
     size_t q_region;  // dense: bytes of the dQ partial sums (0: no split)
     size_t fo_region; // forward: bytes of the pass-2 partial sums (0: no split)
+    int fo_rows;      // forward: queries per pass-2 workgroup (256; 128 with O_ste)
 };
 
 int validate_problem(const attnqat_problem* p, Plan& pl) {
@@ -356,17 +357,23 @@ int validate_problem(const attnqat_problem* p, Plan& pl) {
     // per 256-query block in rounds of one per compute unit; the planned
     // split of the last round sizes their partial regions (two slots of 256
     // x D fp32 per last-round workgroup)
-    const int64_t nqw = pl.BH * ((pl.Nq + 255) / 256), nkt = (pl.Nk + 63) / 64;
-    const StreamSplit sq = stream_split(nqw, nkt, aq::kPlanCus);
+    // (pass 2 with O_ste: 128-query blocks whose slots hold O and O_ste)
+    const int64_t nkt = (pl.Nk + 63) / 64;
+    const StreamSplit sq = stream_split(pl.BH * ((pl.Nq + 255) / 256), nkt, aq::kPlanCus);
     pl.q_region = pl.sparse ? 0 : (size_t)(2 * sq.chunks) * 256 * pl.D * 4;
-    pl.fo_region = (!pl.sparse && (p->quant_mask & ATTNQAT_QUANT_P) && !p->o_ste) ? pl.q_region : 0;
+    pl.fo_rows = p->o_ste ? 128 : 256;
+    const StreamSplit sf =
+        stream_split(pl.BH * ((pl.Nq + pl.fo_rows - 1) / pl.fo_rows), nkt, aq::kPlanCus);
+    pl.fo_region = (!pl.sparse && (p->quant_mask & ATTNQAT_QUANT_P))
+                       ? (size_t)(2 * sf.chunks) * 256 * pl.D * 4 : 0;
     return ATTNQAT_OK;
 }
 
-// Last-round split of dense dQ or forward pass 2 on the current device, or
-// none when it does not fit the planned region of `region` bytes.
-void query_split(const Plan& pl, size_t region, int& full, int& chunk, int& chunks) {
-    const int64_t nqw = pl.BH * ((pl.Nq + 255) / 256);
+// Last-round split of dense dQ or forward pass 2 (blocks of `rows` queries)
+// on the current device, or none when it does not fit the planned region of
+// `region` bytes.
+void query_split(const Plan& pl, int rows, size_t region, int& full, int& chunk, int& chunks) {
+    const int64_t nqw = pl.BH * ((pl.Nq + rows - 1) / rows);
     full = (int)nqw;
     chunk = chunks = 0;
     if (region == 0) return;
@@ -664,7 +671,7 @@ int attnqat_fwd(const attnqat_problem* p, const void* q, const void* k, const vo
     a.osh = pl.o.h;
     a.osn = pl.o.n;
     if (!pl.sparse) {
-        query_split(pl, pl.fo_region, a.fo_full, a.fo_chunk, a.fo_chunks);
+        query_split(pl, pl.fo_rows, pl.fo_region, a.fo_full, a.fo_chunk, a.fo_chunks);
         a.fo_part = (float*)(ws + L.fopart);
     }
     const DimArgs da{a, (int)pl.D};
@@ -834,7 +841,7 @@ int attnqat_bwd(const attnqat_problem* p, const void* q, const void* k, const vo
         a.dkdv_part = (float*)(ws + L.dkdvpart);
         // dense dQ: one workgroup per 256-query block, its last round shared
         // out along the key tiles, partial sums in the same region
-        query_split(pl, L.dkdvpart_bytes, a.dq_full, a.dq_chunk, a.dq_chunks);
+        query_split(pl, 256, L.dkdvpart_bytes, a.dq_full, a.dq_chunk, a.dq_chunks);
         a.dq_part = (float*)(ws + L.dkdvpart);
     }
     const DimArgs da{a, (int)pl.D};

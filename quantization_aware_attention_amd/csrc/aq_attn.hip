@@ -1840,14 +1840,13 @@ __global__ __launch_bounds__(512) void fwd_out_ste_pc_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int pair = wave & 3, role = wave >> 2;  // 0 producer, 1 consumer
     const int l32 = lane & 31, hh = lane >> 5;
-    int qblk, bh;
-    xcd_work(qblk, bh);
-    const int q = qblk * (NT * 32) + pair * 32 + l32;
-    const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
-    const uint16_t* Kb = a.Kw + (size_t)bh * a.Nk_pad * D;
-    const uint16_t* Vtb = a.Vt + (size_t)bh * D * a.Nk_pad;
-    const int nt = (a.Nk + BN - 1) / BN;
+    // A one-dimensional grid: whole 128-query blocks, or up to two segments
+    // of the last round's key tiles (work_segments), whose fp32 partial sums
+    // of O and O_ste fwd_out_ste_fixup_kernel adds.
+    const int nt = (a.Nk + BN - 1) / BN, nqb = (a.Nq + NT * 32 - 1) / (NT * 32);
     const bool last_partial = nt * BN > a.Nk;
+    Seg sg[2];
+    const int ns = work_segments(a.fo_full, a.BH * nqb, nt, a.fo_chunk, sg);
     // this wave's DMA blocks: blocks wave, wave + 8, ... of each tile (where
     // they exist); K rows in perm32 order, lane i fills slot 16 i
     constexpr int NJ = (KBLK + NWV - 1) / NWV;
@@ -1863,106 +1862,151 @@ __global__ __launch_bounds__(512) void fwd_out_ste_pc_kernel(AttnArgs a) {
         const int vr = blk * 8 + (lane >> 3), vc = lane & 7;
         voff[j] = (uint32_t)(vr * a.Nk_pad + ((vc ^ swz<BN>(vr)) << 3)) * 2u;
     }
-    auto issue_k = [&](int t) {
+    auto segment = [&](const Seg& sgi) {
+        const int qblk = sgi.blk % nqb, bh = sgi.blk / nqb;
+        const int t0 = sgi.t0, t1 = sgi.t1, slot = sgi.slot;
+        const int q = qblk * (NT * 32) + pair * 32 + l32;
+        const uint16_t* Qb = a.Qw + (size_t)bh * a.Nq_pad * D;
+        const uint16_t* Kb = a.Kw + (size_t)bh * a.Nk_pad * D;
+        const uint16_t* Vtb = a.Vt + (size_t)bh * D * a.Nk_pad;
+        auto issue_k = [&](int t) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-            if (wave + j * NWV < KBLK)
-                dma16(lds_addr(sK[t & 1] + (wave + j * NWV) * 512), Kb + (size_t)t * BN * D, koff[j]);
-    };
-    auto issue_v = [&](int t) {
+            for (int j = 0; j < NJ; ++j)
+                if (wave + j * NWV < KBLK)
+                    dma16(lds_addr(sK[t & 1] + (wave + j * NWV) * 512), Kb + (size_t)t * BN * D, koff[j]);
+        };
+        auto issue_v = [&](int t) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-            if (wave + j * NWV < VBLK)
-                dma16(lds_addr(sV[t & 1] + (wave + j * NWV) * 512), Vtb + t * BN, voff[j]);
-    };
-    if (role == 0) {
-        u32x4 qf[D / 16];
+            for (int j = 0; j < NJ; ++j)
+                if (wave + j * NWV < VBLK)
+                    dma16(lds_addr(sV[t & 1] + (wave + j * NWV) * 512), Vtb + t * BN, voff[j]);
+        };
+        if (role == 0) {
+            u32x4 qf[D / 16];
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c)
-            qf[c] = *(const u32x4*)(Qb + (size_t)q * D + c * 16 + hh * 8);
-        float off, post;
-        p_offset<true>(a, bh, q, off, post);
-        // let these loads land before any tile copy is issued (the copies
-        // are invisible to the compiler's wait counts)
-        wait_vm<0>();
-        issue_k(0);
-        wait_vm<0>();
-        __syncthreads();
-        for (int t = 0; t <= nt; ++t) {
-            if (t > 0) {
-                wait_vm<0>();
-                __syncthreads();
-            }
-            if (t + 1 < nt) issue_k(t + 1);
-            if (t < nt) issue_v(t);
-            if (t >= nt) continue;
-            const uint16_t* K = sK[t & 1];
-            uint32_t* X = &sX[t & 1][pair][0][0][0][0];
-            auto run = [&](auto tail) {
-                constexpr bool TL = decltype(tail)::value;
-                const f32x16 s0 = scores_T<D>(K, 0, qf, l32, hh);
-                lds_mfma_chain<D / 16, 4>();
-                const f32x16 s1 = scores_T<D>(K, 32, qf, l32, hh);
-                u32x4 q0[2], p0[2], q1[2], p1[2];
-                F::template probs<TL>(s0, t * BN, a.Nk, a.c, off, hh, q0, p0);
-                mfma_chain_front<D / 16, 1, 4, 64, 0>();
-                F::template probs<TL>(s1, t * BN + 32, a.Nk, a.c, off, hh, q1, p1);
-#pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    *(u32x4*)(X + ((0 * 4 + 0 * 2 + g) * 64 + lane) * 4) = q0[g];
-                    *(u32x4*)(X + ((0 * 4 + 1 * 2 + g) * 64 + lane) * 4) = q1[g];
-                    *(u32x4*)(X + ((1 * 4 + 0 * 2 + g) * 64 + lane) * 4) = p0[g];
-                    *(u32x4*)(X + ((1 * 4 + 1 * 2 + g) * 64 + lane) * 4) = p1[g];
-                }
-            };
-            if (last_partial && t == nt - 1) run(std::true_type{});
-            else run(std::false_type{});
-        }
-    } else {
-        f32x16 o[D / 32], os[D / 32];
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[db] = os[db] = f32x16{};
-        issue_k(0);
-        wait_vm<0>();
-        __syncthreads();
-        for (int t = 0; t <= nt; ++t) {
-            if (t > 0) {
-                wait_vm<0>();
-                __syncthreads();
-            }
-            if (t + 1 < nt) issue_k(t + 1);
-            if (t < nt) issue_v(t);
-            if (t == 0) continue;
-            const uint16_t* V = sV[(t - 1) & 1];
-            const uint32_t* X = &sX[(t - 1) & 1][pair][0][0][0][0];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                u32x4 bq[2], bp[2];
-#pragma unroll
-                for (int g = 0; g < 2; ++g) {
-                    bq[g] = *(const u32x4*)(X + ((0 * 4 + kb * 2 + g) * 64 + lane) * 4);
-                    bp[g] = *(const u32x4*)(X + ((1 * 4 + kb * 2 + g) * 64 + lane) * 4);
-                }
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-#pragma unroll
-                    for (int g = 0; g < 2; ++g) {
-                        const u32x4 vf =
-                            *(const u32x4*)(V + toff<BN>(db * 32 + l32, 4 * kb + 2 * hh + g));
-                        o[db] = mfma(vf, bq[g], o[db]);
-                        os[db] = mfma(vf, bp[g], os[db]);
-                    }
-                }
-            }
-            mfma_chain_m<D / 4, 2, 4, 0>();
-        }
-        if (q < a.Nq) {
+            for (int c = 0; c < D / 16; ++c)
+                qf[c] = *(const u32x4*)(Qb + (size_t)q * D + c * 16 + hh * 8);
             float off, post;
             p_offset<true>(a, bh, q, off, post);
-            const int64_t b = bh / a.H, h = bh % a.H;
-            store_rows_T<D>(a.o + b * a.osb + h * a.osh + (int64_t)q * a.osn, o, post, hh);
-            store_rows_T<D>(a.o_ste + b * a.osb + h * a.osh + (int64_t)q * a.osn, os, post, hh);
+            // let these loads land before any tile copy is issued (the copies
+            // are invisible to the compiler's wait counts)
+            wait_vm<0>();
+            issue_k(t0);
+            wait_vm<0>();
+            __syncthreads();
+            for (int t = t0; t <= t1; ++t) {
+                if (t > t0) {
+                    wait_vm<0>();
+                    __syncthreads();
+                }
+                if (t + 1 < t1) issue_k(t + 1);
+                if (t < t1) issue_v(t);
+                if (t >= t1) continue;
+                const uint16_t* K = sK[t & 1];
+                uint32_t* X = &sX[t & 1][pair][0][0][0][0];
+                auto run = [&](auto tail) {
+                    constexpr bool TL = decltype(tail)::value;
+                    const f32x16 s0 = scores_T<D>(K, 0, qf, l32, hh);
+                    lds_mfma_chain<D / 16, 4>();
+                    const f32x16 s1 = scores_T<D>(K, 32, qf, l32, hh);
+                    u32x4 q0[2], p0[2], q1[2], p1[2];
+                    F::template probs<TL>(s0, t * BN, a.Nk, a.c, off, hh, q0, p0);
+                    mfma_chain_front<D / 16, 1, 4, 64, 0>();
+                    F::template probs<TL>(s1, t * BN + 32, a.Nk, a.c, off, hh, q1, p1);
+#pragma unroll
+                    for (int g = 0; g < 2; ++g) {
+                        *(u32x4*)(X + ((0 * 4 + 0 * 2 + g) * 64 + lane) * 4) = q0[g];
+                        *(u32x4*)(X + ((0 * 4 + 1 * 2 + g) * 64 + lane) * 4) = q1[g];
+                        *(u32x4*)(X + ((1 * 4 + 0 * 2 + g) * 64 + lane) * 4) = p0[g];
+                        *(u32x4*)(X + ((1 * 4 + 1 * 2 + g) * 64 + lane) * 4) = p1[g];
+                    }
+                };
+                if (last_partial && t == nt - 1) run(std::true_type{});
+                else run(std::false_type{});
+            }
+        } else {
+            f32x16 o[D / 32], os[D / 32];
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db) o[db] = os[db] = f32x16{};
+            issue_k(t0);
+            wait_vm<0>();
+            __syncthreads();
+            for (int t = t0; t <= t1; ++t) {
+                if (t > t0) {
+                    wait_vm<0>();
+                    __syncthreads();
+                }
+                if (t + 1 < t1) issue_k(t + 1);
+                if (t < t1) issue_v(t);
+                if (t == t0) continue;
+                const uint16_t* V = sV[(t - 1) & 1];
+                const uint32_t* X = &sX[(t - 1) & 1][pair][0][0][0][0];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    u32x4 bq[2], bp[2];
+#pragma unroll
+                    for (int g = 0; g < 2; ++g) {
+                        bq[g] = *(const u32x4*)(X + ((0 * 4 + kb * 2 + g) * 64 + lane) * 4);
+                        bp[g] = *(const u32x4*)(X + ((1 * 4 + kb * 2 + g) * 64 + lane) * 4);
+                    }
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+                        for (int g = 0; g < 2; ++g) {
+                            const u32x4 vf =
+                                *(const u32x4*)(V + toff<BN>(db * 32 + l32, 4 * kb + 2 * hh + g));
+                            o[db] = mfma(vf, bq[g], o[db]);
+                            os[db] = mfma(vf, bp[g], os[db]);
+                        }
+                    }
+                }
+                mfma_chain_m<D / 4, 2, 4, 0>();
+            }
+            if (slot >= 0) {  // slot: [O, O_ste][128 queries][D]
+                float* dst = a.fo_part + ((size_t)slot * 256 + pair * 32 + l32) * D;
+                store_rows_f32<D>(dst, o, hh);
+                store_rows_f32<D>(dst + 128 * D, os, hh);
+            } else if (q < a.Nq) {
+                float off, post;
+                p_offset<true>(a, bh, q, off, post);
+                const int64_t b = bh / a.H, h = bh % a.H;
+                store_rows_T<D>(a.o + b * a.osb + h * a.osh + (int64_t)q * a.osn, o, post, hh);
+                store_rows_T<D>(a.o_ste + b * a.osb + h * a.osh + (int64_t)q * a.osn, os, post, hh);
+            }
         }
+    };
+    segment(sg[0]);
+    if (ns > 1) {
+        __syncthreads();  // every wave is done with the tile buffers
+        segment(sg[1]);
+    }
+}
+
+// Sums the partial sums of every last-round query block of a dense forward
+// pass 2 with O_ste that splits its last round (in chunk order) and writes
+// the block's O and O_ste (times the row's output factor) as bf16. One
+// workgroup per 128-query block; a slot holds [O, O_ste][128 queries][D].
+template <int D>
+__global__ __launch_bounds__(256) void fwd_out_ste_fixup_kernel(AttnArgs a) {
+    constexpr int QW = 128;
+    const int j = blockIdx.x, w = a.fo_full + j;
+    const int nqb = (a.Nq + QW - 1) / QW, nt = (a.Nk + 63) / 64;
+    const int bh = w / nqb, qblk = w % nqb;
+    const int64_t b = bh / a.H, h = bh % a.H;
+    // 8 consecutive d values per thread and pass
+    for (int e = threadIdx.x * 8; e < 2 * QW * D; e += 256 * 8) {
+        const int which = e / (QW * D), q = qblk * QW + (e / D) % QW, d = e % D;
+        if (q >= a.Nq) continue;
+        f32x4_t x0, x1;
+        sum_slots<D>(a.fo_part, j, nt, a.fo_chunk, e, x0, x1);
+        float off, f;
+        p_offset<true>(a, bh, q, off, f);
+        u32x4 v;
+        v[0] = pack_rne(x0[0] * f, x0[1] * f);
+        v[1] = pack_rne(x0[2] * f, x0[3] * f);
+        v[2] = pack_rne(x1[0] * f, x1[1] * f);
+        v[3] = pack_rne(x1[2] * f, x1[3] * f);
+        *(u32x4*)((which ? a.o_ste : a.o) + b * a.osb + h * a.osh + (int64_t)q * a.osn + d) = v;
     }
 }
 
@@ -2012,8 +2056,15 @@ static void fwd_out_ste_go(const AttnArgs& a, bool sp, hipStream_t st) {
     // and both products (the two output accumulators and the quantizer need
     // more than the 256 registers of two waves per SIMD); dense: producer /
     // consumer pairs, 128 queries per workgroup
-    if (sp) fwd_out_ste_kernel<D, QP, 4, true><<<dim3(a.nbq, a.BH), 256, 0, st>>>(a);
-    else fwd_out_ste_pc_kernel<D><<<dim3((a.Nq + 127) / 128, a.BH), 512, 0, st>>>(a);
+    if (sp) {
+        fwd_out_ste_kernel<D, QP, 4, true><<<dim3(a.nbq, a.BH), 256, 0, st>>>(a);
+    } else {
+        // one workgroup per whole 128-query block, then a.fo_chunks
+        // workgroups sharing the last round's blocks; the fixup finishes them
+        const int split = a.BH * ((a.Nq + 127) / 128) - a.fo_full;
+        fwd_out_ste_pc_kernel<D><<<a.fo_full + (a.fo_chunk ? a.fo_chunks : 0), 512, 0, st>>>(a);
+        if (a.fo_chunk) fwd_out_ste_fixup_kernel<D><<<split, 256, 0, st>>>(a);
+    }
 }
 
 // Pass 2 runs only when P is quantized (otherwise the single-pass forward

@@ -347,12 +347,14 @@ def test_workspace_starts_with_the_index_flag(L):
 
 def test_forward_split_region(L):
     """The pass-2 partial region exists only where the dense producer/consumer
-    pass 2 runs (P quantized, no O_ste) and its last round is partial."""
+    pass 2 runs (P quantized) and its last round is partly filled."""
     def fwd_ws(**kw):
         return L.attnqat_fwd_workspace_bytes(ctypes.byref(_prob(**kw)))
     ops = 256 + 3 * 2 * 1024 * 64 * 2
     assert fwd_ws(Nq=1024, Nk=1024, quant_mask=7) == ops        # no P quantizer: one pass
-    assert fwd_ws(Nq=1024, Nk=1024, o_ste=30 * A) == ops        # pass 2 with O_ste
+    # pass 2 with O_ste: 16 blocks of 128 queries x 16 key tiles shared out
+    # to 32 workgroups of 8 tiles, two slots of [O, O_ste][128][64] each
+    assert fwd_ws(Nq=1024, Nk=1024, o_ste=30 * A) == ops + 2 * 32 * 256 * 64 * 4
     # 256 heads x 256 queries: one whole round of 256 workgroups
     full = 256 + 3 * 256 * 256 * 64 * 2
     assert fwd_ws(H=256, Nq=256, Nk=256) == full
