@@ -84,7 +84,13 @@ def load(path: str | None = None) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    path = path or LIB_PATH
+    _lib = open_library(path or LIB_PATH)
+    return _lib
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """Open a build of the library at `path` and declare its C signatures,
+    without making it the one the functions below call (load does that)."""
     if not os.path.exists(path):
         raise AttnQatError(f"{path} is missing: build it with quantization_aware_attention_amd."
                            "build.build() (there is no fallback path)")
@@ -136,7 +142,6 @@ def load(path: str | None = None) -> ctypes.CDLL:
     if len(rts) > 1:
         raise AttnQatError(f"two HIP runtimes are mapped ({sorted(rts)}); streams would not "
                            "be shared with torch")
-    _lib = lib
     return lib
 
 

@@ -30,33 +30,53 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found; the Attn-QAT library needs ROCm's hipcc to build")
 
 
+# Debug build of the same sources whose kernels fill their LDS arrays with
+# NaN before first use (AQ_LDS_POISON): the tests compare it with the release
+# library bit for bit, so a read of LDS a kernel never wrote would show.
+POISON_PATH = os.path.join(PKG_DIR, "libattnqat_ldspoison.so")
+
 # Machine probes for the benchmark (matrix-core rate and clock), kept out of
 # the attention library.
 PROBE_SOURCES = ["aq_probe.hip"]
 PROBE_PATH = os.path.join(PKG_DIR, "libaq_probe.so")
 
 
-def _compile(sources, out, verbose):
+def _start(sources, out, verbose, extra=()):
     srcs = [os.path.join(CSRC, s) for s in sources]
     tmp = out + ".tmp"
-    cmd = [hipcc()] + HIP_FLAGS + srcs + ["-o", tmp]
+    cmd = [hipcc()] + HIP_FLAGS + list(extra) + srcs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
-                     if "packed-fp32-ops" not in l and l.strip())
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
+    proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    return proc, tmp, out
+
+
+def _finish(job, verbose):
+    proc, tmp, out = job
+    text, _ = proc.communicate()
+    msgs = "\n".join(l for l in text.splitlines() if "packed-fp32-ops" not in l and l.strip())
+    if proc.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({proc.returncode}) for {out}:\n{msgs}")
     if verbose and msgs:
         print(msgs)
     os.replace(tmp, out)
 
 
 def build(verbose: bool = False) -> str:
-    """Compile the library (LIB_PATH) and the benchmark's probe library
-    (PROBE_PATH); return LIB_PATH."""
-    _compile(SOURCES, LIB_PATH, verbose)
-    _compile(PROBE_SOURCES, PROBE_PATH, verbose)
+    """Compile the library (LIB_PATH), its LDS-poisoning debug twin
+    (POISON_PATH) and the benchmark's probe library (PROBE_PATH), in
+    parallel; return LIB_PATH."""
+    jobs = [_start(SOURCES, LIB_PATH, verbose),
+            _start(SOURCES, POISON_PATH, verbose, ["-DAQ_LDS_POISON"]),
+            _start(PROBE_SOURCES, PROBE_PATH, verbose)]
+    errors = []
+    for j in jobs:  # wait for every compiler before reporting a failure
+        try:
+            _finish(j, verbose)
+        except RuntimeError as e:
+            errors.append(e)
+    if errors:
+        raise errors[0]
     return LIB_PATH
 
 

@@ -456,6 +456,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_lse_kernel(AttnArgs a) {
     constexpr int BN = FwdLse<D>::BN;
     static_assert(!SPARSE || NW == 4, "sparse workgroups cover one 128-query block");
     __shared__ __attribute__((aligned(1024))) uint16_t sK0[BN * D], sK1[BN * D];
+    lds_poison(sK0, sK1);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
     int qblk = blockIdx.x, bh = blockIdx.y;
@@ -591,6 +592,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_out_kernel(AttnA
         uint16_t v[D * BN];
     };
     __shared__ __attribute__((aligned(1024))) Buf s0, s1;
+    lds_poison(s0, s1);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
     int qblk = blockIdx.x, bh = blockIdx.y;
@@ -707,6 +709,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_out_ste_kernel(AttnArgs a) {
         uint16_t v[D * BN];
     };
     __shared__ __attribute__((aligned(1024))) Buf s0, s1;
+    lds_poison(s0, s1);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
     int qblk = blockIdx.x, bh = blockIdx.y;
@@ -775,6 +778,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void fwd_single_kernel(At
         uint16_t v[D * BN];
     };
     __shared__ __attribute__((aligned(1024))) Buf s0, s1;
+    lds_poison(s0, s1);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
     int qblk = blockIdx.x, bh = blockIdx.y;
@@ -959,6 +963,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(AttnArgs a) {
         uint16_t kt[D * BN];
     };
     __shared__ __attribute__((aligned(1024))) Buf s0, s1;
+    lds_poison(s0, s1);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
     constexpr int QW = NW * 32 * QB;  // queries per workgroup
@@ -1101,6 +1106,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_sparse_kernel(AttnArgs a) {
         uint16_t v[BN * D];  // toff<D>
     };
     __shared__ __attribute__((aligned(1024))) Buf s0, s1;
+    lds_poison(s0, s1);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
@@ -1344,6 +1350,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) Tile ring[3];
     // exchange slots per step parity and wave pair: transposed Pq, then dS
     __shared__ __attribute__((aligned(1024))) uint16_t sX[2][4][2 * 32 * 32];
+    lds_poison(ring, sX);
     __shared__ int lst[SPARSE ? kMaxBlockList : 1];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1660,6 +1667,7 @@ __global__ __launch_bounds__(1024) void fwd_out_pc_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) uint16_t sV[2][D * BN];
     // exchange: [parity][pair][32-key block][chunk j][lane][4 dwords]
     __shared__ __attribute__((aligned(1024))) uint32_t sX[2][NP][2][2][64 * 4];
+    lds_poison(sK, sV, sX);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int pair = wave & 7;
@@ -1836,6 +1844,7 @@ __global__ __launch_bounds__(512) void fwd_out_ste_pc_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(1024))) uint16_t sV[2][D * BN];
     // exchange: [parity][pair][Pq, P][32-key block][chunk g][lane][4 dwords]
     __shared__ __attribute__((aligned(1024))) uint32_t sX[2][NT][2][2][2][64 * 4];
+    lds_poison(sK, sV, sX);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int pair = wave & 3, role = wave >> 2;  // 0 producer, 1 consumer

@@ -90,6 +90,30 @@ __device__ __forceinline__ uint32_t pack_rne(float lo, float hi) {
 // agree on everything the kernels feed them (finite values and -inf).
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
+// Debug builds (AQ_LDS_POISON) fill the LDS arrays in which a kernel stages
+// operands and partial results with the 32-bit word 0x7FF87FF8 before their
+// first use, then synchronise the workgroup. Read as bf16, fp16, fp32 or
+// fp64 every element is a NaN, so a read of LDS that the kernel never wrote
+// shows up as NaN in its outputs. Release builds compile the call to
+// nothing. Integer arrays (block lists) are never passed: a poisoned index
+// would address memory instead of producing a NaN.
+template <class... T>
+__device__ __forceinline__ void lds_poison(T&... x) {
+#ifdef AQ_LDS_POISON
+    const unsigned nt = blockDim.x * blockDim.y * blockDim.z;
+    const unsigned tid = threadIdx.x + blockDim.x * (threadIdx.y + blockDim.y * threadIdx.z);
+    auto fill = [&](auto& v) {
+        static_assert(sizeof(v) % 4 == 0, "LDS arrays are poisoned in 4-byte words");
+        uint32_t* w = reinterpret_cast<uint32_t*>(&v);
+        for (unsigned i = tid; i < sizeof(v) / 4; i += nt) w[i] = 0x7FF87FF8u;
+    };
+    (fill(x), ...);
+    __syncthreads();
+#else
+    ((void)x, ...);
+#endif
+}
+
 // Value of x held by lane l ^ 32.
 __device__ __forceinline__ float partner_lane(float x) {
     auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -108,6 +108,7 @@ template <int D>
 __global__ __launch_bounds__(256) void mx_quant_vt_kernel(MxArgs a) {
     constexpr int TB = 256 / D, ROWS = TB * 32, RS = D + 2;  // row stride in elements
     __shared__ __attribute__((aligned(16))) uint16_t tile[ROWS * RS];
+    lds_poison(tile);
     const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
     const int tok0 = blockIdx.x * ROWS;
     const uint16_t* src = a.v + b * a.vsb + h * a.vsh;
@@ -272,6 +273,7 @@ __device__ __forceinline__ void mx_tiles(const MxArgs& a, int64_t bh, int n_tile
 template <int D, int NW>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 3 : 1) void mx_fwd_kernel(MxArgs a) {
     __shared__ __attribute__((aligned(16))) MxLds<D> L[2];
+    lds_poison(L);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
     const int64_t bh = blockIdx.y;

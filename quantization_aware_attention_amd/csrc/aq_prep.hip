@@ -127,6 +127,7 @@ __global__ __launch_bounds__(256) void fq_axis_n_kernel(FqArgs a) {
 template <bool QUANT, bool F16>
 __global__ __launch_bounds__(256) void fq_n_transpose_kernel(FqArgs a) {
     __shared__ uint16_t tile[64][64 + 2];
+    lds_poison(tile);
     const int64_t bh = blockIdx.z, b = bh / a.H, h = bh % a.H;
     const int n0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
     const uint16_t* s = a.x + b * a.xsb + h * a.xsh;
@@ -183,6 +184,7 @@ __global__ __launch_bounds__(256) void transpose_perm_kernel(const uint16_t* __r
                                                              uint16_t* __restrict__ dst,
                                                              int Npad, int D) {
     __shared__ uint16_t tile[64][64 + 2];
+    lds_poison(tile);
     const int bh = blockIdx.z;
     const int n0 = blockIdx.x * 64, d0 = blockIdx.y * 64;
     const uint16_t* s = src + (size_t)bh * Npad * D;

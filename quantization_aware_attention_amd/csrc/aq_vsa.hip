@@ -134,6 +134,7 @@ template <int D>
 __global__ __launch_bounds__(256) void vsa_pool_kernel(VsaArgs a) {
     constexpr int C = D / 8, R = 256 / C;
     __shared__ double part[R][D];
+    lds_poison(part);
     const int which = blockIdx.z;  // 0 = q, 1 = k, 2 = v
     const int nb = which == 0 ? a.nbq : a.nbk;
     const int j = blockIdx.x;
@@ -176,6 +177,7 @@ __global__ __launch_bounds__(256) void vsa_coarse_fwd_kernel(VsaArgs a) {
     __shared__ float pw[kVsaRows][kVsaMaxBlocks];
     __shared__ float part[kVsaRows][256];
     __shared__ float red[4];
+    lds_poison(qs, pw, part, red);
     const int i0 = blockIdx.x * kVsaRows, nr = min(kVsaRows, a.nbq - i0);
     const int64_t bh = blockIdx.y, row0 = bh * a.nbq + i0;
     load_rows<D, true>(qs, a.qbar, row0, nr);
@@ -243,6 +245,7 @@ template <int D>
 __global__ __launch_bounds__(256) void vsa_gate_reduce_kernel(VsaArgs a) {
     constexpr int C = D / 8, R = 256 / C;
     __shared__ float part[R][D];
+    lds_poison(part);
     const int i = blockIdx.x;
     const int64_t bh = blockIdx.y, row = bh * a.nbq + i;
     const int c = threadIdx.x % C, r = threadIdx.x / C;
@@ -285,6 +288,7 @@ __global__ __launch_bounds__(256) void vsa_coarse_bwd_q_kernel(VsaArgs a) {
     __shared__ float dsw[kVsaRows][kVsaMaxBlocks];
     __shared__ float part[kVsaRows][256];
     __shared__ float red[4];
+    lds_poison(qs, gs, dsw, part, red);
     const int i0 = blockIdx.x * kVsaRows, nr = min(kVsaRows, a.nbq - i0);
     const int64_t bh = blockIdx.y, row0 = bh * a.nbq + i0;
     load_rows<D, true>(qs, a.qbar, row0, nr);
@@ -325,6 +329,7 @@ __global__ __launch_bounds__(256) void vsa_coarse_bwd_k_kernel(VsaArgs a) {
     __shared__ float ks[kVsaRows][D], vs[kVsaRows][D];
     __shared__ float ws[kVsaRows][kVsaMaxBlocks], ps[kVsaRows][kVsaMaxBlocks];
     __shared__ float part[kVsaRows][256];
+    lds_poison(ks, vs, ws, ps, part);
     const int j0 = blockIdx.x * kVsaRows, nr = min(kVsaRows, a.nbk - j0);
     const int64_t bh = blockIdx.y, row0 = bh * a.nbk + j0;
     load_rows<D, true>(ks, a.kbar, row0, nr);

@@ -382,3 +382,15 @@ def test_noalloc_host_checks(L):
 
 def _fwd_noalloc(L, p, q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A):
     return L.attnqat_fwd_noalloc(ctypes.byref(p), q, k, v, o, lse, None)
+
+
+def test_lds_poison_build_carries_the_poison():
+    """The debug twin that the GPU poisoning test compares with the release
+    library stores the poison word (0x7FF87FF8, as an instruction literal) in
+    its kernels; the release library does not."""
+    from quantization_aware_attention_amd.build import LIB_PATH, POISON_PATH
+    word = (0x7FF87FF8).to_bytes(4, "little")
+    with open(POISON_PATH, "rb") as f:
+        assert f.read().count(word) > 0
+    with open(LIB_PATH, "rb") as f:
+        assert f.read().count(word) == 0
