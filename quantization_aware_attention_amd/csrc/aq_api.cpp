@@ -350,14 +350,11 @@ int validate_problem(const attnqat_problem* p, Plan& pl) {
         if (((uintptr_t)p->kv_block_idx) % 4)
             return fail(ATTNQAT_E_MISALIGNED, "kv_block_idx is not 4-byte aligned");
     }
-    // dense forward pass 2 with producer/consumer pairs (P quantized, no
-    // O_ste) runs one workgroup per 256-query block in rounds of one per
-    // compute unit; the last round's blocks may be split along the keys
-    // dense dQ and forward pass 2 (P quantized, no O_ste) run one workgroup
-    // per 256-query block in rounds of one per compute unit; the planned
-    // split of the last round sizes their partial regions (two slots of 256
-    // x D fp32 per last-round workgroup)
-    // (pass 2 with O_ste: 128-query blocks whose slots hold O and O_ste)
+    // dense dQ and the dense producer/consumer pass 2 (P quantized) run one
+    // workgroup per 256-query block (128 for pass 2 with O_ste) in rounds of
+    // one per compute unit; the planned split of the last round sizes their
+    // partial regions: two slots of 256 x D fp32 per last-round workgroup (a
+    // pass-2 slot with O_ste holds O and O_ste of 128 queries)
     const int64_t nkt = (pl.Nk + 63) / 64;
     const StreamSplit sq = stream_split(pl.BH * ((pl.Nq + 255) / 256), nkt, aq::kPlanCus);
     pl.q_region = pl.sparse ? 0 : (size_t)(2 * sq.chunks) * 256 * pl.D * 4;
