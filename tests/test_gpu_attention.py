@@ -72,20 +72,21 @@ def test_ragged_and_cross(gpu_lib, Nq, Nk, D, mask):
     _compare(got, ref, mask, f"Nq={Nq} Nk={Nk} D={D}")
 
 
-@pytest.mark.parametrize("N,D", [(2100, 128), (1500, 64)])
-def test_last_round_shared_out(gpu_lib, N, D):
+@pytest.mark.parametrize("Nq,Nk,D", [(2100, 2100, 128), (1500, 1500, 64), (1100, 2400, 64)])
+def test_last_round_shared_out(gpu_lib, Nq, Nk, D):
     """Dense pass 2 and dQ run one workgroup per 256 queries; a round that
     does not fill the compute units is shared out along the key tiles (2 x 2
     heads x 2100 tokens: 36 query blocks of 33 tiles in chunks of 9 tiles, so
     chunks cross block boundaries; 1500 tokens: 24 blocks of 24 tiles in
-    chunks of 8) and a fixup adds the partial sums; ragged last query block
-    and key tile."""
-    bits = {"q": random_bf16(61, (2, 2, N, D)), "k": random_bf16(62, (2, 2, N, D)),
-            "v": random_bf16(63, (2, 2, N, D)), "do": random_bf16(64, (2, 2, N, D))}
+    chunks of 8; 1100 queries against 2400 keys: 20 blocks of 38 tiles in
+    chunks of 8, crossing) and a fixup adds the partial sums; ragged last
+    query block and key tile."""
+    bits = {"q": random_bf16(61, (2, 2, Nq, D)), "k": random_bf16(62, (2, 2, Nk, D)),
+            "v": random_bf16(63, (2, 2, Nk, D)), "do": random_bf16(64, (2, 2, Nq, D))}
     sc = 1.0 / np.sqrt(D)
     got = _run_pair(gpu_lib, bits, 15, sc)
     ref = _oracle(bits, 15, sc)
-    _compare(got, ref, 15, f"shared-out N={N} D={D}")
+    _compare(got, ref, 15, f"shared-out Nq={Nq} Nk={Nk} D={D}")
 
 
 def test_sm_scale_is_honoured(gpu_lib):
