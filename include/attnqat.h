@@ -159,7 +159,13 @@ int attnqat_fakequant_nvfp4(const void* x, attnqat_strides xs, void* y, attnqat_
                             uint8_t* scale_codes, int64_t B, int64_t H, int64_t N, int64_t D,
                             int group_axis, void* stream);
 
-/* Workspace bytes attnqat_fwd needs for problem p (quantized operand copies). */
+/*
+ * Workspace bytes attnqat_fwd needs for problem p: the quantized operand
+ * copies and, for a dense problem with the P quantizer whose pass 2 leaves
+ * its last round of workgroups (one per compute unit, planned for 256) at
+ * most 4/5 full, the fp32 partial sums of that round (at most 64 MiB at
+ * D = 128). Depends on p only.
+ */
 size_t attnqat_fwd_workspace_bytes(const attnqat_problem* p);
 
 /*
