@@ -106,6 +106,10 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run one plain 1 GiB device copy (a kernel "
                          "of known traffic for scaling HBM byte counters)")
+    ap.add_argument("--power", action="store_true",
+                    help="after the timed steps, sample board power and shader clocks "
+                         "(amd-smi) while the MFMA probe, the forward and the backward each "
+                         "run in a loop (about 20 s)")
     return ap.parse_args()
 
 
@@ -252,6 +256,77 @@ def copy_calibration(torch, dev):
     return 1 << 30
 
 
+def board_power(torch, phases, secs=5.0):
+    """Board power and shader clocks read with amd-smi about every 0.5 s while
+    each phase (name, callable) runs in a loop on a second thread, after 1.5 s
+    of warm-up."""
+    import re
+    import shutil
+    import subprocess
+    import threading
+    smi = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+
+    def read():
+        r = subprocess.run([smi, "metric", "-p", "-c", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        if r.returncode != 0:
+            return [], []
+        pw = re.findall(r'"socket_power":\s*\{\s*"value":\s*(\d+)', r.stdout)
+        ck = re.findall(r'"gfx_\d+":\s*\{\s*"clk":\s*\{\s*"value":\s*(\d+)', r.stdout)
+        return [int(x) for x in pw], [int(x) for x in ck]
+
+    pw0, _ = read()
+    out = {"tool": "amd-smi metric -p -c", "idle_socket_power_w": pw0[0] if pw0 else None}
+    for name, fn in phases:
+        stop = threading.Event()
+
+        def loop():
+            while not stop.is_set():
+                fn()
+                torch.cuda.synchronize()
+
+        th = threading.Thread(target=loop)
+        th.start()
+        time.sleep(1.5)
+        pws, cks = [], []
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < secs:
+            a, b = read()
+            pws += a
+            cks += b
+            time.sleep(0.5)
+        stop.set()
+        th.join()
+        out[name] = {"samples": len(pws),
+                     "socket_power_w": [min(pws), max(pws)] if pws else None,
+                     "gfx_clock_mhz_mean": round(sum(cks) / len(cks)) if cks else None,
+                     "gfx_clock_mhz_range": [min(cks), max(cks)] if cks else None}
+        print(f"[bench] power {name}: {out[name]}", file=sys.stderr, flush=True)
+    return out
+
+
+def mfma_probe_fn(torch, dev):
+    """One call of the MFMA-only probe kernel (about 2.7e12 FLOPs), or None."""
+    import ctypes
+    from quantization_aware_attention_amd.build import PROBE_PATH
+    if not os.path.exists(PROBE_PATH):
+        return None
+    lib = ctypes.CDLL(PROBE_PATH)
+    fn = lib.aq_probe_mfma_peak
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                   ctypes.c_void_p]
+    sink = torch.empty(1024 * 256, dtype=torch.float32, device=dev)
+    stamps = torch.zeros(4, dtype=torch.int64, device=dev)
+    tf, mhz = ctypes.c_double(), ctypes.c_double()
+
+    def run():
+        fn(1024, 10000, sink.data_ptr(), stamps.data_ptr(), ctypes.byref(tf), ctypes.byref(mhz),
+           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    return run
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -372,6 +447,18 @@ def main():
     }
     # Standalone fake quantization of one input (HBM-bound): 4 bytes per
     # element (2 read, 2 written), along d (Q's layout) and along tokens (V's).
+    if args.power:
+        def fwd_only():
+            qaa.fwd(q, k, v, w.sm_scale, mask, kv_idx, out=o, lse=lse, workspace=ws_f,
+                    validate_index=False)
+
+        def bwd_only():
+            qaa.bwd(q, k, v, o, lse, do, w.sm_scale, mask, kv_idx, dq=dq, dk=dk, dv=dv,
+                    workspace=ws_b, validate_index=False)
+        probe = mfma_probe_fn(torch, dev)
+        phases = ([("mfma_probe", probe)] if probe else []) + [("forward", fwd_only),
+                                                               ("backward", bwd_only)]
+        out["board_power"] = board_power(torch, phases)
     if args.main_only:
         if args.copy_calibration:
             out["copy_calibration_bytes"] = copy_calibration(torch, dev)
