@@ -67,6 +67,11 @@ def test_noalloc_matches_workspace_entry_point(gpu_lib):
     # d = 64) over the scratch the first call left behind
     small = _inputs(510, (1, 2, 300, 64))
     _same(_noalloc(gpu_lib, small, 0.125, 15), _with_workspace(gpu_lib, small, 0.125, 15))
+    # a smaller problem whose pass 2 also shares its last round out (2 heads x
+    # 700 tokens: 6 query blocks of 11 key tiles in chunks of 9), over the
+    # partial sums the first call (16 blocks of 16 tiles, chunks of 8) left
+    mid = _inputs(520, (1, 2, 700, 128))
+    _same(_noalloc(gpu_lib, mid, 0.0884, 15), _with_workspace(gpu_lib, mid, 0.0884, 15))
     # quantization off (single-pass forward) and a block-sparse call
     _same(_noalloc(gpu_lib, small, 0.125, 0), _with_workspace(gpu_lib, small, 0.125, 0))
     idx = torch.tensor([[0, 2], [1, 2], [0, 1]], dtype=torch.int32,
