@@ -262,6 +262,16 @@ def copy_calibration(torch, dev):
     return 1 << 30
 
 
+def device_info(torch):
+    """Name, architecture, compute units and the HIP runtime of device 0."""
+    prop = torch.cuda.get_device_properties(0)
+    return {"name": torch.cuda.get_device_name(0) or None,
+            "arch": getattr(prop, "gcnArchName", None),
+            "compute_units": prop.multi_processor_count,
+            "memory_gib": round(prop.total_memory / 2 ** 30, 1),
+            "hip_runtime": torch.version.hip}
+
+
 def board_power(torch, phases, secs=5.0):
     """Board power and shader clocks read with amd-smi about every 0.5 s while
     each phase (name, callable) runs in a loop on a second thread, after 1.5 s
@@ -449,7 +459,7 @@ def main():
         "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": roof, "kernels": kernels, "input_sha256_16": hashes,
         "kernel_source_sha256_16": src_hash,
-        "device": torch.cuda.get_device_name(0),
+        "device": device_info(torch),
     }
     # Standalone fake quantization of one input (HBM-bound): 4 bytes per
     # element (2 read, 2 written), along d (Q's layout) and along tokens (V's).
